@@ -1,0 +1,219 @@
+"""Benchmark: FlashOptim fused compressed AdamW step on one MI355X.
+
+A step is one pass of the fused kernel over the whole Llama-3.1-8B-shaped
+parameter list (291 tensors, 8,030,261,248 parameters): rebuild the master
+weight from BF16 + INT8, dequantise INT8 / UINT8 moments (FP16 scale per 32),
+AdamW, requantise, re-split -- one launch of flashopt_adamw_step.  All state
+and gradients are resident in HBM before timing starts; two gradient sets are
+drawn up front and the steps alternate between them (two list handles over
+the same state).
+
+Prints one JSON line (rank 0).  --gpus N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from compressed_adamw_state_amd import flashopt as F          # noqa: E402
+from compressed_adamw_state_amd import workloads as W          # noqa: E402
+
+METRIC = "fused AdamW step params/s + achieved HBM GB/s (% peak) at Llama-3.1-8B shapes"
+HBM_PEAK_GBS = 8000.0
+KERNEL = "step_kernel<0>"    # the AdamW instantiation of the fused step kernel
+SOURCES = ["compressed_adamw_state_amd/csrc/flashopt.hip",
+           "compressed_adamw_state_amd/csrc/codec.hpp"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for s in SOURCES:
+        h.update(open(os.path.join(ROOT, s), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w: W.Workload) -> int:
+    """Bytes the method must move per step: read theta', rho, m, v codes, both
+    scales and the BF16 grad; write everything but the grad."""
+    total = 0
+    for t in w.tensors:
+        n, g = t.numel, (t.numel + 31) // 32
+        rd = 2 * n + n + n + 2 * g + 2 * n
+        wr = 2 * n + n + n + 2 * g
+        if w.optimizer == "adamw":
+            rd += n + 2 * g
+            wr += n + 2 * g
+        total += rd + wr
+    return total
+
+
+def read_traffic(workload: str, kernel_hash: str, bytes_per_launch: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_adamw_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_hash or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def build_state(w: W.Workload, grad_sets: int):
+    dev = torch.device("cuda")
+    states = []
+    for i, spec in enumerate(w.tensors):
+        theta = W.draw_theta(w, i, dev)
+        st = F.TensorState(spec.numel, w.optimizer, dev)
+        F.flashopt_split(theta, st.theta, st.rho)
+        del theta
+        states.append(st)
+    grads = []
+    for k in range(grad_sets):
+        grads.append([W.draw_grad(w, i, k + 1, dev) for i in range(len(w.tensors))])
+    lists = [F.FlashoptList(states, g) for g in grads]
+    F.flashopt_state_zero(lists[0])
+    torch.cuda.synchronize()
+    return states, grads, lists
+
+
+def cpu_baseline(seconds: float, threads: int):
+    """The oracle as it stands, on a bounded sample of the workload: a
+    2^25-parameter group-aligned slice with the Llama workload's
+    distributions (theta ~ N(0, 0.02), grads N(0, 1e-4)), stepped on
+    `threads` host threads (chunks of whole groups) until `seconds` pass."""
+    import oracle
+    n = 1 << 25
+    g = torch.Generator().manual_seed(1234)
+    theta = (torch.randn(n, generator=g) * 0.02).numpy()
+    st = oracle.State(theta, "adamw")
+    hp = W.ADAMW_HP
+    grads = [(torch.randn(n, generator=g) * 1e-4).to(torch.bfloat16).view(torch.int16).numpy()
+             .view(np.uint16) for _ in range(2)]
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step_chunked(st, grads[steps % 2], steps + 1, hp, nthreads=threads)
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} AdamW steps over a {n}-parameter slice (Llama-3.1-8B "
+                      f"distributions), {threads} threads, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama31_8b")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs the fused step on one GPU only; --gpus must be 1 "
+              "(sharding is described in DESIGN.md, not run)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    F.lib()
+
+    w = W.WORKLOADS[args.workload]
+    assert w.optimizer == "adamw" and not w.release
+    log(f"bench: building {w.name} state ({w.numel} params, {len(w.tensors)} tensors)")
+    t0 = time.perf_counter()
+    states, grads, lists = build_state(w, grad_sets=2)
+    log(f"bench: state ready in {time.perf_counter() - t0:.1f} s")
+    hp = w.hparams
+    stream = torch.cuda.current_stream()
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        F.flashopt_adamw_step(lists[t % 2], hp, t, stream)
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        t += 1
+        starts[k].record(stream)
+        F.flashopt_adamw_step(lists[t % 2], hp, t, stream)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) / 1e3   # seconds
+    total = float(per.sum())
+    log(f"bench: {args.steps} timed steps, wall {wall * 1e3:.1f} ms, kernel sum {total * 1e3:.1f} ms")
+
+    nparams = w.numel
+    bytes_step = algorithmic_bytes(w)
+    avg = total / args.steps
+    achieved = bytes_step / avg / 1e9
+    khash = source_hash()
+    traffic = read_traffic(w.name, khash, bytes_step)
+    out = {
+        "metric": METRIC,
+        "value": nparams * args.steps / wall,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: Llama-3.1-8B-shaped list, {len(w.tensors)} tensors, "
+                               f"{nparams} params, AdamW lr 1e-3 betas (0.9, 0.999) eps 1e-8 "
+                               f"wd 0.01, bf16 grads N(0, 1e-4)",
+                   "state": "theta' bf16 + rho int8 + m int8 + v uint8 + fp16 scale per 32",
+                   "launches_per_step": 1},
+        "hbm_gb_s": achieved,
+        "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBS,
+        "step_ms_median": float(np.median(per) * 1e3),
+        "step_ms_min": float(per.min() * 1e3),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": KERNEL,
+                     "algorithmic_bytes_per_launch": bytes_step,
+                     "avg_launch_ms": avg * 1e3, "source_sha256_16": khash},
+        "cpu_baseline": None,
+    }
+    del states, grads, lists
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.cpu_threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,42 @@
+"""Build the HIP library libflashopt.so for gfx950 (in-tree, with hipcc).
+
+Flags that the bit-exact arithmetic relies on:
+  -ffp-contract=off                          no fused multiply-add contraction
+  -fhip-fp32-correctly-rounded-divide-sqrt   IEEE binary32 division and sqrt
+  -fno-gpu-flush-denormals-to-zero           binary32 subnormals kept
+  -Xclang -target-feature -Xclang -packed-fp32-ops   no packed FP32 instructions
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "flashopt.hip")
+LIB = os.path.join(PKG, "libflashopt.so")
+ARCH = os.environ.get("FLASHOPT_ARCH", "gfx950")
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", *FLAGS, *extra, "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

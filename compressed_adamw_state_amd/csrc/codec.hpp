@@ -1,0 +1,172 @@
+// Device-side codec of FlashOptim's compressed state for gfx950.
+//
+// Method: "FlashOptim: Optimizers for Memory Efficient Training" (digest
+// page), section "Core method": weight splitting (Eq. 1-2, Alg. 1),
+// optimizer-state quantisation with companding (Alg. 2-3), fused step
+// (Alg. 4).  The exact binary32 operation order is the one documented in
+// include/flashopt.h; every function here performs those operations one by
+// one (this file is compiled with -ffp-contract=off and correctly rounded
+// division / square root).
+//
+// Lane layout used by every kernel: a wavefront of 64 lanes covers 512
+// consecutive elements per sub-tile, lane l owning elements [8l, 8l+8).
+// A quantisation group (32 elements) is therefore exactly one quad of lanes
+// (4l..4l+3), so the group max is two DPP quad-permute steps, with no LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flashopt {
+
+constexpr int kGroup = 32;
+constexpr int kWave = 64;
+constexpr int kLaneElems = 8;                       // elements per lane per sub-tile
+constexpr int kSubTile = kWave * kLaneElems;        // 512 elements
+constexpr int kSubTiles = 4;
+constexpr int kTile = kSubTile * kSubTiles;         // 2048 elements per wave iteration
+
+// RN(1/127) and RN(1/255) as bit patterns.
+constexpr uint32_t kK8Bits = 0x3C010204u;
+constexpr uint32_t kK255Bits = 0x3B808081u;
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
+
+// ---- format conversions ---------------------------------------------------
+
+// BF16 is the upper half of a binary32 pattern.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return as_f32(b << 16); }
+
+// binary32 -> BF16, round to nearest even; NaN keeps its payload, made quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+    uint32_t b = as_u32(x);
+    uint32_t rounded = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+    bool nan = (b & 0x7FFFFFFFu) > 0x7F800000u;
+    return nan ? ((b >> 16) | 0x40u) : rounded;
+}
+
+// binary32 -> FP16 (v_cvt_f16_f32: round to nearest even, FP16 subnormals kept).
+__device__ __forceinline__ uint32_t f32_to_f16(float x) {
+    _Float16 h = (_Float16)x;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// ---- weight split (Eq. 1-2) -----------------------------------------------
+
+// ULP(theta')/2 from the exponent bits of theta' (as binary32 bits): the
+// power of two 2^(E-127) times 2^-8, where E is clamped to [1, 254] (zero and
+// subnormal theta' use the smallest normal spacing; for Inf/NaN theta' any
+// finite h leaves theta' unchanged).  The product is exact, also when it is
+// subnormal.
+__device__ __forceinline__ float half_ulp(uint32_t theta_bits) {
+    uint32_t e = theta_bits & 0x7F800000u;
+    e = min(max(e, 0x00800000u), 0x7F000000u);
+    return as_f32(e) * 0x1p-8f;
+}
+
+// Rebuilt master weight: theta' + (rho * K8) * h.
+__device__ __forceinline__ float unsplit(uint32_t tb, int32_t rho) {
+    uint32_t tbits = tb << 16;
+    float t = as_f32(tbits);
+    float h = half_ulp(tbits);
+    float c = (float)rho * as_f32(kK8Bits);
+    float d = c * h;
+    return t + d;
+}
+
+// Split: theta' = BF16(x); rho = clamp(rne(127 * (x - theta') / h), +-127).
+// (x - theta') is exact, and dividing by the power of two h is done exactly by
+// ldexp with the negated exponent.
+struct Split { uint32_t tb; int32_t rho; };
+
+__device__ __forceinline__ Split split(float x) {
+    uint32_t tb = f32_to_bf16(x);
+    uint32_t tbits = tb << 16;
+    float t = as_f32(tbits);
+    uint32_t E = (tbits >> 23) & 0xFFu;
+    int shift = 135 - (int)max(E, 1u);
+    float e = __builtin_amdgcn_ldexpf(x - t, shift);
+    float y = e * 127.0f;
+    float r = __builtin_rintf(y);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    Split s;
+    s.tb = tb;
+    s.rho = (E == 0xFFu) ? 0 : (int32_t)r;
+    return s;
+}
+
+// ---- companding (Alg. 2-3) ------------------------------------------------
+
+__device__ __forceinline__ float phi_m(float x) {
+    float num = 2.0f * x;
+    float den = 1.0f + fabsf(x);
+    return num / den;
+}
+
+__device__ __forceinline__ float phi_m_inv(float z) {
+    float den = 2.0f - fabsf(z);
+    return z / den;
+}
+
+// Per-group dequantisation factors: s*K8 (momentum), s*K255 (variance).
+__device__ __forceinline__ float m_step(uint32_t s16) { return f16_to_f32(s16) * as_f32(kK8Bits); }
+__device__ __forceinline__ float v_step(uint32_t s16) { return f16_to_f32(s16) * as_f32(kK255Bits); }
+
+__device__ __forceinline__ float dequant_m(int32_t q, float d) {
+    float z = (float)q * d;
+    return phi_m_inv(z);
+}
+
+__device__ __forceinline__ float dequant_v(uint32_t q, float d) {
+    float z = (float)q * d;
+    return z * z;
+}
+
+// ---- group maximum over a quad of lanes (DPP quad_perm) --------------------
+
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t a) {
+    // quad_perm [1,0,3,2] then [2,3,0,1]; every lane of the quad ends with the max
+    uint32_t b = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
+    a = max(a, b);
+    b = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false);
+    return max(a, b);
+}
+
+// Scale of a group from the quad-reduced max |z| bit pattern, capped.
+__device__ __forceinline__ uint32_t group_scale(uint32_t amax_bits, uint32_t cap) {
+    uint32_t s16 = f32_to_f16(as_f32(amax_bits));
+    return min(s16, cap);
+}
+
+// Reciprocal factor 127/s (or 255/s); 0 when the scale is 0 (all codes 0).
+__device__ __forceinline__ float code_factor(uint32_t s16, float qmax) {
+    float s = f16_to_f32(s16);
+    float r = qmax / s;
+    return s16 == 0u ? 0.0f : r;
+}
+
+__device__ __forceinline__ int32_t code_m(float z, float r) {
+    float y = z * r;
+    float q = __builtin_rintf(y);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int32_t)q;
+}
+
+__device__ __forceinline__ uint32_t code_v(float w, float r) {
+    float y = w * r;
+    float q = __builtin_rintf(y);
+    q = fminf(fmaxf(q, 0.0f), 255.0f);
+    return (uint32_t)q;
+}
+
+// ---- the update rules (fused-step section) -----------------------------------
+
+struct AdamScalars { float b1, c1, b2, c2, alpha, kappa, eps, lambda; };
+struct SgdScalars { float mu, eta, omega; };
+
+}  // namespace flashopt

@@ -1,0 +1,857 @@
+// HIP kernels for gfx950 and the C ABI declared in include/flashopt.h.
+//
+// Method: "FlashOptim: Optimizers for Memory Efficient Training" (digest
+// page), section "Core method" -- weight splitting (Eq. 1-2, Alg. 1),
+// companded group quantisation (Alg. 2-3) and the fused optimizer step
+// (Alg. 4), including gradient release.
+//
+// Design (MI355X): the step is an elementwise read-modify-write stream with a
+// 32-element group reduction, bound by HBM bandwidth (12.25 bytes per
+// parameter for AdamW).  One launch covers a whole ragged tensor list.  Each
+// wavefront walks 2048-element tiles (grid-stride); a tile never crosses a
+// tensor boundary, and the tile -> tensor lookup is a scalar binary search
+// over per-tensor tile offsets kept in a small device table.  Within a tile,
+// lane l owns 8 consecutive elements of each 512-element sub-tile, so every
+// load is a fully coalesced 16-byte (BF16) or 8-byte (INT8) vector access,
+// and a quantisation group is one quad of lanes reduced with DPP.  Whole
+// tiles take an unguarded vector path; the last tile of a tensor takes a
+// guarded element-wise path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "codec.hpp"
+#include "flashopt.h"
+
+namespace flashopt {
+
+struct DevTensor {                  // device descriptor of one tensor (64 bytes)
+    uint16_t* theta;
+    int8_t* rho;
+    int8_t* mq;
+    uint16_t* ms;
+    uint8_t* vq;
+    uint16_t* vs;
+    const uint16_t* grad;
+    int64_t numel;
+};
+static_assert(sizeof(DevTensor) == 64, "descriptor layout");
+
+struct ListArgs {
+    const DevTensor* table;         // device table, or nullptr: use `one`
+    const int64_t* tile_begin;      // device [count + 1] first tile of each tensor
+    DevTensor one;
+    int32_t count;
+    int64_t total_tiles;
+};
+
+enum Opt { kAdamW = 0, kSgd = 1 };
+
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Largest i in [0, count) with tile_begin[i] <= tile (skips empty tensors).
+__device__ __forceinline__ int32_t find_tensor(const int64_t* tile_begin, int32_t count,
+                                               int64_t tile) {
+    int32_t lo = 0, hi = count - 1;
+    while (lo < hi) {
+        int32_t mid = (lo + hi + 1) >> 1;
+        if (tile_begin[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---- per-lane element staging ------------------------------------------------
+
+struct Lane8 {                      // one lane's 8 elements of one sub-tile
+    uint32_t th[8];                 // BF16 theta' bits
+    uint32_t gr[8];                 // BF16 grad bits
+    int32_t rho[8];
+    int32_t qm[8];
+    uint32_t qv[8];
+    uint32_t ms, vs;                // the group's FP16 scales
+};
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, uint32_t* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = w[i] & 0xFFFFu; o[2 * i + 1] = w[i] >> 16; }
+}
+
+__device__ __forceinline__ void unpack_s8x8(const uint2 v, int32_t* o) {
+    const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (int32_t)(int8_t)(uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+}
+
+__device__ __forceinline__ void unpack_u8x8(const uint2 v, uint32_t* o) {
+    const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+}
+
+__device__ __forceinline__ uint4 pack_u16x8(const uint32_t* v) {
+    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                      v[6] | (v[7] << 16));
+}
+
+__device__ __forceinline__ uint2 pack_u8x8(const uint32_t* v) {
+    return make_uint2((v[0] & 0xFF) | ((v[1] & 0xFF) << 8) | ((v[2] & 0xFF) << 16) | (v[3] << 24),
+                      (v[4] & 0xFF) | ((v[5] & 0xFF) << 8) | ((v[6] & 0xFF) << 16) | (v[7] << 24));
+}
+
+template <int kOpt, bool kFull>
+__device__ __forceinline__ void load_lane(const DevTensor& T, int64_t e, Lane8& L) {
+    const int64_t n = T.numel;
+    const int64_t g = e >> 5;
+    if (kFull) {
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(T.theta + e), L.th);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(T.grad + e), L.gr);
+        unpack_s8x8(*reinterpret_cast<const uint2*>(T.rho + e), L.rho);
+        unpack_s8x8(*reinterpret_cast<const uint2*>(T.mq + e), L.qm);
+        L.ms = T.ms[g];
+        if (kOpt == kAdamW) {
+            unpack_u8x8(*reinterpret_cast<const uint2*>(T.vq + e), L.qv);
+            L.vs = T.vs[g];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = e + j < n;
+            L.th[j] = ok ? T.theta[e + j] : 0u;
+            L.gr[j] = ok ? T.grad[e + j] : 0u;
+            L.rho[j] = ok ? T.rho[e + j] : 0;
+            L.qm[j] = ok ? T.mq[e + j] : 0;
+            if (kOpt == kAdamW) L.qv[j] = ok ? T.vq[e + j] : 0u;
+        }
+        const bool gok = (e & ~int64_t(31)) < n;       // the lane's group has valid elements
+        L.ms = gok ? T.ms[g] : 0u;
+        if (kOpt == kAdamW) L.vs = gok ? T.vs[g] : 0u;
+    }
+}
+
+// ---- the fused step on one sub-tile of one lane ----------------------------
+
+template <int kOpt, bool kFull>
+__device__ __forceinline__ void step_lane(const DevTensor& T, int64_t e, int lane,
+                                          const Lane8& L, const AdamScalars& a,
+                                          const SgdScalars& s) {
+    float z[8], w[8], tn[8];
+    uint32_t amax_m = 0, amax_v = 0;
+    const float dm = m_step(L.ms);
+    const float dv = (kOpt == kAdamW) ? v_step(L.vs) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float theta_hat = unsplit(L.th[j], L.rho[j]);
+        const float m = dequant_m(L.qm[j], dm);
+        const float g = bf16_to_f32(L.gr[j]);
+        float m_new, theta_new;
+        if (kOpt == kAdamW) {
+            const float v = dequant_v(L.qv[j], dv);
+            const float bm = a.b1 * m;
+            const float cg = a.c1 * g;
+            m_new = bm + cg;
+            const float bv = a.b2 * v;
+            const float gg = g * g;
+            const float cgg = a.c2 * gg;
+            const float v_new = bv + cgg;
+            const float root = __builtin_sqrtf(v_new);
+            const float den0 = root * a.kappa;
+            const float den = den0 + a.eps;
+            const float u = m_new / den;
+            const float decayed = a.lambda * theta_hat;
+            const float stp = a.alpha * u;
+            theta_new = decayed - stp;
+            w[j] = root;
+            amax_v = max(amax_v, as_u32(root));
+        } else {
+            const float decay = s.omega * theta_hat;
+            const float g2 = g + decay;
+            const float mb = s.mu * m;
+            m_new = mb + g2;
+            const float stp = s.eta * m_new;
+            theta_new = theta_hat - stp;
+        }
+        z[j] = phi_m(m_new);
+        tn[j] = theta_new;
+        amax_m = max(amax_m, as_u32(z[j]) & 0x7FFFFFFFu);
+    }
+    // group scales: every lane of the quad computes the same value
+    const uint32_t sm16 = group_scale(quad_max_u32(amax_m), 0x3FFFu);
+    const float rm = code_factor(sm16, 127.0f);
+    uint32_t sv16 = 0;
+    float rv = 0.0f;
+    if (kOpt == kAdamW) {
+        sv16 = group_scale(quad_max_u32(amax_v), 0x7BFFu);
+        rv = code_factor(sv16, 255.0f);
+    }
+    uint32_t otb[8], orho[8], oqm[8], oqv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        oqm[j] = (uint32_t)code_m(z[j], rm);
+        if (kOpt == kAdamW) oqv[j] = code_v(w[j], rv);
+        const Split sp = split(tn[j]);
+        otb[j] = sp.tb;
+        orho[j] = (uint32_t)sp.rho;
+    }
+    const int64_t g = e >> 5;
+    if (kFull) {
+        *reinterpret_cast<uint4*>(T.theta + e) = pack_u16x8(otb);
+        *reinterpret_cast<uint2*>(T.rho + e) = pack_u8x8(orho);
+        *reinterpret_cast<uint2*>(T.mq + e) = pack_u8x8(oqm);
+        if (kOpt == kAdamW) *reinterpret_cast<uint2*>(T.vq + e) = pack_u8x8(oqv);
+        if ((lane & 3) == 0) {
+            T.ms[g] = (uint16_t)sm16;
+            if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
+        }
+    } else {
+        const int64_t n = T.numel;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (e + j < n) {
+                T.theta[e + j] = (uint16_t)otb[j];
+                T.rho[e + j] = (int8_t)orho[j];
+                T.mq[e + j] = (int8_t)oqm[j];
+                if (kOpt == kAdamW) T.vq[e + j] = (uint8_t)oqv[j];
+            }
+        }
+        if ((lane & 3) == 0 && e < n) {
+            T.ms[g] = (uint16_t)sm16;
+            if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
+        }
+    }
+}
+
+template <int kOpt, bool kFull>
+__device__ __forceinline__ void step_tile(const DevTensor& T, int64_t e0, int lane,
+                                          const AdamScalars& a, const SgdScalars& s) {
+    Lane8 L[kSubTiles];
+#pragma unroll
+    for (int k = 0; k < kSubTiles; ++k)
+        load_lane<kOpt, kFull>(T, e0 + k * kSubTile + lane * kLaneElems, L[k]);
+#pragma unroll
+    for (int k = 0; k < kSubTiles; ++k)
+        step_lane<kOpt, kFull>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L[k], a, s);
+}
+
+template <int kOpt>
+__global__ __launch_bounds__(256) void step_kernel(ListArgs A, AdamScalars a, SgdScalars s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t tile = wave; tile < A.total_tiles; tile += nwaves) {
+        DevTensor T;
+        int64_t local = tile;
+        if (A.table != nullptr) {
+            const int32_t i = find_tensor(A.tile_begin, A.count, tile);
+            T = A.table[i];
+            local = tile - A.tile_begin[i];
+        } else {
+            T = A.one;
+        }
+        const int64_t e0 = local * kTile;
+        if (e0 + kTile <= T.numel) step_tile<kOpt, true>(T, e0, lane, a, s);
+        else step_tile<kOpt, false>(T, e0, lane, a, s);
+    }
+}
+
+// ---- flat-buffer kernels: split / unsplit / quantise / dequantise ----------
+
+// Each wave walks 512-element chunks; lane l owns chunk elements [8l, 8l+8).
+#define FLAT_LOOP(n)                                                                   \
+    const int lane = threadIdx.x & (kWave - 1);                                          \
+    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) +            \
+                                 (threadIdx.x / kWave));                                 \
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);                    \
+    for (int64_t c = wave; c * kSubTile < (n); c += nwaves)
+
+__global__ __launch_bounds__(256) void split_kernel(const float* x, int64_t n, uint16_t* tb,
+                                                     int8_t* rho) {
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        const bool full = (c + 1) * kSubTile <= n;
+        float v[8];
+        if (full) {
+            const float4 a = *reinterpret_cast<const float4*>(x + e);
+            const float4 b = *reinterpret_cast<const float4*>(x + e + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (e + j < n) ? x[e + j] : 0.0f;
+        }
+        uint32_t otb[8], orho[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const Split sp = split(v[j]);
+            otb[j] = sp.tb;
+            orho[j] = (uint32_t)sp.rho;
+        }
+        if (full) {
+            *reinterpret_cast<uint4*>(tb + e) = pack_u16x8(otb);
+            *reinterpret_cast<uint2*>(rho + e) = pack_u8x8(orho);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (e + j < n) { tb[e + j] = (uint16_t)otb[j]; rho[e + j] = (int8_t)orho[j]; }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void unsplit_kernel(const uint16_t* tb, const int8_t* rho,
+                                                       int64_t n, float* out) {
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        const bool full = (c + 1) * kSubTile <= n;
+        uint32_t th[8];
+        int32_t r[8];
+        if (full) {
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(tb + e), th);
+            unpack_s8x8(*reinterpret_cast<const uint2*>(rho + e), r);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                th[j] = (e + j < n) ? tb[e + j] : 0u;
+                r[j] = (e + j < n) ? rho[e + j] : 0;
+            }
+        }
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = unsplit(th[j], r[j]);
+        if (full) {
+            *reinterpret_cast<float4*>(out + e) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(out + e + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) if (e + j < n) out[e + j] = o[j];
+        }
+    }
+}
+
+// kind 0: momentum (phi_m, INT8), kind 1: variance (sqrt, UINT8)
+template <int kKind>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* x, int64_t n, uint8_t* q,
+                                                        uint16_t* scale) {
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        const bool full = (c + 1) * kSubTile <= n;
+        float v[8];
+        if (full) {
+            const float4 a = *reinterpret_cast<const float4*>(x + e);
+            const float4 b = *reinterpret_cast<const float4*>(x + e + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (e + j < n) ? x[e + j] : 0.0f;
+        }
+        float z[8];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            z[j] = (kKind == 0) ? phi_m(v[j]) : __builtin_sqrtf(v[j]);
+            amax = max(amax, as_u32(z[j]) & 0x7FFFFFFFu);
+        }
+        const uint32_t s16 = group_scale(quad_max_u32(amax), kKind == 0 ? 0x3FFFu : 0x7BFFu);
+        const float r = code_factor(s16, kKind == 0 ? 127.0f : 255.0f);
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            o[j] = (kKind == 0) ? (uint32_t)code_m(z[j], r) : code_v(z[j], r);
+        if (full) {
+            *reinterpret_cast<uint2*>(q + e) = pack_u8x8(o);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) if (e + j < n) q[e + j] = (uint8_t)o[j];
+        }
+        if ((lane & 3) == 0 && e < n) scale[e >> 5] = (uint16_t)s16;
+    }
+}
+
+template <int kKind>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* q, const uint16_t* scale,
+                                                          int64_t n, float* out) {
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        const bool full = (c + 1) * kSubTile <= n;
+        uint32_t u[8];
+        if (full) {
+            unpack_u8x8(*reinterpret_cast<const uint2*>(q + e), u);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) u[j] = (e + j < n) ? q[e + j] : 0u;
+        }
+        const uint32_t s16 = (e < n) ? scale[e >> 5] : 0u;
+        float o[8];
+        if (kKind == 0) {
+            const float d = m_step(s16);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = dequant_m((int32_t)(int8_t)(uint8_t)u[j], d);
+        } else {
+            const float d = v_step(s16);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = dequant_v(u[j], d);
+        }
+        if (full) {
+            *reinterpret_cast<float4*>(out + e) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(out + e + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) if (e + j < n) out[e + j] = o[j];
+        }
+    }
+}
+
+// ---- list maintenance kernels ----------------------------------------------
+
+// Zero codes and scales of a list, one tile per wave iteration.
+__global__ __launch_bounds__(256) void zero_kernel(ListArgs A) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    for (int64_t tile = wave; tile < A.total_tiles; tile += nwaves) {
+        const int32_t i = find_tensor(A.tile_begin, A.count, tile);
+        const DevTensor T = A.table[i];
+        const int64_t e0 = (tile - A.tile_begin[i]) * kTile;
+        for (int k = 0; k < kSubTiles; ++k) {
+            const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
+            for (int j = 0; j < 8; ++j) {
+                if (e + j < T.numel) {
+                    T.mq[e + j] = 0;
+                    if (T.vq) T.vq[e + j] = 0;
+                }
+            }
+            if ((lane & 3) == 0 && e < T.numel) {
+                T.ms[e >> 5] = 0;
+                if (T.vs) T.vs[e >> 5] = 0;
+            }
+        }
+    }
+}
+
+constexpr int kGradBatch = 200;
+struct GradBatch {
+    int32_t first, count;
+    const uint16_t* ptr[kGradBatch];
+};
+
+__global__ void set_grads_kernel(DevTensor* table, GradBatch b) {
+    const int i = threadIdx.x;
+    if (i < b.count) table[b.first + i].grad = b.ptr[i];
+}
+
+// ---- host side -------------------------------------------------------------
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kBlocksPerCU = 8;
+
+static int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cu <= 0)
+            cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
+static unsigned grid_for(int64_t wave_items) {
+    int64_t blocks = (wave_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t cap = (int64_t)cu_count() * kBlocksPerCU;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return (unsigned)blocks;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int64_t tiles_of(int64_t n) { return (n + kTile - 1) / kTile; }
+
+static constexpr int64_t kMaxNumel = int64_t(1) << 60;
+
+static int launch_status() {
+    return hipGetLastError() == hipSuccess ? FLASHOPT_OK : FLASHOPT_ERR_HIP;
+}
+
+static AdamScalars adam_scalars(const flashopt_adamw_hparams& hp, int64_t t, double* p1c,
+                                double* p2c, int64_t* tc, double* b1c, double* b2c) {
+    // p1 = beta1^t and p2 = beta2^t by t successive multiplications; continue
+    // from the cached power when t does not go backwards (same operation
+    // sequence, so the same value), stop early once both are zero.
+    double p1 = 1.0, p2 = 1.0;
+    int64_t k = 0;
+    if (*tc > 0 && *tc <= t && *b1c == hp.beta1 && *b2c == hp.beta2) {
+        p1 = *p1c; p2 = *p2c; k = *tc;
+    }
+    for (; k < t; ++k) {
+        if (p1 == 0.0 && p2 == 0.0) { k = t; break; }
+        p1 = p1 * hp.beta1;
+        p2 = p2 * hp.beta2;
+    }
+    *p1c = p1; *p2c = p2; *tc = t; *b1c = hp.beta1; *b2c = hp.beta2;
+    AdamScalars a;
+    a.b1 = (float)hp.beta1;
+    a.c1 = (float)(1.0 - hp.beta1);
+    a.b2 = (float)hp.beta2;
+    a.c2 = (float)(1.0 - hp.beta2);
+    a.alpha = (float)(hp.lr / (1.0 - p1));
+    a.kappa = (float)(1.0 / std::sqrt(1.0 - p2));
+    a.eps = (float)hp.eps;
+    a.lambda = (float)(1.0 - hp.lr * hp.weight_decay);
+    return a;
+}
+
+static int check_adam(const flashopt_adamw_hparams* hp, int64_t step) {
+    if (!hp) return FLASHOPT_ERR_NULL;
+    if (step < 1) return FLASHOPT_ERR_STEP;
+    if (!(hp->lr >= 0.0) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) ||
+        !(hp->weight_decay >= 0.0) || !std::isfinite(hp->lr) || !std::isfinite(hp->eps) ||
+        !std::isfinite(hp->weight_decay))
+        return FLASHOPT_ERR_ARG;
+    return FLASHOPT_OK;
+}
+
+static int check_sgd(const flashopt_sgd_hparams* hp, int64_t step) {
+    if (!hp) return FLASHOPT_ERR_NULL;
+    if (step < 1) return FLASHOPT_ERR_STEP;
+    if (!(hp->lr >= 0.0) || !(hp->momentum >= 0.0 && hp->momentum < 1.0) ||
+        !(hp->weight_decay >= 0.0) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+        return FLASHOPT_ERR_ARG;
+    return FLASHOPT_OK;
+}
+
+static int check_tensor(const flashopt_tensor& t) {
+    if (t.numel < 0 || t.numel > kMaxNumel) return FLASHOPT_ERR_SIZE;
+    if ((t.v_code == nullptr) != (t.v_scale == nullptr)) return FLASHOPT_ERR_ARG;
+    if (t.numel == 0) return FLASHOPT_OK;
+    if (!t.theta || !t.rho || !t.m_code || !t.m_scale) return FLASHOPT_ERR_NULL;
+    if (!aligned(t.theta, 16) || !aligned(t.rho, 8) || !aligned(t.m_code, 8) ||
+        !aligned(t.m_scale, 2) || (t.v_code && !aligned(t.v_code, 8)) ||
+        (t.v_scale && !aligned(t.v_scale, 2)) || (t.grad && !aligned(t.grad, 16)))
+        return FLASHOPT_ERR_ALIGN;
+    return FLASHOPT_OK;
+}
+
+static DevTensor to_dev(const flashopt_tensor& t) {
+    DevTensor d;
+    d.theta = t.theta; d.rho = t.rho; d.mq = t.m_code; d.ms = t.m_scale;
+    d.vq = t.v_code; d.vs = t.v_scale; d.grad = t.grad; d.numel = t.numel;
+    return d;
+}
+
+}  // namespace flashopt
+
+using namespace flashopt;
+
+struct flashopt_list {
+    int32_t count = 0;
+    int64_t total_tiles = 0;
+    int64_t numel = 0;
+    DevTensor* d_table = nullptr;
+    int64_t* d_tile_begin = nullptr;
+    std::vector<flashopt_tensor> host;
+    std::vector<int64_t> tile_begin;
+    bool all_have_v = true;
+    bool all_have_grad = true;
+    // cached bias-correction powers (see adam_scalars)
+    double p1 = 1.0, p2 = 1.0, b1 = -1.0, b2 = -1.0;
+    int64_t t = 0;
+};
+
+extern "C" {
+
+const char* flashopt_status_string(int s) {
+    switch (s) {
+        case FLASHOPT_OK: return "ok";
+        case FLASHOPT_ERR_NULL: return "required pointer is NULL";
+        case FLASHOPT_ERR_SIZE: return "element or tensor count out of range";
+        case FLASHOPT_ERR_ALIGN: return "pointer misaligned";
+        case FLASHOPT_ERR_ARG: return "argument out of range or state array missing";
+        case FLASHOPT_ERR_STEP: return "step counter must be >= 1";
+        case FLASHOPT_ERR_WORKSPACE: return "device workspace too small or misaligned";
+        case FLASHOPT_ERR_HIP: return "HIP runtime error";
+        case FLASHOPT_ERR_INDEX: return "tensor index out of range";
+        default: return "unknown status";
+    }
+}
+
+int flashopt_split(const float* theta, int64_t n, uint16_t* theta_bf16, int8_t* rho,
+                   void* stream) {
+    if (n < 0 || n > kMaxNumel) return FLASHOPT_ERR_SIZE;
+    if (n == 0) return FLASHOPT_OK;
+    if (!theta || !theta_bf16 || !rho) return FLASHOPT_ERR_NULL;
+    if (!aligned(theta, 16) || !aligned(theta_bf16, 16) || !aligned(rho, 8))
+        return FLASHOPT_ERR_ALIGN;
+    const int64_t chunks = (n + kSubTile - 1) / kSubTile;
+    hipLaunchKernelGGL(split_kernel, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                       (hipStream_t)stream, theta, n, theta_bf16, rho);
+    return launch_status();
+}
+
+int flashopt_unsplit(const uint16_t* theta_bf16, const int8_t* rho, int64_t n, float* out,
+                     void* stream) {
+    if (n < 0 || n > kMaxNumel) return FLASHOPT_ERR_SIZE;
+    if (n == 0) return FLASHOPT_OK;
+    if (!theta_bf16 || !rho || !out) return FLASHOPT_ERR_NULL;
+    if (!aligned(theta_bf16, 16) || !aligned(rho, 8) || !aligned(out, 16))
+        return FLASHOPT_ERR_ALIGN;
+    const int64_t chunks = (n + kSubTile - 1) / kSubTile;
+    hipLaunchKernelGGL(unsplit_kernel, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                       (hipStream_t)stream, theta_bf16, rho, n, out);
+    return launch_status();
+}
+
+static int quantize_common(int kind, const float* x, int64_t n, void* q, uint16_t* scale,
+                           void* stream) {
+    if (n < 0 || n > kMaxNumel) return FLASHOPT_ERR_SIZE;
+    if (n == 0) return FLASHOPT_OK;
+    if (!x || !q || !scale) return FLASHOPT_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 2)) return FLASHOPT_ERR_ALIGN;
+    const int64_t chunks = (n + kSubTile - 1) / kSubTile;
+    if (kind == 0)
+        hipLaunchKernelGGL(quantize_kernel<0>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, x, n, (uint8_t*)q, scale);
+    else
+        hipLaunchKernelGGL(quantize_kernel<1>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, x, n, (uint8_t*)q, scale);
+    return launch_status();
+}
+
+static int dequantize_common(int kind, const void* q, const uint16_t* scale, int64_t n,
+                             float* out, void* stream) {
+    if (n < 0 || n > kMaxNumel) return FLASHOPT_ERR_SIZE;
+    if (n == 0) return FLASHOPT_OK;
+    if (!q || !scale || !out) return FLASHOPT_ERR_NULL;
+    if (!aligned(q, 8) || !aligned(scale, 2) || !aligned(out, 16)) return FLASHOPT_ERR_ALIGN;
+    const int64_t chunks = (n + kSubTile - 1) / kSubTile;
+    if (kind == 0)
+        hipLaunchKernelGGL(dequantize_kernel<0>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, (const uint8_t*)q, scale, n, out);
+    else
+        hipLaunchKernelGGL(dequantize_kernel<1>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, (const uint8_t*)q, scale, n, out);
+    return launch_status();
+}
+
+int flashopt_quantize_m(const float* m, int64_t n, int8_t* q, uint16_t* scale, void* stream) {
+    return quantize_common(0, m, n, q, scale, stream);
+}
+int flashopt_dequantize_m(const int8_t* q, const uint16_t* scale, int64_t n, float* m,
+                          void* stream) {
+    return dequantize_common(0, q, scale, n, m, stream);
+}
+int flashopt_quantize_v(const float* v, int64_t n, uint8_t* q, uint16_t* scale, void* stream) {
+    return quantize_common(1, v, n, q, scale, stream);
+}
+int flashopt_dequantize_v(const uint8_t* q, const uint16_t* scale, int64_t n, float* v,
+                          void* stream) {
+    return dequantize_common(1, q, scale, n, v, stream);
+}
+
+size_t flashopt_list_workspace_bytes(int32_t count) {
+    if (count < 0) return 0;
+    const size_t tb = ((size_t)count + 1) * sizeof(int64_t);
+    const size_t tb_padded = (tb + 255) / 256 * 256;
+    return tb_padded + (size_t)count * sizeof(DevTensor);
+}
+
+int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, void* workspace,
+                         size_t workspace_bytes, void* stream, flashopt_list** out) {
+    if (!out) return FLASHOPT_ERR_NULL;
+    *out = nullptr;
+    if (count < 0) return FLASHOPT_ERR_SIZE;
+    if (count > 0 && !tensors) return FLASHOPT_ERR_NULL;
+    const size_t need = flashopt_list_workspace_bytes(count);
+    if (count > 0) {
+        if (!workspace) return FLASHOPT_ERR_NULL;
+        if (workspace_bytes < need || !aligned(workspace, 256)) return FLASHOPT_ERR_WORKSPACE;
+    }
+    flashopt_list* L = new (std::nothrow) flashopt_list();
+    if (!L) return FLASHOPT_ERR_ARG;
+    L->count = count;
+    L->host.assign(tensors, tensors + count);
+    L->tile_begin.resize((size_t)count + 1);
+    int64_t tiles = 0;
+    std::vector<DevTensor> dev((size_t)count);
+    for (int32_t i = 0; i < count; ++i) {
+        const int st = check_tensor(tensors[i]);
+        if (st != FLASHOPT_OK) { delete L; return st; }
+        L->tile_begin[i] = tiles;
+        tiles += tiles_of(tensors[i].numel);
+        L->numel += tensors[i].numel;
+        if (tensors[i].numel > 0) {
+            if (!tensors[i].v_code) L->all_have_v = false;
+            if (!tensors[i].grad) L->all_have_grad = false;
+        }
+        dev[i] = to_dev(tensors[i]);
+    }
+    L->tile_begin[count] = tiles;
+    L->total_tiles = tiles;
+    if (count > 0) {
+        const size_t tb = ((size_t)count + 1) * sizeof(int64_t);
+        const size_t tb_padded = (tb + 255) / 256 * 256;
+        L->d_tile_begin = (int64_t*)workspace;
+        L->d_table = (DevTensor*)((char*)workspace + tb_padded);
+        hipStream_t s = (hipStream_t)stream;
+        if (hipMemcpyAsync(L->d_tile_begin, L->tile_begin.data(), tb, hipMemcpyHostToDevice, s) !=
+                hipSuccess ||
+            hipMemcpyAsync(L->d_table, dev.data(), dev.size() * sizeof(DevTensor),
+                           hipMemcpyHostToDevice, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess) {
+            delete L;
+            return FLASHOPT_ERR_HIP;
+        }
+    }
+    *out = L;
+    return FLASHOPT_OK;
+}
+
+int flashopt_list_destroy(flashopt_list* L) {
+    delete L;
+    return FLASHOPT_OK;
+}
+
+int64_t flashopt_list_numel(const flashopt_list* L) { return L ? L->numel : -1; }
+
+int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (L->count == 0) return FLASHOPT_OK;
+    if (!grads) return FLASHOPT_ERR_NULL;
+    bool all = true;
+    for (int32_t i = 0; i < L->count; ++i) {
+        if (grads[i] && !aligned(grads[i], 16)) return FLASHOPT_ERR_ALIGN;
+        if (!grads[i] && L->host[i].numel > 0) all = false;
+    }
+    for (int32_t first = 0; first < L->count; first += kGradBatch) {
+        GradBatch b;
+        b.first = first;
+        b.count = std::min<int32_t>(kGradBatch, L->count - first);
+        for (int i = 0; i < b.count; ++i) b.ptr[i] = grads[first + i];
+        hipLaunchKernelGGL(set_grads_kernel, dim3(1), dim3(kGradBatch), 0, (hipStream_t)stream,
+                           L->d_table, b);
+        const int st = launch_status();
+        if (st != FLASHOPT_OK) return st;
+    }
+    for (int32_t i = 0; i < L->count; ++i) L->host[i].grad = grads[i];
+    L->all_have_grad = all;
+    return FLASHOPT_OK;
+}
+
+int flashopt_state_zero(const flashopt_list* L, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (L->total_tiles == 0) return FLASHOPT_OK;
+    ListArgs A{};
+    A.table = L->d_table;
+    A.tile_begin = L->d_tile_begin;
+    A.count = L->count;
+    A.total_tiles = L->total_tiles;
+    hipLaunchKernelGGL(zero_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
+                       (hipStream_t)stream, A);
+    return launch_status();
+}
+
+static int launch_list(int opt, const flashopt_list* L, const AdamScalars& a,
+                       const SgdScalars& s, void* stream) {
+    if (L->total_tiles == 0) return FLASHOPT_OK;
+    ListArgs A{};
+    A.table = L->d_table;
+    A.tile_begin = L->d_tile_begin;
+    A.count = L->count;
+    A.total_tiles = L->total_tiles;
+    if (opt == kAdamW)
+        hipLaunchKernelGGL(step_kernel<kAdamW>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
+                           (hipStream_t)stream, A, a, s);
+    else
+        hipLaunchKernelGGL(step_kernel<kSgd>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
+                           (hipStream_t)stream, A, a, s);
+    return launch_status();
+}
+
+static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint16_t* grad,
+                      const AdamScalars& a, const SgdScalars& s, void* stream) {
+    const flashopt_tensor& t = L->host[index];
+    if (t.numel == 0) return FLASHOPT_OK;
+    ListArgs A{};
+    A.table = nullptr;
+    A.tile_begin = nullptr;
+    A.one = to_dev(t);
+    A.one.grad = grad;
+    A.count = 1;
+    A.total_tiles = tiles_of(t.numel);
+    if (opt == kAdamW)
+        hipLaunchKernelGGL(step_kernel<kAdamW>, dim3(grid_for(A.total_tiles)), dim3(kBlock), 0,
+                           (hipStream_t)stream, A, a, s);
+    else
+        hipLaunchKernelGGL(step_kernel<kSgd>, dim3(grid_for(A.total_tiles)), dim3(kBlock), 0,
+                           (hipStream_t)stream, A, a, s);
+    return launch_status();
+}
+
+int flashopt_adamw_step(const flashopt_list* L, const flashopt_adamw_hparams* hp, int64_t step,
+                        void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    int st = check_adam(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (!L->all_have_v) return FLASHOPT_ERR_ARG;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    flashopt_list* M = const_cast<flashopt_list*>(L);   // only the scalar cache changes
+    const AdamScalars a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
+    return launch_list(kAdamW, L, a, SgdScalars{}, stream);
+}
+
+int flashopt_sgd_step(const flashopt_list* L, const flashopt_sgd_hparams* hp, int64_t step,
+                      void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    int st = check_sgd(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    SgdScalars s{(float)hp->momentum, (float)hp->lr, (float)hp->weight_decay};
+    return launch_list(kSgd, L, AdamScalars{}, s, stream);
+}
+
+int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,
+                            const flashopt_adamw_hparams* hp, int64_t step, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
+    int st = check_adam(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    const flashopt_tensor& t = L->host[index];
+    if (t.numel > 0) {
+        if (!grad) return FLASHOPT_ERR_NULL;
+        if (!aligned(grad, 16)) return FLASHOPT_ERR_ALIGN;
+        if (!t.v_code) return FLASHOPT_ERR_ARG;
+    }
+    flashopt_list* M = const_cast<flashopt_list*>(L);
+    const AdamScalars a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
+    return launch_one(kAdamW, L, index, grad, a, SgdScalars{}, stream);
+}
+
+int flashopt_sgd_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,
+                          const flashopt_sgd_hparams* hp, int64_t step, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
+    int st = check_sgd(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    const flashopt_tensor& t = L->host[index];
+    if (t.numel > 0) {
+        if (!grad) return FLASHOPT_ERR_NULL;
+        if (!aligned(grad, 16)) return FLASHOPT_ERR_ALIGN;
+    }
+    SgdScalars s{(float)hp->momentum, (float)hp->lr, (float)hp->weight_decay};
+    return launch_one(kSgd, L, index, grad, AdamScalars{}, s, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,275 @@
+"""Thin Python binding of libflashopt.so (include/flashopt.h).
+
+Argument marshalling only: each function below forwards to the C entry point
+of the same name; every step of the optimizer runs in the HIP kernels.  torch
+is used for device memory and streams: tensors are passed by data pointer,
+streams by their HIP handle.  There is no fallback: if the HIP library is
+missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashopt.so")
+GROUP = 32
+
+STATUS = {0: "ok", -1: "null pointer", -2: "size", -3: "alignment", -4: "argument",
+          -5: "step", -6: "workspace", -7: "HIP error", -8: "index"}
+
+
+class FlashoptError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status} ({STATUS.get(status, '?')})")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("theta", ctypes.c_void_p), ("rho", ctypes.c_void_p),
+                ("m_code", ctypes.c_void_p), ("m_scale", ctypes.c_void_p),
+                ("v_code", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("grad", ctypes.c_void_p)]
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class SGDHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("weight_decay", ctypes.c_double)]
+
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = {
+    "flashopt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "flashopt_split": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
+    "flashopt_unsplit": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "flashopt_quantize_m": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
+    "flashopt_dequantize_m": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "flashopt_quantize_v": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
+    "flashopt_dequantize_v": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "flashopt_list_workspace_bytes": (_SZ, [_I32]),
+    "flashopt_list_create": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32, _P, _SZ, _P,
+                                            ctypes.POINTER(_P)]),
+    "flashopt_list_destroy": (ctypes.c_int, [_P]),
+    "flashopt_list_numel": (_I64, [_P]),
+    "flashopt_list_set_grads": (ctypes.c_int, [_P, ctypes.POINTER(_P), _P]),
+    "flashopt_state_zero": (ctypes.c_int, [_P, _P]),
+    "flashopt_adamw_step": (ctypes.c_int, [_P, ctypes.POINTER(AdamWHparams), _I64, _P]),
+    "flashopt_sgd_step": (ctypes.c_int, [_P, ctypes.POINTER(SGDHparams), _I64, _P]),
+    "flashopt_adamw_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(AdamWHparams),
+                                               _I64, _P]),
+    "flashopt_sgd_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(SGDHparams), _I64,
+                                             _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree HIP library (building it only if it is absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise FlashoptError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("expected a contiguous device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def groups(n: int) -> int:
+    return (n + GROUP - 1) // GROUP
+
+
+# ---- flat buffers ---------------------------------------------------------
+
+def flashopt_split(theta, theta_bf16, rho, stream=None) -> None:
+    _check("flashopt_split", lib().flashopt_split(_ptr(theta), theta.numel(), _ptr(theta_bf16),
+                                                  _ptr(rho), _stream(stream)))
+
+
+def flashopt_unsplit(theta_bf16, rho, theta_out, stream=None) -> None:
+    _check("flashopt_unsplit", lib().flashopt_unsplit(_ptr(theta_bf16), _ptr(rho),
+                                                      theta_bf16.numel(), _ptr(theta_out),
+                                                      _stream(stream)))
+
+
+def flashopt_quantize_m(m, q, scale, stream=None) -> None:
+    _check("flashopt_quantize_m", lib().flashopt_quantize_m(_ptr(m), m.numel(), _ptr(q),
+                                                            _ptr(scale), _stream(stream)))
+
+
+def flashopt_dequantize_m(q, scale, m_out, stream=None) -> None:
+    _check("flashopt_dequantize_m", lib().flashopt_dequantize_m(_ptr(q), _ptr(scale), q.numel(),
+                                                                _ptr(m_out), _stream(stream)))
+
+
+def flashopt_quantize_v(v, q, scale, stream=None) -> None:
+    _check("flashopt_quantize_v", lib().flashopt_quantize_v(_ptr(v), v.numel(), _ptr(q),
+                                                            _ptr(scale), _stream(stream)))
+
+
+def flashopt_dequantize_v(q, scale, v_out, stream=None) -> None:
+    _check("flashopt_dequantize_v", lib().flashopt_dequantize_v(_ptr(q), _ptr(scale), q.numel(),
+                                                                _ptr(v_out), _stream(stream)))
+
+
+# ---- tensor lists -----------------------------------------------------------
+
+class TensorState:
+    """Device arrays of one tensor's compressed state (allocated with torch)."""
+
+    def __init__(self, numel: int, optimizer: str, device):
+        g = groups(numel)
+        self.numel = numel
+        self.theta = torch.empty(numel, dtype=torch.bfloat16, device=device)
+        self.rho = torch.empty(numel, dtype=torch.int8, device=device)
+        self.m_code = torch.zeros(numel, dtype=torch.int8, device=device)
+        self.m_scale = torch.zeros(g, dtype=torch.float16, device=device)
+        if optimizer == "adamw":
+            self.v_code = torch.zeros(numel, dtype=torch.uint8, device=device)
+            self.v_scale = torch.zeros(g, dtype=torch.float16, device=device)
+        else:
+            self.v_code = self.v_scale = None
+
+    def arrays(self) -> dict:
+        return {"theta": self.theta, "rho": self.rho, "m_code": self.m_code,
+                "m_scale": self.m_scale, "v_code": self.v_code, "v_scale": self.v_scale}
+
+
+class FlashoptList:
+    """A flashopt_list handle over a list of TensorState (device workspace from torch)."""
+
+    def __init__(self, states: Sequence[TensorState], grads: Sequence[Optional[torch.Tensor]],
+                 stream=None):
+        self.states = list(states)
+        count = len(self.states)
+        arr = (Tensor * max(count, 1))()
+        for i, (st, g) in enumerate(zip(self.states, grads)):
+            arr[i] = Tensor(st.numel, _ptr(st.theta), _ptr(st.rho), _ptr(st.m_code),
+                            _ptr(st.m_scale), _ptr(st.v_code), _ptr(st.v_scale), _ptr(g))
+        self.grads = list(grads)
+        nbytes = lib().flashopt_list_workspace_bytes(count)
+        dev = self.states[0].theta.device if count else torch.device("cuda")
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        h = ctypes.c_void_p()
+        _check("flashopt_list_create",
+               lib().flashopt_list_create(arr, count, _ptr(self.workspace), nbytes,
+                                          _stream(stream), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.flashopt_list_destroy(h)
+            self.handle = None
+
+    def numel(self) -> int:
+        return lib().flashopt_list_numel(self.handle)
+
+
+def flashopt_list_set_grads(lst: FlashoptList, grads: Sequence[Optional[torch.Tensor]],
+                            stream=None) -> None:
+    arr = (ctypes.c_void_p * max(len(grads), 1))(*[_ptr(g) for g in grads])
+    _check("flashopt_list_set_grads", lib().flashopt_list_set_grads(lst.handle, arr,
+                                                                    _stream(stream)))
+    lst.grads = list(grads)
+
+
+def flashopt_state_zero(lst: FlashoptList, stream=None) -> None:
+    _check("flashopt_state_zero", lib().flashopt_state_zero(lst.handle, _stream(stream)))
+
+
+def _adam(hp: dict) -> AdamWHparams:
+    return AdamWHparams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+
+
+def _sgd(hp: dict) -> SGDHparams:
+    return SGDHparams(hp["lr"], hp["momentum"], hp["weight_decay"])
+
+
+def flashopt_adamw_step(lst: FlashoptList, hp: dict, step: int, stream=None) -> None:
+    h = _adam(hp)
+    _check("flashopt_adamw_step", lib().flashopt_adamw_step(lst.handle, ctypes.byref(h), step,
+                                                            _stream(stream)))
+
+
+def flashopt_sgd_step(lst: FlashoptList, hp: dict, step: int, stream=None) -> None:
+    h = _sgd(hp)
+    _check("flashopt_sgd_step", lib().flashopt_sgd_step(lst.handle, ctypes.byref(h), step,
+                                                        _stream(stream)))
+
+
+def flashopt_adamw_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: int,
+                            stream=None) -> None:
+    h = _adam(hp)
+    _check("flashopt_adamw_step_one",
+           lib().flashopt_adamw_step_one(lst.handle, index, _ptr(grad), ctypes.byref(h), step,
+                                         _stream(stream)))
+
+
+def flashopt_sgd_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: int,
+                          stream=None) -> None:
+    h = _sgd(hp)
+    _check("flashopt_sgd_step_one",
+           lib().flashopt_sgd_step_one(lst.handle, index, _ptr(grad), ctypes.byref(h), step,
+                                       _stream(stream)))
+
+
+def step(lst: FlashoptList, optimizer: str, hp: dict, t: int, stream=None) -> None:
+    if optimizer == "adamw":
+        flashopt_adamw_step(lst, hp, t, stream)
+    else:
+        flashopt_sgd_step(lst, hp, t, stream)
+
+
+def step_one(lst: FlashoptList, optimizer: str, index: int, grad, hp: dict, t: int,
+             stream=None) -> None:
+    if optimizer == "adamw":
+        flashopt_adamw_step_one(lst, index, grad, hp, t, stream)
+    else:
+        flashopt_sgd_step_one(lst, index, grad, hp, t, stream)
+
+
+def build_list(theta_fp32: List[torch.Tensor], optimizer: str,
+               grads: Sequence[Optional[torch.Tensor]], stream=None):
+    """Allocate compressed state for fp32 master weights, split them and zero
+    the optimizer state; returns (states, list handle)."""
+    states = []
+    for th in theta_fp32:
+        st = TensorState(th.numel(), optimizer, th.device)
+        flashopt_split(th.reshape(-1), st.theta, st.rho, stream)
+        states.append(st)
+    lst = FlashoptList(states, grads, stream)
+    flashopt_state_zero(lst, stream)
+    return states, lst

@@ -1,0 +1,174 @@
+/*
+ * flashopt.h -- C ABI of the MI355X (gfx950) implementation of FlashOptim's
+ * fused compressed optimizer step.
+ *
+ * Method: "FlashOptim: Optimizers for Memory Efficient Training" (arXiv
+ * 2602.23349v1), as summarised by its digest page:
+ *   - section "Core method > Weight splitting: ULP-based error correction"
+ *     (Eq. 1-2, Alg. 1): the FP32 master weight is stored as a BF16 weight
+ *     theta' plus an INT8 code rho of the error theta - theta' normalised by
+ *     ULP(theta')/2;
+ *   - section "Core method > Optimizer-state quantisation with companding"
+ *     (Alg. 2-3): momentum m is stored as INT8 codes of phi_m(m) = 2m/(1+|m|),
+ *     variance v as UINT8 codes of phi_v(v) = sqrt(v), each with one FP16
+ *     scale per group of 32 elements;
+ *   - section "Core method > Fused optimizer step" (Alg. 4): one pass per
+ *     parameter dequantises, rebuilds the master weight, applies AdamW (or
+ *     SGD with momentum), requantises the states and re-splits the weight;
+ *     gradient release steps each tensor as soon as its gradient exists.
+ *
+ * Arithmetic (every operation IEEE binary32, round to nearest even, no fused
+ * multiply-add, subnormals kept; K8 = RN(1/127), K255 = RN(1/255)):
+ *   h         = ULP(theta')/2 = 2^(max(E,1)-135), E = exponent field of theta'
+ *   rebuild   theta_hat = theta' + (rho*K8)*h                 (theta' Inf/NaN: theta')
+ *   dequant   m = z/(2-|z|), z = q*(s*K8);  v = z*z, z = q*(s*K255)
+ *   AdamW     m' = b1*m + c1*g;  v' = b2*v + c2*(g*g);  w = sqrt(v');
+ *             theta_n = lambda*theta_hat - alpha*(m'/(w*kappa + eps))
+ *   SGD       g' = g + wd*theta_hat;  b' = mu*b + g';  theta_n = theta_hat - lr*b'
+ *   requant   z = (2m')/(1+|m'|) (momentum) or w (variance); a = max |z| over
+ *             the group's elements; s = FP16(a) capped at 0x3FFF (momentum) or
+ *             0x7BFF (variance); q = 0 if s = 0 else clamp(rne(z*(127/s)), +-127)
+ *             (variance: 255/s, [0,255])
+ *   re-split  theta' = BF16_rne(theta_n); rho = clamp(rne(127*(theta_n-theta')/h), +-127)
+ *             (0 when theta' is Inf/NaN)
+ * with per-call scalars computed on the host in double and rounded once:
+ *   p1 = beta1^t, p2 = beta2^t (t successive multiplications), b1 = beta1,
+ *   c1 = 1-beta1, b2 = beta2, c2 = 1-beta2, alpha = lr/(1-p1),
+ *   kappa = 1/sqrt(1-p2), lambda = 1-lr*wd.
+ *
+ * Memory and ownership.  Every array argument is DEVICE memory on the
+ * current HIP device, owned by the caller (the library never allocates device
+ * memory); streams are hipStream_t values passed as void* (NULL = the null
+ * stream).  Element arrays are dense, 1-D, row-major flattenings of the
+ * tensor.  Groups of 32 restart at element 0 of every tensor; a tensor of n
+ * elements has ceil(n/32) scales per state, the last group possibly partial
+ * (its scale covers only its valid elements).  BF16 and FP16 values are passed
+ * as their uint16 bit patterns.
+ *
+ * Alignment: BF16 arrays (theta', grad) 16 bytes; INT8/UINT8 code arrays
+ * 8 bytes; scale arrays 2 bytes; FP32 arrays 16 bytes.
+ *
+ * Errors.  Every call validates its arguments on the host before launching
+ * anything and returns a flashopt_status; a failed validation launches
+ * nothing.  FLASHOPT_ERR_HIP reports a launch failure (hipGetLastError).
+ * Faults inside kernels surface asynchronously at the caller's next
+ * synchronisation.  Calls are ordered on the given stream and never
+ * synchronise the device, except flashopt_list_create (documented there).
+ * Non-finite gradients are outside the contract (they propagate).
+ * No C++ exception crosses this interface.  A list handle must not be used
+ * from two host threads at once.
+ */
+#ifndef FLASHOPT_H
+#define FLASHOPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLASHOPT_GROUP 32
+
+typedef enum flashopt_status {
+    FLASHOPT_OK = 0,
+    FLASHOPT_ERR_NULL = -1,      /* a required pointer is NULL                         */
+    FLASHOPT_ERR_SIZE = -2,      /* negative or too large element count / list count   */
+    FLASHOPT_ERR_ALIGN = -3,     /* a pointer violates the alignment above             */
+    FLASHOPT_ERR_ARG = -4,       /* hyper-parameter out of range, missing state array  */
+    FLASHOPT_ERR_STEP = -5,      /* step counter t < 1                                 */
+    FLASHOPT_ERR_WORKSPACE = -6, /* device workspace too small                         */
+    FLASHOPT_ERR_HIP = -7,       /* HIP runtime error (launch, copy, device query)     */
+    FLASHOPT_ERR_INDEX = -8      /* tensor index out of range                          */
+} flashopt_status;
+
+/* One parameter tensor and its compressed state (all DEVICE pointers). */
+typedef struct flashopt_tensor {
+    int64_t numel;           /* n >= 0                                                   */
+    uint16_t* theta;         /* [n] BF16 theta'; the model weight the forward pass reads */
+    int8_t* rho;             /* [n] INT8 weight-error codes                              */
+    int8_t* m_code;          /* [n] INT8 momentum codes (SGD: momentum buffer codes)     */
+    uint16_t* m_scale;       /* [ceil(n/32)] FP16 momentum scales                        */
+    uint8_t* v_code;         /* [n] UINT8 variance codes; NULL for an SGD-only list      */
+    uint16_t* v_scale;       /* [ceil(n/32)] FP16 variance scales; NULL with v_code      */
+    const uint16_t* grad;    /* [n] BF16 gradient, read only; may be NULL when only the
+                                *_step_one entry points (gradient release) are used    */
+} flashopt_tensor;
+
+typedef struct flashopt_adamw_hparams {
+    double lr;            /* >= 0                                  */
+    double beta1;         /* [0, 1)                                */
+    double beta2;         /* [0, 1)                                */
+    double eps;           /* > 0                                   */
+    double weight_decay;  /* >= 0, decoupled (scaled by lr)        */
+} flashopt_adamw_hparams;
+
+typedef struct flashopt_sgd_hparams {
+    double lr;            /* >= 0                                  */
+    double momentum;      /* [0, 1); dampening 0, no Nesterov      */
+    double weight_decay;  /* >= 0, L2 added to the gradient        */
+} flashopt_sgd_hparams;
+
+typedef struct flashopt_list flashopt_list;   /* opaque; host memory owned by the library */
+
+const char* flashopt_status_string(int status);
+
+/* ---- flat buffers: weight split / rebuild (weight-splitting section, Eq. 1-2,
+ * Alg. 1).  split: theta (FP32 [n]) -> theta' (BF16 [n]) and rho (INT8 [n]),
+ * used once at optimizer construction.  unsplit: the reverse, writing the
+ * rebuilt FP32 master weight (export, checkpoint conversion). */
+int flashopt_split(const float* theta, int64_t n, uint16_t* theta_bf16, int8_t* rho,
+                   void* stream);
+int flashopt_unsplit(const uint16_t* theta_bf16, const int8_t* rho, int64_t n,
+                     float* theta_out, void* stream);
+
+/* ---- flat buffers: companded group quantisers (companding section, Alg. 2-3).
+ * Import an FP32 optimizer state into the compressed form, or export it.
+ * quantize_v takes the variance v itself (it applies phi_v = sqrt). */
+int flashopt_quantize_m(const float* m, int64_t n, int8_t* q, uint16_t* scale, void* stream);
+int flashopt_dequantize_m(const int8_t* q, const uint16_t* scale, int64_t n, float* m,
+                          void* stream);
+int flashopt_quantize_v(const float* v, int64_t n, uint8_t* q, uint16_t* scale, void* stream);
+int flashopt_dequantize_v(const uint8_t* q, const uint16_t* scale, int64_t n, float* v,
+                          void* stream);
+
+/* ---- ragged tensor lists (a flat buffer is a list of one).
+ * The list keeps a device descriptor table in a caller-provided DEVICE
+ * workspace of at least flashopt_list_workspace_bytes(count) bytes (256-byte
+ * aligned), which must outlive the handle.  flashopt_list_create validates
+ * every descriptor, uploads the table on `stream` and waits for that copy
+ * (it is a set-up call); afterwards the descriptors' pointers are fixed,
+ * except the gradients (flashopt_list_set_grads).  count may be 0. */
+size_t flashopt_list_workspace_bytes(int32_t count);
+int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, void* workspace,
+                         size_t workspace_bytes, void* stream, flashopt_list** out);
+int flashopt_list_destroy(flashopt_list* list);
+int64_t flashopt_list_numel(const flashopt_list* list);
+/* grads: HOST array of `count` device pointers (entries may be NULL).  The new
+ * pointers are written into the device table in stream order (kernel
+ * arguments, no host staging buffer), so steps enqueued later see them. */
+int flashopt_list_set_grads(flashopt_list* list, const uint16_t* const* grads, void* stream);
+/* Zero every code and scale of the list (the initial state: m = v = 0). */
+int flashopt_state_zero(const flashopt_list* list, void* stream);
+
+/* ---- the fused step (fused-step section, Alg. 4): ONE launch over the whole
+ * list.  step is the 1-based AdamW counter t shared by all tensors of one
+ * optimizer step.  AdamW needs v_code / v_scale on every tensor. */
+int flashopt_adamw_step(const flashopt_list* list, const flashopt_adamw_hparams* hp,
+                        int64_t step, void* stream);
+int flashopt_sgd_step(const flashopt_list* list, const flashopt_sgd_hparams* hp,
+                      int64_t step, void* stream);
+
+/* ---- gradient release (fused-step section): step tensor `index` of the list
+ * now, reading `grad` (device BF16 [numel], overriding the descriptor's
+ * pointer); the caller may free or reuse grad once this launch has run.
+ * Same arithmetic and results as the whole-list step. */
+int flashopt_adamw_step_one(const flashopt_list* list, int32_t index, const uint16_t* grad,
+                            const flashopt_adamw_hparams* hp, int64_t step, void* stream);
+int flashopt_sgd_step_one(const flashopt_list* list, int32_t index, const uint16_t* grad,
+                          const flashopt_sgd_hparams* hp, int64_t step, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHOPT_H */

@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every symbol include/flashopt.h declares,
+and validates arguments on the host (no GPU call is made by these tests:
+every case fails validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_adamw_state_amd import flashopt as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "flashopt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flashopt_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = F.lib()
+    names = declared_symbols()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(F.SIGNATURES), set(names) ^ set(F.SIGNATURES)
+
+
+def test_status_strings():
+    lib = F.lib()
+    for s in range(-8, 1):
+        assert lib.flashopt_status_string(s)
+    assert lib.flashopt_status_string(0) == b"ok"
+
+
+def test_host_validation_without_gpu():
+    lib = F.lib()
+    P = ctypes.c_void_p
+    fake = P(0x10000)                                  # never dereferenced: validation fails first
+    mis = P(0x10001)
+    assert lib.flashopt_split(None, 10, fake, fake, None) == -1
+    assert lib.flashopt_split(fake, -1, fake, fake, None) == -2
+    assert lib.flashopt_split(mis, 10, fake, fake, None) == -3
+    assert lib.flashopt_split(fake, 0, None, None, None) == 0   # empty: nothing to do
+    assert lib.flashopt_unsplit(fake, fake, 5, mis, None) == -3
+    assert lib.flashopt_quantize_m(fake, 5, None, fake, None) == -1
+    assert lib.flashopt_dequantize_v(fake, P(0x10003), 5, fake, None) == -3
+    assert lib.flashopt_list_workspace_bytes(0) >= 8
+    assert lib.flashopt_list_workspace_bytes(291) >= 291 * 64
+    out = P()
+    arr = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake, None, None, fake))
+    ws = P(0x100000)
+    need = lib.flashopt_list_workspace_bytes(1)
+    assert lib.flashopt_list_create(arr, 1, ws, need - 1, None, ctypes.byref(out)) == -6
+    assert lib.flashopt_list_create(arr, 1, P(0x100010), need, None, ctypes.byref(out)) == -6
+    assert lib.flashopt_list_create(arr, -1, ws, need, None, ctypes.byref(out)) == -2
+    bad = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake, fake, None, fake))
+    assert lib.flashopt_list_create(bad, 1, ws, need, None, ctypes.byref(out)) == -4
+    mis_t = (F.Tensor * 1)(F.Tensor(10, P(0x10008), fake, fake, fake, None, None, fake))
+    assert lib.flashopt_list_create(mis_t, 1, ws, need, None, ctypes.byref(out)) == -3
+    neg = (F.Tensor * 1)(F.Tensor(-5, fake, fake, fake, fake, None, None, fake))
+    assert lib.flashopt_list_create(neg, 1, ws, need, None, ctypes.byref(out)) == -2
+    hp = F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    assert lib.flashopt_adamw_step(None, ctypes.byref(hp), 1, None) == -1
+    # an empty list is created without touching the device
+    assert lib.flashopt_list_create(None, 0, None, 0, None, ctypes.byref(out)) == 0
+    L = out
+    assert lib.flashopt_list_numel(L) == 0
+    assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 0, None) == -5
+    for bad_hp in (F.AdamWHparams(-1, 0.9, 0.999, 1e-8, 0), F.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0),
+                   F.AdamWHparams(1e-3, 0.9, 0.999, 0.0, 0), F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, -1),
+                   F.AdamWHparams(float("nan"), 0.9, 0.999, 1e-8, 0)):
+        assert lib.flashopt_adamw_step(L, ctypes.byref(bad_hp), 1, None) == -4
+    assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == 0    # nothing to launch
+    sgd = F.SGDHparams(0.1, 1.0, 0.0)
+    assert lib.flashopt_sgd_step(L, ctypes.byref(sgd), 1, None) == -4
+    assert lib.flashopt_adamw_step_one(L, 0, fake, ctypes.byref(hp), 1, None) == -8
+    assert lib.flashopt_state_zero(L, None) == 0
+    assert lib.flashopt_list_destroy(L) == 0

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle,
+bit for bit on every BF16 / INT8 / UINT8 code and FP16 scale, and on the
+rebuilt FP32 weights.  Sizes span several 2048-element tiles and ragged tails;
+the five workloads run at full size, the large ones compared on sampled groups
+in the same launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_adamw_state_amd import flashopt as F
+from compressed_adamw_state_amd import workloads as W
+
+from parity import Run, i8, log, u16, u8
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 31, 32, 33, 511, 512, 513, 1000, 2047, 2048, 2049, 4097, 6143, 32 * 777 + 5,
+          (1 << 20) + 7, 0, 64]
+
+
+def dev(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(x).cuda()
+
+
+def special_floats(rng, n):
+    """Normal weights plus zeros, subnormals, bf16 ties, huge and tiny values."""
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    bits = x.view(np.uint32)
+    k = n // 16
+    bits[:k] = (bits[:k] & 0xFFFF0000) | 0x8000                       # exact bf16 ties
+    bits[k:2 * k] = rng.integers(1, 1 << 23, k).astype(np.uint32)     # fp32 subnormals
+    bits[2 * k:3 * k] = 0
+    extremes = np.array([0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F7FFF, 0x00800000, 0x80000001,
+                         0x3F800000, 0xBF800000, 0x7F000000], np.uint32)
+    room = min(extremes.size, n - 3 * k)
+    bits[3 * k:3 * k + room] = extremes[:room]
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("n", [1, 31, 513, 4097, (1 << 20) + 7])
+def test_split_unsplit(n):
+    rng = np.random.default_rng(n)
+    x = special_floats(rng, n)
+    tb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    rho = torch.empty(n, dtype=torch.int8, device="cuda")
+    F.flashopt_split(dev(x), tb, rho)
+    otb, orho = oracle.split(x)
+    np.testing.assert_array_equal(u16(tb), otb)
+    np.testing.assert_array_equal(i8(rho), orho)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    F.flashopt_unsplit(tb, rho, out)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32),
+                                  oracle.unsplit(otb, orho).view(np.uint32))
+
+
+def test_split_structured_all_upper_halves():
+    # every bf16 pattern x 16 tails (ties, neighbours, random) -- covers every
+    # exponent, sign, Inf and NaN input of the encoder
+    rng = np.random.default_rng(1)
+    tails = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF] + list(rng.integers(0, 1 << 16, 10)),
+                     np.uint32)
+    bits = ((np.arange(1 << 16, dtype=np.uint32)[:, None] << 16) | tails[None, :]).reshape(-1)
+    x = bits.view(np.float32)
+    finite = np.isfinite(x)
+    tb = torch.empty(x.size, dtype=torch.bfloat16, device="cuda")
+    rho = torch.empty(x.size, dtype=torch.int8, device="cuda")
+    F.flashopt_split(dev(x), tb, rho)
+    otb, orho = oracle.split(x)
+    gtb, grho = u16(tb), i8(rho)
+    np.testing.assert_array_equal(gtb[finite], otb[finite])
+    np.testing.assert_array_equal(grho, orho)
+    nan = ~finite & np.isnan(x)
+    assert np.all((gtb[nan] & 0x7F80) == 0x7F80) and np.all(gtb[nan] & 0x7F)
+
+
+def test_unsplit_every_pattern_and_code():
+    tb = np.repeat(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16), 256)
+    rho = np.tile(np.arange(-128, 128, dtype=np.int16).astype(np.int8), 1 << 16)
+    out = torch.empty(tb.size, dtype=torch.float32, device="cuda")
+    F.flashopt_unsplit(dev(tb).view(torch.bfloat16), dev(rho), out)
+    got = out.cpu().numpy()
+    exp = oracle.unsplit(tb, rho)
+    fin = np.isfinite(exp)
+    np.testing.assert_array_equal(got[fin].view(np.uint32), exp[fin].view(np.uint32))
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+
+
+@pytest.mark.parametrize("scale", [1e-7, 1e-5, 1e-3, 1.0, 1e3])
+@pytest.mark.parametrize("n", [33, 4097, 100_003])
+def test_quantizers(scale, n):
+    rng = np.random.default_rng(int(n + scale * 1e7) % 99991)
+    m = (rng.standard_t(3, n) * scale).astype(np.float32)
+    m[: n // 20] = 0.0
+    q = torch.empty(n, dtype=torch.int8, device="cuda")
+    s = torch.empty((n + 31) // 32, dtype=torch.float16, device="cuda")
+    F.flashopt_quantize_m(dev(m), q, s)
+    oq, os_ = oracle.quant_m(m)
+    np.testing.assert_array_equal(i8(q), oq)
+    np.testing.assert_array_equal(u16(s), os_)
+    back = torch.empty(n, dtype=torch.float32, device="cuda")
+    F.flashopt_dequantize_m(q, s, back)
+    np.testing.assert_array_equal(back.cpu().numpy().view(np.uint32),
+                                  oracle.dequant_m(oq, os_).view(np.uint32))
+    v = (m.astype(np.float64) ** 2).astype(np.float32)
+    qv = torch.empty(n, dtype=torch.uint8, device="cuda")
+    F.flashopt_quantize_v(dev(v), qv, s)
+    oqv, osv = oracle.quant_v(v)
+    np.testing.assert_array_equal(u8(qv), oqv)
+    np.testing.assert_array_equal(u16(s), osv)
+    F.flashopt_dequantize_v(qv, s, back)
+    np.testing.assert_array_equal(back.cpu().numpy().view(np.uint32),
+                                  oracle.dequant_v(oqv, osv).view(np.uint32))
+
+
+def test_quantizer_every_code_and_scale():
+    # dequantise every (code, FP16 scale) pair the format can hold
+    s = np.arange(0x7C00, dtype=np.uint16)                 # all finite non-negative scales
+    n = s.size * 32
+    q = (np.arange(n) * 37 % 255 - 127).astype(np.int8)
+    back = torch.empty(n, dtype=torch.float32, device="cuda")
+    F.flashopt_dequantize_m(dev(q), dev(np.minimum(s, 0x3FFF)).view(torch.float16), back)
+    exp = oracle.dequant_m(q, np.minimum(s, 0x3FFF))
+    np.testing.assert_array_equal(back.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+    qv = (np.arange(n) * 53 % 256).astype(np.uint8)
+    F.flashopt_dequantize_v(dev(qv), dev(s).view(torch.float16), back)
+    np.testing.assert_array_equal(back.cpu().numpy().view(np.uint32),
+                                  oracle.dequant_v(qv, s).view(np.uint32))
+
+
+@pytest.mark.parametrize("opt", ["adamw", "sgd"])
+def test_ragged_list_every_step(opt):
+    w = W.ragged(RAGGED, seed=11, steps=4, optimizer=opt, grad_scale=1e-3 if opt == "adamw" else 1e-2)
+    r = Run(w, "full")
+    r.compare("init")
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        r.compare(f"step {t}")
+
+
+@pytest.mark.parametrize("opt", ["adamw", "sgd"])
+def test_release_mode_matches_list_mode(opt):
+    base = W.ragged(RAGGED[:12], seed=12, steps=3, optimizer=opt)
+    rel = W.Workload(base.name, base.tensors, opt, 3, base.seed, base.grad_dist, base.grad_scale,
+                     base.hparams, release=True)
+    a, b = Run(base, "full"), Run(rel, "full")
+    for t in range(1, 4):
+        a.step(t)
+        b.step(t)
+        b.compare(f"release step {t}")
+        for sa, sb in zip(a.states, b.states):
+            assert torch.equal(sa.theta.view(torch.int16), sb.theta.view(torch.int16))
+            assert torch.equal(sa.m_code, sb.m_code)
+
+
+def test_hyperparameter_variants():
+    w = W.ragged([4097, 33, 2048 * 3 + 1], seed=13, steps=3)
+    r = Run(w, "full")
+    for t, hp in enumerate([dict(lr=3e-2, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1),
+                            dict(lr=1e-4, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0),
+                            dict(lr=1e-3, beta1=0.99, beta2=0.9999, eps=1e-12, weight_decay=0.5)],
+                           1):
+        r.step(t, hp)
+        r.compare(f"hp {t}")
+    r.step(1000, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01))
+    r.compare("t=1000")
+
+
+def test_set_grads_and_state_zero():
+    w = W.ragged([3000, 70], seed=14, steps=2)
+    r = Run(w, "full")
+    r.step(1)
+    new = [torch.zeros(s.numel, dtype=torch.bfloat16, device="cuda") for s in r.states]
+    F.flashopt_list_set_grads(r.lst, new)
+    r.grads = new
+    r.step(2)
+    r.compare("after set_grads")
+    F.flashopt_state_zero(r.lst)
+    torch.cuda.synchronize()
+    for s in r.states:
+        assert not s.m_code.any() and not s.v_code.any()
+        assert not s.m_scale.view(torch.int16).any() and not s.v_scale.view(torch.int16).any()
+
+
+def test_config1_flat1m_all_steps():
+    w = W.WORKLOADS["flat1m"]
+    r = Run(w, "full")
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        n = r.compare(f"step {t}")
+    log(f"flat1m: {w.steps} steps, {n} elements compared per step")
+
+
+def test_config3_resnet50_sgd():
+    w = W.WORKLOADS["resnet50"]
+    r = Run(w, "full")
+    for t in range(1, w.steps + 1):
+        r.step(t, threads=16)
+        if t in (1, 2, w.steps):
+            n = r.compare(f"step {t}")
+            log(f"resnet50 step {t}: {n} elements compared")
+
+
+def test_config2_gpt2_sampled():
+    w = W.WORKLOADS["gpt2_small"]
+    r = Run(w, "sampled", samples_per_tensor=6)
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        if t % 25 == 0 or t == 1:
+            n = r.compare(f"step {t}")
+            log(f"gpt2 step {t}: {n} sampled elements compared")
+
+
+def test_config4_llama8b_sampled():
+    w = W.WORKLOADS["llama31_8b"]
+    r = Run(w, "sampled", samples_per_tensor=4)
+    log("llama8b: state built")
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        if t in (1, 2, 10, w.steps):
+            n = r.compare(f"step {t}")
+            log(f"llama8b step {t}: {n} sampled elements compared")
+
+
+def test_config5_llama13b_release_sampled():
+    w = W.WORKLOADS["llama2_13b"]
+    r = Run(w, "sampled", samples_per_tensor=4)
+    log("llama13b: state built")
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        if t in (1, w.steps) or t % 3 == 0:
+            n = r.compare(f"step {t}")
+            log(f"llama13b release step {t}: {n} sampled elements compared")
