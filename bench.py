@@ -96,6 +96,26 @@ def build_state(w: W.Workload, grad_sets: int):
     return states, grads, lists
 
 
+def copy_ceiling(nbytes: int, stream, reps: int = 5):
+    """A plain streaming copy of known size (torch's elementwise bitwise_not on
+    int32: reads nbytes, writes nbytes) -- the practical HBM ceiling for a
+    pure stream, and the reference the rocprofv3 HBM counters are scaled by."""
+    n = nbytes // 4
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        torch.bitwise_not(src, out=dst)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    best = min(ev[r].elapsed_time(ev[r + 1]) for r in range(reps)) / 1e3
+    return {"kernel": "torch bitwise_not int32", "bytes_read": 4 * n, "bytes_written": 4 * n,
+            "best_ms": best * 1e3, "gb_s": 8 * n / best / 1e9}
+
+
 def cpu_baseline(seconds: float, threads: int):
     """The oracle as it stands, on a bounded sample of the workload: a
     2^25-parameter group-aligned slice with the Llama workload's
@@ -131,6 +151,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 32,
+                    help="size of the plain copy kernel timed after the steps (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -209,6 +231,9 @@ def main():
     }
     del states, grads, lists
     torch.cuda.synchronize()
+    if args.copy_bytes:
+        out["copy_ceiling"] = copy_ceiling(args.copy_bytes, stream)
+        log(f"bench: plain copy {out['copy_ceiling']['gb_s']:.0f} GB/s")
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.cpu_threads)

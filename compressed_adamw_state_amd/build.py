@@ -28,6 +28,21 @@ FLAGS = [
 ]
 
 
+TEST_SRC = os.path.join(ROOT, "tests", "hip", "codec_exhaustive.hip")
+TEST_LIB = os.path.join(ROOT, "tests", "hip", "libcodec_exhaustive.so")
+
+
+def build_test_lib(verbose: bool = False) -> str:
+    """The exhaustive device check of the codec's short sequences (tests only)."""
+    tmp = TEST_LIB + ".tmp"
+    cmd = ["hipcc", *FLAGS, "-o", tmp, TEST_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, TEST_LIB)
+    return TEST_LIB
+
+
 def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp"
     cmd = ["hipcc", *FLAGS, *extra, "-o", tmp, SRC]

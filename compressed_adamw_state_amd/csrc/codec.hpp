@@ -69,14 +69,20 @@ __device__ __forceinline__ float half_ulp(uint32_t theta_bits) {
     return as_f32(e) * 0x1p-8f;
 }
 
-// Rebuilt master weight: theta' + (rho * K8) * h.
-__device__ __forceinline__ float unsplit(uint32_t tb, int32_t rho) {
-    uint32_t tbits = tb << 16;
-    float t = as_f32(tbits);
-    float h = half_ulp(tbits);
-    float c = (float)rho * as_f32(kK8Bits);
-    float d = c * h;
+// Rebuilt master weight: theta' + (rho * K8) * h, from theta' as binary32 bits.
+// Computed as (rho * (K8 * 2^-8)) * 2^(E-127): K8 * 2^-8 is exact, and for
+// |rho| >= 1 the first product is at least 2^-15, so scaling by 2^-8 commutes
+// with its rounding; the second product rounds once, like (rho*K8) * h.
+__device__ __forceinline__ float unsplit_bits(uint32_t tbits, int32_t rho) {
+    const float t = as_f32(tbits);
+    const uint32_t e = min(max(tbits & 0x7F800000u, 0x00800000u), 0x7F000000u);
+    const float c = (float)rho * as_f32(kK8Bits - 0x04000000u);   // K8 * 2^-8
+    const float d = c * as_f32(e);
     return t + d;
+}
+
+__device__ __forceinline__ float unsplit(uint32_t tb, int32_t rho) {
+    return unsplit_bits(tb << 16, rho);
 }
 
 // Split: theta' = BF16(x); rho = clamp(rne(127 * (x - theta') / h), +-127).
@@ -162,6 +168,77 @@ __device__ __forceinline__ uint32_t code_v(float w, float r) {
     float q = __builtin_rintf(y);
     q = fminf(fmaxf(q, 0.0f), 255.0f);
     return (uint32_t)q;
+}
+
+// ---- short exactly rounded sequences ----------------------------------------
+//
+// Each function below returns the same bits as the IEEE operation it replaces
+// (the compiler's correctly rounded division / square root above) on the
+// whole domain where it is used; the GPU test suite checks this exhaustively
+// over all 2^32 binary32 inputs (and all 2^16 FP16 scales).  They cost 4-9
+// instructions instead of ~11 (division) and ~17 (square root).
+
+// RN(a/b) from the hardware reciprocal estimate and one FMA correction of
+// the quotient.  Exact for phi_m (a = 2x, b = 1+|x|, all x), phi_m^-1
+// (a = z, b = 2-|z|, |z| < 2) and the code factors 127/s, 255/s.
+__device__ __forceinline__ float div_rcp1(float a, float b) {
+    const float y = __builtin_amdgcn_rcpf(b);
+    const float q = a * y;
+    const float r = __builtin_fmaf(-b, q, a);
+    return __builtin_fmaf(r, y, q);
+}
+
+__device__ __forceinline__ float phi_m_fast(float x) {
+    const float num = 2.0f * x;
+    const float den = 1.0f + fabsf(x);
+    return div_rcp1(num, den);
+}
+
+__device__ __forceinline__ float phi_m_inv_fast(float z) {
+    const float den = 2.0f - fabsf(z);
+    return div_rcp1(z, den);
+}
+
+__device__ __forceinline__ float code_factor_fast(uint32_t s16, float qmax) {
+    const float r = div_rcp1(qmax, f16_to_f32(s16));
+    return s16 == 0u ? 0.0f : r;
+}
+
+// Square root: the hardware estimate, then the neighbour below or above when
+// the residual shows the true root is past the midpoint.  Exact for x = 0 and
+// every x >= 2^-96; sqrt_fast_bad() flags the inputs in between.
+__device__ __forceinline__ float sqrt_fast(float x) {
+    const float y = __builtin_amdgcn_sqrtf(x);
+    const float lo = as_f32(as_u32(y) - 1u);
+    const float hi = as_f32(as_u32(y) + 1u);
+    const float rl = __builtin_fmaf(-lo, y, x);
+    const float rh = __builtin_fmaf(-hi, y, x);
+    const float t = (rl <= 0.0f) ? lo : y;
+    return (rh > 0.0f) ? hi : t;
+}
+
+__device__ __forceinline__ bool sqrt_fast_bad(float x) {
+    return as_u32(x) - 1u < 0x0F7FFFFFu;          // 0 < x < 2^-96 (x >= 0)
+}
+
+// Re-split of two weights with the gfx950 BF16 convert (RNE).  For theta'
+// with exponent field E in [14, 254], 127 * 2^(135-E) is a normal binary32
+// built from the exponent bits, and (x - theta') times it is exactly
+// e * 127 (|e| <= 1, so no clamp is needed); outside that range `bad` is set.
+__device__ __forceinline__ uint32_t split2_fast(float x0, float x1, int32_t& r0, int32_t& r1,
+                                                bool& bad) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {x0, x1};
+    const uint32_t packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const uint32_t t0b = packed << 16, t1b = packed & 0xFFFF0000u;
+    const uint32_t e0 = t0b & 0x7F800000u, e1 = t1b & 0x7F800000u;
+    const float y0 = (x0 - as_f32(t0b)) * as_f32(0x867E0000u - e0);
+    const float y1 = (x1 - as_f32(t1b)) * as_f32(0x867E0000u - e1);
+    r0 = (int32_t)__builtin_rintf(y0);
+    r1 = (int32_t)__builtin_rintf(y1);
+    bad = bad || (e0 - 0x07000000u >= 0x78800000u) || (e1 - 0x07000000u >= 0x78800000u);
+    return packed;
 }
 
 // ---- the update rules (fused-step section) -----------------------------------

@@ -229,16 +229,184 @@ __device__ __forceinline__ void step_lane(const DevTensor& T, int64_t e, int lan
     }
 }
 
+// ---- whole sub-tiles: short exact sequences on the packed registers --------
+
+struct Raw {                        // one lane's packed loads of one sub-tile
+    uint4 th, gr;                   // 8 BF16 theta', 8 BF16 grads
+    uint2 rho, qm, qv;              // 8 INT8 rho, 8 INT8 momentum, 8 UINT8 variance codes
+    uint32_t ms, vs;                // the group's FP16 scales
+};
+
+template <int kOpt>
+__device__ __forceinline__ void load_raw(const DevTensor& T, int64_t e, Raw& R) {
+    const int64_t g = e >> 5;
+    R.th = *reinterpret_cast<const uint4*>(T.theta + e);
+    R.gr = *reinterpret_cast<const uint4*>(T.grad + e);
+    R.rho = *reinterpret_cast<const uint2*>(T.rho + e);
+    R.qm = *reinterpret_cast<const uint2*>(T.mq + e);
+    R.ms = T.ms[g];
+    if (kOpt == kAdamW) {
+        R.qv = *reinterpret_cast<const uint2*>(T.vq + e);
+        R.vs = T.vs[g];
+    }
+}
+
+__device__ __forceinline__ void raw_to_lane(const Raw& R, Lane8& L) {
+    unpack_bf16x8(R.th, L.th);
+    unpack_bf16x8(R.gr, L.gr);
+    unpack_s8x8(R.rho, L.rho);
+    unpack_s8x8(R.qm, L.qm);
+    unpack_u8x8(R.qv, L.qv);
+    L.ms = R.ms;
+    L.vs = R.vs;
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t word(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+
+// binary32 bits of the j-th BF16 of a lane's 8 (low half first)
+__device__ __forceinline__ uint32_t bf16_bits(const uint4& v, int j) {
+    const uint32_t w = word(v, j >> 1);
+    return (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
+}
+__device__ __forceinline__ int32_t s8(const uint2& v, int j) {
+    return (int32_t)(int8_t)(uint8_t)(word(v, j >> 2) >> (8 * (j & 3)));
+}
+__device__ __forceinline__ uint32_t u8(const uint2& v, int j) {
+    return (word(v, j >> 2) >> (8 * (j & 3))) & 0xFFu;
+}
+
+// The general sequences for one whole sub-tile, kept out of line (all
+// arguments by value) so the compiler can neither hoist them into the fast
+// path nor keep the fast path's registers in memory.
+template <int kOpt>
+__device__ __attribute__((noinline)) void step_general_full(
+    uint16_t* theta, int8_t* rho, int8_t* mq, uint16_t* ms, uint8_t* vq, uint16_t* vs,
+    int64_t e, int lane, uint4 th, uint4 gr, uint2 rh, uint2 qm, uint2 qv, uint32_t msv,
+    uint32_t vsv, AdamScalars a, SgdScalars s) {
+    DevTensor T;
+    T.theta = theta; T.rho = rho; T.mq = mq; T.ms = ms; T.vq = vq; T.vs = vs;
+    T.grad = nullptr; T.numel = e + kLaneElems;
+    Raw R;
+    R.th = th; R.gr = gr; R.rho = rh; R.qm = qm; R.qv = qv; R.ms = msv; R.vs = vsv;
+    Lane8 L;
+    raw_to_lane(R, L);
+    step_lane<kOpt, true>(T, e, lane, L, a, s);
+}
+
+template <int kOpt>
+__device__ __forceinline__ void step_fast(const DevTensor& T, int64_t e, int lane, const Raw& R,
+                                          const AdamScalars& a, const SgdScalars& s) {
+    float z[8], w[8], tn[8];
+    uint32_t amax_m = 0, amax_v = 0;
+    bool bad = false;
+    const float dm = m_step(R.ms);
+    const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float theta_hat = unsplit_bits(bf16_bits(R.th, j), s8(R.rho, j));
+        const float m = phi_m_inv_fast((float)s8(R.qm, j) * dm);
+        const float g = as_f32(bf16_bits(R.gr, j));
+        float m_new, theta_new;
+        if (kOpt == kAdamW) {
+            const float zv = (float)u8(R.qv, j) * dv;
+            const float v = zv * zv;
+            const float bm = a.b1 * m;
+            const float cg = a.c1 * g;
+            m_new = bm + cg;
+            const float bv = a.b2 * v;
+            const float gg = g * g;
+            const float cgg = a.c2 * gg;
+            const float v_new = bv + cgg;
+            const float root = sqrt_fast(v_new);
+            bad = bad || sqrt_fast_bad(v_new);
+            const float den0 = root * a.kappa;
+            const float den = den0 + a.eps;
+            const float u = m_new / den;
+            const float decayed = a.lambda * theta_hat;
+            const float stp = a.alpha * u;
+            theta_new = decayed - stp;
+            w[j] = root;
+            amax_v = max(amax_v, as_u32(root));
+        } else {
+            const float decay = s.omega * theta_hat;
+            const float g2 = g + decay;
+            const float mb = s.mu * m;
+            m_new = mb + g2;
+            const float stp = s.eta * m_new;
+            theta_new = theta_hat - stp;
+        }
+        z[j] = phi_m_fast(m_new);
+        tn[j] = theta_new;
+        amax_m = max(amax_m, as_u32(z[j]) & 0x7FFFFFFFu);
+    }
+    const uint32_t sm16 = group_scale(quad_max_u32(amax_m), 0x3FFFu);
+    const float rm = code_factor_fast(sm16, 127.0f);
+    uint32_t sv16 = 0;
+    uint32_t qv0 = 0, qv1 = 0;
+    if (kOpt == kAdamW) {
+        sv16 = group_scale(quad_max_u32(amax_v), 0x7BFFu);
+        const float rv = code_factor_fast(sv16, 255.0f);
+        // clamp(rne(w * 255/s), 0, 255), packed four per word
+        qv0 = __builtin_amdgcn_cvt_pk_u8_f32(w[0] * rv, 0, qv0);
+        qv0 = __builtin_amdgcn_cvt_pk_u8_f32(w[1] * rv, 1, qv0);
+        qv0 = __builtin_amdgcn_cvt_pk_u8_f32(w[2] * rv, 2, qv0);
+        qv0 = __builtin_amdgcn_cvt_pk_u8_f32(w[3] * rv, 3, qv0);
+        qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[4] * rv, 0, qv1);
+        qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[5] * rv, 1, qv1);
+        qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[6] * rv, 2, qv1);
+        qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[7] * rv, 3, qv1);
+    }
+    uint32_t oqm[8], orho[8], otb[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oqm[j] = (uint32_t)code_m(z[j], rm);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        int32_t r0, r1;
+        otb[p] = split2_fast(tn[2 * p], tn[2 * p + 1], r0, r1, bad);
+        orho[2 * p] = (uint32_t)r0;
+        orho[2 * p + 1] = (uint32_t)r1;
+    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        // rare inputs (tiny variance, theta' beyond the fast exponent range):
+        // the whole wave redoes this sub-tile with the general sequences
+        step_general_full<kOpt>(T.theta, T.rho, T.mq, T.ms, T.vq, T.vs, e, lane, R.th, R.gr,
+                                R.rho, R.qm, R.qv, R.ms, R.vs, a, s);
+        return;
+    }
+    const int64_t g = e >> 5;
+    *reinterpret_cast<uint4*>(T.theta + e) = make_uint4(otb[0], otb[1], otb[2], otb[3]);
+    *reinterpret_cast<uint2*>(T.rho + e) = pack_u8x8(orho);
+    *reinterpret_cast<uint2*>(T.mq + e) = pack_u8x8(oqm);
+    if (kOpt == kAdamW) *reinterpret_cast<uint2*>(T.vq + e) = make_uint2(qv0, qv1);
+    if ((lane & 3) == 0) {
+        T.ms[g] = (uint16_t)sm16;
+        if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
+    }
+}
+
 template <int kOpt, bool kFull>
 __device__ __forceinline__ void step_tile(const DevTensor& T, int64_t e0, int lane,
                                           const AdamScalars& a, const SgdScalars& s) {
-    Lane8 L[kSubTiles];
+    if (kFull) {
+        Raw R[kSubTiles];
 #pragma unroll
-    for (int k = 0; k < kSubTiles; ++k)
-        load_lane<kOpt, kFull>(T, e0 + k * kSubTile + lane * kLaneElems, L[k]);
+        for (int k = 0; k < kSubTiles; ++k)
+            load_raw<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, R[k]);
 #pragma unroll
-    for (int k = 0; k < kSubTiles; ++k)
-        step_lane<kOpt, kFull>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L[k], a, s);
+        for (int k = 0; k < kSubTiles; ++k)
+            step_fast<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k], a, s);
+    } else {
+        Lane8 L[kSubTiles];
+#pragma unroll
+        for (int k = 0; k < kSubTiles; ++k)
+            load_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, L[k]);
+#pragma unroll
+        for (int k = 0; k < kSubTiles; ++k)
+            step_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L[k], a, s);
+    }
 }
 
 template <int kOpt>

@@ -1,0 +1,91 @@
+// Exhaustive device checks of the short exactly rounded sequences in
+// compressed_adamw_state_amd/csrc/codec.hpp: on every binary32 input of the
+// domain where the fused kernel uses them, each must return the same bits as
+// the general sequence it replaces (correctly rounded division and square
+// root, the emulated BF16 round-to-nearest-even, the float clamp-and-round
+// of the variance codes).  Test infrastructure: the tests load this library
+// and read back one mismatch counter per check and per thread.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.hpp"
+
+using namespace flashopt;
+
+constexpr int kChecks = 8;
+
+__global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* example) {
+    const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t nth = (uint64_t)gridDim.x * blockDim.x;
+    uint32_t c[kChecks] = {0};
+    uint32_t ex[kChecks] = {0};
+    for (uint64_t i = tid; i < (1ull << 32); i += nth) {
+        const uint32_t bits = (uint32_t)i;
+        const float x = as_f32(bits);
+        const bool finite = (bits & 0x7F800000u) != 0x7F800000u;
+        const float ax = fabsf(x);
+        if (!finite) continue;
+        // 0: phi_m, every x with |x| <= 2^125 except -0 (a momentum is never -0)
+        if (ax <= 0x1p125f && bits != 0x80000000u && as_u32(phi_m_fast(x)) != as_u32(phi_m(x))) {
+            c[0]++; ex[0] = bits;
+        }
+        // 1: phi_m^-1, every |z| < 2 except -0
+        if (ax < 2.0f && bits != 0x80000000u &&
+            as_u32(phi_m_inv_fast(x)) != as_u32(phi_m_inv(x))) {
+            c[1]++; ex[1] = bits;
+        }
+        // 2: square root, every x >= 0 not flagged for the general path
+        if (!(bits >> 31) && !sqrt_fast_bad(x) &&
+            as_u32(sqrt_fast(x)) != as_u32(__builtin_sqrtf(x))) {
+            c[2]++; ex[2] = bits;
+        }
+        // 3: re-split of x (paired with -x), when neither is flagged
+        {
+            bool bad = false;
+            int32_t r0, r1;
+            const uint32_t packed = split2_fast(x, -x, r0, r1, bad);
+            const Split s0 = split(x), s1 = split(-x);
+            if (!bad && (packed != (s0.tb | (s1.tb << 16)) || r0 != s0.rho || r1 != s1.rho)) {
+                c[3]++; ex[3] = bits;
+            }
+            // 4: the flag is raised exactly outside theta' exponent [14, 254]
+            const uint32_t E = (s0.tb >> 7) & 0xFFu;
+            if (bad != (E < 14u || E == 255u)) { c[4]++; ex[4] = bits; }
+        }
+        // 5: variance code via the packed convert == clamp(rne(y), 0, 255), y in [0, 512]
+        if (!(bits >> 31) && x <= 512.0f) {
+            const uint32_t got = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0u) & 0xFFu;
+            if (got != code_v(x, 1.0f)) { c[5]++; ex[5] = bits; }
+        }
+        // 6: the general path is used for 0 < x < 2^-96 only
+        if (!(bits >> 31) && sqrt_fast_bad(x) != (x > 0.0f && x < 0x1p-96f)) {
+            c[6]++; ex[6] = bits;
+        }
+    }
+    for (int k = 0; k < kChecks; ++k) {
+        count[tid * kChecks + k] = c[k];
+        example[tid * kChecks + k] = ex[k];
+    }
+}
+
+// 7: per-group code factors 127/s and 255/s for every FP16 scale pattern
+__global__ void all_scales(uint32_t* bad) {
+    const uint32_t s16 = blockIdx.x * blockDim.x + threadIdx.x;    // grid covers 2^16 exactly
+    uint32_t b = 0;
+    const uint32_t mag = s16 & 0x7FFFu;
+    if (mag < 0x7C00u) {
+        if (as_u32(code_factor_fast(mag, 127.0f)) != as_u32(code_factor(mag, 127.0f))) b |= 1u;
+        if (as_u32(code_factor_fast(mag, 255.0f)) != as_u32(code_factor(mag, 255.0f))) b |= 2u;
+    }
+    bad[s16] = b;
+}
+
+extern "C" int codec_exhaustive_checks(void) { return kChecks; }
+
+extern "C" int codec_exhaustive_run(uint32_t* count, uint32_t* example, int blocks,
+                                    uint32_t* scale_bad) {
+    hipLaunchKernelGGL(all_inputs, dim3(blocks), dim3(256), 0, 0, count, example);
+    hipLaunchKernelGGL(all_scales, dim3(256), dim3(256), 0, 0, scale_bad);
+    if (hipGetLastError() != hipSuccess) return -1;
+    return hipDeviceSynchronize() == hipSuccess ? 0 : -2;
+}

@@ -1,0 +1,47 @@
+"""Exhaustive device check of the fused kernel's short exactly rounded
+sequences (tests/hip/codec_exhaustive.hip): over all 2^32 binary32 inputs
+and all 2^16 FP16 scales, each must equal the general sequence it replaces
+wherever the kernel uses it.  This is what licenses the fast path; the
+oracle parity tests then check the whole step."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+NAMES = ["phi_m", "phi_m_inverse", "sqrt", "split", "split_flag", "variance_code", "sqrt_flag", "-"]
+
+
+def _lib():
+    path = os.path.join(HERE, "hip", "libcodec_exhaustive.so")
+    if not os.path.exists(path):
+        from compressed_adamw_state_amd import build
+        build.build_test_lib()
+    return ctypes.CDLL(path)
+
+
+def test_short_sequences_match_general_sequences_on_every_input():
+    L = _lib()
+    k = L.codec_exhaustive_checks()
+    blocks = 2048
+    nth = blocks * 256
+    count = torch.zeros(nth * k, dtype=torch.int32, device="cuda")
+    example = torch.zeros(nth * k, dtype=torch.int32, device="cuda")
+    scale_bad = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    rc = L.codec_exhaustive_run(ctypes.c_void_p(count.data_ptr()),
+                                ctypes.c_void_p(example.data_ptr()), blocks,
+                                ctypes.c_void_p(scale_bad.data_ptr()))
+    assert rc == 0
+    c = count.view(nth, k).cpu().numpy().astype(np.int64).sum(axis=0)
+    ex = example.view(nth, k).cpu().numpy().view(np.uint32)
+    report = {NAMES[i]: int(c[i]) for i in range(k)}
+    print("mismatches per check:", report, flush=True)
+    for i in range(k):
+        assert c[i] == 0, (NAMES[i], int(c[i]), [hex(v) for v in ex[ex[:, i] != 0, i][:5]])
+    sb = scale_bad.cpu().numpy()
+    assert not (sb & 1).any(), "127/s differs for some FP16 scale"
+    assert not (sb & 2).any(), "255/s differs for some FP16 scale"
