@@ -29,25 +29,65 @@
 
 namespace flashopt {
 
-struct DevTensor {                  // device descriptor of one tensor (64 bytes)
-    uint16_t* theta;
-    int8_t* rho;
-    int8_t* mq;
-    uint16_t* ms;
-    uint8_t* vq;
-    uint16_t* vs;
-    const uint16_t* grad;
+#define GLOBAL __attribute__((address_space(1)))
+
+// Device descriptor of one tensor as it sits in the table and in kernel
+// arguments: plain 64-bit addresses (64 bytes per tensor).
+struct DevTensor {
+    uint64_t theta, rho, mq, ms, vq, vs, grad;
     int64_t numel;
 };
 static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 
-struct ListArgs {
-    const DevTensor* table;         // device table, or nullptr: use `one`
-    const int64_t* tile_begin;      // device [count + 1] first tile of each tensor
-    DevTensor one;
-    int32_t count;
-    int64_t total_tiles;
+// The same descriptor as global-address-space pointers: with these every
+// element access compiles to global_load / global_store (not flat), so the
+// waits only count vector memory traffic.
+struct GTensor {
+    GLOBAL uint16_t* theta;
+    GLOBAL int8_t* rho;
+    GLOBAL int8_t* mq;
+    GLOBAL uint16_t* ms;
+    GLOBAL uint8_t* vq;
+    GLOBAL uint16_t* vs;
+    const GLOBAL uint16_t* grad;
+    int64_t numel;
 };
+
+__device__ __forceinline__ GTensor view(const DevTensor& d) {
+    GTensor t;
+    t.theta = (GLOBAL uint16_t*)d.theta;
+    t.rho = (GLOBAL int8_t*)d.rho;
+    t.mq = (GLOBAL int8_t*)d.mq;
+    t.ms = (GLOBAL uint16_t*)d.ms;
+    t.vq = (GLOBAL uint8_t*)d.vq;
+    t.vs = (GLOBAL uint16_t*)d.vs;
+    t.grad = (const GLOBAL uint16_t*)d.grad;
+    t.numel = d.numel;
+    return t;
+}
+
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16- and 8-byte global accesses (clang vectors: no HIP vector-type
+// constructors, which do not take address-space-qualified references)
+__device__ __forceinline__ uint4 ld4(const GLOBAL void* p) {
+    const u32x4 v = *(const GLOBAL u32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld2(const GLOBAL void* p) {
+    const u32x2 v = *(const GLOBAL u32x2*)p;
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st4(GLOBAL void* p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    *(GLOBAL u32x4*)p = w;
+}
+__device__ __forceinline__ void st2(GLOBAL void* p, uint2 v) {
+    const u32x2 w = {v.x, v.y};
+    *(GLOBAL u32x2*)p = w;
+}
 
 enum Opt { kAdamW = 0, kSgd = 1 };
 
@@ -58,8 +98,8 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
 }
 
 // Largest i in [0, count) with tile_begin[i] <= tile (skips empty tensors).
-__device__ __forceinline__ int32_t find_tensor(const int64_t* tile_begin, int32_t count,
-                                               int64_t tile) {
+__device__ __forceinline__ int32_t find_tensor(const int64_t* __restrict__ tile_begin,
+                                               int32_t count, int64_t tile) {
     int32_t lo = 0, hi = count - 1;
     while (lo < hi) {
         int32_t mid = (lo + hi + 1) >> 1;
@@ -67,6 +107,44 @@ __device__ __forceinline__ int32_t find_tensor(const int64_t* tile_begin, int32_
     }
     return lo;
 }
+
+// Walks a wave's increasing tile indices through the tensor list: one binary
+// search for the first tile, then a forward scan (scalar loads of the small
+// tile_begin table; a wave's next tile is at most a few tensors further).
+struct TileCursor {
+    int32_t i;
+    int64_t begin, end;
+    GTensor T;
+
+    __device__ __forceinline__ void start(const DevTensor* __restrict__ table,
+                                          const int64_t* __restrict__ tile_begin, int32_t count,
+                                          const DevTensor& one, int64_t total, int64_t tile) {
+        if (table != nullptr) {
+            i = find_tensor(tile_begin, count, tile);
+            begin = tile_begin[i];
+            end = tile_begin[i + 1];
+            T = view(table[i]);
+        } else {
+            i = 0;
+            begin = 0;
+            end = total;
+            T = view(one);
+        }
+    }
+
+    // tile < total; for the single-tensor form end == total, so no advance
+    __device__ __forceinline__ void seek(const DevTensor* __restrict__ table,
+                                         const int64_t* __restrict__ tile_begin, int64_t tile) {
+        if (tile >= end) {
+            do {
+                ++i;
+                begin = end;
+                end = tile_begin[i + 1];
+            } while (tile >= end);
+            T = view(table[i]);
+        }
+    }
+};
 
 // ---- per-lane element staging ------------------------------------------------
 
@@ -108,17 +186,17 @@ __device__ __forceinline__ uint2 pack_u8x8(const uint32_t* v) {
 }
 
 template <int kOpt, bool kFull>
-__device__ __forceinline__ void load_lane(const DevTensor& T, int64_t e, Lane8& L) {
+__device__ __forceinline__ void load_lane(const GTensor& T, int64_t e, Lane8& L) {
     const int64_t n = T.numel;
     const int64_t g = e >> 5;
     if (kFull) {
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(T.theta + e), L.th);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(T.grad + e), L.gr);
-        unpack_s8x8(*reinterpret_cast<const uint2*>(T.rho + e), L.rho);
-        unpack_s8x8(*reinterpret_cast<const uint2*>(T.mq + e), L.qm);
+        unpack_bf16x8(ld4(T.theta + e), L.th);
+        unpack_bf16x8(ld4(T.grad + e), L.gr);
+        unpack_s8x8(ld2(T.rho + e), L.rho);
+        unpack_s8x8(ld2(T.mq + e), L.qm);
         L.ms = T.ms[g];
         if (kOpt == kAdamW) {
-            unpack_u8x8(*reinterpret_cast<const uint2*>(T.vq + e), L.qv);
+            unpack_u8x8(ld2(T.vq + e), L.qv);
             L.vs = T.vs[g];
         }
     } else {
@@ -140,7 +218,7 @@ __device__ __forceinline__ void load_lane(const DevTensor& T, int64_t e, Lane8& 
 // ---- the fused step on one sub-tile of one lane ----------------------------
 
 template <int kOpt, bool kFull>
-__device__ __forceinline__ void step_lane(const DevTensor& T, int64_t e, int lane,
+__device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
                                           const Lane8& L, const AdamScalars& a,
                                           const SgdScalars& s) {
     float z[8], w[8], tn[8];
@@ -203,10 +281,10 @@ __device__ __forceinline__ void step_lane(const DevTensor& T, int64_t e, int lan
     }
     const int64_t g = e >> 5;
     if (kFull) {
-        *reinterpret_cast<uint4*>(T.theta + e) = pack_u16x8(otb);
-        *reinterpret_cast<uint2*>(T.rho + e) = pack_u8x8(orho);
-        *reinterpret_cast<uint2*>(T.mq + e) = pack_u8x8(oqm);
-        if (kOpt == kAdamW) *reinterpret_cast<uint2*>(T.vq + e) = pack_u8x8(oqv);
+        st4(T.theta + e, pack_u16x8(otb));
+        st2(T.rho + e, pack_u8x8(orho));
+        st2(T.mq + e, pack_u8x8(oqm));
+        if (kOpt == kAdamW) st2(T.vq + e, pack_u8x8(oqv));
         if ((lane & 3) == 0) {
             T.ms[g] = (uint16_t)sm16;
             if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
@@ -238,15 +316,15 @@ struct Raw {                        // one lane's packed loads of one sub-tile
 };
 
 template <int kOpt>
-__device__ __forceinline__ void load_raw(const DevTensor& T, int64_t e, Raw& R) {
+__device__ __forceinline__ void load_raw(const GTensor& T, int64_t e, Raw& R) {
     const int64_t g = e >> 5;
-    R.th = *reinterpret_cast<const uint4*>(T.theta + e);
-    R.gr = *reinterpret_cast<const uint4*>(T.grad + e);
-    R.rho = *reinterpret_cast<const uint2*>(T.rho + e);
-    R.qm = *reinterpret_cast<const uint2*>(T.mq + e);
+    R.th = ld4(T.theta + e);
+    R.gr = ld4(T.grad + e);
+    R.rho = ld2(T.rho + e);
+    R.qm = ld2(T.mq + e);
     R.ms = T.ms[g];
     if (kOpt == kAdamW) {
-        R.qv = *reinterpret_cast<const uint2*>(T.vq + e);
+        R.qv = ld2(T.vq + e);
         R.vs = T.vs[g];
     }
 }
@@ -278,30 +356,11 @@ __device__ __forceinline__ uint32_t u8(const uint2& v, int j) {
     return (word(v, j >> 2) >> (8 * (j & 3))) & 0xFFu;
 }
 
-// The general sequences for one whole sub-tile, kept out of line (all
-// arguments by value) so the compiler can neither hoist them into the fast
-// path nor keep the fast path's registers in memory.
 template <int kOpt>
-__device__ __attribute__((noinline)) void step_general_full(
-    uint16_t* theta, int8_t* rho, int8_t* mq, uint16_t* ms, uint8_t* vq, uint16_t* vs,
-    int64_t e, int lane, uint4 th, uint4 gr, uint2 rh, uint2 qm, uint2 qv, uint32_t msv,
-    uint32_t vsv, AdamScalars a, SgdScalars s) {
-    DevTensor T;
-    T.theta = theta; T.rho = rho; T.mq = mq; T.ms = ms; T.vq = vq; T.vs = vs;
-    T.grad = nullptr; T.numel = e + kLaneElems;
-    Raw R;
-    R.th = th; R.gr = gr; R.rho = rh; R.qm = qm; R.qv = qv; R.ms = msv; R.vs = vsv;
-    Lane8 L;
-    raw_to_lane(R, L);
-    step_lane<kOpt, true>(T, e, lane, L, a, s);
-}
-
-template <int kOpt>
-__device__ __forceinline__ void step_fast(const DevTensor& T, int64_t e, int lane, const Raw& R,
+__device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane, const Raw& R,
                                           const AdamScalars& a, const SgdScalars& s) {
     float z[8], w[8], tn[8];
     uint32_t amax_m = 0, amax_v = 0;
-    bool bad = false;
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
 #pragma unroll
@@ -320,8 +379,9 @@ __device__ __forceinline__ void step_fast(const DevTensor& T, int64_t e, int lan
             const float gg = g * g;
             const float cgg = a.c2 * gg;
             const float v_new = bv + cgg;
-            const float root = sqrt_fast(v_new);
-            bad = bad || sqrt_fast_bad(v_new);
+            float root = sqrt_fast(v_new);
+            if (__builtin_expect(sqrt_fast_bad(v_new), 0))
+                root = __builtin_sqrtf(v_new);       // 0 < v' < 2^-96: IEEE square root
             const float den0 = root * a.kappa;
             const float den = den0 + a.eps;
             const float u = m_new / den;
@@ -365,22 +425,23 @@ __device__ __forceinline__ void step_fast(const DevTensor& T, int64_t e, int lan
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         int32_t r0, r1;
+        bool bad = false;
         otb[p] = split2_fast(tn[2 * p], tn[2 * p + 1], r0, r1, bad);
+        if (__builtin_expect(bad, 0)) {
+            // theta' exponent outside [14, 254] (tiny, zero or non-finite): general split
+            const Split s0 = split(tn[2 * p]), s1 = split(tn[2 * p + 1]);
+            otb[p] = s0.tb | (s1.tb << 16);
+            r0 = s0.rho;
+            r1 = s1.rho;
+        }
         orho[2 * p] = (uint32_t)r0;
         orho[2 * p + 1] = (uint32_t)r1;
     }
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-        // rare inputs (tiny variance, theta' beyond the fast exponent range):
-        // the whole wave redoes this sub-tile with the general sequences
-        step_general_full<kOpt>(T.theta, T.rho, T.mq, T.ms, T.vq, T.vs, e, lane, R.th, R.gr,
-                                R.rho, R.qm, R.qv, R.ms, R.vs, a, s);
-        return;
-    }
     const int64_t g = e >> 5;
-    *reinterpret_cast<uint4*>(T.theta + e) = make_uint4(otb[0], otb[1], otb[2], otb[3]);
-    *reinterpret_cast<uint2*>(T.rho + e) = pack_u8x8(orho);
-    *reinterpret_cast<uint2*>(T.mq + e) = pack_u8x8(oqm);
-    if (kOpt == kAdamW) *reinterpret_cast<uint2*>(T.vq + e) = make_uint2(qv0, qv1);
+    st4(T.theta + e, make_uint4(otb[0], otb[1], otb[2], otb[3]));
+    st2(T.rho + e, pack_u8x8(orho));
+    st2(T.mq + e, pack_u8x8(oqm));
+    if (kOpt == kAdamW) st2(T.vq + e, make_uint2(qv0, qv1));
     if ((lane & 3) == 0) {
         T.ms[g] = (uint16_t)sm16;
         if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
@@ -388,7 +449,7 @@ __device__ __forceinline__ void step_fast(const DevTensor& T, int64_t e, int lan
 }
 
 template <int kOpt, bool kFull>
-__device__ __forceinline__ void step_tile(const DevTensor& T, int64_t e0, int lane,
+__device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane,
                                           const AdamScalars& a, const SgdScalars& s) {
     if (kFull) {
         Raw R[kSubTiles];
@@ -410,23 +471,21 @@ __device__ __forceinline__ void step_tile(const DevTensor& T, int64_t e0, int la
 }
 
 template <int kOpt>
-__global__ __launch_bounds__(256) void step_kernel(ListArgs A, AdamScalars a, SgdScalars s) {
+__global__ __launch_bounds__(256) void step_kernel(const DevTensor* __restrict__ table,
+                                                   const int64_t* __restrict__ tile_begin,
+                                                   int32_t count, int64_t total_tiles,
+                                                   DevTensor one, AdamScalars a, SgdScalars s) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-    for (int64_t tile = wave; tile < A.total_tiles; tile += nwaves) {
-        DevTensor T;
-        int64_t local = tile;
-        if (A.table != nullptr) {
-            const int32_t i = find_tensor(A.tile_begin, A.count, tile);
-            T = A.table[i];
-            local = tile - A.tile_begin[i];
-        } else {
-            T = A.one;
-        }
-        const int64_t e0 = local * kTile;
-        if (e0 + kTile <= T.numel) step_tile<kOpt, true>(T, e0, lane, a, s);
-        else step_tile<kOpt, false>(T, e0, lane, a, s);
+    if (wave >= total_tiles) return;
+    TileCursor cur;
+    cur.start(table, tile_begin, count, one, total_tiles, wave);
+    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+        cur.seek(table, tile_begin, tile);
+        const int64_t e0 = (tile - cur.begin) * kTile;
+        if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true>(cur.T, e0, lane, a, s);
+        else step_tile<kOpt, false>(cur.T, e0, lane, a, s);
     }
 }
 
@@ -580,14 +639,19 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* q, const
 // ---- list maintenance kernels ----------------------------------------------
 
 // Zero codes and scales of a list, one tile per wave iteration.
-__global__ __launch_bounds__(256) void zero_kernel(ListArgs A) {
+__global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__ table,
+                                                   const int64_t* __restrict__ tile_begin,
+                                                   int32_t count, int64_t total_tiles) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
-    for (int64_t tile = wave; tile < A.total_tiles; tile += nwaves) {
-        const int32_t i = find_tensor(A.tile_begin, A.count, tile);
-        const DevTensor T = A.table[i];
-        const int64_t e0 = (tile - A.tile_begin[i]) * kTile;
+    if (wave >= total_tiles) return;
+    TileCursor cur;
+    cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
+    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+        cur.seek(table, tile_begin, tile);
+        const GTensor& T = cur.T;
+        const int64_t e0 = (tile - cur.begin) * kTile;
         for (int k = 0; k < kSubTiles; ++k) {
             const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
             for (int j = 0; j < 8; ++j) {
@@ -612,7 +676,7 @@ struct GradBatch {
 
 __global__ void set_grads_kernel(DevTensor* table, GradBatch b) {
     const int i = threadIdx.x;
-    if (i < b.count) table[b.first + i].grad = b.ptr[i];
+    if (i < b.count) table[b.first + i].grad = (uint64_t)b.ptr[i];
 }
 
 // ---- host side -------------------------------------------------------------
@@ -715,8 +779,9 @@ static int check_tensor(const flashopt_tensor& t) {
 
 static DevTensor to_dev(const flashopt_tensor& t) {
     DevTensor d;
-    d.theta = t.theta; d.rho = t.rho; d.mq = t.m_code; d.ms = t.m_scale;
-    d.vq = t.v_code; d.vs = t.v_scale; d.grad = t.grad; d.numel = t.numel;
+    d.theta = (uint64_t)t.theta; d.rho = (uint64_t)t.rho; d.mq = (uint64_t)t.m_code;
+    d.ms = (uint64_t)t.m_scale; d.vq = (uint64_t)t.v_code; d.vs = (uint64_t)t.v_scale;
+    d.grad = (uint64_t)t.grad; d.numel = t.numel;
     return d;
 }
 
@@ -921,51 +986,39 @@ int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void
 int flashopt_state_zero(const flashopt_list* L, void* stream) {
     if (!L) return FLASHOPT_ERR_NULL;
     if (L->total_tiles == 0) return FLASHOPT_OK;
-    ListArgs A{};
-    A.table = L->d_table;
-    A.tile_begin = L->d_tile_begin;
-    A.count = L->count;
-    A.total_tiles = L->total_tiles;
     hipLaunchKernelGGL(zero_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                       (hipStream_t)stream, A);
+                       (hipStream_t)stream, (const DevTensor*)L->d_table,
+                       (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+    return launch_status();
+}
+
+static int launch_step(int opt, const DevTensor* table, const int64_t* tile_begin, int32_t count,
+                       int64_t total_tiles, const DevTensor& one, const AdamScalars& a,
+                       const SgdScalars& s, void* stream) {
+    if (total_tiles == 0) return FLASHOPT_OK;
+    const dim3 grid(grid_for(total_tiles));
+    if (opt == kAdamW)
+        hipLaunchKernelGGL(step_kernel<kAdamW>, grid, dim3(kBlock), 0, (hipStream_t)stream, table,
+                           tile_begin, count, total_tiles, one, a, s);
+    else
+        hipLaunchKernelGGL(step_kernel<kSgd>, grid, dim3(kBlock), 0, (hipStream_t)stream, table,
+                           tile_begin, count, total_tiles, one, a, s);
     return launch_status();
 }
 
 static int launch_list(int opt, const flashopt_list* L, const AdamScalars& a,
                        const SgdScalars& s, void* stream) {
-    if (L->total_tiles == 0) return FLASHOPT_OK;
-    ListArgs A{};
-    A.table = L->d_table;
-    A.tile_begin = L->d_tile_begin;
-    A.count = L->count;
-    A.total_tiles = L->total_tiles;
-    if (opt == kAdamW)
-        hipLaunchKernelGGL(step_kernel<kAdamW>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                           (hipStream_t)stream, A, a, s);
-    else
-        hipLaunchKernelGGL(step_kernel<kSgd>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                           (hipStream_t)stream, A, a, s);
-    return launch_status();
+    return launch_step(opt, L->d_table, L->d_tile_begin, L->count, L->total_tiles, DevTensor{},
+                       a, s, stream);
 }
 
 static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint16_t* grad,
                       const AdamScalars& a, const SgdScalars& s, void* stream) {
     const flashopt_tensor& t = L->host[index];
     if (t.numel == 0) return FLASHOPT_OK;
-    ListArgs A{};
-    A.table = nullptr;
-    A.tile_begin = nullptr;
-    A.one = to_dev(t);
-    A.one.grad = grad;
-    A.count = 1;
-    A.total_tiles = tiles_of(t.numel);
-    if (opt == kAdamW)
-        hipLaunchKernelGGL(step_kernel<kAdamW>, dim3(grid_for(A.total_tiles)), dim3(kBlock), 0,
-                           (hipStream_t)stream, A, a, s);
-    else
-        hipLaunchKernelGGL(step_kernel<kSgd>, dim3(grid_for(A.total_tiles)), dim3(kBlock), 0,
-                           (hipStream_t)stream, A, a, s);
-    return launch_status();
+    DevTensor one = to_dev(t);
+    one.grad = (uint64_t)grad;
+    return launch_step(opt, nullptr, nullptr, 1, tiles_of(t.numel), one, a, s, stream);
 }
 
 int flashopt_adamw_step(const flashopt_list* L, const flashopt_adamw_hparams* hp, int64_t step,
