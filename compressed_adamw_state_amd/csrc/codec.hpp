@@ -222,21 +222,25 @@ __device__ __forceinline__ bool sqrt_fast_bad(float x) {
 }
 
 // Re-split of two weights with the gfx950 BF16 convert (RNE).  For theta'
-// with exponent field E in [14, 254], 127 * 2^(135-E) is a normal binary32
-// built from the exponent bits, and (x - theta') times it is exactly
-// e * 127 (|e| <= 1, so no clamp is needed); outside that range `bad` is set.
-__device__ __forceinline__ uint32_t split2_fast(float x0, float x1, int32_t& r0, int32_t& r1,
-                                                bool& bad) {
+// with exponent field E in [14, 254], F = 127 * 2^(135-E) is a normal binary32
+// built from the exponent bits, and (x - theta') * F is exactly e * 127 with
+// |e| <= 1 (no clamp needed); adding 128 is exact too, so one FMA gives
+// e*127 + 128 without rounding, and the packed u8 convert rounds it to
+// nearest even: that byte is rho + 128 (the caller flips bit 7 of each byte).
+// Returns the packed BF16 pair, writes the two biased codes into bytes
+// `byte` and `byte + 1` of `codes`, and sets `bad` outside that exponent range.
+template <int kByte>
+__device__ __forceinline__ uint32_t split2_fast(float x0, float x1, uint32_t& codes, bool& bad) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const f32x2 v = {x0, x1};
     const uint32_t packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
     const uint32_t t0b = packed << 16, t1b = packed & 0xFFFF0000u;
     const uint32_t e0 = t0b & 0x7F800000u, e1 = t1b & 0x7F800000u;
-    const float y0 = (x0 - as_f32(t0b)) * as_f32(0x867E0000u - e0);
-    const float y1 = (x1 - as_f32(t1b)) * as_f32(0x867E0000u - e1);
-    r0 = (int32_t)__builtin_rintf(y0);
-    r1 = (int32_t)__builtin_rintf(y1);
+    const float y0 = __builtin_fmaf(x0 - as_f32(t0b), as_f32(0x867E0000u - e0), 128.0f);
+    const float y1 = __builtin_fmaf(x1 - as_f32(t1b), as_f32(0x867E0000u - e1), 128.0f);
+    codes = __builtin_amdgcn_cvt_pk_u8_f32(y0, kByte, codes);
+    codes = __builtin_amdgcn_cvt_pk_u8_f32(y1, kByte + 1, codes);
     bad = bad || (e0 - 0x07000000u >= 0x78800000u) || (e1 - 0x07000000u >= 0x78800000u);
     return packed;
 }

@@ -360,7 +360,8 @@ template <int kOpt>
 __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane, const Raw& R,
                                           const AdamScalars& a, const SgdScalars& s) {
     float z[8], w[8], tn[8];
-    uint32_t amax_m = 0, amax_v = 0;
+    float amax_m = 0.0f, amax_v = 0.0f;    // group max of |z| and of w (float max == integer
+                                           // max of the bit patterns for finite values)
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
 #pragma unroll
@@ -389,7 +390,7 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
             const float stp = a.alpha * u;
             theta_new = decayed - stp;
             w[j] = root;
-            amax_v = max(amax_v, as_u32(root));
+            amax_v = fmaxf(amax_v, root);
         } else {
             const float decay = s.omega * theta_hat;
             const float g2 = g + decay;
@@ -400,14 +401,14 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
         }
         z[j] = phi_m_fast(m_new);
         tn[j] = theta_new;
-        amax_m = max(amax_m, as_u32(z[j]) & 0x7FFFFFFFu);
+        amax_m = fmaxf(amax_m, fabsf(z[j]));
     }
-    const uint32_t sm16 = group_scale(quad_max_u32(amax_m), 0x3FFFu);
+    const uint32_t sm16 = group_scale(quad_max_u32(as_u32(amax_m)), 0x3FFFu);
     const float rm = code_factor_fast(sm16, 127.0f);
     uint32_t sv16 = 0;
     uint32_t qv0 = 0, qv1 = 0;
     if (kOpt == kAdamW) {
-        sv16 = group_scale(quad_max_u32(amax_v), 0x7BFFu);
+        sv16 = group_scale(quad_max_u32(as_u32(amax_v)), 0x7BFFu);
         const float rv = code_factor_fast(sv16, 255.0f);
         // clamp(rne(w * 255/s), 0, 255), packed four per word
         qv0 = __builtin_amdgcn_cvt_pk_u8_f32(w[0] * rv, 0, qv0);
@@ -419,27 +420,31 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
         qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[6] * rv, 2, qv1);
         qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[7] * rv, 3, qv1);
     }
-    uint32_t oqm[8], orho[8], otb[4];
+    uint32_t oqm[8], otb[4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) oqm[j] = (uint32_t)code_m(z[j], rm);
+    uint32_t rc[2] = {0u, 0u};                      // rho + 128, four per word
+    bool bad[4] = {false, false, false, false};
+    otb[0] = split2_fast<0>(tn[0], tn[1], rc[0], bad[0]);
+    otb[1] = split2_fast<2>(tn[2], tn[3], rc[0], bad[1]);
+    otb[2] = split2_fast<0>(tn[4], tn[5], rc[1], bad[2]);
+    otb[3] = split2_fast<2>(tn[6], tn[7], rc[1], bad[3]);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        int32_t r0, r1;
-        bool bad = false;
-        otb[p] = split2_fast(tn[2 * p], tn[2 * p + 1], r0, r1, bad);
-        if (__builtin_expect(bad, 0)) {
+        if (__builtin_expect(bad[p], 0)) {
             // theta' exponent outside [14, 254] (tiny, zero or non-finite): general split
             const Split s0 = split(tn[2 * p]), s1 = split(tn[2 * p + 1]);
             otb[p] = s0.tb | (s1.tb << 16);
-            r0 = s0.rho;
-            r1 = s1.rho;
+            const int sh = 16 * (p & 1);
+            const uint32_t pair = ((uint32_t)(s0.rho + 128) & 0xFFu) |
+                                  (((uint32_t)(s1.rho + 128) & 0xFFu) << 8);
+            rc[p >> 1] = (rc[p >> 1] & ~(0xFFFFu << sh)) | (pair << sh);
         }
-        orho[2 * p] = (uint32_t)r0;
-        orho[2 * p + 1] = (uint32_t)r1;
     }
+    const uint2 orho = make_uint2(rc[0] ^ 0x80808080u, rc[1] ^ 0x80808080u);
     const int64_t g = e >> 5;
     st4(T.theta + e, make_uint4(otb[0], otb[1], otb[2], otb[3]));
-    st2(T.rho + e, pack_u8x8(orho));
+    st2(T.rho + e, orho);
     st2(T.mq + e, pack_u8x8(oqm));
     if (kOpt == kAdamW) st2(T.vq + e, make_uint2(qv0, qv1));
     if ((lane & 3) == 0) {

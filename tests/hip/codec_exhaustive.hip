@@ -42,10 +42,13 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
         // 3: re-split of x (paired with -x), when neither is flagged
         {
             bool bad = false;
-            int32_t r0, r1;
-            const uint32_t packed = split2_fast(x, -x, r0, r1, bad);
+            uint32_t codes = 0x5A5A5A5Au;                 // bytes 0, 1 must be overwritten
+            const uint32_t packed = split2_fast<0>(x, -x, codes, bad);
             const Split s0 = split(x), s1 = split(-x);
-            if (!bad && (packed != (s0.tb | (s1.tb << 16)) || r0 != s0.rho || r1 != s1.rho)) {
+            const int32_t r0 = (int32_t)(int8_t)(uint8_t)((codes ^ 0x80u) & 0xFFu);
+            const int32_t r1 = (int32_t)(int8_t)(uint8_t)(((codes >> 8) ^ 0x80u) & 0xFFu);
+            if (!bad && (packed != (s0.tb | (s1.tb << 16)) || r0 != s0.rho || r1 != s1.rho ||
+                         (codes >> 16) != 0x5A5Au)) {
                 c[3]++; ex[3] = bits;
             }
             // 4: the flag is raised exactly outside theta' exponent [14, 254]
