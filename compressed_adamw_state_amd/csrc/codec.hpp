@@ -227,10 +227,12 @@ __device__ __forceinline__ bool sqrt_fast_bad(float x) {
 // |e| <= 1 (no clamp needed); adding 128 is exact too, so one FMA gives
 // e*127 + 128 without rounding, and the packed u8 convert rounds it to
 // nearest even: that byte is rho + 128 (the caller flips bit 7 of each byte).
-// Returns the packed BF16 pair, writes the two biased codes into bytes
-// `byte` and `byte + 1` of `codes`, and sets `bad` outside that exponent range.
+// Returns the packed BF16 pair, writes the two biased codes into bytes kByte
+// and kByte + 1 of `codes`, and folds the two exponent fields into emin/emax;
+// the results are exact when split_fast_ok(emin, emax) holds.
 template <int kByte>
-__device__ __forceinline__ uint32_t split2_fast(float x0, float x1, uint32_t& codes, bool& bad) {
+__device__ __forceinline__ uint32_t split2_fast(float x0, float x1, uint32_t& codes,
+                                                uint32_t& emin, uint32_t& emax) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const f32x2 v = {x0, x1};
@@ -241,8 +243,23 @@ __device__ __forceinline__ uint32_t split2_fast(float x0, float x1, uint32_t& co
     const float y1 = __builtin_fmaf(x1 - as_f32(t1b), as_f32(0x867E0000u - e1), 128.0f);
     codes = __builtin_amdgcn_cvt_pk_u8_f32(y0, kByte, codes);
     codes = __builtin_amdgcn_cvt_pk_u8_f32(y1, kByte + 1, codes);
-    bad = bad || (e0 - 0x07000000u >= 0x78800000u) || (e1 - 0x07000000u >= 0x78800000u);
+    emin = min(emin, min(e0, e1));
+    emax = max(emax, max(e0, e1));
     return packed;
+}
+
+__device__ __forceinline__ bool split_fast_ok(uint32_t emin, uint32_t emax) {
+    return emin >= 0x07000000u && emax <= 0x7F000000u;    // E in [14, 254]
+}
+
+// Momentum code clamp(rne(z * r), -127, 127) as the low byte of the result:
+// clamping first is the same (rounding is monotone, +-127 are integers), and
+// adding 1.5 * 2^23 rounds to nearest even, leaving the integer in the low
+// mantissa bits (two's complement in the low byte).
+__device__ __forceinline__ uint32_t code_m_bits(float z, float r) {
+    const float y = z * r;
+    const float c = __builtin_amdgcn_fmed3f(y, -127.0f, 127.0f);
+    return as_u32(c + 12582912.0f);
 }
 
 // ---- the update rules (fused-step section) -----------------------------------

@@ -356,51 +356,68 @@ __device__ __forceinline__ uint32_t u8(const uint2& v, int j) {
     return (word(v, j >> 2) >> (8 * (j & 3))) & 0xFFu;
 }
 
+// low bytes of four words, packed into one word
+__device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);     // a0 b0 0 0
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);     // c0 d0 0 0
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);                 // a0 b0 c0 d0
+}
+
 template <int kOpt>
 __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane, const Raw& R,
                                           const AdamScalars& a, const SgdScalars& s) {
-    float z[8], w[8], tn[8];
-    float amax_m = 0.0f, amax_v = 0.0f;    // group max of |z| and of w (float max == integer
-                                           // max of the bit patterns for finite values)
+    float z[8], w[8], tn[8], m_new[8], v_new[8], theta_hat[8];
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
+    uint32_t vmin = 0xFFFFFFFFu;           // min over (bits(v') - 1): flags 0 < v' < 2^-96
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float theta_hat = unsplit_bits(bf16_bits(R.th, j), s8(R.rho, j));
+        theta_hat[j] = unsplit_bits(bf16_bits(R.th, j), s8(R.rho, j));
         const float m = phi_m_inv_fast((float)s8(R.qm, j) * dm);
         const float g = as_f32(bf16_bits(R.gr, j));
-        float m_new, theta_new;
         if (kOpt == kAdamW) {
             const float zv = (float)u8(R.qv, j) * dv;
             const float v = zv * zv;
             const float bm = a.b1 * m;
             const float cg = a.c1 * g;
-            m_new = bm + cg;
+            m_new[j] = bm + cg;
             const float bv = a.b2 * v;
             const float gg = g * g;
             const float cgg = a.c2 * gg;
-            const float v_new = bv + cgg;
-            float root = sqrt_fast(v_new);
-            if (__builtin_expect(sqrt_fast_bad(v_new), 0))
-                root = __builtin_sqrtf(v_new);       // 0 < v' < 2^-96: IEEE square root
-            const float den0 = root * a.kappa;
-            const float den = den0 + a.eps;
-            const float u = m_new / den;
-            const float decayed = a.lambda * theta_hat;
-            const float stp = a.alpha * u;
-            theta_new = decayed - stp;
-            w[j] = root;
-            amax_v = fmaxf(amax_v, root);
+            v_new[j] = bv + cgg;
+            w[j] = sqrt_fast(v_new[j]);
+            vmin = min(vmin, as_u32(v_new[j]) - 1u);
         } else {
-            const float decay = s.omega * theta_hat;
+            const float decay = s.omega * theta_hat[j];
             const float g2 = g + decay;
             const float mb = s.mu * m;
-            m_new = mb + g2;
-            const float stp = s.eta * m_new;
-            theta_new = theta_hat - stp;
+            m_new[j] = mb + g2;
+            const float stp = s.eta * m_new[j];
+            tn[j] = theta_hat[j] - stp;
         }
-        z[j] = phi_m_fast(m_new);
-        tn[j] = theta_new;
+    }
+    if (kOpt == kAdamW) {
+        if (__builtin_expect(vmin < 0x0F7FFFFFu, 0)) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)                 // 0 < v' < 2^-96: IEEE square root
+                if (sqrt_fast_bad(v_new[j])) w[j] = __builtin_sqrtf(v_new[j]);
+        }
+    }
+    // group maxima of |z| and w as floats (== the integer max of the bit patterns
+    // for every finite value)
+    float amax_m = 0.0f, amax_v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (kOpt == kAdamW) {
+            const float den0 = w[j] * a.kappa;
+            const float den = den0 + a.eps;
+            const float u = m_new[j] / den;
+            const float decayed = a.lambda * theta_hat[j];
+            const float stp = a.alpha * u;
+            tn[j] = decayed - stp;
+            amax_v = fmaxf(amax_v, w[j]);
+        }
+        z[j] = phi_m_fast(m_new[j]);
         amax_m = fmaxf(amax_m, fabsf(z[j]));
     }
     const uint32_t sm16 = group_scale(quad_max_u32(as_u32(amax_m)), 0x3FFFu);
@@ -420,19 +437,22 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
         qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[6] * rv, 2, qv1);
         qv1 = __builtin_amdgcn_cvt_pk_u8_f32(w[7] * rv, 3, qv1);
     }
-    uint32_t oqm[8], otb[4];
+    uint32_t mb[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) oqm[j] = (uint32_t)code_m(z[j], rm);
+    for (int j = 0; j < 8; ++j) mb[j] = code_m_bits(z[j], rm);
+    const uint2 oqm = make_uint2(pack_lo_bytes(mb[0], mb[1], mb[2], mb[3]),
+                                 pack_lo_bytes(mb[4], mb[5], mb[6], mb[7]));
+    uint32_t otb[4];
     uint32_t rc[2] = {0u, 0u};                      // rho + 128, four per word
-    bool bad[4] = {false, false, false, false};
-    otb[0] = split2_fast<0>(tn[0], tn[1], rc[0], bad[0]);
-    otb[1] = split2_fast<2>(tn[2], tn[3], rc[0], bad[1]);
-    otb[2] = split2_fast<0>(tn[4], tn[5], rc[1], bad[2]);
-    otb[3] = split2_fast<2>(tn[6], tn[7], rc[1], bad[3]);
+    uint32_t emin = 0xFFFFFFFFu, emax = 0u;         // exponent fields of the new theta'
+    otb[0] = split2_fast<0>(tn[0], tn[1], rc[0], emin, emax);
+    otb[1] = split2_fast<2>(tn[2], tn[3], rc[0], emin, emax);
+    otb[2] = split2_fast<0>(tn[4], tn[5], rc[1], emin, emax);
+    otb[3] = split2_fast<2>(tn[6], tn[7], rc[1], emin, emax);
+    if (__builtin_expect(!split_fast_ok(emin, emax), 0)) {
+        // some theta' exponent outside [14, 254] (tiny, zero or non-finite): general split
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        if (__builtin_expect(bad[p], 0)) {
-            // theta' exponent outside [14, 254] (tiny, zero or non-finite): general split
+        for (int p = 0; p < 4; ++p) {
             const Split s0 = split(tn[2 * p]), s1 = split(tn[2 * p + 1]);
             otb[p] = s0.tb | (s1.tb << 16);
             const int sh = 16 * (p & 1);
@@ -445,7 +465,7 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     const int64_t g = e >> 5;
     st4(T.theta + e, make_uint4(otb[0], otb[1], otb[2], otb[3]));
     st2(T.rho + e, orho);
-    st2(T.mq + e, pack_u8x8(oqm));
+    st2(T.mq + e, oqm);
     if (kOpt == kAdamW) st2(T.vq + e, make_uint2(qv0, qv1));
     if ((lane & 3) == 0) {
         T.ms[g] = (uint16_t)sm16;

@@ -39,11 +39,12 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
             as_u32(sqrt_fast(x)) != as_u32(__builtin_sqrtf(x))) {
             c[2]++; ex[2] = bits;
         }
-        // 3: re-split of x (paired with -x), when neither is flagged
+        // 3: re-split of x (paired with -x), when the exponent range is fast
         {
-            bool bad = false;
             uint32_t codes = 0x5A5A5A5Au;                 // bytes 0, 1 must be overwritten
-            const uint32_t packed = split2_fast<0>(x, -x, codes, bad);
+            uint32_t emin = 0xFFFFFFFFu, emax = 0u;
+            const uint32_t packed = split2_fast<0>(x, -x, codes, emin, emax);
+            const bool bad = !split_fast_ok(emin, emax);
             const Split s0 = split(x), s1 = split(-x);
             const int32_t r0 = (int32_t)(int8_t)(uint8_t)((codes ^ 0x80u) & 0xFFu);
             const int32_t r1 = (int32_t)(int8_t)(uint8_t)(((codes >> 8) ^ 0x80u) & 0xFFu);
@@ -60,6 +61,10 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
             const uint32_t got = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0u) & 0xFFu;
             if (got != code_v(x, 1.0f)) { c[5]++; ex[5] = bits; }
         }
+        // 7: momentum code from the rounding add == clamp(rne(y), +-127), y in [-1000, 1000]
+        if (ax <= 1000.0f && (code_m_bits(x, 1.0f) & 0xFFu) != ((uint32_t)code_m(x, 1.0f) & 0xFFu)) {
+            c[7]++; ex[7] = bits;
+        }
         // 6: the general path is used for 0 < x < 2^-96 only
         if (!(bits >> 31) && sqrt_fast_bad(x) != (x > 0.0f && x < 0x1p-96f)) {
             c[6]++; ex[6] = bits;
@@ -71,7 +76,7 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
     }
 }
 
-// 7: per-group code factors 127/s and 255/s for every FP16 scale pattern
+// per-group code factors 127/s and 255/s for every FP16 scale pattern
 __global__ void all_scales(uint32_t* bad) {
     const uint32_t s16 = blockIdx.x * blockDim.x + threadIdx.x;    // grid covers 2^16 exactly
     uint32_t b = 0;

@@ -13,7 +13,8 @@ import torch
 pytestmark = pytest.mark.gpu
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-NAMES = ["phi_m", "phi_m_inverse", "sqrt", "split", "split_flag", "variance_code", "sqrt_flag", "-"]
+NAMES = ["phi_m", "phi_m_inverse", "sqrt", "split", "split_flag", "variance_code", "sqrt_flag",
+         "momentum_code"]
 
 
 def _lib():
