@@ -708,26 +708,15 @@ __global__ void set_grads_kernel(DevTensor* table, GradBatch b) {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kBlocksPerCU = 8;
-
-static int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cu <= 0)
-            cu = 256;
-        cached[dev] = cu;
-    }
-    return cached[dev];
-}
+// One wave per work item (tile or chunk) up to kMaxBlocks blocks; the kernels
+// fall back to a wave-stride loop beyond that.  Many short-lived waves let the
+// dispatcher refill a CU the moment one finishes, which keeps every SIMD busy
+// to the end of the launch (a fixed resident grid left a tail of idle SIMDs).
+constexpr int64_t kMaxBlocks = int64_t(1) << 23;    // 2^31 threads
 
 static unsigned grid_for(int64_t wave_items) {
     int64_t blocks = (wave_items + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = (int64_t)cu_count() * kBlocksPerCU;
-    if (blocks > cap) blocks = cap;
+    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     if (blocks < 1) blocks = 1;
     return (unsigned)blocks;
 }
