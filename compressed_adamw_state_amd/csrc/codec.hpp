@@ -262,9 +262,58 @@ __device__ __forceinline__ uint32_t code_m_bits(float z, float r) {
     return as_u32(c + 12582912.0f);
 }
 
+// RN(1/b) for every positive normal b whose reciprocal is normal: the
+// hardware estimate refined by one Newton step.
+__device__ __forceinline__ float rcp_rn(float b) {
+    const float y = __builtin_amdgcn_rcpf(b);
+    const float e = __builtin_fmaf(-b, y, 1.0f);
+    return __builtin_fmaf(e, y, y);
+}
+
+// RN(a/b) from r = RN(1/b) by Markstein's correction: q0 = RN(a*r), the
+// residual a - b*q0 in one FMA, then RN(q0 + residual*r).  Exact whenever
+// nothing leaves the normal range: b and 1/b normal, the residual
+// representable (e(b) + e(q0) >= -103) and 2^-125 <= |q0| < 2^126.  The
+// caller bounds e(b) from below, turns that into a window [2^L, 2^126) for
+// |q0|, and tests quot_key(q0) < span, a single unsigned compare.
+__device__ __forceinline__ float div_rn(float a, float b, float r, float& q0) {
+    q0 = a * r;
+    const float res = __builtin_fmaf(-b, q0, a);
+    return __builtin_fmaf(res, r, q0);
+}
+
+// 2|q0| - 2^(L+1) as bit patterns (mod 2^32); below span = 2(bits(2^126) -
+// bits(2^L)) exactly when |q0| is in [2^L, 2^126).  neg_lo2 = -2 bits(2^L).
+__device__ __forceinline__ uint32_t quot_key(float q0, uint32_t neg_lo2) {
+    return (as_u32(q0) << 1) + neg_lo2;
+}
+
+// The window for the Adam quotient u = m' / (w*kappa + eps): the denominator
+// is at least eps and below 2^92 (w < 2^64, kappa <= 2^27) or not finite, so
+// with e(b) >= e(eps) the residual is exact once e(q0) >= -103 - e(eps):
+// L = max(-125, -103 - e(eps)).  eps subnormal or >= 2^100 gives span 0
+// (every element takes the IEEE division).
+__host__ __device__ inline void quot_window(float eps, uint32_t& neg_lo2, uint32_t& span) {
+    const uint32_t eb = (__builtin_bit_cast(uint32_t, eps) >> 23) & 0xFFu;
+    neg_lo2 = 0u;
+    span = 0u;
+    if (eb >= 1u && eb <= 127u + 99u) {
+        int L = -103 - ((int)eb - 127);
+        if (L < -125) L = -125;
+        const uint32_t lo = (uint32_t)(L + 127) << 23, hi = (uint32_t)(126 + 127) << 23;
+        neg_lo2 = 0u - 2u * lo;
+        span = 2u * (hi - lo);
+    }
+}
+
 // ---- the update rules (fused-step section) -----------------------------------
 
-struct AdamScalars { float b1, c1, b2, c2, alpha, kappa, eps, lambda; };
+// quot_neg_lo2 / quot_span: the fast-quotient window for u = m' / (w*kappa +
+// eps) (see div_rn); span 0 sends every element to the IEEE division.
+struct AdamScalars {
+    float b1, c1, b2, c2, alpha, kappa, eps, lambda;
+    uint32_t quot_neg_lo2, quot_span;
+};
 struct SgdScalars { float mu, eta, omega; };
 
 }  // namespace flashopt

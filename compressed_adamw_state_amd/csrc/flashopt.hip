@@ -406,17 +406,37 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     // group maxima of |z| and w as floats (== the integer max of the bit patterns
     // for every finite value)
     float amax_m = 0.0f, amax_v = 0.0f;
+    if (kOpt == kAdamW) {
+        // u = m' / (w*kappa + eps) by div_rn; a lane with any quotient outside
+        // the window redoes its eight with the IEEE division
+        float u[8];
+        uint32_t qkey = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (kOpt == kAdamW) {
+        for (int j = 0; j < 8; ++j) {
             const float den0 = w[j] * a.kappa;
             const float den = den0 + a.eps;
-            const float u = m_new[j] / den;
+            float q0;
+            u[j] = div_rn(m_new[j], den, rcp_rn(den), q0);
+            qkey = max(qkey, quot_key(q0, a.quot_neg_lo2));
+        }
+        if (__builtin_expect(qkey >= a.quot_span, 0)) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float den0 = w[j] * a.kappa;
+                const float den = den0 + a.eps;
+                u[j] = m_new[j] / den;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
             const float decayed = a.lambda * theta_hat[j];
-            const float stp = a.alpha * u;
+            const float stp = a.alpha * u[j];
             tn[j] = decayed - stp;
             amax_v = fmaxf(amax_v, w[j]);
         }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
         z[j] = phi_m_fast(m_new[j]);
         amax_m = fmaxf(amax_m, fabsf(z[j]));
     }
@@ -756,6 +776,7 @@ static AdamScalars adam_scalars(const flashopt_adamw_hparams& hp, int64_t t, dou
     a.kappa = (float)(1.0 / std::sqrt(1.0 - p2));
     a.eps = (float)hp.eps;
     a.lambda = (float)(1.0 - hp.lr * hp.weight_decay);
+    quot_window(a.eps, a.quot_neg_lo2, a.quot_span);
     return a;
 }
 

@@ -4,7 +4,9 @@
 // the general sequence it replaces (correctly rounded division and square
 // root, the emulated BF16 round-to-nearest-even, the float clamp-and-round
 // of the variance codes).  Test infrastructure: the tests load this library
-// and read back one mismatch counter per check and per thread.
+// and read back one mismatch counter per check and per thread.  A second
+// kernel checks the Adam quotient sequence (div_rn) against the IEEE division
+// on every pair of significands.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -12,7 +14,7 @@
 
 using namespace flashopt;
 
-constexpr int kChecks = 8;
+constexpr int kChecks = 10;
 
 __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* example) {
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -65,6 +67,31 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
         if (ax <= 1000.0f && (code_m_bits(x, 1.0f) & 0xFFu) != ((uint32_t)code_m(x, 1.0f) & 0xFFu)) {
             c[7]++; ex[7] = bits;
         }
+        // 8: Newton-refined reciprocal == RN(1/x) for every x in [2^-126, 2^126)
+        if (!(bits >> 31) && bits >= 0x00800000u && bits < 0x7E800000u &&
+            as_u32(rcp_rn(x)) != as_u32(1.0f / x)) {
+            c[8]++; ex[8] = bits;
+        }
+        // 9: Adam quotient x / b inside the window of a pseudo-random eps, with
+        //    b >= eps of any exponent up to 2^100 (plus Inf), against IEEE
+        {
+            uint32_t h = bits * 0x9E3779B1u;
+            h ^= h >> 15; h *= 0x85EBCA77u; h ^= h >> 13;
+            const uint32_t ee = 1u + (h & 0xFFu) % 226u;             // eps exponent field
+            const float eps = as_f32((ee << 23) | ((h >> 8) & 0x7FFFFFu));
+            uint32_t neg_lo2, span;
+            quot_window(eps, neg_lo2, span);
+            uint32_t h2 = h * 0xC2B2AE35u; h2 ^= h2 >> 16;
+            const uint32_t be = ee + (h2 & 0xFFu) % (227u - ee);      // up to 2^100
+            float b = as_f32((be << 23) | ((h2 * 0x27D4EB2Fu) >> 9));
+            if (b < eps) b = eps;
+            if ((h2 >> 24) == 0u) b = __builtin_inff();
+            float q0;
+            const float q = div_rn(x, b, rcp_rn(b), q0);
+            if (quot_key(q0, neg_lo2) < span && as_u32(q) != as_u32(x / b)) {
+                c[9]++; ex[9] = bits;
+            }
+        }
         // 6: the general path is used for 0 < x < 2^-96 only
         if (!(bits >> 31) && sqrt_fast_bad(x) != (x > 0.0f && x < 0x1p-96f)) {
             c[6]++; ex[6] = bits;
@@ -88,7 +115,33 @@ __global__ void all_scales(uint32_t* bad) {
     bad[s16] = b;
 }
 
+// div_rn(a, b) == a / b for every pair of significands: b = 1.j (one thread
+// per j, 2^23 threads) and a = 1.i for i in [i0, i0 + n).  Both operations
+// scale exactly by powers of two while the window conditions hold, so this
+// covers every exponent inside the window.
+__global__ void __launch_bounds__(256) all_quotients(uint32_t i0, uint32_t n, uint32_t* bad) {
+    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;      // grid covers 2^23 exactly
+    const float b = as_f32(0x3F800000u | j);
+    const float r = rcp_rn(b);
+    uint32_t c = 0;
+    for (uint32_t i = i0; i < i0 + n; ++i) {
+        const float a = as_f32(0x3F800000u | i);
+        float q0;
+        c += as_u32(div_rn(a, b, r, q0)) != as_u32(a / b);
+    }
+    bad[j] += c;
+}
+
 extern "C" int codec_exhaustive_checks(void) { return kChecks; }
+
+// one slice of the significand pairs: a = 1.i for i in [i0, i0 + n), n > 0,
+// i0 + n <= 2^23; bad has 2^23 counters (accumulated)
+extern "C" int codec_quotient_slice(uint32_t i0, uint32_t n, uint32_t* bad) {
+    if (n == 0 || i0 + n > (1u << 23)) return -3;
+    hipLaunchKernelGGL(all_quotients, dim3((1u << 23) / 256), dim3(256), 0, 0, i0, n, bad);
+    if (hipGetLastError() != hipSuccess) return -1;
+    return hipDeviceSynchronize() == hipSuccess ? 0 : -2;
+}
 
 extern "C" int codec_exhaustive_run(uint32_t* count, uint32_t* example, int blocks,
                                     uint32_t* scale_bad) {

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 NAMES = ["phi_m", "phi_m_inverse", "sqrt", "split", "split_flag", "variance_code", "sqrt_flag",
-         "momentum_code"]
+         "momentum_code", "reciprocal", "quotient_window"]
 
 
 def _lib():
@@ -46,3 +46,17 @@ def test_short_sequences_match_general_sequences_on_every_input():
     sb = scale_bad.cpu().numpy()
     assert not (sb & 1).any(), "127/s differs for some FP16 scale"
     assert not (sb & 2).any(), "255/s differs for some FP16 scale"
+
+
+def test_adam_quotient_on_every_significand_pair():
+    # div_rn against the IEEE division for all 2^46 pairs (a, b) in [1, 2)^2,
+    # in 16 slices of 2^19 numerators
+    L = _lib()
+    bad = torch.zeros(1 << 23, dtype=torch.int32, device="cuda")
+    for k in range(16):
+        rc = L.codec_quotient_slice(ctypes.c_uint32(k << 19), ctypes.c_uint32(1 << 19),
+                                    ctypes.c_void_p(bad.data_ptr()))
+        assert rc == 0
+        print(f"quotient slice {k}: {int(bad.sum())} mismatches so far", flush=True)
+    b = bad.cpu().numpy()
+    assert not b.any(), [hex(0x3F800000 | int(j)) for j in np.nonzero(b)[0][:5]]

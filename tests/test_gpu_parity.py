@@ -169,6 +169,21 @@ def test_hyperparameter_variants():
     r.compare("t=1000")
 
 
+@pytest.mark.parametrize("grad_scale", [1e-4, 1e18, 1e-38])
+def test_adam_quotient_window_edges(grad_scale):
+    # zeros, subnormal and outlier gradients (1e18: squares overflow, so some
+    # denominators are Inf; 1e-38: quotients far below the fast window) under
+    # eps values that move the window (1e-30 narrows it, 1e-40 is subnormal in
+    # binary32 and closes it, 1e3 is large)
+    base = W.ragged([4097, 1000, 33], seed=15, steps=1)
+    w = W.Workload("quotient_edges", base.tensors, "adamw", 4, 15, "mixed", grad_scale,
+                   W.ADAMW_HP, special_theta=True)
+    r = Run(w, "full")
+    for t, eps in enumerate([1e-8, 1e-30, 1e-40, 1e3], 1):
+        r.step(t, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=eps, weight_decay=0.01))
+        r.compare(f"grad scale {grad_scale}, eps {eps}")
+
+
 def test_set_grads_and_state_zero():
     w = W.ragged([3000, 70], seed=14, steps=2)
     r = Run(w, "full")
