@@ -81,6 +81,21 @@ __device__ __forceinline__ float unsplit_bits(uint32_t tbits, int32_t rho) {
     return t + d;
 }
 
+// The same rebuild as one FMA: (rho*K8*2^-8) * 2^(E-127) is a power-of-two
+// scaling of the first product, exact when the clamped field E is at least 16
+// (|rho| >= 1 makes the first product at least 2^-15), so fma rounds once to
+// the same t + d.  Folds E into emin; the caller redoes the lane with
+// unsplit_bits() when emin < 16.
+__device__ __forceinline__ float unsplit_fma(uint32_t tbits, int32_t rho, uint32_t& emin) {
+    const float t = as_f32(tbits);
+    const uint32_t e = min(max(tbits & 0x7F800000u, 0x00800000u), 0x7F000000u);
+    emin = min(emin, e);
+    const float c = (float)rho * as_f32(kK8Bits - 0x04000000u);   // K8 * 2^-8
+    return __builtin_fmaf(c, as_f32(e), t);
+}
+
+__device__ __forceinline__ bool unsplit_fma_ok(uint32_t emin) { return emin >= (16u << 23); }
+
 __device__ __forceinline__ float unsplit(uint32_t tb, int32_t rho) {
     return unsplit_bits(tb << 16, rho);
 }
@@ -136,10 +151,12 @@ __device__ __forceinline__ float dequant_v(uint32_t q, float d) {
 // ---- group maximum over a quad of lanes (DPP quad_perm) --------------------
 
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t a) {
-    // quad_perm [1,0,3,2] then [2,3,0,1]; every lane of the quad ends with the max
-    uint32_t b = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false);
+    // quad_perm [1,0,3,2] then [2,3,0,1]; every lane of the quad ends with the
+    // max.  The DPP moves take 0 (the identity of the max) as the old value, so
+    // each step compiles to a single v_max_u32 with a DPP source.
+    uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);
     a = max(a, b);
-    b = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false);
+    b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false);
     return max(a, b);
 }
 
@@ -192,6 +209,17 @@ __device__ __forceinline__ float phi_m_fast(float x) {
     const float num = 2.0f * x;
     const float den = 1.0f + fabsf(x);
     return div_rcp1(num, den);
+}
+
+// phi_m(x) / 2 = x / (1+|x|) by the same sequence: every step of phi_m_fast
+// scaled by 1/2, so 2 * phi_m_half_fast(x) == phi_m(x) wherever the halved
+// value is normal (|phi_m(x)| >= 2^-125).  Below that both are too small to
+// move a code or a scale (codes round |z| * 127/s < 2^-94 to 0; the FP16 scale
+// of a group maximum below 2^-25 is 0).  The fused step keeps z/2 and folds
+// the factor 2 into the group maximum and the code factor 254/s.
+__device__ __forceinline__ float phi_m_half_fast(float x) {
+    const float den = 1.0f + fabsf(x);
+    return div_rcp1(x, den);
 }
 
 __device__ __forceinline__ float phi_m_inv_fast(float z) {

@@ -370,9 +370,15 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
     uint32_t vmin = 0xFFFFFFFFu;           // min over (bits(v') - 1): flags 0 < v' < 2^-96
+    uint32_t tmin = 0xFFFFFFFFu;           // min clamped exponent field of theta'
+#pragma unroll
+    for (int j = 0; j < 8; ++j) theta_hat[j] = unsplit_fma(bf16_bits(R.th, j), s8(R.rho, j), tmin);
+    if (__builtin_expect(!unsplit_fma_ok(tmin), 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) theta_hat[j] = unsplit_bits(bf16_bits(R.th, j), s8(R.rho, j));
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        theta_hat[j] = unsplit_bits(bf16_bits(R.th, j), s8(R.rho, j));
         const float m = phi_m_inv_fast((float)s8(R.qm, j) * dm);
         const float g = as_f32(bf16_bits(R.gr, j));
         if (kOpt == kAdamW) {
@@ -437,11 +443,12 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        z[j] = phi_m_fast(m_new[j]);
+        z[j] = phi_m_half_fast(m_new[j]);             // phi_m(m') / 2
         amax_m = fmaxf(amax_m, fabsf(z[j]));
     }
-    const uint32_t sm16 = group_scale(quad_max_u32(as_u32(amax_m)), 0x3FFFu);
-    const float rm = code_factor_fast(sm16, 127.0f);
+    const uint32_t sm16 =
+        group_scale(as_u32(2.0f * as_f32(quad_max_u32(as_u32(amax_m)))), 0x3FFFu);
+    const float rm = code_factor_fast(sm16, 254.0f);   // 2 * 127/s, exactly
     uint32_t sv16 = 0;
     uint32_t qv0 = 0, qv1 = 0;
     if (kOpt == kAdamW) {

@@ -14,7 +14,7 @@
 
 using namespace flashopt;
 
-constexpr int kChecks = 10;
+constexpr int kChecks = 12;
 
 __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* example) {
     const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -92,6 +92,27 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
                 c[9]++; ex[9] = bits;
             }
         }
+        // 10: halved phi_m: 2 * phi_m_half_fast(x) == phi_m(x) where |phi_m(x)| >= 2^-125,
+        //     and below that the halved value stays below 2^-125 too
+        if (ax <= 0x1p125f && bits != 0x80000000u) {
+            const float z = phi_m(x), h = phi_m_half_fast(x);
+            if (fabsf(z) >= 0x1p-125f ? as_u32(2.0f * h) != as_u32(z) : !(fabsf(h) < 0x1p-125f)) {
+                c[10]++; ex[10] = bits;
+            }
+        }
+        // 11: unsplit as one FMA == unsplit_bits for every BF16 theta' and code
+        //     byte (first 2^24 inputs: theta' = bits >> 8, rho = low byte), when
+        //     the flag allows it; the flag is raised exactly for fields below 16
+        if (bits < (1u << 24)) {
+            const uint32_t tbits = (bits >> 8) << 16;
+            const int32_t rho = (int32_t)(int8_t)(uint8_t)(bits & 0xFFu);
+            uint32_t emin = 0xFFFFFFFFu;
+            const float f = unsplit_fma(tbits, rho, emin);
+            const float g = unsplit_bits(tbits, rho);
+            const uint32_t E = (tbits >> 23) & 0xFFu;
+            const bool ok = unsplit_fma_ok(emin);
+            if ((ok && as_u32(f) != as_u32(g)) || ok != (E >= 16u)) { c[11]++; ex[11] = bits; }
+        }
         // 6: the general path is used for 0 < x < 2^-96 only
         if (!(bits >> 31) && sqrt_fast_bad(x) != (x > 0.0f && x < 0x1p-96f)) {
             c[6]++; ex[6] = bits;
@@ -111,6 +132,8 @@ __global__ void all_scales(uint32_t* bad) {
     if (mag < 0x7C00u) {
         if (as_u32(code_factor_fast(mag, 127.0f)) != as_u32(code_factor(mag, 127.0f))) b |= 1u;
         if (as_u32(code_factor_fast(mag, 255.0f)) != as_u32(code_factor(mag, 255.0f))) b |= 2u;
+        if (as_u32(code_factor_fast(mag, 254.0f)) != as_u32(2.0f * code_factor(mag, 127.0f)))
+            b |= 4u;
     }
     bad[s16] = b;
 }

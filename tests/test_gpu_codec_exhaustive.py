@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 NAMES = ["phi_m", "phi_m_inverse", "sqrt", "split", "split_flag", "variance_code", "sqrt_flag",
-         "momentum_code", "reciprocal", "quotient_window"]
+         "momentum_code", "reciprocal", "quotient_window", "phi_m_half", "unsplit_fma"]
 
 
 def _lib():
@@ -46,6 +46,7 @@ def test_short_sequences_match_general_sequences_on_every_input():
     sb = scale_bad.cpu().numpy()
     assert not (sb & 1).any(), "127/s differs for some FP16 scale"
     assert not (sb & 2).any(), "255/s differs for some FP16 scale"
+    assert not (sb & 4).any(), "254/s is not 2 * 127/s for some FP16 scale"
 
 
 def test_adam_quotient_on_every_significand_pair():
