@@ -23,8 +23,8 @@ constexpr int kGroup = 32;
 constexpr int kWave = 64;
 constexpr int kLaneElems = 8;                       // elements per lane per sub-tile
 constexpr int kSubTile = kWave * kLaneElems;        // 512 elements
-constexpr int kSubTiles = 2;
-constexpr int kTile = kSubTile * kSubTiles;         // 1024 elements per wave
+constexpr int kSubTiles = 4;
+constexpr int kTile = kSubTile * kSubTiles;         // 2048 elements per wave
 
 // RN(1/127) and RN(1/255) as bit patterns.
 constexpr uint32_t kK8Bits = 0x3C010204u;

@@ -500,25 +500,29 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     }
 }
 
+// A full tile streams its sub-tiles through two register buffers: the loads
+// of sub-tile k+2 are issued as soon as sub-tile k is done, so one sub-tile's
+// loads are always in flight behind the arithmetic.  The partial last tile of
+// a tensor goes one bounds-checked sub-tile at a time.
 template <int kOpt, bool kFull>
 __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane,
                                           const AdamScalars& a, const SgdScalars& s) {
     if (kFull) {
-        Raw R[kSubTiles];
+        Raw R[2];
+        load_raw<kOpt>(T, e0 + lane * kLaneElems, R[0]);
+        if (kSubTiles > 1) load_raw<kOpt>(T, e0 + kSubTile + lane * kLaneElems, R[1]);
 #pragma unroll
-        for (int k = 0; k < kSubTiles; ++k)
-            load_raw<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, R[k]);
-#pragma unroll
-        for (int k = 0; k < kSubTiles; ++k)
-            step_fast<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k], a, s);
+        for (int k = 0; k < kSubTiles; ++k) {
+            step_fast<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1], a, s);
+            if (k + 2 < kSubTiles)
+                load_raw<kOpt>(T, e0 + (k + 2) * kSubTile + lane * kLaneElems, R[k & 1]);
+        }
     } else {
-        Lane8 L[kSubTiles];
-#pragma unroll
-        for (int k = 0; k < kSubTiles; ++k)
-            load_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, L[k]);
-#pragma unroll
-        for (int k = 0; k < kSubTiles; ++k)
-            step_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L[k], a, s);
+        for (int k = 0; k < kSubTiles; ++k) {
+            Lane8 L;
+            load_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, L);
+            step_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, a, s);
+        }
     }
 }
 

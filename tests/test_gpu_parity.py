@@ -1,6 +1,6 @@
 """GPU parity: the HIP kernels (through the C ABI) against the CPU oracle,
 bit for bit on every BF16 / INT8 / UINT8 code and FP16 scale, and on the
-rebuilt FP32 weights.  Sizes span several 1024-element tiles and ragged tails;
+rebuilt FP32 weights.  Sizes span several 2048-element tiles and ragged tails;
 the five workloads run at full size, the large ones compared on sampled groups
 in the same launch configuration the benchmark times."""
 import numpy as np
@@ -15,7 +15,7 @@ from parity import Run, i8, log, u16, u8
 
 pytestmark = pytest.mark.gpu
 
-RAGGED = [1, 31, 32, 33, 511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2048, 2049, 4097, 6143, 32 * 777 + 5,
+RAGGED = [1, 31, 32, 33, 511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4097, 6143, 32 * 777 + 5,
           (1 << 20) + 7, 0, 64]
 
 
