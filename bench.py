@@ -62,20 +62,18 @@ def algorithmic_bytes(w: W.Workload) -> int:
     return total
 
 
-def read_traffic(workload: str, kernel_hash: str, bytes_per_launch: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_adamw_{workload}.txt")
+def read_profile(kind: str, workload: str, kernel_hash: str) -> dict:
+    """key: value lines of a committed rocprofv3 summary (profiles/), if it was
+    taken on the current kernel source; else {}."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_adamw_{workload}.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != kernel_hash or "hbm_bytes_per_launch" not in kv:
-        return None
-    return float(kv["hbm_bytes_per_launch"])
+    return kv if kv.get("source_sha256_16") == kernel_hash else {}
 
 
 def build_state(w: W.Workload, grad_sets: int):
@@ -116,6 +114,49 @@ def copy_ceiling(nbytes: int, stream, reps: int = 5):
             "best_ms": best * 1e3, "gb_s": 8 * n / best / 1e9}
 
 
+def stream_probe(lst, stream, bytes_step: int, reps: int = 5):
+    """The step's exact loads and stores with no arithmetic (flashopt_stream_probe):
+    the practical floor of its access pattern.  Overwrites the state."""
+    F.flashopt_stream_probe(lst, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        F.flashopt_stream_probe(lst, stream)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    best = min(ev[r].elapsed_time(ev[r + 1]) for r in range(reps)) / 1e3
+    return {"kernel": "probe_kernel (flashopt_stream_probe)", "best_ms": best * 1e3,
+            "gb_s": bytes_step / best / 1e9}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_single_thread_flat1m(seconds: float = 3.0) -> float:
+    """One-thread oracle params/s on the flat 1M-parameter AdamW workload."""
+    import oracle
+    w = W.WORKLOADS["flat1m"]
+    n = w.numel
+    st = oracle.State(W.draw_theta(w, 0).numpy(), "adamw")
+    grads = [W.draw_grad(w, 0, t).view(torch.int16).numpy().view(np.uint16) for t in (1, 2)]
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step(st, grads[steps % 2], steps + 1, w.hparams)
+        steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n * steps / (time.perf_counter() - t0)
+
+
 def cpu_baseline(seconds: float, threads: int):
     """The oracle as it stands, on a bounded sample of the workload: a
     2^25-parameter group-aligned slice with the Llama workload's
@@ -139,7 +180,9 @@ def cpu_baseline(seconds: float, threads: int):
     dt = time.perf_counter() - t0
     return {"value": n * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} AdamW steps over a {n}-parameter slice (Llama-3.1-8B "
-                      f"distributions), {threads} threads, {dt:.1f} s"}
+                      f"distributions), {threads} threads, {dt:.1f} s",
+            "cpu_model": cpu_model(),
+            "single_thread_flat1m_params_s": cpu_single_thread_flat1m()}
 
 
 def main():
@@ -173,10 +216,16 @@ def main():
     stream = torch.cuda.current_stream()
 
     t = 0
-    for _ in range(args.warmup):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k in range(args.warmup):
         t += 1
+        if k == 0:
+            e0.record(stream)
         F.flashopt_adamw_step(lists[t % 2], hp, t, stream)
+        if k == 0:
+            e1.record(stream)
     torch.cuda.synchronize()
+    step1_ms = e0.elapsed_time(e1) if args.warmup > 0 else None
     log(f"bench: {args.warmup} warmup steps done")
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -199,7 +248,10 @@ def main():
     avg = total / args.steps
     achieved = bytes_step / avg / 1e9
     khash = source_hash()
-    traffic = read_traffic(w.name, khash, bytes_step)
+    traffic_kv = read_profile("traffic", w.name, khash)
+    traffic = float(traffic_kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in traffic_kv \
+        else None
+    sq = read_profile("sq", w.name, khash)
     out = {
         "metric": METRIC,
         "value": nparams * args.steps / wall,
@@ -222,13 +274,21 @@ def main():
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBS,
         "step_ms_median": float(np.median(per) * 1e3),
         "step_ms_min": float(per.min() * 1e3),
+        "step1_ms": step1_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel": KERNEL,
                      "algorithmic_bytes_per_launch": bytes_step,
-                     "avg_launch_ms": avg * 1e3, "source_sha256_16": khash},
+                     "avg_launch_ms": avg * 1e3, "source_sha256_16": khash,
+                     "valu_instructions_per_param":
+                         float(sq["valu_instructions_per_param"]) if sq else None,
+                     "valu_busy": (float(sq["valu_time_ms_at_measured_clock"]) /
+                                   float(sq["kernel_time_ms"])) if sq else None},
         "cpu_baseline": None,
     }
+    out["stream_probe"] = stream_probe(lists[0], stream, bytes_step)
+    out["stream_probe"]["step_over_probe"] = avg * 1e3 / out["stream_probe"]["best_ms"]
+    log(f"bench: stream probe {out['stream_probe']['gb_s']:.0f} GB/s")
     del states, grads, lists
     torch.cuda.synchronize()
     if args.copy_bytes:

@@ -26,6 +26,7 @@
 
 #include "codec.hpp"
 #include "flashopt.h"
+#include "flashopt_probe.h"
 
 namespace flashopt {
 
@@ -724,6 +725,72 @@ __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__
     }
 }
 
+// ---- bandwidth probe ---------------------------------------------------------
+//
+// The AdamW step's memory traffic with the arithmetic taken out: the same
+// tiles, launch shape, loads (with the same two-buffer pipeline) and stores,
+// and one XOR per word in place of the update (theta' ^= g, rho ^= q_m,
+// q_m ^= q_v, q_v ^= rho, scales ^= 1).  Its time is the practical floor of
+// the step's access pattern on this device.
+__device__ __forceinline__ void probe_sub(const GTensor& T, int64_t e, int lane, const Raw& R) {
+    st4(T.theta + e, make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
+                                R.th.w ^ R.gr.w));
+    st2(T.rho + e, make_uint2(R.rho.x ^ R.qm.x, R.rho.y ^ R.qm.y));
+    st2(T.mq + e, make_uint2(R.qm.x ^ R.qv.x, R.qm.y ^ R.qv.y));
+    st2(T.vq + e, make_uint2(R.qv.x ^ R.rho.x, R.qv.y ^ R.rho.y));
+    if ((lane & 3) == 0) {
+        T.ms[e >> 5] = (uint16_t)(R.ms ^ 1u);
+        T.vs[e >> 5] = (uint16_t)(R.vs ^ 1u);
+    }
+}
+
+__global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict__ table,
+                                                    const int64_t* __restrict__ tile_begin,
+                                                    int32_t count, int64_t total_tiles) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    if (wave >= total_tiles) return;
+    TileCursor cur;
+    cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
+    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+        cur.seek(table, tile_begin, tile);
+        const GTensor& T = cur.T;
+        const int64_t e0 = (tile - cur.begin) * kTile;
+        if (e0 + kTile <= T.numel) {
+            Raw R[2];
+            load_raw<kAdamW>(T, e0 + lane * kLaneElems, R[0]);
+            if (kSubTiles > 1) load_raw<kAdamW>(T, e0 + kSubTile + lane * kLaneElems, R[1]);
+#pragma unroll
+            for (int k = 0; k < kSubTiles; ++k) {
+                probe_sub(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1]);
+                if (k + 2 < kSubTiles)
+                    load_raw<kAdamW>(T, e0 + (k + 2) * kSubTile + lane * kLaneElems, R[k & 1]);
+            }
+        } else {
+            for (int k = 0; k < kSubTiles; ++k) {
+                const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t i = e + j;
+                    if (i < T.numel) {
+                        const uint16_t th = T.theta[i], gr = T.grad[i];
+                        const int8_t rho = T.rho[i], qm = T.mq[i];
+                        const uint8_t qv = T.vq[i];
+                        T.theta[i] = (uint16_t)(th ^ gr);
+                        T.rho[i] = (int8_t)(rho ^ qm);
+                        T.mq[i] = (int8_t)(qm ^ (int8_t)qv);
+                        T.vq[i] = (uint8_t)(qv ^ (uint8_t)rho);
+                    }
+                }
+                if ((lane & 3) == 0 && e < T.numel) {
+                    T.ms[e >> 5] = (uint16_t)(T.ms[e >> 5] ^ 1u);
+                    T.vs[e >> 5] = (uint16_t)(T.vs[e >> 5] ^ 1u);
+                }
+            }
+        }
+    }
+}
+
 constexpr int kGradBatch = 200;
 struct GradBatch {
     int32_t first, count;
@@ -1033,6 +1100,17 @@ int flashopt_state_zero(const flashopt_list* L, void* stream) {
     if (!L) return FLASHOPT_ERR_NULL;
     if (L->total_tiles == 0) return FLASHOPT_OK;
     hipLaunchKernelGGL(zero_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
+                       (hipStream_t)stream, (const DevTensor*)L->d_table,
+                       (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+    return launch_status();
+}
+
+int flashopt_stream_probe(const flashopt_list* L, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (!L->all_have_v) return FLASHOPT_ERR_ARG;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    if (L->total_tiles == 0) return FLASHOPT_OK;
+    hipLaunchKernelGGL(probe_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
                        (hipStream_t)stream, (const DevTensor*)L->d_table,
                        (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
     return launch_status();

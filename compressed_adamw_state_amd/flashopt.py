@@ -67,6 +67,7 @@ SIGNATURES = {
                                                _I64, _P]),
     "flashopt_sgd_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(SGDHparams), _I64,
                                              _P]),
+    "flashopt_stream_probe": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None
@@ -208,6 +209,13 @@ def flashopt_list_set_grads(lst: FlashoptList, grads: Sequence[Optional[torch.Te
 
 def flashopt_state_zero(lst: FlashoptList, stream=None) -> None:
     _check("flashopt_state_zero", lib().flashopt_state_zero(lst.handle, _stream(stream)))
+
+
+def flashopt_stream_probe(lst: FlashoptList, stream=None) -> None:
+    """Bandwidth probe (include/flashopt_probe.h): the AdamW step's exact
+    loads and stores with one XOR per word instead of the update.  Overwrites
+    the state."""
+    _check("flashopt_stream_probe", lib().flashopt_stream_probe(lst.handle, _stream(stream)))
 
 
 def _adam(hp: dict) -> AdamWHparams:

@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol include/flashopt.h declares,
+"""The C-ABI library loads, exports every symbol include/*.h declares,
 and validates arguments on the host (no GPU call is made by these tests:
 every case fails validation before any HIP call)."""
 import ctypes
@@ -13,9 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "flashopt.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(flashopt_\w+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(flashopt_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -63,6 +67,7 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_create(neg, 1, ws, need, None, ctypes.byref(out)) == -2
     hp = F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
     assert lib.flashopt_adamw_step(None, ctypes.byref(hp), 1, None) == -1
+    assert lib.flashopt_stream_probe(None, None) == -1
     # an empty list is created without touching the device
     assert lib.flashopt_list_create(None, 0, None, 0, None, ctypes.byref(out)) == 0
     L = out
