@@ -232,17 +232,16 @@ __device__ __forceinline__ float code_factor_fast(uint32_t s16, float qmax) {
     return s16 == 0u ? 0.0f : r;
 }
 
-// Square root: the hardware estimate, then the neighbour below or above when
-// the residual shows the true root is past the midpoint.  Exact for x = 0 and
-// every x >= 2^-96; sqrt_fast_bad() flags the inputs in between.
+// Square root from the hardware reciprocal square root: q = rsq(x), g = x*q,
+// the residual x - g*g in one FMA, and the correction g + residual*(q/2) in
+// one more.  Exact for x = 0 (the max keeps q finite) and for every finite
+// x >= 2^-96; sqrt_fast_bad() flags the inputs in between, and Inf or NaN x
+// give NaN (the fused step's quotient guard catches those lanes).
 __device__ __forceinline__ float sqrt_fast(float x) {
-    const float y = __builtin_amdgcn_sqrtf(x);
-    const float lo = as_f32(as_u32(y) - 1u);
-    const float hi = as_f32(as_u32(y) + 1u);
-    const float rl = __builtin_fmaf(-lo, y, x);
-    const float rh = __builtin_fmaf(-hi, y, x);
-    const float t = (rl <= 0.0f) ? lo : y;
-    return (rh > 0.0f) ? hi : t;
+    const float q = __builtin_amdgcn_rsqf(fmaxf(x, 0x1p-96f));
+    const float g = x * q;
+    const float d = __builtin_fmaf(-g, g, x);
+    return __builtin_fmaf(d, 0.5f * q, g);
 }
 
 __device__ __forceinline__ bool sqrt_fast_bad(float x) {

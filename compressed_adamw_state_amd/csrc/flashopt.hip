@@ -427,8 +427,10 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
             qkey = max(qkey, quot_key(q0, a.quot_neg_lo2));
         }
         if (__builtin_expect(qkey >= a.quot_span, 0)) {
+            // also where v' is Inf or NaN: sqrt_fast returned NaN there
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
+                w[j] = __builtin_sqrtf(v_new[j]);
                 const float den0 = w[j] * a.kappa;
                 const float den = den0 + a.eps;
                 u[j] = m_new[j] / den;

@@ -26,7 +26,13 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
         const float x = as_f32(bits);
         const bool finite = (bits & 0x7F800000u) != 0x7F800000u;
         const float ax = fabsf(x);
-        if (!finite) continue;
+        if (!finite) {
+            // 2: the square root turns +Inf and every NaN into NaN (caught by the step's guard)
+            if ((!(bits >> 31) || (bits & 0x007FFFFFu)) && !__builtin_isnan(sqrt_fast(x))) {
+                c[2]++; ex[2] = bits;
+            }
+            continue;
+        }
         // 0: phi_m, every x with |x| <= 2^125 except -0 (a momentum is never -0)
         if (ax <= 0x1p125f && bits != 0x80000000u && as_u32(phi_m_fast(x)) != as_u32(phi_m(x))) {
             c[0]++; ex[0] = bits;
