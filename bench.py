@@ -82,7 +82,7 @@ def build_state(w: W.Workload, grad_sets: int):
     for i, spec in enumerate(w.tensors):
         theta = W.draw_theta(w, i, dev)
         st = F.TensorState(spec.numel, w.optimizer, dev)
-        F.flashopt_split(theta, st.theta, st.rho)
+        F.flashopt_tensor_init(st, theta)
         del theta
         states.append(st)
     grads = []
@@ -268,7 +268,7 @@ def main():
         "config": {"workload": f"{w.name}: Llama-3.1-8B-shaped list, {len(w.tensors)} tensors, "
                                f"{nparams} params, AdamW lr 1e-3 betas (0.9, 0.999) eps 1e-8 "
                                f"wd 0.01, bf16 grads N(0, 1e-4)",
-                   "state": "theta' bf16 + rho int8 + m int8 + v uint8 + fp16 scale per 32",
+                   "state": "theta' bf16 + 24-byte code records (rho, m, v per 8 elements) + fp16 scale pair per 32",
                    "launches_per_step": 1},
         "hbm_gb_s": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBS,

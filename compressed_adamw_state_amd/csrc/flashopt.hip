@@ -7,15 +7,17 @@
 //
 // Design (MI355X): the step is an elementwise read-modify-write stream with a
 // 32-element group reduction, bound by HBM bandwidth (12.25 bytes per
-// parameter for AdamW).  One launch covers a whole ragged tensor list.  Each
-// wavefront walks 2048-element tiles (grid-stride); a tile never crosses a
-// tensor boundary, and the tile -> tensor lookup is a scalar binary search
-// over per-tensor tile offsets kept in a small device table.  Within a tile,
-// lane l owns 8 consecutive elements of each 512-element sub-tile, so every
-// load is a fully coalesced 16-byte (BF16) or 8-byte (INT8) vector access,
-// and a quantisation group is one quad of lanes reduced with DPP.  Whole
-// tiles take an unguarded vector path; the last tile of a tensor takes a
-// guarded element-wise path.
+// parameter for AdamW).  One launch covers a whole ragged tensor list, one
+// wavefront per 2048-element tile; a tile never crosses a tensor boundary,
+// and the tile -> tensor lookup is a scalar binary search over per-tensor
+// tile offsets kept in a small device table.  Within a tile, lane l owns 8
+// consecutive elements of each 512-element sub-tile: one 16-byte BF16 load
+// each for theta' and the gradient, and one 8-element code record (rho, m
+// and v codes interleaved, so the state is one stream rather than three) read
+// as three 8-byte loads; a quantisation group is one quad of lanes reduced
+// with DPP, its two FP16 scales one 32-bit word.  Whole tiles take an
+// unguarded vector path; the last tile of a tensor takes a guarded
+// element-wise path.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -32,11 +34,23 @@ namespace flashopt {
 
 #define GLOBAL __attribute__((address_space(1)))
 
+enum Opt { kAdamW = 0, kSgd = 1 };
+
+// State layout of one tensor (see include/flashopt.h): a code record per 8
+// elements -- rho[8], m_code[8] and, for AdamW, v_code[8] -- and per 32-element
+// group the FP16 m scale followed, for AdamW, by the v scale.
+template <int kOpt> struct Layout {
+    static constexpr int kRec = kOpt == kAdamW ? 24 : 16;   // bytes per 8-element record
+    static constexpr int kScl = kOpt == kAdamW ? 2 : 1;     // FP16 scales per group
+};
+constexpr int kRhoOff = 0, kMOff = 8, kVOff = 16;          // field offsets in a record
+
 // Device descriptor of one tensor as it sits in the table and in kernel
 // arguments: plain 64-bit addresses (64 bytes per tensor).
 struct DevTensor {
-    uint64_t theta, rho, mq, ms, vq, vs, grad;
+    uint64_t theta, codes, scales, grad;
     int64_t numel;
+    uint64_t reserved[3];
 };
 static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 
@@ -45,11 +59,8 @@ static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 // waits only count vector memory traffic.
 struct GTensor {
     GLOBAL uint16_t* theta;
-    GLOBAL int8_t* rho;
-    GLOBAL int8_t* mq;
-    GLOBAL uint16_t* ms;
-    GLOBAL uint8_t* vq;
-    GLOBAL uint16_t* vs;
+    GLOBAL uint8_t* codes;
+    GLOBAL uint16_t* scales;
     const GLOBAL uint16_t* grad;
     int64_t numel;
 };
@@ -57,14 +68,17 @@ struct GTensor {
 __device__ __forceinline__ GTensor view(const DevTensor& d) {
     GTensor t;
     t.theta = (GLOBAL uint16_t*)d.theta;
-    t.rho = (GLOBAL int8_t*)d.rho;
-    t.mq = (GLOBAL int8_t*)d.mq;
-    t.ms = (GLOBAL uint16_t*)d.ms;
-    t.vq = (GLOBAL uint8_t*)d.vq;
-    t.vs = (GLOBAL uint16_t*)d.vs;
+    t.codes = (GLOBAL uint8_t*)d.codes;
+    t.scales = (GLOBAL uint16_t*)d.scales;
     t.grad = (const GLOBAL uint16_t*)d.grad;
     t.numel = d.numel;
     return t;
+}
+
+// byte address of field `off` of element i's record entry
+template <int kOpt>
+__device__ __forceinline__ GLOBAL uint8_t* code_at(const GTensor& T, int64_t i, int off) {
+    return T.codes + (i >> 3) * Layout<kOpt>::kRec + off + (i & 7);
 }
 
 
@@ -89,8 +103,6 @@ __device__ __forceinline__ void st2(GLOBAL void* p, uint2 v) {
     const u32x2 w = {v.x, v.y};
     *(GLOBAL u32x2*)p = w;
 }
-
-enum Opt { kAdamW = 0, kSgd = 1 };
 
 __device__ __forceinline__ int64_t uniform(int64_t x) {
     uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
@@ -186,39 +198,29 @@ __device__ __forceinline__ uint2 pack_u8x8(const uint32_t* v) {
                       (v[4] & 0xFF) | ((v[5] & 0xFF) << 8) | ((v[6] & 0xFF) << 16) | (v[7] << 24));
 }
 
-template <int kOpt, bool kFull>
+// One lane's 8 elements of a partial sub-tile, loaded element by element
+// with bounds checks (the last tile of a tensor).
+template <int kOpt>
 __device__ __forceinline__ void load_lane(const GTensor& T, int64_t e, Lane8& L) {
     const int64_t n = T.numel;
-    const int64_t g = e >> 5;
-    if (kFull) {
-        unpack_bf16x8(ld4(T.theta + e), L.th);
-        unpack_bf16x8(ld4(T.grad + e), L.gr);
-        unpack_s8x8(ld2(T.rho + e), L.rho);
-        unpack_s8x8(ld2(T.mq + e), L.qm);
-        L.ms = T.ms[g];
-        if (kOpt == kAdamW) {
-            unpack_u8x8(ld2(T.vq + e), L.qv);
-            L.vs = T.vs[g];
-        }
-    } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool ok = e + j < n;
-            L.th[j] = ok ? T.theta[e + j] : 0u;
-            L.gr[j] = ok ? T.grad[e + j] : 0u;
-            L.rho[j] = ok ? T.rho[e + j] : 0;
-            L.qm[j] = ok ? T.mq[e + j] : 0;
-            if (kOpt == kAdamW) L.qv[j] = ok ? T.vq[e + j] : 0u;
-        }
-        const bool gok = (e & ~int64_t(31)) < n;       // the lane's group has valid elements
-        L.ms = gok ? T.ms[g] : 0u;
-        if (kOpt == kAdamW) L.vs = gok ? T.vs[g] : 0u;
+    for (int j = 0; j < 8; ++j) {
+        const bool ok = e + j < n;
+        L.th[j] = ok ? T.theta[e + j] : 0u;
+        L.gr[j] = ok ? T.grad[e + j] : 0u;
+        L.rho[j] = ok ? (int8_t)*code_at<kOpt>(T, e + j, kRhoOff) : 0;
+        L.qm[j] = ok ? (int8_t)*code_at<kOpt>(T, e + j, kMOff) : 0;
+        if (kOpt == kAdamW) L.qv[j] = ok ? *code_at<kOpt>(T, e + j, kVOff) : 0u;
     }
+    const int64_t g = e >> 5;
+    const bool gok = (e & ~int64_t(31)) < n;           // the lane's group has valid elements
+    L.ms = gok ? T.scales[g * Layout<kOpt>::kScl] : 0u;
+    if (kOpt == kAdamW) L.vs = gok ? T.scales[g * Layout<kOpt>::kScl + 1] : 0u;
 }
 
 // ---- the fused step on one sub-tile of one lane ----------------------------
 
-template <int kOpt, bool kFull>
+template <int kOpt>
 __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
                                           const Lane8& L, const AdamScalars& a,
                                           const SgdScalars& s) {
@@ -281,30 +283,19 @@ __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
         orho[j] = (uint32_t)sp.rho;
     }
     const int64_t g = e >> 5;
-    if (kFull) {
-        st4(T.theta + e, pack_u16x8(otb));
-        st2(T.rho + e, pack_u8x8(orho));
-        st2(T.mq + e, pack_u8x8(oqm));
-        if (kOpt == kAdamW) st2(T.vq + e, pack_u8x8(oqv));
-        if ((lane & 3) == 0) {
-            T.ms[g] = (uint16_t)sm16;
-            if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
-        }
-    } else {
-        const int64_t n = T.numel;
+    const int64_t n = T.numel;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (e + j < n) {
-                T.theta[e + j] = (uint16_t)otb[j];
-                T.rho[e + j] = (int8_t)orho[j];
-                T.mq[e + j] = (int8_t)oqm[j];
-                if (kOpt == kAdamW) T.vq[e + j] = (uint8_t)oqv[j];
-            }
+    for (int j = 0; j < 8; ++j) {
+        if (e + j < n) {
+            T.theta[e + j] = (uint16_t)otb[j];
+            *code_at<kOpt>(T, e + j, kRhoOff) = (uint8_t)orho[j];
+            *code_at<kOpt>(T, e + j, kMOff) = (uint8_t)oqm[j];
+            if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kVOff) = (uint8_t)oqv[j];
         }
-        if ((lane & 3) == 0 && e < n) {
-            T.ms[g] = (uint16_t)sm16;
-            if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
-        }
+    }
+    if ((lane & 3) == 0 && e < n) {
+        T.scales[g * Layout<kOpt>::kScl] = (uint16_t)sm16;
+        if (kOpt == kAdamW) T.scales[g * Layout<kOpt>::kScl + 1] = (uint16_t)sv16;
     }
 }
 
@@ -312,32 +303,26 @@ __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
 
 struct Raw {                        // one lane's packed loads of one sub-tile
     uint4 th, gr;                   // 8 BF16 theta', 8 BF16 grads
-    uint2 rho, qm, qv;              // 8 INT8 rho, 8 INT8 momentum, 8 UINT8 variance codes
+    uint2 rho, qm, qv;              // the code record: 8 rho, 8 momentum, 8 variance codes
     uint32_t ms, vs;                // the group's FP16 scales
 };
 
 template <int kOpt>
 __device__ __forceinline__ void load_raw(const GTensor& T, int64_t e, Raw& R) {
     const int64_t g = e >> 5;
+    const GLOBAL uint8_t* rec = T.codes + (e >> 3) * Layout<kOpt>::kRec;
     R.th = ld4(T.theta + e);
     R.gr = ld4(T.grad + e);
-    R.rho = ld2(T.rho + e);
-    R.qm = ld2(T.mq + e);
-    R.ms = T.ms[g];
+    R.rho = ld2(rec + kRhoOff);
+    R.qm = ld2(rec + kMOff);
     if (kOpt == kAdamW) {
-        R.qv = ld2(T.vq + e);
-        R.vs = T.vs[g];
+        R.qv = ld2(rec + kVOff);
+        const uint32_t w = *(const GLOBAL uint32_t*)(T.scales + 2 * g);   // m | v << 16
+        R.ms = w & 0xFFFFu;
+        R.vs = w >> 16;
+    } else {
+        R.ms = T.scales[g];
     }
-}
-
-__device__ __forceinline__ void raw_to_lane(const Raw& R, Lane8& L) {
-    unpack_bf16x8(R.th, L.th);
-    unpack_bf16x8(R.gr, L.gr);
-    unpack_s8x8(R.rho, L.rho);
-    unpack_s8x8(R.qm, L.qm);
-    unpack_u8x8(R.qv, L.qv);
-    L.ms = R.ms;
-    L.vs = R.vs;
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
@@ -493,13 +478,14 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     }
     const uint2 orho = make_uint2(rc[0] ^ 0x80808080u, rc[1] ^ 0x80808080u);
     const int64_t g = e >> 5;
+    GLOBAL uint8_t* rec = T.codes + (e >> 3) * Layout<kOpt>::kRec;
     st4(T.theta + e, make_uint4(otb[0], otb[1], otb[2], otb[3]));
-    st2(T.rho + e, orho);
-    st2(T.mq + e, oqm);
-    if (kOpt == kAdamW) st2(T.vq + e, make_uint2(qv0, qv1));
+    st2(rec + kRhoOff, orho);
+    st2(rec + kMOff, oqm);
+    if (kOpt == kAdamW) st2(rec + kVOff, make_uint2(qv0, qv1));
     if ((lane & 3) == 0) {
-        T.ms[g] = (uint16_t)sm16;
-        if (kOpt == kAdamW) T.vs[g] = (uint16_t)sv16;
+        if (kOpt == kAdamW) *(GLOBAL uint32_t*)(T.scales + 2 * g) = sm16 | (sv16 << 16);
+        else T.scales[g] = (uint16_t)sm16;
     }
 }
 
@@ -523,14 +509,16 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
     } else {
         for (int k = 0; k < kSubTiles; ++k) {
             Lane8 L;
-            load_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, L);
-            step_lane<kOpt, false>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, a, s);
+            load_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, L);
+            step_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, a, s);
         }
     }
 }
 
+// Five waves per SIMD: the AdamW instantiation fits in 96 VGPRs without
+// spilling, and the fifth wave covers more memory latency (measured ~0.5 %).
 template <int kOpt>
-__global__ __launch_bounds__(256) void step_kernel(const DevTensor* __restrict__ table,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
                                                    const int64_t* __restrict__ tile_begin,
                                                    int32_t count, int64_t total_tiles,
                                                    DevTensor one, AdamScalars a, SgdScalars s) {
@@ -697,7 +685,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* q, const
 
 // ---- list maintenance kernels ----------------------------------------------
 
-// Zero codes and scales of a list, one tile per wave iteration.
+// Zero the momentum / variance codes and the scales of a list (rho kept), one
+// tile per wave.
+template <int kOpt>
 __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__ table,
                                                    const int64_t* __restrict__ tile_begin,
                                                    int32_t count, int64_t total_tiles) {
@@ -715,14 +705,64 @@ __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__
             const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
             for (int j = 0; j < 8; ++j) {
                 if (e + j < T.numel) {
-                    T.mq[e + j] = 0;
-                    if (T.vq) T.vq[e + j] = 0;
+                    *code_at<kOpt>(T, e + j, kMOff) = 0;
+                    if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kVOff) = 0;
                 }
             }
             if ((lane & 3) == 0 && e < T.numel) {
-                T.ms[e >> 5] = 0;
-                if (T.vs) T.vs[e >> 5] = 0;
+                T.scales[(e >> 5) * Layout<kOpt>::kScl] = 0;
+                if (kOpt == kAdamW) T.scales[(e >> 5) * Layout<kOpt>::kScl + 1] = 0;
             }
+        }
+    }
+}
+
+// ---- one tensor: initialise from / export to FP32 ----------------------------
+
+// theta' and rho from the FP32 weights (Eq. 1-2), momentum and variance codes
+// and scales zero.
+template <int kOpt>
+__global__ __launch_bounds__(256) void init_kernel(DevTensor d, const float* x) {
+    const GTensor T = view(d);
+    const int64_t n = T.numel;
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        for (int j = 0; j < 8; ++j) {
+            if (e + j < n) {
+                const Split sp = split(x[e + j]);
+                T.theta[e + j] = (uint16_t)sp.tb;
+                *code_at<kOpt>(T, e + j, kRhoOff) = (uint8_t)sp.rho;
+                *code_at<kOpt>(T, e + j, kMOff) = 0;
+                if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kVOff) = 0;
+            }
+        }
+        if ((lane & 3) == 0 && e < n) {
+            T.scales[(e >> 5) * Layout<kOpt>::kScl] = 0;
+            if (kOpt == kAdamW) T.scales[(e >> 5) * Layout<kOpt>::kScl + 1] = 0;
+        }
+    }
+}
+
+// The rebuilt FP32 master weight, momentum and (AdamW) variance; any output
+// pointer may be null.
+template <int kOpt>
+__global__ __launch_bounds__(256) void export_kernel(DevTensor d, float* theta_out, float* m_out,
+                                                     float* v_out) {
+    const GTensor T = view(d);
+    const int64_t n = T.numel;
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        if (e >= n) continue;
+        const int64_t g = e >> 5;
+        const float dm = m_step(T.scales[g * Layout<kOpt>::kScl]);
+        const float dv = kOpt == kAdamW ? v_step(T.scales[g * Layout<kOpt>::kScl + 1]) : 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i = e + j;
+            if (i >= n) break;
+            if (theta_out)
+                theta_out[i] = unsplit(T.theta[i], (int8_t)*code_at<kOpt>(T, i, kRhoOff));
+            if (m_out) m_out[i] = dequant_m((int8_t)*code_at<kOpt>(T, i, kMOff), dm);
+            if (kOpt == kAdamW && v_out) v_out[i] = dequant_v(*code_at<kOpt>(T, i, kVOff), dv);
         }
     }
 }
@@ -732,18 +772,17 @@ __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__
 // The AdamW step's memory traffic with the arithmetic taken out: the same
 // tiles, launch shape, loads (with the same two-buffer pipeline) and stores,
 // and one XOR per word in place of the update (theta' ^= g, rho ^= q_m,
-// q_m ^= q_v, q_v ^= rho, scales ^= 1).  Its time is the practical floor of
-// the step's access pattern on this device.
+// q_m ^= q_v, q_v ^= rho, both scales ^= 1).  Its time is the practical floor
+// of the step's access pattern on this device.
 __device__ __forceinline__ void probe_sub(const GTensor& T, int64_t e, int lane, const Raw& R) {
+    GLOBAL uint8_t* rec = T.codes + (e >> 3) * Layout<kAdamW>::kRec;
     st4(T.theta + e, make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
                                 R.th.w ^ R.gr.w));
-    st2(T.rho + e, make_uint2(R.rho.x ^ R.qm.x, R.rho.y ^ R.qm.y));
-    st2(T.mq + e, make_uint2(R.qm.x ^ R.qv.x, R.qm.y ^ R.qv.y));
-    st2(T.vq + e, make_uint2(R.qv.x ^ R.rho.x, R.qv.y ^ R.rho.y));
-    if ((lane & 3) == 0) {
-        T.ms[e >> 5] = (uint16_t)(R.ms ^ 1u);
-        T.vs[e >> 5] = (uint16_t)(R.vs ^ 1u);
-    }
+    st2(rec + kRhoOff, make_uint2(R.rho.x ^ R.qm.x, R.rho.y ^ R.qm.y));
+    st2(rec + kMOff, make_uint2(R.qm.x ^ R.qv.x, R.qm.y ^ R.qv.y));
+    st2(rec + kVOff, make_uint2(R.qv.x ^ R.rho.x, R.qv.y ^ R.rho.y));
+    if ((lane & 3) == 0)
+        *(GLOBAL uint32_t*)(T.scales + 2 * (e >> 5)) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
 }
 
 __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict__ table,
@@ -775,18 +814,19 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
                 for (int j = 0; j < 8; ++j) {
                     const int64_t i = e + j;
                     if (i < T.numel) {
-                        const uint16_t th = T.theta[i], gr = T.grad[i];
-                        const int8_t rho = T.rho[i], qm = T.mq[i];
-                        const uint8_t qv = T.vq[i];
-                        T.theta[i] = (uint16_t)(th ^ gr);
-                        T.rho[i] = (int8_t)(rho ^ qm);
-                        T.mq[i] = (int8_t)(qm ^ (int8_t)qv);
-                        T.vq[i] = (uint8_t)(qv ^ (uint8_t)rho);
+                        GLOBAL uint8_t* r = code_at<kAdamW>(T, i, kRhoOff);
+                        GLOBAL uint8_t* m = code_at<kAdamW>(T, i, kMOff);
+                        GLOBAL uint8_t* v = code_at<kAdamW>(T, i, kVOff);
+                        const uint8_t rho = *r, qm = *m, qv = *v;
+                        T.theta[i] = (uint16_t)(T.theta[i] ^ T.grad[i]);
+                        *r = (uint8_t)(rho ^ qm);
+                        *m = (uint8_t)(qm ^ qv);
+                        *v = (uint8_t)(qv ^ rho);
                     }
                 }
                 if ((lane & 3) == 0 && e < T.numel) {
-                    T.ms[e >> 5] = (uint16_t)(T.ms[e >> 5] ^ 1u);
-                    T.vs[e >> 5] = (uint16_t)(T.vs[e >> 5] ^ 1u);
+                    GLOBAL uint32_t* w = (GLOBAL uint32_t*)(T.scales + 2 * (e >> 5));
+                    *w = *w ^ 0x00010001u;
                 }
             }
         }
@@ -880,23 +920,25 @@ static int check_sgd(const flashopt_sgd_hparams* hp, int64_t step) {
     return FLASHOPT_OK;
 }
 
-static int check_tensor(const flashopt_tensor& t) {
+static bool valid_kind(int32_t kind) { return kind == FLASHOPT_KIND_ADAMW || kind == FLASHOPT_KIND_SGD; }
+
+static int check_tensor(const flashopt_tensor& t, int32_t kind) {
     if (t.numel < 0 || t.numel > kMaxNumel) return FLASHOPT_ERR_SIZE;
-    if ((t.v_code == nullptr) != (t.v_scale == nullptr)) return FLASHOPT_ERR_ARG;
     if (t.numel == 0) return FLASHOPT_OK;
-    if (!t.theta || !t.rho || !t.m_code || !t.m_scale) return FLASHOPT_ERR_NULL;
-    if (!aligned(t.theta, 16) || !aligned(t.rho, 8) || !aligned(t.m_code, 8) ||
-        !aligned(t.m_scale, 2) || (t.v_code && !aligned(t.v_code, 8)) ||
-        (t.v_scale && !aligned(t.v_scale, 2)) || (t.grad && !aligned(t.grad, 16)))
+    if (!t.theta || !t.codes || !t.scales) return FLASHOPT_ERR_NULL;
+    if (!aligned(t.theta, 16) || !aligned(t.codes, 8) ||
+        !aligned(t.scales, kind == FLASHOPT_KIND_ADAMW ? 4 : 2) || (t.grad && !aligned(t.grad, 16)))
         return FLASHOPT_ERR_ALIGN;
     return FLASHOPT_OK;
 }
 
 static DevTensor to_dev(const flashopt_tensor& t) {
-    DevTensor d;
-    d.theta = (uint64_t)t.theta; d.rho = (uint64_t)t.rho; d.mq = (uint64_t)t.m_code;
-    d.ms = (uint64_t)t.m_scale; d.vq = (uint64_t)t.v_code; d.vs = (uint64_t)t.v_scale;
-    d.grad = (uint64_t)t.grad; d.numel = t.numel;
+    DevTensor d{};
+    d.theta = (uint64_t)t.theta;
+    d.codes = (uint64_t)t.codes;
+    d.scales = (uint64_t)t.scales;
+    d.grad = (uint64_t)t.grad;
+    d.numel = t.numel;
     return d;
 }
 
@@ -912,7 +954,7 @@ struct flashopt_list {
     int64_t* d_tile_begin = nullptr;
     std::vector<flashopt_tensor> host;
     std::vector<int64_t> tile_begin;
-    bool all_have_v = true;
+    int32_t kind = FLASHOPT_KIND_ADAMW;
     bool all_have_grad = true;
     // cached bias-correction powers (see adam_scalars)
     double p1 = 1.0, p2 = 1.0, b1 = -1.0, b2 = -1.0;
@@ -1016,10 +1058,58 @@ size_t flashopt_list_workspace_bytes(int32_t count) {
     return tb_padded + (size_t)count * sizeof(DevTensor);
 }
 
-int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, void* workspace,
-                         size_t workspace_bytes, void* stream, flashopt_list** out) {
+size_t flashopt_codes_bytes(int32_t kind, int64_t numel) {
+    if (!valid_kind(kind) || numel < 0 || numel > kMaxNumel) return 0;
+    return (size_t)((numel + 7) / 8) * (kind == FLASHOPT_KIND_ADAMW ? 24 : 16);
+}
+
+size_t flashopt_scales_bytes(int32_t kind, int64_t numel) {
+    if (!valid_kind(kind) || numel < 0 || numel > kMaxNumel) return 0;
+    return (size_t)((numel + 31) / 32) * (kind == FLASHOPT_KIND_ADAMW ? 4 : 2);
+}
+
+int flashopt_tensor_init(const flashopt_tensor* t, int32_t kind, const float* theta,
+                         void* stream) {
+    if (!t) return FLASHOPT_ERR_NULL;
+    if (!valid_kind(kind)) return FLASHOPT_ERR_ARG;
+    const int st = check_tensor(*t, kind);
+    if (st != FLASHOPT_OK) return st;
+    if (t->numel == 0) return FLASHOPT_OK;
+    if (!theta) return FLASHOPT_ERR_NULL;
+    const int64_t chunks = (t->numel + kSubTile - 1) / kSubTile;
+    if (kind == FLASHOPT_KIND_ADAMW)
+        hipLaunchKernelGGL(init_kernel<kAdamW>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, to_dev(*t), theta);
+    else
+        hipLaunchKernelGGL(init_kernel<kSgd>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, to_dev(*t), theta);
+    return launch_status();
+}
+
+int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta, float* m,
+                           float* v, void* stream) {
+    if (!t) return FLASHOPT_ERR_NULL;
+    if (!valid_kind(kind)) return FLASHOPT_ERR_ARG;
+    const int st = check_tensor(*t, kind);
+    if (st != FLASHOPT_OK) return st;
+    if (kind == FLASHOPT_KIND_SGD) v = nullptr;
+    if (t->numel == 0 || (!theta && !m && !v)) return FLASHOPT_OK;
+    const int64_t chunks = (t->numel + kSubTile - 1) / kSubTile;
+    if (kind == FLASHOPT_KIND_ADAMW)
+        hipLaunchKernelGGL(export_kernel<kAdamW>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, to_dev(*t), theta, m, v);
+    else
+        hipLaunchKernelGGL(export_kernel<kSgd>, dim3(grid_for(chunks)), dim3(kBlock), 0,
+                           (hipStream_t)stream, to_dev(*t), theta, m, v);
+    return launch_status();
+}
+
+int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, int32_t kind,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         flashopt_list** out) {
     if (!out) return FLASHOPT_ERR_NULL;
     *out = nullptr;
+    if (!valid_kind(kind)) return FLASHOPT_ERR_ARG;
     if (count < 0) return FLASHOPT_ERR_SIZE;
     if (count > 0 && !tensors) return FLASHOPT_ERR_NULL;
     const size_t need = flashopt_list_workspace_bytes(count);
@@ -1030,20 +1120,18 @@ int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, void* wo
     flashopt_list* L = new (std::nothrow) flashopt_list();
     if (!L) return FLASHOPT_ERR_ARG;
     L->count = count;
+    L->kind = kind;
     L->host.assign(tensors, tensors + count);
     L->tile_begin.resize((size_t)count + 1);
     int64_t tiles = 0;
     std::vector<DevTensor> dev((size_t)count);
     for (int32_t i = 0; i < count; ++i) {
-        const int st = check_tensor(tensors[i]);
+        const int st = check_tensor(tensors[i], kind);
         if (st != FLASHOPT_OK) { delete L; return st; }
         L->tile_begin[i] = tiles;
         tiles += tiles_of(tensors[i].numel);
         L->numel += tensors[i].numel;
-        if (tensors[i].numel > 0) {
-            if (!tensors[i].v_code) L->all_have_v = false;
-            if (!tensors[i].grad) L->all_have_grad = false;
-        }
+        if (tensors[i].numel > 0 && !tensors[i].grad) L->all_have_grad = false;
         dev[i] = to_dev(tensors[i]);
     }
     L->tile_begin[count] = tiles;
@@ -1101,15 +1189,20 @@ int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void
 int flashopt_state_zero(const flashopt_list* L, void* stream) {
     if (!L) return FLASHOPT_ERR_NULL;
     if (L->total_tiles == 0) return FLASHOPT_OK;
-    hipLaunchKernelGGL(zero_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                       (hipStream_t)stream, (const DevTensor*)L->d_table,
-                       (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+    if (L->kind == FLASHOPT_KIND_ADAMW)
+        hipLaunchKernelGGL(zero_kernel<kAdamW>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
+                           (hipStream_t)stream, (const DevTensor*)L->d_table,
+                           (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+    else
+        hipLaunchKernelGGL(zero_kernel<kSgd>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
+                           (hipStream_t)stream, (const DevTensor*)L->d_table,
+                           (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
     return launch_status();
 }
 
 int flashopt_stream_probe(const flashopt_list* L, void* stream) {
     if (!L) return FLASHOPT_ERR_NULL;
-    if (!L->all_have_v) return FLASHOPT_ERR_ARG;
+    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     if (L->total_tiles == 0) return FLASHOPT_OK;
     hipLaunchKernelGGL(probe_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
@@ -1152,7 +1245,7 @@ int flashopt_adamw_step(const flashopt_list* L, const flashopt_adamw_hparams* hp
     if (!L) return FLASHOPT_ERR_NULL;
     int st = check_adam(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (!L->all_have_v) return FLASHOPT_ERR_ARG;
+    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     flashopt_list* M = const_cast<flashopt_list*>(L);   // only the scalar cache changes
     const AdamScalars a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
@@ -1164,6 +1257,7 @@ int flashopt_sgd_step(const flashopt_list* L, const flashopt_sgd_hparams* hp, in
     if (!L) return FLASHOPT_ERR_NULL;
     int st = check_sgd(hp, step);
     if (st != FLASHOPT_OK) return st;
+    if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     SgdScalars s{(float)hp->momentum, (float)hp->lr, (float)hp->weight_decay};
     return launch_list(kSgd, L, AdamScalars{}, s, stream);
@@ -1175,11 +1269,11 @@ int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_
     if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
     int st = check_adam(hp, step);
     if (st != FLASHOPT_OK) return st;
+    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
     const flashopt_tensor& t = L->host[index];
     if (t.numel > 0) {
         if (!grad) return FLASHOPT_ERR_NULL;
         if (!aligned(grad, 16)) return FLASHOPT_ERR_ALIGN;
-        if (!t.v_code) return FLASHOPT_ERR_ARG;
     }
     flashopt_list* M = const_cast<flashopt_list*>(L);
     const AdamScalars a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
@@ -1192,6 +1286,7 @@ int flashopt_sgd_step_one(const flashopt_list* L, int32_t index, const uint16_t*
     if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
     int st = check_sgd(hp, step);
     if (st != FLASHOPT_OK) return st;
+    if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
     const flashopt_tensor& t = L->host[index];
     if (t.numel > 0) {
         if (!grad) return FLASHOPT_ERR_NULL;

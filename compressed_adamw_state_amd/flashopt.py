@@ -28,11 +28,14 @@ class FlashoptError(RuntimeError):
         self.status = status
 
 
+KIND = {"adamw": 0, "sgd": 1}          # flashopt_kind
+RECORD = {"adamw": 24, "sgd": 16}      # code-record bytes per 8 elements
+SCALES = {"adamw": 2, "sgd": 1}        # FP16 scales per 32-element group
+
+
 class Tensor(ctypes.Structure):
-    _fields_ = [("numel", ctypes.c_int64), ("theta", ctypes.c_void_p), ("rho", ctypes.c_void_p),
-                ("m_code", ctypes.c_void_p), ("m_scale", ctypes.c_void_p),
-                ("v_code", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("grad", ctypes.c_void_p)]
+    _fields_ = [("numel", ctypes.c_int64), ("theta", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("grad", ctypes.c_void_p)]
 
 
 class AdamWHparams(ctypes.Structure):
@@ -55,7 +58,11 @@ SIGNATURES = {
     "flashopt_quantize_v": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
     "flashopt_dequantize_v": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "flashopt_list_workspace_bytes": (_SZ, [_I32]),
-    "flashopt_list_create": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32, _P, _SZ, _P,
+    "flashopt_codes_bytes": (_SZ, [_I32, _I64]),
+    "flashopt_scales_bytes": (_SZ, [_I32, _I64]),
+    "flashopt_tensor_init": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32, _P, _P]),
+    "flashopt_tensor_export": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32, _P, _P, _P, _P]),
+    "flashopt_list_create": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32, _I32, _P, _SZ, _P,
                                             ctypes.POINTER(_P)]),
     "flashopt_list_destroy": (ctypes.c_int, [_P]),
     "flashopt_list_numel": (_I64, [_P]),
@@ -148,45 +155,65 @@ def flashopt_dequantize_v(q, scale, v_out, stream=None) -> None:
 # ---- tensor lists -----------------------------------------------------------
 
 class TensorState:
-    """Device arrays of one tensor's compressed state (allocated with torch)."""
+    """Device arrays of one tensor's compressed state (allocated with torch):
+    BF16 theta', the interleaved code records and the FP16 scales, in the
+    layout of include/flashopt.h."""
 
     def __init__(self, numel: int, optimizer: str, device):
-        g = groups(numel)
         self.numel = numel
+        self.optimizer = optimizer
+        self.kind = KIND[optimizer]
         self.theta = torch.empty(numel, dtype=torch.bfloat16, device=device)
-        self.rho = torch.empty(numel, dtype=torch.int8, device=device)
-        self.m_code = torch.zeros(numel, dtype=torch.int8, device=device)
-        self.m_scale = torch.zeros(g, dtype=torch.float16, device=device)
-        if optimizer == "adamw":
-            self.v_code = torch.zeros(numel, dtype=torch.uint8, device=device)
-            self.v_scale = torch.zeros(g, dtype=torch.float16, device=device)
-        else:
-            self.v_code = self.v_scale = None
+        self.codes = torch.zeros(lib().flashopt_codes_bytes(self.kind, numel), dtype=torch.uint8,
+                                 device=device)
+        self.scales = torch.zeros(lib().flashopt_scales_bytes(self.kind, numel) // 2,
+                                  dtype=torch.int16, device=device)
 
-    def arrays(self) -> dict:
-        return {"theta": self.theta, "rho": self.rho, "m_code": self.m_code,
-                "m_scale": self.m_scale, "v_code": self.v_code, "v_scale": self.v_scale}
+    def descriptor(self, grad: Optional[torch.Tensor] = None) -> Tensor:
+        return Tensor(self.numel, _ptr(self.theta), _ptr(self.codes), _ptr(self.scales),
+                      _ptr(grad))
+
+
+def flashopt_tensor_init(st: TensorState, theta_fp32: torch.Tensor, stream=None) -> None:
+    """theta', rho from FP32 weights (device [numel]); codes and scales zero."""
+    d = st.descriptor()
+    _check("flashopt_tensor_init", lib().flashopt_tensor_init(ctypes.byref(d), st.kind,
+                                                              _ptr(theta_fp32), _stream(stream)))
+
+
+def flashopt_tensor_export(st: TensorState, theta_out=None, m_out=None, v_out=None,
+                           stream=None) -> None:
+    """Rebuilt FP32 master weight and dequantised m, v (device [numel] each, any None)."""
+    d = st.descriptor()
+    _check("flashopt_tensor_export",
+           lib().flashopt_tensor_export(ctypes.byref(d), st.kind, _ptr(theta_out), _ptr(m_out),
+                                        _ptr(v_out), _stream(stream)))
 
 
 class FlashoptList:
-    """A flashopt_list handle over a list of TensorState (device workspace from torch)."""
+    """A flashopt_list handle over a list of TensorState of one optimizer kind
+    (device workspace from torch)."""
 
     def __init__(self, states: Sequence[TensorState], grads: Sequence[Optional[torch.Tensor]],
-                 stream=None):
+                 stream=None, optimizer: Optional[str] = None):
         self.states = list(states)
         count = len(self.states)
+        if optimizer is None:
+            optimizer = self.states[0].optimizer if count else "adamw"
+        if any(st.optimizer != optimizer for st in self.states):
+            raise ValueError("every tensor of a list needs the list's optimizer layout")
+        self.optimizer = optimizer
         arr = (Tensor * max(count, 1))()
         for i, (st, g) in enumerate(zip(self.states, grads)):
-            arr[i] = Tensor(st.numel, _ptr(st.theta), _ptr(st.rho), _ptr(st.m_code),
-                            _ptr(st.m_scale), _ptr(st.v_code), _ptr(st.v_scale), _ptr(g))
+            arr[i] = st.descriptor(g)
         self.grads = list(grads)
         nbytes = lib().flashopt_list_workspace_bytes(count)
         dev = self.states[0].theta.device if count else torch.device("cuda")
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         h = ctypes.c_void_p()
         _check("flashopt_list_create",
-               lib().flashopt_list_create(arr, count, _ptr(self.workspace), nbytes,
-                                          _stream(stream), ctypes.byref(h)))
+               lib().flashopt_list_create(arr, count, KIND[optimizer], _ptr(self.workspace),
+                                          nbytes, _stream(stream), ctypes.byref(h)))
         self.handle = h
 
     def __del__(self):
@@ -271,13 +298,12 @@ def step_one(lst: FlashoptList, optimizer: str, index: int, grad, hp: dict, t: i
 
 def build_list(theta_fp32: List[torch.Tensor], optimizer: str,
                grads: Sequence[Optional[torch.Tensor]], stream=None):
-    """Allocate compressed state for fp32 master weights, split them and zero
-    the optimizer state; returns (states, list handle)."""
+    """Allocate compressed state for fp32 master weights, split them (zero
+    optimizer state); returns (states, list handle)."""
     states = []
     for th in theta_fp32:
         st = TensorState(th.numel(), optimizer, th.device)
-        flashopt_split(th.reshape(-1), st.theta, st.rho, stream)
+        flashopt_tensor_init(st, th.reshape(-1).contiguous(), stream)
         states.append(st)
-    lst = FlashoptList(states, grads, stream)
-    flashopt_state_zero(lst, stream)
+    lst = FlashoptList(states, grads, stream, optimizer)
     return states, lst

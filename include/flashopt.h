@@ -45,8 +45,9 @@
  * (its scale covers only its valid elements).  BF16 and FP16 values are passed
  * as their uint16 bit patterns.
  *
- * Alignment: BF16 arrays (theta', grad) 16 bytes; INT8/UINT8 code arrays
- * 8 bytes; scale arrays 2 bytes; FP32 arrays 16 bytes.
+ * Alignment: BF16 arrays (theta', grad) 16 bytes; code records and flat
+ * INT8/UINT8 code arrays 8 bytes; AdamW scale arrays 4 bytes, SGD and flat
+ * scale arrays 2 bytes; FP32 arrays 16 bytes.
  *
  * Errors.  Every call validates its arguments on the host before launching
  * anything and returns a flashopt_status; a failed validation launches
@@ -75,22 +76,40 @@ typedef enum flashopt_status {
     FLASHOPT_ERR_NULL = -1,      /* a required pointer is NULL                         */
     FLASHOPT_ERR_SIZE = -2,      /* negative or too large element count / list count   */
     FLASHOPT_ERR_ALIGN = -3,     /* a pointer violates the alignment above             */
-    FLASHOPT_ERR_ARG = -4,       /* hyper-parameter out of range, missing state array  */
+    FLASHOPT_ERR_ARG = -4,       /* hyper-parameter out of range, wrong kind           */
     FLASHOPT_ERR_STEP = -5,      /* step counter t < 1                                 */
     FLASHOPT_ERR_WORKSPACE = -6, /* device workspace too small                         */
     FLASHOPT_ERR_HIP = -7,       /* HIP runtime error (launch, copy, device query)     */
     FLASHOPT_ERR_INDEX = -8      /* tensor index out of range                          */
 } flashopt_status;
 
-/* One parameter tensor and its compressed state (all DEVICE pointers). */
+/* Optimizer kind of a tensor's state layout (and of a list). */
+typedef enum flashopt_kind {
+    FLASHOPT_KIND_ADAMW = 0,     /* rho, momentum and variance codes; two scales per group */
+    FLASHOPT_KIND_SGD = 1        /* rho and momentum codes; one scale per group            */
+} flashopt_kind;
+
+/* One parameter tensor and its compressed state (all DEVICE pointers).
+ *
+ * State layout.  The per-element codes are interleaved in records of 8
+ * consecutive elements, so the fused step reads and writes the state as one
+ * stream (HBM bandwidth on this device falls with the number of concurrent
+ * streams):
+ *   codes[r*R + 0 + j]  = rho of element 8r+j          (INT8, two's complement)
+ *   codes[r*R + 8 + j]  = momentum code of element 8r+j (INT8; SGD: momentum buffer)
+ *   codes[r*R + 16 + j] = variance code of element 8r+j (UINT8; AdamW only)
+ * with R = 24 (AdamW) or 16 (SGD), r < ceil(n/8), j < 8; the last record's
+ * entries past n are padding (never read as state, may be overwritten).
+ *   scales[2g], scales[2g+1] = FP16 momentum and variance scales of group g (AdamW)
+ *   scales[g]                = FP16 momentum scale of group g (SGD)
+ * for g < ceil(n/32).  flashopt_codes_bytes / flashopt_scales_bytes give the
+ * sizes.  The values are exactly those of the flat arrays the quantisers and
+ * split below produce, only their placement differs. */
 typedef struct flashopt_tensor {
     int64_t numel;           /* n >= 0                                                   */
     uint16_t* theta;         /* [n] BF16 theta'; the model weight the forward pass reads */
-    int8_t* rho;             /* [n] INT8 weight-error codes                              */
-    int8_t* m_code;          /* [n] INT8 momentum codes (SGD: momentum buffer codes)     */
-    uint16_t* m_scale;       /* [ceil(n/32)] FP16 momentum scales                        */
-    uint8_t* v_code;         /* [n] UINT8 variance codes; NULL for an SGD-only list      */
-    uint16_t* v_scale;       /* [ceil(n/32)] FP16 variance scales; NULL with v_code      */
+    uint8_t* codes;          /* code records, layout above                               */
+    uint16_t* scales;        /* FP16 scales, layout above                                */
     const uint16_t* grad;    /* [n] BF16 gradient, read only; may be NULL when only the
                                 *_step_one entry points (gradient release) are used    */
 } flashopt_tensor;
@@ -132,6 +151,22 @@ int flashopt_quantize_v(const float* v, int64_t n, uint8_t* q, uint16_t* scale, 
 int flashopt_dequantize_v(const uint8_t* q, const uint16_t* scale, int64_t n, float* v,
                           void* stream);
 
+/* ---- one tensor's compressed state.
+ * Sizes in bytes of the code records and the scale array for n elements
+ * (0 for an unknown kind or n out of range). */
+size_t flashopt_codes_bytes(int32_t kind, int64_t numel);
+size_t flashopt_scales_bytes(int32_t kind, int64_t numel);
+/* Initialise from FP32 master weights (device [n]): theta' and rho by the split
+ * (weight-splitting section, Eq. 1-2), momentum and variance codes and all
+ * scales zero (m = v = 0).  t->grad is not used. */
+int flashopt_tensor_init(const flashopt_tensor* t, int32_t kind, const float* theta,
+                         void* stream);
+/* Export to FP32 (device [n] each; any may be NULL, v ignored for SGD): the
+ * rebuilt master weight theta' + (rho*K8)*h, and the dequantised momentum and
+ * variance (companding section, Alg. 2-3) -- checkpoint conversion. */
+int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta, float* m,
+                           float* v, void* stream);
+
 /* ---- ragged tensor lists (a flat buffer is a list of one).
  * The list keeps a device descriptor table in a caller-provided DEVICE
  * workspace of at least flashopt_list_workspace_bytes(count) bytes (256-byte
@@ -140,20 +175,25 @@ int flashopt_dequantize_v(const uint8_t* q, const uint16_t* scale, int64_t n, fl
  * (it is a set-up call); afterwards the descriptors' pointers are fixed,
  * except the gradients (flashopt_list_set_grads).  count may be 0. */
 size_t flashopt_list_workspace_bytes(int32_t count);
-int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, void* workspace,
-                         size_t workspace_bytes, void* stream, flashopt_list** out);
+/* kind: FLASHOPT_KIND_ADAMW (steps with flashopt_adamw_step*) or
+ * FLASHOPT_KIND_SGD (flashopt_sgd_step*); a step of the other kind returns
+ * FLASHOPT_ERR_ARG. */
+int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, int32_t kind,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         flashopt_list** out);
 int flashopt_list_destroy(flashopt_list* list);
 int64_t flashopt_list_numel(const flashopt_list* list);
 /* grads: HOST array of `count` device pointers (entries may be NULL).  The new
  * pointers are written into the device table in stream order (kernel
  * arguments, no host staging buffer), so steps enqueued later see them. */
 int flashopt_list_set_grads(flashopt_list* list, const uint16_t* const* grads, void* stream);
-/* Zero every code and scale of the list (the initial state: m = v = 0). */
+/* Zero the momentum and variance codes and every scale of the list (m = v = 0;
+ * theta' and rho are kept). */
 int flashopt_state_zero(const flashopt_list* list, void* stream);
 
 /* ---- the fused step (fused-step section, Alg. 4): ONE launch over the whole
  * list.  step is the 1-based AdamW counter t shared by all tensors of one
- * optimizer step.  AdamW needs v_code / v_scale on every tensor. */
+ * optimizer step.  The list's kind must match the step. */
 int flashopt_adamw_step(const flashopt_list* list, const flashopt_adamw_hparams* hp,
                         int64_t step, void* stream);
 int flashopt_sgd_step(const flashopt_list* list, const flashopt_sgd_hparams* hp,

@@ -36,6 +36,26 @@ def u8(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy().view(np.uint8)
 
 
+def state_fields(st: F.TensorState, idx=None, gidx=None) -> dict:
+    """theta', rho, m_code, v_code (elements idx) and m_scale, v_scale (groups
+    gidx) of a device TensorState as numpy arrays, read out of the interleaved
+    code records and scale pairs (include/flashopt.h); None selects all."""
+    dev = st.codes.device
+    n = st.numel
+    if idx is None:
+        idx = torch.arange(n, device=dev)
+    if gidx is None:
+        gidx = torch.arange((n + GROUP - 1) // GROUP, device=dev)
+    R, S = F.RECORD[st.optimizer], F.SCALES[st.optimizer]
+    base = (idx >> 3) * R + (idx & 7)
+    out = {"theta": u16(st.theta[idx]), "rho": i8(st.codes[base]),
+           "m_code": i8(st.codes[base + 8]), "m_scale": u16(st.scales[gidx * S])}
+    if st.optimizer == "adamw":
+        out["v_code"] = u8(st.codes[base + 16])
+        out["v_scale"] = u16(st.scales[gidx * S + 1])
+    return out
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -56,7 +76,7 @@ class Run:
             theta = W.draw_theta(w, i, self.gen_dev)
             st = F.TensorState(n, opt, self.dev)
             theta_d = theta.to(self.dev)
-            F.flashopt_split(theta_d, st.theta, st.rho)
+            F.flashopt_tensor_init(st, theta_d)
             self.states.append(st)
             self.grads.append(None if w.release else
                               torch.zeros(n, dtype=torch.bfloat16, device=self.dev))
@@ -118,24 +138,20 @@ class Run:
         checked = 0
         for i, st in enumerate(self.states):
             name = self.w.tensors[i].name
+            keys = [("theta", "tb"), ("rho", "rho"), ("m_code", "qm"), ("m_scale", "sm")]
+            if st.optimizer == "adamw":
+                keys += [("v_code", "qv"), ("v_scale", "sv")]
             if self.mode == "full":
                 o = self.orc[i]
-                pairs = [("theta", u16(st.theta), o.tb), ("rho", i8(st.rho), o.rho),
-                         ("m_code", i8(st.m_code), o.qm), ("m_scale", u16(st.m_scale), o.sm)]
-                if st.v_code is not None:
-                    pairs += [("v_code", u8(st.v_code), o.qv), ("v_scale", u16(st.v_scale), o.sv)]
+                f = state_fields(st)
+                pairs = [(k, f[k], getattr(o, ok)) for k, ok in keys]
                 checked += st.numel
             else:
                 idx = self._sample_index(i)
                 gidx = torch.tensor(self.samples[i], device=self.dev)
+                f = state_fields(st, idx, gidx)
                 cat = lambda k: np.concatenate([getattr(s, k) for s in self.orc[i]])
-                pairs = [("theta", u16(st.theta[idx]), cat("tb")),
-                         ("rho", i8(st.rho[idx]), cat("rho")),
-                         ("m_code", i8(st.m_code[idx]), cat("qm")),
-                         ("m_scale", u16(st.m_scale[gidx]), cat("sm"))]
-                if st.v_code is not None:
-                    pairs += [("v_code", u8(st.v_code[idx]), cat("qv")),
-                              ("v_scale", u16(st.v_scale[gidx]), cat("sv"))]
+                pairs = [(k, f[k], cat(ok)) for k, ok in keys]
                 checked += int(idx.numel())
             for k, got, exp in pairs:
                 if not np.array_equal(got, exp):

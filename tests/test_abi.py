@@ -53,23 +53,35 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_workspace_bytes(0) >= 8
     assert lib.flashopt_list_workspace_bytes(291) >= 291 * 64
     out = P()
-    arr = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake, None, None, fake))
+    A, S = 0, 1                                        # flashopt_kind
+    assert lib.flashopt_codes_bytes(A, 17) == 3 * 24 and lib.flashopt_codes_bytes(S, 17) == 3 * 16
+    assert lib.flashopt_scales_bytes(A, 33) == 2 * 4 and lib.flashopt_scales_bytes(S, 33) == 2 * 2
+    assert lib.flashopt_codes_bytes(7, 17) == 0 and lib.flashopt_scales_bytes(A, -1) == 0
+    arr = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake))
     ws = P(0x100000)
     need = lib.flashopt_list_workspace_bytes(1)
-    assert lib.flashopt_list_create(arr, 1, ws, need - 1, None, ctypes.byref(out)) == -6
-    assert lib.flashopt_list_create(arr, 1, P(0x100010), need, None, ctypes.byref(out)) == -6
-    assert lib.flashopt_list_create(arr, -1, ws, need, None, ctypes.byref(out)) == -2
-    bad = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake, fake, None, fake))
-    assert lib.flashopt_list_create(bad, 1, ws, need, None, ctypes.byref(out)) == -4
-    mis_t = (F.Tensor * 1)(F.Tensor(10, P(0x10008), fake, fake, fake, None, None, fake))
-    assert lib.flashopt_list_create(mis_t, 1, ws, need, None, ctypes.byref(out)) == -3
-    neg = (F.Tensor * 1)(F.Tensor(-5, fake, fake, fake, fake, None, None, fake))
-    assert lib.flashopt_list_create(neg, 1, ws, need, None, ctypes.byref(out)) == -2
+    assert lib.flashopt_list_create(arr, 1, A, ws, need - 1, None, ctypes.byref(out)) == -6
+    assert lib.flashopt_list_create(arr, 1, A, P(0x100010), need, None, ctypes.byref(out)) == -6
+    assert lib.flashopt_list_create(arr, -1, A, ws, need, None, ctypes.byref(out)) == -2
+    assert lib.flashopt_list_create(arr, 1, 5, ws, need, None, ctypes.byref(out)) == -4
+    nul = (F.Tensor * 1)(F.Tensor(10, fake, None, fake, fake))
+    assert lib.flashopt_list_create(nul, 1, A, ws, need, None, ctypes.byref(out)) == -1
+    mis_t = (F.Tensor * 1)(F.Tensor(10, P(0x10008), fake, fake, fake))
+    assert lib.flashopt_list_create(mis_t, 1, A, ws, need, None, ctypes.byref(out)) == -3
+    mis_s = (F.Tensor * 1)(F.Tensor(10, fake, fake, P(0x10002), fake))  # AdamW scales need 4 B
+    assert lib.flashopt_list_create(mis_s, 1, A, ws, need, None, ctypes.byref(out)) == -3
+    neg = (F.Tensor * 1)(F.Tensor(-5, fake, fake, fake, fake))
+    assert lib.flashopt_list_create(neg, 1, A, ws, need, None, ctypes.byref(out)) == -2
+    assert lib.flashopt_tensor_init(arr, 3, fake, None) == -4
+    assert lib.flashopt_tensor_init(arr, A, None, None) == -1
+    assert lib.flashopt_tensor_init(mis_t, A, fake, None) == -3
+    assert lib.flashopt_tensor_export(None, A, fake, None, None, None) == -1
+    assert lib.flashopt_tensor_export(arr, A, None, None, None, None) == 0   # nothing requested
     hp = F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
     assert lib.flashopt_adamw_step(None, ctypes.byref(hp), 1, None) == -1
     assert lib.flashopt_stream_probe(None, None) == -1
     # an empty list is created without touching the device
-    assert lib.flashopt_list_create(None, 0, None, 0, None, ctypes.byref(out)) == 0
+    assert lib.flashopt_list_create(None, 0, A, None, 0, None, ctypes.byref(out)) == 0
     L = out
     assert lib.flashopt_list_numel(L) == 0
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 0, None) == -5
@@ -80,6 +92,8 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == 0    # nothing to launch
     sgd = F.SGDHparams(0.1, 1.0, 0.0)
     assert lib.flashopt_sgd_step(L, ctypes.byref(sgd), 1, None) == -4
+    sgd = F.SGDHparams(0.1, 0.9, 0.0)
+    assert lib.flashopt_sgd_step(L, ctypes.byref(sgd), 1, None) == -4   # AdamW list
     assert lib.flashopt_adamw_step_one(L, 0, fake, ctypes.byref(hp), 1, None) == -8
     assert lib.flashopt_state_zero(L, None) == 0
     assert lib.flashopt_list_destroy(L) == 0

@@ -11,7 +11,7 @@ import oracle
 from compressed_adamw_state_amd import flashopt as F
 from compressed_adamw_state_amd import workloads as W
 
-from parity import Run, i8, log, u16, u8
+from parity import Run, i8, log, state_fields, u16, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -153,7 +153,7 @@ def test_release_mode_matches_list_mode(opt):
         b.compare(f"release step {t}")
         for sa, sb in zip(a.states, b.states):
             assert torch.equal(sa.theta.view(torch.int16), sb.theta.view(torch.int16))
-            assert torch.equal(sa.m_code, sb.m_code)
+            assert torch.equal(sa.codes, sb.codes) and torch.equal(sa.scales, sb.scales)
 
 
 def test_hyperparameter_variants():
@@ -193,11 +193,15 @@ def test_set_grads_and_state_zero():
     r.grads = new
     r.step(2)
     r.compare("after set_grads")
+    before = [state_fields(s) for s in r.states]
     F.flashopt_state_zero(r.lst)
     torch.cuda.synchronize()
-    for s in r.states:
-        assert not s.m_code.any() and not s.v_code.any()
-        assert not s.m_scale.view(torch.int16).any() and not s.v_scale.view(torch.int16).any()
+    for s, b in zip(r.states, before):
+        f = state_fields(s)
+        for k in ("m_code", "v_code", "m_scale", "v_scale"):
+            assert not f[k].any(), k
+        np.testing.assert_array_equal(f["rho"], b["rho"])       # the weight split is kept
+        np.testing.assert_array_equal(f["theta"], b["theta"])
 
 
 def test_config1_flat1m_all_steps():

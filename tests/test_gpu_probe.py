@@ -1,19 +1,16 @@
 """The bandwidth probe (include/flashopt_probe.h) reads and writes every byte
 of the AdamW step's state and gradients: its documented XOR of the values it
-read, checked word for word on a ragged list (full tiles and partial tails)."""
+read, checked on every element of a ragged list (full tiles and partial
+tails), through the interleaved code records."""
 import numpy as np
 import pytest
 import torch
 
 from compressed_adamw_state_amd import flashopt as F
 
+from parity import state_fields
+
 pytestmark = pytest.mark.gpu
-
-
-def _rand_bytes(n, dtype, gen):
-    b = torch.randint(0, 256, (n * torch.empty(0, dtype=dtype).element_size(),),
-                      generator=gen, dtype=torch.uint8)
-    return b.view(dtype).cuda()
 
 
 def test_stream_probe_touches_every_byte():
@@ -22,26 +19,24 @@ def test_stream_probe_touches_every_byte():
     states, grads, before = [], [], []
     for n in sizes:
         st = F.TensorState(n, "adamw", "cuda")
-        st.theta.copy_(_rand_bytes(n, torch.int16, gen).view(torch.bfloat16))
-        st.rho.copy_(_rand_bytes(n, torch.int8, gen))
-        st.m_code.copy_(_rand_bytes(n, torch.int8, gen))
-        st.v_code.copy_(_rand_bytes(n, torch.uint8, gen))
-        g = (n + 31) // 32
-        st.m_scale.copy_(_rand_bytes(g, torch.int16, gen).view(torch.float16))
-        st.v_scale.copy_(_rand_bytes(g, torch.int16, gen).view(torch.float16))
-        gr = _rand_bytes(n, torch.int16, gen).view(torch.bfloat16)
+        st.theta.view(torch.int16).copy_(torch.randint(-2 ** 15, 2 ** 15, (n,), generator=gen,
+                                                       dtype=torch.int16))
+        st.codes.copy_(torch.randint(0, 256, st.codes.shape, generator=gen, dtype=torch.uint8))
+        st.scales.copy_(torch.randint(-2 ** 15, 2 ** 15, st.scales.shape, generator=gen,
+                                      dtype=torch.int16))
+        gr = torch.randint(-2 ** 15, 2 ** 15, (n,), generator=gen, dtype=torch.int16)
+        grads.append(gr.cuda().view(torch.bfloat16))
         states.append(st)
-        grads.append(gr)
-        before.append({k: v.clone() for k, v in st.arrays().items()})
+        before.append(state_fields(st))
     lst = F.FlashoptList(states, grads)
     F.flashopt_stream_probe(lst)
     torch.cuda.synchronize()
     for st, gr, b in zip(states, grads, before):
-        h = lambda t: t.view(torch.int16).cpu().numpy() if t.element_size() == 2 else \
-            t.cpu().numpy().view(np.uint8)
-        np.testing.assert_array_equal(h(st.theta), h(b["theta"]) ^ h(gr))
-        np.testing.assert_array_equal(h(st.rho), h(b["rho"]) ^ h(b["m_code"]))
-        np.testing.assert_array_equal(h(st.m_code), h(b["m_code"]) ^ h(b["v_code"]))
-        np.testing.assert_array_equal(h(st.v_code), h(b["v_code"]) ^ h(b["rho"]))
-        np.testing.assert_array_equal(h(st.m_scale), h(b["m_scale"]) ^ 1)
-        np.testing.assert_array_equal(h(st.v_scale), h(b["v_scale"]) ^ 1)
+        f = state_fields(st)
+        g = gr.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(f["theta"], b["theta"] ^ g)
+        np.testing.assert_array_equal(f["rho"], b["rho"] ^ b["m_code"])
+        np.testing.assert_array_equal(f["m_code"], b["m_code"] ^ b["v_code"].view(np.int8))
+        np.testing.assert_array_equal(f["v_code"], b["v_code"] ^ b["rho"].view(np.uint8))
+        np.testing.assert_array_equal(f["m_scale"], b["m_scale"] ^ 1)
+        np.testing.assert_array_equal(f["v_scale"], b["v_scale"] ^ 1)
