@@ -68,6 +68,7 @@ def lib():
             "orc_adamw_step": (None, [_I64, _P, _P, _P, _P, _P, _P, _P,
                                       _D, _D, _D, _D, _D, _I64, _P, _P, _P]),
             "orc_sgd_step": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _I64, _P, _P]),
+            "orc_lion_step": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
         }
         for name in ("bf16_rne_array", "f16_rne_array", "f16_to_f32_array", "phi_m_array",
                      "phi_m_inv_array", "phi_v_array", "phi_v_inv_array"):
@@ -261,10 +262,23 @@ def sgd_step(st: State, grad_bits, t: int, lr, momentum, weight_decay, want_fp32
     return outs if want_fp32 else None
 
 
+def lion_step(st: State, grad_bits, lr, beta1, beta2, weight_decay, want_fp32=False):
+    g = _c(grad_bits, np.uint16).reshape(-1)
+    assert g.size == st.n
+    outs = [np.empty(st.n, np.float32) for _ in range(2)] if want_fp32 else [None] * 2
+    ptrs = [None if o is None else _ptr(o) for o in outs]
+    lib().orc_lion_step(st.n, _ptr(st.tb), _ptr(st.rho), _ptr(st.qm), _ptr(st.sm), _ptr(g),
+                        lr, beta1, beta2, weight_decay, *ptrs)
+    return outs if want_fp32 else None
+
+
 def step(st: State, grad_bits, t: int, hp: dict, want_fp32=False):
     if st.optimizer == "adamw":
         return adamw_step(st, grad_bits, t, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                           hp["weight_decay"], want_fp32)
+    if st.optimizer == "lion":
+        return lion_step(st, grad_bits, hp["lr"], hp["beta1"], hp["beta2"], hp["weight_decay"],
+                         want_fp32)
     return sgd_step(st, grad_bits, t, hp["lr"], hp["momentum"], hp["weight_decay"], want_fp32)
 
 

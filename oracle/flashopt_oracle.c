@@ -469,6 +469,61 @@ void orc_sgd_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qb, uint16_t* sb
     }
 }
 
+/* Lion (named by the FlashOptim page as FlashLion; its update rule is the
+ * published Lion algorithm, not printed on the page): with one compressed
+ * momentum m per parameter,
+ *     c = b1*m + c1*g,  theta_new = lambda*theta_hat - eta*sign(c),
+ *     m_new = b2*m + c2*g,
+ * sign(0) = 0, lambda = 1 - lr*wd (decoupled decay), every line one binary32
+ * operation rounded to nearest.  m is stored like the AdamW momentum:
+ * phi_m companding, INT8 codes, one FP16 scale per group. */
+static float sign1(float c)
+{
+    if (c > 0.0f) return 1.0f;
+    if (c < 0.0f) return -1.0f;
+    return c;                              /* +-0 -> 0 (sign of a zero is dropped below); NaN stays NaN */
+}
+
+void orc_lion_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
+                   const uint16_t* grad, double lr, double beta1, double beta2, double wd,
+                   float* theta_out, float* m_out)
+{
+    const float b1 = (float)beta1, c1 = (float)(1.0 - beta1);
+    const float b2 = (float)beta2, c2 = (float)(1.0 - beta2);
+    const float eta = (float)lr;
+    const float lambda = (float)(1.0 - lr * wd);
+    for (int64_t g = 0; g * GROUP < n; ++g) {
+        int len = group_len(n, g);
+        int64_t o = g * GROUP;
+        float mn[GROUP], z[GROUP], tn[GROUP];
+        for (int j = 0; j < len; ++j) {
+            float theta_hat = unsplit1(tb[o + j], rho[o + j]);
+            float m = dequant_m1(qm[o + j], sm[g]);
+            float gr = orc_bf16_to_f32(grad[o + j]);
+
+            float bm = b1 * m;
+            float cg = c1 * gr;
+            float c = bm + cg;
+            float sgn = sign1(c);
+            if (sgn == 0.0f) sgn = 0.0f;   /* a zero direction is +0 */
+            float decayed = lambda * theta_hat;
+            float step = eta * sgn;
+            float theta_new = decayed - step;
+            float b2m = b2 * m;
+            float c2g = c2 * gr;
+            float m_new = b2m + c2g;
+
+            mn[j] = m_new;
+            tn[j] = theta_new;
+            if (theta_out) theta_out[o + j] = theta_new;
+            if (m_out) m_out[o + j] = m_new;
+        }
+        for (int j = 0; j < len; ++j) z[j] = orc_phi_m(mn[j]);
+        quant_group_m(z, len, qm + o, sm + g);
+        for (int j = 0; j < len; ++j) split1(tn[j], &tb[o + j], &rho[o + j]);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Array helpers for exhaustive checks.                                      */
 

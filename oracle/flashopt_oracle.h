@@ -52,6 +52,13 @@ void orc_sgd_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qb, uint16_t* sb
                   const uint16_t* grad, double lr, double momentum, double wd, int64_t t,
                   float* theta_out, float* b_out);
 
+/* Lion with the compressed single momentum (one scale per group): sign update
+ * of the interpolated momentum, decoupled weight decay.  theta_out / m_out
+ * (nullable) receive theta_new and m_new before requantisation and re-split. */
+void orc_lion_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
+                   const uint16_t* grad, double lr, double beta1, double beta2, double wd,
+                   float* theta_out, float* m_out);
+
 void orc_bf16_rne_array(const float* x, int64_t n, uint16_t* out);
 void orc_f16_rne_array(const float* x, int64_t n, uint16_t* out);
 void orc_f16_to_f32_array(const uint16_t* h, int64_t n, float* out);
