@@ -342,5 +342,20 @@ struct AdamScalars {
     uint32_t quot_neg_lo2, quot_span;
 };
 struct SgdScalars { float mu, eta, omega; };
+// Lion: b1, c1 = 1-beta1 (direction), b2, c2 = 1-beta2 (momentum), eta = lr,
+// lambda = 1 - lr*wd.
+struct LionScalars { float b1, c1, b2, c2, eta, lambda; };
+// One kernel argument for every optimizer; each instantiation reads its own.
+struct StepScalars {
+    AdamScalars a;
+    SgdScalars s;
+    LionScalars l;
+};
+
+// Lion's step direction sign(c): +1, -1, +0 for a zero c (of either sign),
+// NaN for NaN.
+__device__ __forceinline__ float lion_sign(float c) {
+    return c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : (c == c ? 0.0f : c));
+}
 
 }  // namespace flashopt

@@ -34,11 +34,12 @@ namespace flashopt {
 
 #define GLOBAL __attribute__((address_space(1)))
 
-enum Opt { kAdamW = 0, kSgd = 1 };
+enum Opt { kAdamW = 0, kSgd = 1, kLion = 2 };
 
 // State layout of one tensor (see include/flashopt.h): a code record per 8
 // elements -- rho[8], m_code[8] and, for AdamW, v_code[8] -- and per 32-element
-// group the FP16 m scale followed, for AdamW, by the v scale.
+// group the FP16 m scale followed, for AdamW, by the v scale.  SGD and Lion
+// keep one momentum, so they share the 16-byte record.
 template <int kOpt> struct Layout {
     static constexpr int kRec = kOpt == kAdamW ? 24 : 16;   // bytes per 8-element record
     static constexpr int kScl = kOpt == kAdamW ? 2 : 1;     // FP16 scales per group
@@ -222,8 +223,10 @@ __device__ __forceinline__ void load_lane(const GTensor& T, int64_t e, Lane8& L)
 
 template <int kOpt>
 __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
-                                          const Lane8& L, const AdamScalars& a,
-                                          const SgdScalars& s) {
+                                          const Lane8& L, const StepScalars& P) {
+    const AdamScalars& a = P.a;
+    const SgdScalars& s = P.s;
+    const LionScalars& l = P.l;
     float z[8], w[8], tn[8];
     uint32_t amax_m = 0, amax_v = 0;
     const float dm = m_step(L.ms);
@@ -252,13 +255,23 @@ __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
             theta_new = decayed - stp;
             w[j] = root;
             amax_v = max(amax_v, as_u32(root));
-        } else {
+        } else if (kOpt == kSgd) {
             const float decay = s.omega * theta_hat;
             const float g2 = g + decay;
             const float mb = s.mu * m;
             m_new = mb + g2;
             const float stp = s.eta * m_new;
             theta_new = theta_hat - stp;
+        } else {
+            const float bm = l.b1 * m;
+            const float cg = l.c1 * g;
+            const float c = bm + cg;
+            const float decayed = l.lambda * theta_hat;
+            const float stp = l.eta * lion_sign(c);
+            theta_new = decayed - stp;
+            const float b2m = l.b2 * m;
+            const float c2g = l.c2 * g;
+            m_new = b2m + c2g;
         }
         z[j] = phi_m(m_new);
         tn[j] = theta_new;
@@ -351,7 +364,10 @@ __device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32
 
 template <int kOpt>
 __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane, const Raw& R,
-                                          const AdamScalars& a, const SgdScalars& s) {
+                                          const StepScalars& P) {
+    const AdamScalars& a = P.a;
+    const SgdScalars& s = P.s;
+    const LionScalars& l = P.l;
     float z[8], w[8], tn[8], m_new[8], v_new[8], theta_hat[8];
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
@@ -379,13 +395,23 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
             v_new[j] = bv + cgg;
             w[j] = sqrt_fast(v_new[j]);
             vmin = min(vmin, as_u32(v_new[j]) - 1u);
-        } else {
+        } else if (kOpt == kSgd) {
             const float decay = s.omega * theta_hat[j];
             const float g2 = g + decay;
             const float mb = s.mu * m;
             m_new[j] = mb + g2;
             const float stp = s.eta * m_new[j];
             tn[j] = theta_hat[j] - stp;
+        } else {
+            const float bm = l.b1 * m;
+            const float cg = l.c1 * g;
+            const float c = bm + cg;
+            const float decayed = l.lambda * theta_hat[j];
+            const float stp = l.eta * lion_sign(c);
+            tn[j] = decayed - stp;
+            const float b2m = l.b2 * m;
+            const float c2g = l.c2 * g;
+            m_new[j] = b2m + c2g;
         }
     }
     if (kOpt == kAdamW) {
@@ -495,14 +521,14 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
 // a tensor goes one bounds-checked sub-tile at a time.
 template <int kOpt, bool kFull>
 __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane,
-                                          const AdamScalars& a, const SgdScalars& s) {
+                                          const StepScalars& P) {
     if (kFull) {
         Raw R[2];
         load_raw<kOpt>(T, e0 + lane * kLaneElems, R[0]);
         if (kSubTiles > 1) load_raw<kOpt>(T, e0 + kSubTile + lane * kLaneElems, R[1]);
 #pragma unroll
         for (int k = 0; k < kSubTiles; ++k) {
-            step_fast<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1], a, s);
+            step_fast<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1], P);
             if (k + 2 < kSubTiles)
                 load_raw<kOpt>(T, e0 + (k + 2) * kSubTile + lane * kLaneElems, R[k & 1]);
         }
@@ -510,7 +536,7 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
         for (int k = 0; k < kSubTiles; ++k) {
             Lane8 L;
             load_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, L);
-            step_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, a, s);
+            step_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, P);
         }
     }
 }
@@ -521,7 +547,7 @@ template <int kOpt>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
                                                    const int64_t* __restrict__ tile_begin,
                                                    int32_t count, int64_t total_tiles,
-                                                   DevTensor one, AdamScalars a, SgdScalars s) {
+                                                   DevTensor one, StepScalars P) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
@@ -531,8 +557,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
     for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const int64_t e0 = (tile - cur.begin) * kTile;
-        if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true>(cur.T, e0, lane, a, s);
-        else step_tile<kOpt, false>(cur.T, e0, lane, a, s);
+        if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true>(cur.T, e0, lane, P);
+        else step_tile<kOpt, false>(cur.T, e0, lane, P);
     }
 }
 
@@ -920,7 +946,34 @@ static int check_sgd(const flashopt_sgd_hparams* hp, int64_t step) {
     return FLASHOPT_OK;
 }
 
-static bool valid_kind(int32_t kind) { return kind == FLASHOPT_KIND_ADAMW || kind == FLASHOPT_KIND_SGD; }
+static bool valid_kind(int32_t kind) {
+    return kind == FLASHOPT_KIND_ADAMW || kind == FLASHOPT_KIND_SGD || kind == FLASHOPT_KIND_LION;
+}
+
+static int check_lion(const flashopt_lion_hparams* hp, int64_t step) {
+    if (!hp) return FLASHOPT_ERR_NULL;
+    if (step < 1) return FLASHOPT_ERR_STEP;
+    if (!(hp->lr >= 0.0) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->weight_decay >= 0.0) ||
+        !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+        return FLASHOPT_ERR_ARG;
+    return FLASHOPT_OK;
+}
+
+static SgdScalars sgd_scalars(const flashopt_sgd_hparams& hp) {
+    return SgdScalars{(float)hp.momentum, (float)hp.lr, (float)hp.weight_decay};
+}
+
+static LionScalars lion_scalars(const flashopt_lion_hparams& hp) {
+    LionScalars l;
+    l.b1 = (float)hp.beta1;
+    l.c1 = (float)(1.0 - hp.beta1);
+    l.b2 = (float)hp.beta2;
+    l.c2 = (float)(1.0 - hp.beta2);
+    l.eta = (float)hp.lr;
+    l.lambda = (float)(1.0 - hp.lr * hp.weight_decay);
+    return l;
+}
 
 static int check_tensor(const flashopt_tensor& t, int32_t kind) {
     if (t.numel < 0 || t.numel > kMaxNumel) return FLASHOPT_ERR_SIZE;
@@ -1092,7 +1145,7 @@ int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta,
     if (!valid_kind(kind)) return FLASHOPT_ERR_ARG;
     const int st = check_tensor(*t, kind);
     if (st != FLASHOPT_OK) return st;
-    if (kind == FLASHOPT_KIND_SGD) v = nullptr;
+    if (kind != FLASHOPT_KIND_ADAMW) v = nullptr;           // one-momentum layouts have no v
     if (t->numel == 0 || (!theta && !m && !v)) return FLASHOPT_OK;
     const int64_t chunks = (t->numel + kSubTile - 1) / kSubTile;
     if (kind == FLASHOPT_KIND_ADAMW)
@@ -1212,32 +1265,44 @@ int flashopt_stream_probe(const flashopt_list* L, void* stream) {
 }
 
 static int launch_step(int opt, const DevTensor* table, const int64_t* tile_begin, int32_t count,
-                       int64_t total_tiles, const DevTensor& one, const AdamScalars& a,
-                       const SgdScalars& s, void* stream) {
+                       int64_t total_tiles, const DevTensor& one, const StepScalars& P,
+                       void* stream) {
     if (total_tiles == 0) return FLASHOPT_OK;
     const dim3 grid(grid_for(total_tiles));
+    hipStream_t st = (hipStream_t)stream;
     if (opt == kAdamW)
-        hipLaunchKernelGGL(step_kernel<kAdamW>, grid, dim3(kBlock), 0, (hipStream_t)stream, table,
-                           tile_begin, count, total_tiles, one, a, s);
+        hipLaunchKernelGGL(step_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table, tile_begin,
+                           count, total_tiles, one, P);
+    else if (opt == kSgd)
+        hipLaunchKernelGGL(step_kernel<kSgd>, grid, dim3(kBlock), 0, st, table, tile_begin,
+                           count, total_tiles, one, P);
     else
-        hipLaunchKernelGGL(step_kernel<kSgd>, grid, dim3(kBlock), 0, (hipStream_t)stream, table,
-                           tile_begin, count, total_tiles, one, a, s);
+        hipLaunchKernelGGL(step_kernel<kLion>, grid, dim3(kBlock), 0, st, table, tile_begin,
+                           count, total_tiles, one, P);
     return launch_status();
 }
 
-static int launch_list(int opt, const flashopt_list* L, const AdamScalars& a,
-                       const SgdScalars& s, void* stream) {
+static int launch_list(int opt, const flashopt_list* L, const StepScalars& P, void* stream) {
     return launch_step(opt, L->d_table, L->d_tile_begin, L->count, L->total_tiles, DevTensor{},
-                       a, s, stream);
+                       P, stream);
 }
 
 static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint16_t* grad,
-                      const AdamScalars& a, const SgdScalars& s, void* stream) {
+                      const StepScalars& P, void* stream) {
     const flashopt_tensor& t = L->host[index];
     if (t.numel == 0) return FLASHOPT_OK;
     DevTensor one = to_dev(t);
     one.grad = (uint64_t)grad;
-    return launch_step(opt, nullptr, nullptr, 1, tiles_of(t.numel), one, a, s, stream);
+    return launch_step(opt, nullptr, nullptr, 1, tiles_of(t.numel), one, P, stream);
+}
+
+static int check_one(const flashopt_list* L, int32_t index, const uint16_t* grad) {
+    if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
+    if (L->host[index].numel > 0) {
+        if (!grad) return FLASHOPT_ERR_NULL;
+        if (!aligned(grad, 16)) return FLASHOPT_ERR_ALIGN;
+    }
+    return FLASHOPT_OK;
 }
 
 int flashopt_adamw_step(const flashopt_list* L, const flashopt_adamw_hparams* hp, int64_t step,
@@ -1248,8 +1313,9 @@ int flashopt_adamw_step(const flashopt_list* L, const flashopt_adamw_hparams* hp
     if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     flashopt_list* M = const_cast<flashopt_list*>(L);   // only the scalar cache changes
-    const AdamScalars a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
-    return launch_list(kAdamW, L, a, SgdScalars{}, stream);
+    StepScalars P{};
+    P.a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
+    return launch_list(kAdamW, L, P, stream);
 }
 
 int flashopt_sgd_step(const flashopt_list* L, const flashopt_sgd_hparams* hp, int64_t step,
@@ -1259,8 +1325,21 @@ int flashopt_sgd_step(const flashopt_list* L, const flashopt_sgd_hparams* hp, in
     if (st != FLASHOPT_OK) return st;
     if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
-    SgdScalars s{(float)hp->momentum, (float)hp->lr, (float)hp->weight_decay};
-    return launch_list(kSgd, L, AdamScalars{}, s, stream);
+    StepScalars P{};
+    P.s = sgd_scalars(*hp);
+    return launch_list(kSgd, L, P, stream);
+}
+
+int flashopt_lion_step(const flashopt_list* L, const flashopt_lion_hparams* hp, int64_t step,
+                       void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    int st = check_lion(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (L->kind != FLASHOPT_KIND_LION) return FLASHOPT_ERR_ARG;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    StepScalars P{};
+    P.l = lion_scalars(*hp);
+    return launch_list(kLion, L, P, stream);
 }
 
 int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,
@@ -1270,14 +1349,12 @@ int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_
     int st = check_adam(hp, step);
     if (st != FLASHOPT_OK) return st;
     if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
-    const flashopt_tensor& t = L->host[index];
-    if (t.numel > 0) {
-        if (!grad) return FLASHOPT_ERR_NULL;
-        if (!aligned(grad, 16)) return FLASHOPT_ERR_ALIGN;
-    }
+    st = check_one(L, index, grad);
+    if (st != FLASHOPT_OK) return st;
     flashopt_list* M = const_cast<flashopt_list*>(L);
-    const AdamScalars a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
-    return launch_one(kAdamW, L, index, grad, a, SgdScalars{}, stream);
+    StepScalars P{};
+    P.a = adam_scalars(*hp, step, &M->p1, &M->p2, &M->t, &M->b1, &M->b2);
+    return launch_one(kAdamW, L, index, grad, P, stream);
 }
 
 int flashopt_sgd_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,
@@ -1287,13 +1364,25 @@ int flashopt_sgd_step_one(const flashopt_list* L, int32_t index, const uint16_t*
     int st = check_sgd(hp, step);
     if (st != FLASHOPT_OK) return st;
     if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
-    const flashopt_tensor& t = L->host[index];
-    if (t.numel > 0) {
-        if (!grad) return FLASHOPT_ERR_NULL;
-        if (!aligned(grad, 16)) return FLASHOPT_ERR_ALIGN;
-    }
-    SgdScalars s{(float)hp->momentum, (float)hp->lr, (float)hp->weight_decay};
-    return launch_one(kSgd, L, index, grad, AdamScalars{}, s, stream);
+    st = check_one(L, index, grad);
+    if (st != FLASHOPT_OK) return st;
+    StepScalars P{};
+    P.s = sgd_scalars(*hp);
+    return launch_one(kSgd, L, index, grad, P, stream);
+}
+
+int flashopt_lion_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,
+                           const flashopt_lion_hparams* hp, int64_t step, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
+    int st = check_lion(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (L->kind != FLASHOPT_KIND_LION) return FLASHOPT_ERR_ARG;
+    st = check_one(L, index, grad);
+    if (st != FLASHOPT_OK) return st;
+    StepScalars P{};
+    P.l = lion_scalars(*hp);
+    return launch_one(kLion, L, index, grad, P, stream);
 }
 
 }  // extern "C"

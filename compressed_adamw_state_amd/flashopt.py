@@ -28,9 +28,9 @@ class FlashoptError(RuntimeError):
         self.status = status
 
 
-KIND = {"adamw": 0, "sgd": 1}          # flashopt_kind
-RECORD = {"adamw": 24, "sgd": 16}      # code-record bytes per 8 elements
-SCALES = {"adamw": 2, "sgd": 1}        # FP16 scales per 32-element group
+KIND = {"adamw": 0, "sgd": 1, "lion": 2}          # flashopt_kind
+RECORD = {"adamw": 24, "sgd": 16, "lion": 16}     # code-record bytes per 8 elements
+SCALES = {"adamw": 2, "sgd": 1, "lion": 1}        # FP16 scales per 32-element group
 
 
 class Tensor(ctypes.Structure):
@@ -45,6 +45,11 @@ class AdamWHparams(ctypes.Structure):
 
 class SGDHparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("weight_decay", ctypes.c_double)]
+
+
+class LionHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("weight_decay", ctypes.c_double)]
 
 
@@ -75,6 +80,9 @@ SIGNATURES = {
     "flashopt_sgd_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(SGDHparams), _I64,
                                              _P]),
     "flashopt_stream_probe": (ctypes.c_int, [_P, _P]),
+    "flashopt_lion_step": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
+    "flashopt_lion_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(LionHparams),
+                                              _I64, _P]),
 }
 
 _lib = None
@@ -281,19 +289,33 @@ def flashopt_sgd_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: i
                                        _stream(stream)))
 
 
+def _lion(hp: dict) -> LionHparams:
+    return LionHparams(hp["lr"], hp["beta1"], hp["beta2"], hp["weight_decay"])
+
+
+def flashopt_lion_step(lst: FlashoptList, hp: dict, step: int, stream=None) -> None:
+    h = _lion(hp)
+    _check("flashopt_lion_step", lib().flashopt_lion_step(lst.handle, ctypes.byref(h), step,
+                                                          _stream(stream)))
+
+
+def flashopt_lion_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: int,
+                           stream=None) -> None:
+    h = _lion(hp)
+    _check("flashopt_lion_step_one",
+           lib().flashopt_lion_step_one(lst.handle, index, _ptr(grad), ctypes.byref(h), step,
+                                        _stream(stream)))
+
+
 def step(lst: FlashoptList, optimizer: str, hp: dict, t: int, stream=None) -> None:
-    if optimizer == "adamw":
-        flashopt_adamw_step(lst, hp, t, stream)
-    else:
-        flashopt_sgd_step(lst, hp, t, stream)
+    {"adamw": flashopt_adamw_step, "sgd": flashopt_sgd_step,
+     "lion": flashopt_lion_step}[optimizer](lst, hp, t, stream)
 
 
 def step_one(lst: FlashoptList, optimizer: str, index: int, grad, hp: dict, t: int,
              stream=None) -> None:
-    if optimizer == "adamw":
-        flashopt_adamw_step_one(lst, index, grad, hp, t, stream)
-    else:
-        flashopt_sgd_step_one(lst, index, grad, hp, t, stream)
+    {"adamw": flashopt_adamw_step_one, "sgd": flashopt_sgd_step_one,
+     "lion": flashopt_lion_step_one}[optimizer](lst, index, grad, hp, t, stream)
 
 
 def build_list(theta_fp32: List[torch.Tensor], optimizer: str,

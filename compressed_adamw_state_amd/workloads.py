@@ -61,6 +61,9 @@ class Workload:
 
 ADAMW_HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 SGD_HP = dict(lr=0.1, momentum=0.9, weight_decay=1e-4)
+# Lion: the published rule's usual setting (a smaller lr and a larger decay than AdamW)
+LION_HP = dict(lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.1)
+HPARAMS = {"adamw": ADAMW_HP, "sgd": SGD_HP, "lion": LION_HP}
 
 
 def gpt2_small() -> List[TensorSpec]:
@@ -147,6 +150,9 @@ WORKLOADS = {
                            ADAMW_HP),
     "llama2_13b": Workload("llama2_13b", tuple(llama2_13b()), "adamw", 10, 4, "mixed", 1e-4,
                            ADAMW_HP, release=True, special_theta=True),
+    # FlashLion at the Llama-3.1-8B shapes (the one-momentum layout, 10.125 B/param)
+    "llama31_8b_lion": Workload("llama31_8b_lion", tuple(llama31_8b()), "lion", 20, 5, "normal",
+                                1e-4, LION_HP),
 }
 
 
@@ -155,7 +161,7 @@ def ragged(sizes: Sequence[int], seed: int = 7, steps: int = 3, optimizer: str =
     """A list of 1-D tensors of arbitrary sizes (tail-group coverage)."""
     t = tuple(TensorSpec(f"t{i}", (n,), "normal") for i, n in enumerate(sizes))
     return Workload(f"ragged{len(sizes)}", t, optimizer, steps, seed, "normal", grad_scale,
-                    ADAMW_HP if optimizer == "adamw" else SGD_HP)
+                    HPARAMS[optimizer])
 
 
 # ---------------------------------------------------------------------------

@@ -86,7 +86,8 @@ typedef enum flashopt_status {
 /* Optimizer kind of a tensor's state layout (and of a list). */
 typedef enum flashopt_kind {
     FLASHOPT_KIND_ADAMW = 0,     /* rho, momentum and variance codes; two scales per group */
-    FLASHOPT_KIND_SGD = 1        /* rho and momentum codes; one scale per group            */
+    FLASHOPT_KIND_SGD = 1,       /* rho and momentum codes; one scale per group            */
+    FLASHOPT_KIND_LION = 2       /* the SGD layout, holding Lion's momentum                */
 } flashopt_kind;
 
 /* One parameter tensor and its compressed state (all DEVICE pointers).
@@ -98,10 +99,10 @@ typedef enum flashopt_kind {
  *   codes[r*R + 0 + j]  = rho of element 8r+j          (INT8, two's complement)
  *   codes[r*R + 8 + j]  = momentum code of element 8r+j (INT8; SGD: momentum buffer)
  *   codes[r*R + 16 + j] = variance code of element 8r+j (UINT8; AdamW only)
- * with R = 24 (AdamW) or 16 (SGD), r < ceil(n/8), j < 8; the last record's
+ * with R = 24 (AdamW) or 16 (SGD, Lion), r < ceil(n/8), j < 8; the last record's
  * entries past n are padding (never read as state, may be overwritten).
  *   scales[2g], scales[2g+1] = FP16 momentum and variance scales of group g (AdamW)
- *   scales[g]                = FP16 momentum scale of group g (SGD)
+ *   scales[g]                = FP16 momentum scale of group g (SGD, Lion)
  * for g < ceil(n/32).  flashopt_codes_bytes / flashopt_scales_bytes give the
  * sizes.  The values are exactly those of the flat arrays the quantisers and
  * split below produce, only their placement differs. */
@@ -127,6 +128,18 @@ typedef struct flashopt_sgd_hparams {
     double momentum;      /* [0, 1); dampening 0, no Nesterov      */
     double weight_decay;  /* >= 0, L2 added to the gradient        */
 } flashopt_sgd_hparams;
+
+/* Lion (named by the FlashOptim page as FlashLion; the update is the published
+ * Lion rule): c = b1*m + c1*g, theta_n = lambda*theta_hat - lr*sign(c) with
+ * sign(0) = 0, m' = b2*m + c2*g; b1 = beta1, c1 = 1-beta1, b2 = beta2,
+ * c2 = 1-beta2, lambda = 1-lr*wd, each rounded once to binary32.  m is stored
+ * like the AdamW momentum (phi_m, INT8, FP16 group scale). */
+typedef struct flashopt_lion_hparams {
+    double lr;            /* >= 0                                  */
+    double beta1;         /* [0, 1): interpolation for the direction */
+    double beta2;         /* [0, 1): momentum decay                 */
+    double weight_decay;  /* >= 0, decoupled (scaled by lr)        */
+} flashopt_lion_hparams;
 
 typedef struct flashopt_list flashopt_list;   /* opaque; host memory owned by the library */
 
@@ -175,9 +188,9 @@ int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta,
  * (it is a set-up call); afterwards the descriptors' pointers are fixed,
  * except the gradients (flashopt_list_set_grads).  count may be 0. */
 size_t flashopt_list_workspace_bytes(int32_t count);
-/* kind: FLASHOPT_KIND_ADAMW (steps with flashopt_adamw_step*) or
- * FLASHOPT_KIND_SGD (flashopt_sgd_step*); a step of the other kind returns
- * FLASHOPT_ERR_ARG. */
+/* kind: FLASHOPT_KIND_ADAMW (steps with flashopt_adamw_step*),
+ * FLASHOPT_KIND_SGD (flashopt_sgd_step*) or FLASHOPT_KIND_LION
+ * (flashopt_lion_step*); a step of another kind returns FLASHOPT_ERR_ARG. */
 int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, int32_t kind,
                          void* workspace, size_t workspace_bytes, void* stream,
                          flashopt_list** out);
@@ -198,6 +211,9 @@ int flashopt_adamw_step(const flashopt_list* list, const flashopt_adamw_hparams*
                         int64_t step, void* stream);
 int flashopt_sgd_step(const flashopt_list* list, const flashopt_sgd_hparams* hp,
                       int64_t step, void* stream);
+/* Lion has no step-dependent scalar; step must still be >= 1. */
+int flashopt_lion_step(const flashopt_list* list, const flashopt_lion_hparams* hp,
+                       int64_t step, void* stream);
 
 /* ---- gradient release (fused-step section): step tensor `index` of the list
  * now, reading `grad` (device BF16 [numel], overriding the descriptor's
@@ -207,6 +223,8 @@ int flashopt_adamw_step_one(const flashopt_list* list, int32_t index, const uint
                             const flashopt_adamw_hparams* hp, int64_t step, void* stream);
 int flashopt_sgd_step_one(const flashopt_list* list, int32_t index, const uint16_t* grad,
                           const flashopt_sgd_hparams* hp, int64_t step, void* stream);
+int flashopt_lion_step_one(const flashopt_list* list, int32_t index, const uint16_t* grad,
+                           const flashopt_lion_hparams* hp, int64_t step, void* stream);
 
 #ifdef __cplusplus
 }

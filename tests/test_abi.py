@@ -95,5 +95,21 @@ def test_host_validation_without_gpu():
     sgd = F.SGDHparams(0.1, 0.9, 0.0)
     assert lib.flashopt_sgd_step(L, ctypes.byref(sgd), 1, None) == -4   # AdamW list
     assert lib.flashopt_adamw_step_one(L, 0, fake, ctypes.byref(hp), 1, None) == -8
+    lion = F.LionHparams(1e-4, 0.9, 0.99, 0.1)
+    assert lib.flashopt_lion_step(None, ctypes.byref(lion), 1, None) == -1
+    assert lib.flashopt_lion_step(L, ctypes.byref(lion), 1, None) == -4     # AdamW list
+    assert lib.flashopt_lion_step_one(L, 0, fake, ctypes.byref(lion), 1, None) == -8
     assert lib.flashopt_state_zero(L, None) == 0
+    assert lib.flashopt_list_destroy(L) == 0
+    # an empty Lion list: hyper-parameter and step checks
+    assert lib.flashopt_list_create(None, 0, 2, None, 0, None, ctypes.byref(out)) == 0
+    L = out
+    assert lib.flashopt_lion_step(L, ctypes.byref(lion), 0, None) == -5
+    for bad_l in (F.LionHparams(-1, 0.9, 0.99, 0), F.LionHparams(1e-4, 1.0, 0.99, 0),
+                  F.LionHparams(1e-4, 0.9, -0.1, 0), F.LionHparams(1e-4, 0.9, 0.99, -1),
+                  F.LionHparams(float("inf"), 0.9, 0.99, 0)):
+        assert lib.flashopt_lion_step(L, ctypes.byref(bad_l), 1, None) == -4
+    assert lib.flashopt_lion_step(L, ctypes.byref(lion), 1, None) == 0      # nothing to launch
+    assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == -4      # Lion list
+    assert lib.flashopt_codes_bytes(2, 17) == 3 * 16 and lib.flashopt_scales_bytes(2, 33) == 4
     assert lib.flashopt_list_destroy(L) == 0

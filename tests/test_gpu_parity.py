@@ -131,9 +131,9 @@ def test_quantizer_every_code_and_scale():
                                   oracle.dequant_v(qv, s).view(np.uint32))
 
 
-@pytest.mark.parametrize("opt", ["adamw", "sgd"])
+@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion"])
 def test_ragged_list_every_step(opt):
-    w = W.ragged(RAGGED, seed=11, steps=4, optimizer=opt, grad_scale=1e-3 if opt == "adamw" else 1e-2)
+    w = W.ragged(RAGGED, seed=11, steps=4, optimizer=opt, grad_scale=1e-2 if opt == "sgd" else 1e-3)
     r = Run(w, "full")
     r.compare("init")
     for t in range(1, w.steps + 1):
@@ -141,7 +141,7 @@ def test_ragged_list_every_step(opt):
         r.compare(f"step {t}")
 
 
-@pytest.mark.parametrize("opt", ["adamw", "sgd"])
+@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion"])
 def test_release_mode_matches_list_mode(opt):
     base = W.ragged(RAGGED[:12], seed=12, steps=3, optimizer=opt)
     rel = W.Workload(base.name, base.tensors, opt, 3, base.seed, base.grad_dist, base.grad_scale,
@@ -182,6 +182,23 @@ def test_adam_quotient_window_edges(grad_scale):
     for t, eps in enumerate([1e-8, 1e-30, 1e-40, 1e3], 1):
         r.step(t, dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=eps, weight_decay=0.01))
         r.compare(f"grad scale {grad_scale}, eps {eps}")
+
+
+def test_lion_hyperparameter_variants_and_edge_gradients():
+    # zero, subnormal and outlier gradients (sign(0) = 0 leaves only the decay),
+    # special weights, and settings that isolate each coefficient
+    base = W.ragged([4097, 1000, 33, 2048 * 2], seed=16, steps=1, optimizer="lion")
+    w = W.Workload("lion_edges", base.tensors, "lion", 6, 16, "mixed", 1e-3, W.LION_HP,
+                   special_theta=True)
+    r = Run(w, "full")
+    for t, hp in enumerate([W.LION_HP,
+                            dict(lr=1e-3, beta1=0.0, beta2=0.0, weight_decay=0.0),
+                            dict(lr=3e-4, beta1=0.99, beta2=0.5, weight_decay=1.0),
+                            dict(lr=0.0, beta1=0.9, beta2=0.99, weight_decay=0.1),
+                            dict(lr=1e-2, beta1=0.5, beta2=0.999, weight_decay=0.0),
+                            W.LION_HP], 1):
+        r.step(t, hp)
+        r.compare(f"lion hp {t}")
 
 
 def test_set_grads_and_state_zero():
@@ -242,6 +259,17 @@ def test_config4_llama8b_sampled():
         if t in (1, 2, 10, w.steps):
             n = r.compare(f"step {t}")
             log(f"llama8b step {t}: {n} sampled elements compared")
+
+
+def test_llama8b_lion_sampled():
+    w = W.WORKLOADS["llama31_8b_lion"]
+    r = Run(w, "sampled", samples_per_tensor=4)
+    log("llama8b lion: state built")
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        if t in (1, 2, w.steps):
+            n = r.compare(f"step {t}")
+            log(f"llama8b lion step {t}: {n} sampled elements compared")
 
 
 def test_config5_llama13b_release_sampled():
