@@ -114,6 +114,31 @@ def copy_ceiling(nbytes: int, stream, reps: int = 5):
             "best_ms": best * 1e3, "gb_s": 8 * n / best / 1e9}
 
 
+def other_optimizer(name: str, steps: int, stream) -> dict:
+    """Time `steps` list steps of another optimizer's workload (after warm-up);
+    state built fresh, freed on return."""
+    w = W.WORKLOADS[name]
+    states, grads, lists = build_state(w, grad_sets=2)
+    for t in (1, 2):
+        F.step(lists[t % 2], w.optimizer, w.hparams, t, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for k in range(steps):
+        F.step(lists[k % 2], w.optimizer, w.hparams, k + 3, stream)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])    # ms
+    del states, grads, lists
+    torch.cuda.synchronize()
+    ms = float(np.median(per))
+    gbs = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+    return {"workload": name, "optimizer": w.optimizer, "params": w.numel,
+            "bytes_per_param": algorithmic_bytes(w) / w.numel, "step_ms_median": ms,
+            "step_ms_min": float(per.min()), "params_s": w.numel / (ms * 1e-3),
+            "algorithmic_gb_s": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS}
+
+
 def stream_probe(lst, stream, bytes_step: int, reps: int = 5):
     """The step's exact loads and stores with no arithmetic (flashopt_stream_probe):
     the practical floor of its access pattern.  Overwrites the state."""
@@ -196,6 +221,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=1 << 32,
                     help="size of the plain copy kernel timed after the steps (0: skip)")
+    ap.add_argument("--no-other-optimizers", action="store_true",
+                    help="skip the FlashLion (Llama-3.1-8B) and FlashSGD (ResNet-50) lines")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -291,6 +318,11 @@ def main():
     log(f"bench: stream probe {out['stream_probe']['gb_s']:.0f} GB/s")
     del states, grads, lists
     torch.cuda.synchronize()
+    if not args.no_other_optimizers:
+        out["other_optimizers"] = [other_optimizer("llama31_8b_lion", 10, stream),
+                                   other_optimizer("resnet50", 10, stream)]
+        for o in out["other_optimizers"]:
+            log(f"bench: {o['optimizer']} {o['workload']}: {o['step_ms_median']:.3f} ms/step")
     if args.copy_bytes:
         out["copy_ceiling"] = copy_ceiling(args.copy_bytes, stream)
         log(f"bench: plain copy {out['copy_ceiling']['gb_s']:.0f} GB/s")
