@@ -167,11 +167,17 @@ class TensorState:
     BF16 theta', the interleaved code records and the FP16 scales, in the
     layout of include/flashopt.h."""
 
-    def __init__(self, numel: int, optimizer: str, device):
+    def __init__(self, numel: int, optimizer: str, device, theta: Optional[torch.Tensor] = None):
+        """theta: an existing contiguous BF16 tensor of numel elements to use as
+        theta' (e.g. a model parameter's data); allocated when None."""
         self.numel = numel
         self.optimizer = optimizer
         self.kind = KIND[optimizer]
-        self.theta = torch.empty(numel, dtype=torch.bfloat16, device=device)
+        if theta is None:
+            theta = torch.empty(numel, dtype=torch.bfloat16, device=device)
+        elif theta.dtype != torch.bfloat16 or theta.numel() != numel or not theta.is_contiguous():
+            raise ValueError("theta must be a contiguous BF16 tensor of numel elements")
+        self.theta = theta.view(-1)
         self.codes = torch.zeros(lib().flashopt_codes_bytes(self.kind, numel), dtype=torch.uint8,
                                  device=device)
         self.scales = torch.zeros(lib().flashopt_scales_bytes(self.kind, numel) // 2,

@@ -1,0 +1,203 @@
+"""Drop-in optimizers over the fused compressed step: FlashAdamW, FlashSGD,
+FlashLion ("FlashOptim: Optimizers for Memory Efficient Training", Practical
+advice: replace the standard optimizer, keep the hyper-parameters).
+
+Each parameter's BF16 data is theta' -- the weight the model computes with
+-- and the optimizer keeps, per parameter, the interleaved code records (rho,
+momentum and, for AdamW, variance codes) and the FP16 group scales in the
+layout of include/flashopt.h.  A parameter given in FP32 is split once at
+construction: its data becomes the BF16 theta' and rho keeps the rest of the
+FP32 value.  Every step is one launch of the library's fused kernel per
+parameter group (or, with gradient release, one launch per parameter from
+its gradient hook, after which the gradient is dropped).
+
+state_dict() holds the codes and scales (3.125 B/param for AdamW, 2.0625
+for SGD and Lion) plus the step counter; with theta' saved as the model's
+own BF16 weights, an AdamW checkpoint is 5.125 B/param (the page's 12 -> 5
+B/param).  Loading it into a fresh optimizer resumes bit for bit.
+
+This module only marshals: every arithmetic operation of the update runs in
+the HIP library, and there is no fallback.
+"""
+from __future__ import annotations
+
+from typing import Iterable, List, Optional
+
+import torch
+
+from . import flashopt as F
+
+
+class _FlashOptimizer(torch.optim.Optimizer):
+    kind = ""                                    # "adamw" | "sgd" | "lion"
+
+    def __init__(self, params, defaults: dict, gradient_release: bool = False):
+        super().__init__(params, defaults)
+        self.gradient_release = gradient_release
+        self._t = 0                              # optimizer steps taken (the AdamW t)
+        self._lists: List[Optional[F.FlashoptList]] = []
+        self._hooks = []
+        for group in self.param_groups:
+            for p in group["params"]:
+                self._init_param(p)
+        self._build_lists()
+        if gradient_release:
+            self._install_release_hooks()
+
+    # -- state -----------------------------------------------------------------
+    def _init_param(self, p: torch.Tensor) -> None:
+        if not p.is_cuda:
+            raise ValueError("FlashOptim parameters must live on the GPU")
+        if p.dtype == torch.float32:
+            st = F.TensorState(p.numel(), self.kind, p.device)
+            F.flashopt_tensor_init(st, p.detach().reshape(-1).contiguous())
+            p.data = st.theta.view(p.shape)      # the model now computes with theta'
+        elif p.dtype == torch.bfloat16:
+            if not p.is_contiguous():
+                raise ValueError("BF16 parameters must be contiguous")
+            # theta' is the parameter's own storage; the split of its exact FP32
+            # value rewrites the same BF16 bits and gives rho = 0
+            st = F.TensorState(p.numel(), self.kind, p.device, theta=p.data.view(-1))
+            F.flashopt_tensor_init(st, p.detach().reshape(-1).float())
+        else:
+            raise ValueError(f"unsupported parameter dtype {p.dtype}")
+        self.state[p]["flash"] = st
+
+    def _build_lists(self) -> None:
+        self._lists = []
+        for group in self.param_groups:
+            states = [self.state[p]["flash"] for p in group["params"]]
+            grads = [None] * len(states)
+            self._lists.append(F.FlashoptList(states, grads, optimizer=self.kind)
+                               if states else None)
+
+    def _hp(self, group) -> dict:
+        raise NotImplementedError
+
+    # -- the step ----------------------------------------------------------------
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        if self.gradient_release:
+            # the hooks already stepped every parameter of this iteration
+            self._t += 1
+            return loss
+        self._t += 1
+        for group, lst in zip(self.param_groups, self._lists):
+            if lst is None:
+                continue
+            grads = []
+            for p in group["params"]:
+                g = p.grad
+                if g is None:
+                    g = torch.zeros_like(p)      # no gradient this step: a zero gradient
+                if g.dtype != torch.bfloat16 or not g.is_contiguous():
+                    raise ValueError("FlashOptim expects contiguous BF16 gradients")
+                grads.append(g.view(-1))
+            F.flashopt_list_set_grads(lst, grads)
+            F.step(lst, self.kind, self._hp(group), self._t)
+        return loss
+
+    def _install_release_hooks(self) -> None:
+        for gi, group in enumerate(self.param_groups):
+            for pi, p in enumerate(group["params"]):
+                def hook(param, gi=gi, pi=pi):
+                    g = param.grad
+                    if g.dtype != torch.bfloat16 or not g.is_contiguous():
+                        raise ValueError("FlashOptim expects contiguous BF16 gradients")
+                    F.step_one(self._lists[gi], self.kind, pi, g.view(-1),
+                               self._hp(self.param_groups[gi]), self._t + 1)
+                    param.grad = None            # gradient release: 2 B/param freed early
+                self._hooks.append(p.register_post_accumulate_grad_hook(hook))
+
+    # -- checkpoints -------------------------------------------------------------
+    def state_dict(self) -> dict:
+        sd = {"kind": self.kind, "t": self._t, "param_groups": [], "state": {}}
+        index = 0
+        for group in self.param_groups:
+            g = {k: v for k, v in group.items() if k != "params"}
+            g["params"] = []
+            for p in group["params"]:
+                st = self.state[p]["flash"]
+                sd["state"][index] = {"numel": st.numel, "codes": st.codes.clone(),
+                                      "scales": st.scales.clone()}
+                g["params"].append(index)
+                index += 1
+            sd["param_groups"].append(g)
+        return sd
+
+    def load_state_dict(self, sd: dict) -> None:
+        if sd.get("kind") != self.kind:
+            raise ValueError(f"checkpoint is for {sd.get('kind')}, not {self.kind}")
+        saved = sd["param_groups"]
+        if len(saved) != len(self.param_groups) or any(
+                len(a["params"]) != len(b["params"]) for a, b in zip(saved, self.param_groups)):
+            raise ValueError("checkpoint has a different parameter layout")
+        for group, sgroup in zip(self.param_groups, saved):
+            for k, v in sgroup.items():
+                if k != "params":
+                    group[k] = v
+            for p, idx in zip(group["params"], sgroup["params"]):
+                src = sd["state"][idx]
+                st = self.state[p]["flash"]
+                if src["numel"] != st.numel:
+                    raise ValueError("checkpoint tensor size differs")
+                st.codes.copy_(src["codes"])
+                st.scales.copy_(src["scales"])
+        self._t = int(sd["t"])
+
+    def export_fp32(self, p: torch.Tensor):
+        """(theta_hat, m, v) of one parameter in FP32 (v None unless AdamW)."""
+        st = self.state[p]["flash"]
+        th = torch.empty(st.numel, dtype=torch.float32, device=st.theta.device)
+        m = torch.empty_like(th)
+        v = torch.empty_like(th) if self.kind == "adamw" else None
+        F.flashopt_tensor_export(st, th, m, v)
+        return th, m, v
+
+
+class FlashAdamW(_FlashOptimizer):
+    """AdamW (decoupled weight decay, bias correction) with FlashOptim's
+    compressed weight and moments."""
+    kind = "adamw"
+
+    def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 1e-2, gradient_release: bool = False):
+        super().__init__(params, dict(lr=lr, betas=tuple(betas), eps=eps,
+                                      weight_decay=weight_decay), gradient_release)
+
+    def _hp(self, group) -> dict:
+        return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],
+                    eps=group["eps"], weight_decay=group["weight_decay"])
+
+
+class FlashSGD(_FlashOptimizer):
+    """SGD with momentum (L2 weight decay, no dampening, no Nesterov) with a
+    compressed momentum buffer."""
+    kind = "sgd"
+
+    def __init__(self, params: Iterable, lr: float = 0.1, momentum: float = 0.9,
+                 weight_decay: float = 0.0, gradient_release: bool = False):
+        super().__init__(params, dict(lr=lr, momentum=momentum, weight_decay=weight_decay),
+                         gradient_release)
+
+    def _hp(self, group) -> dict:
+        return dict(lr=group["lr"], momentum=group["momentum"],
+                    weight_decay=group["weight_decay"])
+
+
+class FlashLion(_FlashOptimizer):
+    """Lion (sign update, decoupled weight decay) with a compressed momentum."""
+    kind = "lion"
+
+    def __init__(self, params: Iterable, lr: float = 1e-4, betas=(0.9, 0.99),
+                 weight_decay: float = 0.0, gradient_release: bool = False):
+        super().__init__(params, dict(lr=lr, betas=tuple(betas), weight_decay=weight_decay),
+                         gradient_release)
+
+    def _hp(self, group) -> dict:
+        return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],
+                    weight_decay=group["weight_decay"])

@@ -1,0 +1,166 @@
+"""The drop-in optimizers (compressed_adamw_state_amd/optim.py) against the
+oracle: FlashAdamW / FlashSGD / FlashLion steps over FP32 and BF16
+parameters give the oracle's codes and scales bit for bit; a checkpoint
+(state_dict of codes and scales, theta' as the model's BF16 weights) resumes
+bit for bit; gradient release from backward hooks equals stepping after
+backward; and the checkpoint holds 3.125 (AdamW) / 2.0625 (SGD, Lion) bytes
+per parameter besides theta'."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_adamw_state_amd import optim as O
+
+from parity import state_fields, u16
+
+pytestmark = pytest.mark.gpu
+
+HP = {"adamw": dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01),
+      "sgd": dict(lr=0.05, momentum=0.9, weight_decay=1e-4),
+      "lion": dict(lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.1)}
+SHAPES = [(4097,), (33, 64), (2048,), (7,)]
+
+
+def make_opt(kind, params, release=False):
+    hp = HP[kind]
+    if kind == "adamw":
+        return O.FlashAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"], gradient_release=release)
+    if kind == "sgd":
+        return O.FlashSGD(params, lr=hp["lr"], momentum=hp["momentum"],
+                          weight_decay=hp["weight_decay"], gradient_release=release)
+    return O.FlashLion(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]),
+                       weight_decay=hp["weight_decay"], gradient_release=release)
+
+
+def compare(opt, params, orcs, label):
+    keys = [("theta", "tb"), ("rho", "rho"), ("m_code", "qm"), ("m_scale", "sm")]
+    if opt.kind == "adamw":
+        keys += [("v_code", "qv"), ("v_scale", "sv")]
+    for i, (p, o) in enumerate(zip(params, orcs)):
+        f = state_fields(opt.state[p]["flash"])
+        np.testing.assert_array_equal(u16(p.data.view(-1)), f["theta"])    # theta' is p
+        for k, ok in keys:
+            np.testing.assert_array_equal(f[k], getattr(o, ok), err_msg=f"{label} param {i} {k}")
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_optimizer_steps_match_oracle(kind, dtype):
+    rng = np.random.default_rng(3)
+    init = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in SHAPES]
+    if dtype == torch.bfloat16:   # the oracle starts from the same BF16 values (rho = 0)
+        init = [torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in init]
+    params = [torch.nn.Parameter(torch.from_numpy(x).cuda().to(dtype)) for x in init]
+    opt = make_opt(kind, params)
+    assert all(p.dtype == torch.bfloat16 for p in params)
+    orcs = [oracle.State(x.reshape(-1), kind) for x in init]
+    compare(opt, params, orcs, "init")
+    for t in range(1, 4):
+        for p, o in zip(params, orcs):
+            g = torch.from_numpy((rng.standard_normal(p.shape) * 1e-3).astype(np.float32))
+            g = g.to(torch.bfloat16)
+            p.grad = g.cuda()
+            oracle.step(o, g.view(torch.int16).numpy().view(np.uint16).reshape(-1), t, HP[kind])
+        opt.step()
+        torch.cuda.synchronize()
+        compare(opt, params, orcs, f"step {t}")
+
+
+@pytest.mark.parametrize("kind", ["adamw", "lion"])
+def test_checkpoint_resumes_bit_for_bit(kind):
+    rng = np.random.default_rng(4)
+    init = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in SHAPES]
+    grads = [[torch.from_numpy((rng.standard_normal(s) * 1e-3).astype(np.float32))
+              .to(torch.bfloat16).cuda() for s in SHAPES] for _ in range(6)]
+
+    def run(params, opt, steps):
+        for gs in steps:
+            for p, g in zip(params, gs):
+                p.grad = g.clone()
+            opt.step()
+
+    a = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
+    oa = make_opt(kind, a)
+    run(a, oa, grads)                                    # six steps without a break
+
+    b = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
+    ob = make_opt(kind, b)
+    run(b, ob, grads[:3])
+    sd = ob.state_dict()
+    weights = [p.detach().clone() for p in b]            # theta', saved with the model
+    nbytes = sum(s["codes"].numel() + 2 * s["scales"].numel() for s in sd["state"].values())
+    numel = sum(p.numel() for p in b)
+    del ob, b
+    c = [torch.nn.Parameter(w) for w in weights]         # a fresh model from the checkpoint
+    oc = make_opt(kind, c)
+    oc.load_state_dict(sd)
+    run(c, oc, grads[3:])
+    torch.cuda.synchronize()
+    for pa, pc in zip(a, c):
+        assert torch.equal(pa.view(torch.int16), pc.view(torch.int16))
+        sa, sc = oa.state[pa]["flash"], oc.state[pc]["flash"]
+        assert torch.equal(sa.codes, sc.codes) and torch.equal(sa.scales, sc.scales)
+    per = {"adamw": 3.125, "lion": 2.0625}[kind]
+    rec, scl = {"adamw": (24, 4), "lion": (16, 2)}[kind]
+    exact = sum((p.numel() + 7) // 8 * rec + (p.numel() + 31) // 32 * scl for p in c)
+    assert nbytes == exact and nbytes <= per * numel + 64 * len(c)
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
+def test_gradient_release_equals_step_after_backward(kind):
+    # an elementwise loss (no reductions whose order could vary between the
+    # two runs): the gradient of sum(c*p + k*p^2/2) is c + k*p
+    torch.manual_seed(5)
+    dims = [(256, 512), (512,), (512, 96), (96,)]
+    init = [torch.randn(d) * 0.02 for d in dims]
+    coef = [(torch.randn(d) * 1e-3).cuda() for d in dims]
+    x = 0.5
+
+    def model(ps, k):
+        loss = 0.0
+        for p, c in zip(ps, coef):
+            pf = p.float()
+            loss = loss + (c * pf + 0.5 * k * pf * pf).sum()
+        return loss
+
+    a = [torch.nn.Parameter(t.clone().cuda()) for t in init]
+    b = [torch.nn.Parameter(t.clone().cuda()) for t in init]
+    oa = make_opt(kind, a)
+    ob = make_opt(kind, b, release=True)
+    for it in range(3):
+        inp = x * (1 + it)
+        model(a, inp).backward()
+        oa.step()
+        oa.zero_grad()
+        model(b, inp).backward()                         # hooks step each parameter
+        assert all(p.grad is None for p in b)            # gradients released
+        ob.step()
+    torch.cuda.synchronize()
+    for pa, pb in zip(a, b):
+        assert torch.equal(pa.view(torch.int16), pb.view(torch.int16))
+        sa, sb = oa.state[pa]["flash"], ob.state[pb]["flash"]
+        assert torch.equal(sa.codes, sb.codes) and torch.equal(sa.scales, sb.scales)
+
+
+def test_export_fp32_matches_oracle_rebuild():
+    rng = np.random.default_rng(6)
+    init = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in SHAPES]
+    params = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
+    opt = make_opt("adamw", params)
+    orcs = [oracle.State(x.reshape(-1), "adamw") for x in init]
+    for p, o in zip(params, orcs):
+        g = torch.from_numpy((rng.standard_normal(p.shape) * 1e-3).astype(np.float32))
+        g = g.to(torch.bfloat16)
+        p.grad = g.cuda()
+        oracle.step(o, g.view(torch.int16).numpy().view(np.uint16).reshape(-1), 1, HP["adamw"])
+    opt.step()
+    for p, o in zip(params, orcs):
+        th, m, v = opt.export_fp32(p)
+        np.testing.assert_array_equal(th.cpu().numpy().view(np.uint32),
+                                      oracle.unsplit(o.tb, o.rho).view(np.uint32))
+        np.testing.assert_array_equal(m.cpu().numpy().view(np.uint32),
+                                      oracle.dequant_m(o.qm, o.sm).view(np.uint32))
+        np.testing.assert_array_equal(v.cpu().numpy().view(np.uint32),
+                                      oracle.dequant_v(o.qv, o.sv).view(np.uint32))
