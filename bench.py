@@ -139,6 +139,42 @@ def other_optimizer(name: str, steps: int, stream) -> dict:
             "algorithmic_gb_s": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS}
 
 
+def wrapper_adamw(steps: int, stream) -> dict:
+    """FlashAdamW.step() through the torch.optim API on the Llama-3.1-8B list:
+    FP32 parameters split at construction, one BF16 gradient set, `steps`
+    timed steps (GPU events and host wall time, so the host-side marshalling
+    shows)."""
+    from compressed_adamw_state_amd import optim as O
+    w = W.WORKLOADS["llama31_8b"]
+    dev = torch.device("cuda")
+    params = []
+    for i in range(len(w.tensors)):
+        params.append(torch.nn.Parameter(W.draw_theta(w, i, dev)))
+    opt = O.FlashAdamW(params, lr=w.hparams["lr"], betas=(w.hparams["beta1"], w.hparams["beta2"]),
+                       eps=w.hparams["eps"], weight_decay=w.hparams["weight_decay"])
+    for i, p in enumerate(params):
+        p.grad = W.draw_grad(w, i, 1, dev).view(p.shape)
+    for _ in range(2):
+        opt.step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(steps):
+        opt.step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) / steps * 1e3
+    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
+    del opt, params
+    torch.cuda.synchronize()
+    ms = float(np.median(per))
+    return {"workload": "llama31_8b", "optimizer": "FlashAdamW (torch.optim API)",
+            "params": w.numel, "step_ms_median": ms, "step_ms_min": float(per.min()),
+            "wall_ms_per_step": wall, "params_s": w.numel / (ms * 1e-3),
+            "algorithmic_gb_s": algorithmic_bytes(w) / (ms * 1e-3) / 1e9}
+
+
 def stream_probe(lst, stream, bytes_step: int, reps: int = 5):
     """The step's exact loads and stores with no arithmetic (flashopt_stream_probe):
     the practical floor of its access pattern.  Overwrites the state."""
@@ -320,7 +356,8 @@ def main():
     torch.cuda.synchronize()
     if not args.no_other_optimizers:
         out["other_optimizers"] = [other_optimizer("llama31_8b_lion", 10, stream),
-                                   other_optimizer("resnet50", 10, stream)]
+                                   other_optimizer("resnet50", 10, stream),
+                                   wrapper_adamw(10, stream)]
         for o in out["other_optimizers"]:
             log(f"bench: {o['optimizer']} {o['workload']}: {o['step_ms_median']:.3f} ms/step")
     if args.copy_bytes:
