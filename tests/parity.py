@@ -63,7 +63,9 @@ def log(msg: str) -> None:
 
 class Run:
     def __init__(self, w: W.Workload, mode: str = "full", samples_per_tensor: int = 4,
-                 seed: int = 0):
+                 seed: int = 0, extra_groups=()):
+        """extra_groups: group indices compared in every tensor that has them
+        (sampled mode), besides the first, the last and random ones."""
         assert mode in ("full", "sampled")
         self.w, self.mode = w, mode
         self.dev = torch.device("cuda")
@@ -84,7 +86,8 @@ class Run:
                 self.orc.append(oracle.State(theta.numpy(), opt))
             else:
                 ng = (n + GROUP - 1) // GROUP
-                pick = {0, ng - 1} | set(rng.integers(0, ng, samples_per_tensor).tolist())
+                pick = {0, ng - 1} | set(rng.integers(0, ng, samples_per_tensor).tolist()) \
+                    | set(extra_groups)
                 pick = sorted(g for g in pick if 0 <= g < ng)
                 self.samples.append(pick)
                 idx = torch.cat([torch.arange(g * GROUP, min(n, g * GROUP + GROUP))

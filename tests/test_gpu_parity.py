@@ -221,6 +221,22 @@ def test_set_grads_and_state_zero():
         np.testing.assert_array_equal(f["theta"], b["theta"])
 
 
+@pytest.mark.parametrize("opt", ["adamw", "lion"])
+def test_tensor_beyond_2_to_31_elements(opt):
+    # one tensor past 32-bit element indices (and past 2^32 code-record bytes
+    # for AdamW), in the launch shape of the benchmark; compared at the first
+    # and last groups, random ones, and the groups around element 2^31
+    n = (1 << 31) + (1 << 20) + 7
+    w = W.Workload("huge", (W.TensorSpec("huge", (n,), "normal"),), opt, 2, 21, "normal", 1e-3,
+                   W.HPARAMS[opt])
+    edge = (1 << 31) // 32
+    r = Run(w, "sampled", samples_per_tensor=8, extra_groups=range(edge - 2, edge + 3))
+    for t in (1, 2):
+        r.step(t)
+        n_cmp = r.compare(f"{opt} huge step {t}")
+    log(f"{opt} tensor of {n} elements: {n_cmp} sampled elements compared")
+
+
 def test_config1_flat1m_all_steps():
     w = W.WORKLOADS["flat1m"]
     r = Run(w, "full")
