@@ -114,18 +114,39 @@ def copy_ceiling(nbytes: int, stream, reps: int = 5):
             "best_ms": best * 1e3, "gb_s": 8 * n / best / 1e9}
 
 
-def other_optimizer(name: str, steps: int, stream) -> dict:
+def other_optimizer(name: str, steps: int, stream, release_streams: int = 1) -> dict:
     """Time `steps` list steps of another optimizer's workload (after warm-up);
-    state built fresh, freed on return."""
+    state built fresh, freed on return.  In gradient-release mode the per-tensor
+    launches go round-robin over `release_streams` streams (tensors are
+    independent, so one launch's tail can overlap the next); each step is
+    bracketed on `stream`."""
     w = W.WORKLOADS[name]
     states, grads, lists = build_state(w, grad_sets=2)
+    side = [stream] + [torch.cuda.Stream() for _ in range(release_streams - 1)]
+
+    def one_step(k, t):
+        if w.release:            # gradient release: one launch per tensor, backward order
+            start = torch.cuda.Event()
+            start.record(stream)
+            for s in side[1:]:
+                s.wait_event(start)
+            for j, i in enumerate(reversed(range(len(w.tensors)))):
+                F.step_one(lists[k % 2], w.optimizer, i, grads[k % 2][i], w.hparams, t,
+                           side[j % len(side)])
+            for s in side[1:]:
+                done = torch.cuda.Event()
+                done.record(s)
+                stream.wait_event(done)
+        else:
+            F.step(lists[k % 2], w.optimizer, w.hparams, t, stream)
+
     for t in (1, 2):
-        F.step(lists[t % 2], w.optimizer, w.hparams, t, stream)
+        one_step(t, t)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for k in range(steps):
-        F.step(lists[k % 2], w.optimizer, w.hparams, k + 3, stream)
+        one_step(k, k + 3)
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])    # ms
@@ -134,6 +155,8 @@ def other_optimizer(name: str, steps: int, stream) -> dict:
     ms = float(np.median(per))
     gbs = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
     return {"workload": name, "optimizer": w.optimizer, "params": w.numel,
+            "launches_per_step": len(w.tensors) if w.release else 1,
+            "streams": len(side) if w.release else 1,
             "bytes_per_param": algorithmic_bytes(w) / w.numel, "step_ms_median": ms,
             "step_ms_min": float(per.min()), "params_s": w.numel / (ms * 1e-3),
             "algorithmic_gb_s": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS}
@@ -357,6 +380,10 @@ def main():
     if not args.no_other_optimizers:
         out["other_optimizers"] = [other_optimizer("llama31_8b_lion", 10, stream),
                                    other_optimizer("resnet50", 10, stream),
+                                   other_optimizer("flat1m", 10, stream),
+                                   other_optimizer("gpt2_small", 10, stream),
+                                   other_optimizer("llama2_13b", 5, stream),
+                                   other_optimizer("llama2_13b", 5, stream, release_streams=2),
                                    wrapper_adamw(10, stream)]
         for o in out["other_optimizers"]:
             log(f"bench: {o['optimizer']} {o['workload']}: {o['step_ms_median']:.3f} ms/step")
