@@ -31,9 +31,16 @@ from . import flashopt as F
 class _FlashOptimizer(torch.optim.Optimizer):
     kind = ""                                    # "adamw" | "sgd" | "lion"
 
-    def __init__(self, params, defaults: dict, gradient_release: bool = False):
+    def __init__(self, params, defaults: dict, gradient_release: bool = False,
+                 release_streams: int = 1):
         super().__init__(params, defaults)
         self.gradient_release = gradient_release
+        # with release_streams > 1 the per-parameter launches from the gradient
+        # hooks go round-robin over that many side streams (default priority):
+        # each overlaps the rest of backward and the tail of the previous one
+        self._side = [torch.cuda.Stream() for _ in range(release_streams)] \
+            if gradient_release and release_streams > 1 else []
+        self._rr = 0
         self._t = 0                              # optimizer steps taken (the AdamW t)
         self._lists: List[Optional[F.FlashoptList]] = []
         self._hooks = []
@@ -82,7 +89,11 @@ class _FlashOptimizer(torch.optim.Optimizer):
             with torch.enable_grad():
                 loss = closure()
         if self.gradient_release:
-            # the hooks already stepped every parameter of this iteration
+            # the hooks already stepped every parameter of this iteration; the
+            # next forward must see their updates
+            cur = torch.cuda.current_stream()
+            for s in self._side:
+                cur.wait_stream(s)
             self._t += 1
             return loss
         self._t += 1
@@ -108,8 +119,17 @@ class _FlashOptimizer(torch.optim.Optimizer):
                     g = param.grad
                     if g.dtype != torch.bfloat16 or not g.is_contiguous():
                         raise ValueError("FlashOptim expects contiguous BF16 gradients")
+                    stream = None
+                    if self._side:
+                        # every backward node that read this parameter has run
+                        # (its gradient is complete), so updating it concurrently
+                        # with the rest of backward is safe
+                        stream = self._side[self._rr % len(self._side)]
+                        self._rr += 1
+                        stream.wait_stream(torch.cuda.current_stream())
+                        g.record_stream(stream)  # the gradient outlives its release
                     F.step_one(self._lists[gi], self.kind, pi, g.view(-1),
-                               self._hp(self.param_groups[gi]), self._t + 1)
+                               self._hp(self.param_groups[gi]), self._t + 1, stream)
                     param.grad = None            # gradient release: 2 B/param freed early
                 self._hooks.append(p.register_post_accumulate_grad_hook(hook))
 
@@ -165,9 +185,10 @@ class FlashAdamW(_FlashOptimizer):
     kind = "adamw"
 
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
-                 weight_decay: float = 1e-2, gradient_release: bool = False):
+                 weight_decay: float = 1e-2, gradient_release: bool = False,
+                 release_streams: int = 1):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), eps=eps,
-                                      weight_decay=weight_decay), gradient_release)
+                                      weight_decay=weight_decay), gradient_release, release_streams)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],
@@ -180,9 +201,10 @@ class FlashSGD(_FlashOptimizer):
     kind = "sgd"
 
     def __init__(self, params: Iterable, lr: float = 0.1, momentum: float = 0.9,
-                 weight_decay: float = 0.0, gradient_release: bool = False):
+                 weight_decay: float = 0.0, gradient_release: bool = False,
+                 release_streams: int = 1):
         super().__init__(params, dict(lr=lr, momentum=momentum, weight_decay=weight_decay),
-                         gradient_release)
+                         gradient_release, release_streams)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], momentum=group["momentum"],
@@ -194,9 +216,10 @@ class FlashLion(_FlashOptimizer):
     kind = "lion"
 
     def __init__(self, params: Iterable, lr: float = 1e-4, betas=(0.9, 0.99),
-                 weight_decay: float = 0.0, gradient_release: bool = False):
+                 weight_decay: float = 0.0, gradient_release: bool = False,
+                 release_streams: int = 1):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), weight_decay=weight_decay),
-                         gradient_release)
+                         gradient_release, release_streams)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],

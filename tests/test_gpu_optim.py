@@ -22,16 +22,19 @@ HP = {"adamw": dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01
 SHAPES = [(4097,), (33, 64), (2048,), (7,)]
 
 
-def make_opt(kind, params, release=False):
+def make_opt(kind, params, release=False, streams=1):
     hp = HP[kind]
     if kind == "adamw":
         return O.FlashAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
-                            weight_decay=hp["weight_decay"], gradient_release=release)
+                            weight_decay=hp["weight_decay"], gradient_release=release,
+                            release_streams=streams)
     if kind == "sgd":
         return O.FlashSGD(params, lr=hp["lr"], momentum=hp["momentum"],
-                          weight_decay=hp["weight_decay"], gradient_release=release)
+                          weight_decay=hp["weight_decay"], gradient_release=release,
+                          release_streams=streams)
     return O.FlashLion(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]),
-                       weight_decay=hp["weight_decay"], gradient_release=release)
+                       weight_decay=hp["weight_decay"], gradient_release=release,
+                       release_streams=streams)
 
 
 def compare(opt, params, orcs, label):
@@ -108,8 +111,9 @@ def test_checkpoint_resumes_bit_for_bit(kind):
     assert nbytes == exact and nbytes <= per * numel + 64 * len(c)
 
 
+@pytest.mark.parametrize("streams", [1, 2])
 @pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
-def test_gradient_release_equals_step_after_backward(kind):
+def test_gradient_release_equals_step_after_backward(kind, streams):
     # an elementwise loss (no reductions whose order could vary between the
     # two runs): the gradient of sum(c*p + k*p^2/2) is c + k*p
     torch.manual_seed(5)
@@ -128,7 +132,7 @@ def test_gradient_release_equals_step_after_backward(kind):
     a = [torch.nn.Parameter(t.clone().cuda()) for t in init]
     b = [torch.nn.Parameter(t.clone().cuda()) for t in init]
     oa = make_opt(kind, a)
-    ob = make_opt(kind, b, release=True)
+    ob = make_opt(kind, b, release=True, streams=streams)
     for it in range(3):
         inp = x * (1 + it)
         model(a, inp).backward()
