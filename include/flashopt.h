@@ -14,17 +14,22 @@
  *     scale per group of 32 elements;
  *   - section "Core method > Fused optimizer step" (Alg. 4): one pass per
  *     parameter dequantises, rebuilds the master weight, applies AdamW (or
- *     SGD with momentum), requantises the states and re-splits the weight;
- *     gradient release steps each tensor as soon as its gradient exists.
+ *     SGD with momentum, or Lion), requantises the states and re-splits the
+ *     weight; gradient release steps each tensor as soon as its gradient
+ *     exists.
  *
  * Arithmetic (every operation IEEE binary32, round to nearest even, no fused
- * multiply-add, subnormals kept; K8 = RN(1/127), K255 = RN(1/255)):
+ * multiply-add, subnormals kept; K8 = RN(1/127), K255 = RN(1/255)) -- the
+ * results are those of this operation sequence; the kernels reach the same
+ * bits with shorter sequences (some with FMA) checked to be identical:
  *   h         = ULP(theta')/2 = 2^(max(E,1)-135), E = exponent field of theta'
  *   rebuild   theta_hat = theta' + (rho*K8)*h                 (theta' Inf/NaN: theta')
  *   dequant   m = z/(2-|z|), z = q*(s*K8);  v = z*z, z = q*(s*K255)
  *   AdamW     m' = b1*m + c1*g;  v' = b2*v + c2*(g*g);  w = sqrt(v');
  *             theta_n = lambda*theta_hat - alpha*(m'/(w*kappa + eps))
  *   SGD       g' = g + wd*theta_hat;  b' = mu*b + g';  theta_n = theta_hat - lr*b'
+ *   Lion      c = b1*m + c1*g;  theta_n = lambda*theta_hat - lr*sign(c);
+ *             m' = b2*m + c2*g  (flashopt_lion_hparams)
  *   requant   z = (2m')/(1+|m'|) (momentum) or w (variance); a = max |z| over
  *             the group's elements; s = FP16(a) capped at 0x3FFF (momentum) or
  *             0x7BFF (variance); q = 0 if s = 0 else clamp(rne(z*(127/s)), +-127)
@@ -46,8 +51,8 @@
  * as their uint16 bit patterns.
  *
  * Alignment: BF16 arrays (theta', grad) 16 bytes; code records and flat
- * INT8/UINT8 code arrays 8 bytes; AdamW scale arrays 4 bytes, SGD and flat
- * scale arrays 2 bytes; FP32 arrays 16 bytes.
+ * INT8/UINT8 code arrays 8 bytes; AdamW scale arrays 4 bytes, SGD / Lion and
+ * flat scale arrays 2 bytes; FP32 arrays 16 bytes.
  *
  * Errors.  Every call validates its arguments on the host before launching
  * anything and returns a flashopt_status; a failed validation launches
