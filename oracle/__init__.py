@@ -56,6 +56,12 @@ def lib():
             "orc_unsplit": (None, [_P, _P, _I64, _P]),
             "orc_split_q": (None, [_P, _I64, ctypes.c_int32, _P, _P]),
             "orc_unsplit_q": (None, [_P, _P, _I64, ctypes.c_int32, _P]),
+            "orc_split_f16_q": (None, [_P, _I64, ctypes.c_int32, _P, _P]),
+            "orc_unsplit_f16_q": (None, [_P, _P, _I64, ctypes.c_int32, _P]),
+            "orc_quant_lin_m": (None, [_P, _I64, _P, _P]),
+            "orc_dequant_lin_m": (None, [_P, _P, _I64, _P]),
+            "orc_quant_lin_v": (None, [_P, _I64, _P, _P]),
+            "orc_dequant_lin_v": (None, [_P, _P, _I64, _P]),
             "orc_phi_m": (ctypes.c_float, [ctypes.c_float]),
             "orc_phi_m_inv": (ctypes.c_float, [ctypes.c_float]),
             "orc_phi_v": (ctypes.c_float, [ctypes.c_float]),
@@ -158,6 +164,22 @@ def unsplit_q(tb, rho, qmax: int) -> np.ndarray:
     return out
 
 
+def split_f16_q(theta, qmax: int):
+    theta = _c(theta, np.float32)
+    hb = np.empty(theta.shape, np.uint16)
+    rho = np.empty(theta.shape, np.int32)
+    lib().orc_split_f16_q(_ptr(theta), theta.size, qmax, _ptr(hb), _ptr(rho))
+    return hb, rho
+
+
+def unsplit_f16_q(hb, rho, qmax: int) -> np.ndarray:
+    hb = _c(hb, np.uint16)
+    rho = _c(rho, np.int32)
+    out = np.empty(hb.shape, np.float32)
+    lib().orc_unsplit_f16_q(_ptr(hb), _ptr(rho), hb.size, qmax, _ptr(out))
+    return out
+
+
 # -- companding and quantisers ----------------------------------------------
 
 def _map(fname, x):
@@ -204,6 +226,38 @@ def dequant_v(q, s) -> np.ndarray:
     assert s.size == groups(q.size)
     out = np.empty(q.shape, np.float32)
     lib().orc_dequant_v(_ptr(q), _ptr(s), q.size, _ptr(out))
+    return out
+
+
+def quant_lin_m(m):
+    m = _c(m, np.float32)
+    q = np.empty(m.shape, np.int8)
+    s = np.empty(groups(m.size), np.uint16)
+    lib().orc_quant_lin_m(_ptr(m), m.size, _ptr(q), _ptr(s))
+    return q, s
+
+
+def dequant_lin_m(q, s) -> np.ndarray:
+    q = _c(q, np.int8)
+    s = _c(s, np.uint16)
+    out = np.empty(q.shape, np.float32)
+    lib().orc_dequant_lin_m(_ptr(q), _ptr(s), q.size, _ptr(out))
+    return out
+
+
+def quant_lin_v(v):
+    v = _c(v, np.float32)
+    q = np.empty(v.shape, np.uint8)
+    s = np.empty(groups(v.size), np.uint16)
+    lib().orc_quant_lin_v(_ptr(v), v.size, _ptr(q), _ptr(s))
+    return q, s
+
+
+def dequant_lin_v(q, s) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint16)
+    out = np.empty(q.shape, np.float32)
+    lib().orc_dequant_lin_v(_ptr(q), _ptr(s), q.size, _ptr(out))
     return out
 
 

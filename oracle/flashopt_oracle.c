@@ -177,9 +177,20 @@ static float clampf(float x, float lo, float hi)
     return x;
 }
 
+/* rne(qmax * e) of an exact |e| <= 1 with the product itself exact (in double:
+ * 24 + 16 bits), for any code width up to 16 bits.  With qmax = 127 and a BF16
+ * base the binary32 product is already exact, so this equals split1's code. */
+static int32_t code_of(float e, int32_t qmax)
+{
+    double y = (double)e * (double)qmax;
+    double r = round_half_even(fabs(y)) * (y < 0 ? -1.0 : 1.0);
+    if (r > qmax) r = qmax;
+    if (r < -qmax) r = -qmax;
+    return (int32_t)r;
+}
+
 void orc_split_q(const float* theta, int64_t n, int32_t qmax, uint16_t* tb, int32_t* rho)
 {
-    float qf = (float)qmax;
     for (int64_t i = 0; i < n; ++i) {
         float x = theta[i];
         uint16_t b = orc_bf16_rne(x);
@@ -189,9 +200,7 @@ void orc_split_q(const float* theta, int64_t n, int32_t qmax, uint16_t* tb, int3
         float h = half_ulp(b);
         float diff = x - t;               /* exact (Sterbenz; or t == 0) */
         float e = diff / h;               /* exact: h is a power of two, |e| <= 1 */
-        float y = e * qf;
-        float r = clampf(rne_to_int(y), -qf, qf);
-        rho[i] = (int32_t)r;
+        rho[i] = code_of(e, qmax);
     }
 }
 
@@ -202,6 +211,45 @@ void orc_unsplit_q(const uint16_t* tb, const int32_t* rho, int64_t n, int32_t qm
         float t = orc_bf16_to_f32(tb[i]);
         if (!isfinite(t)) { out[i] = t; continue; }
         float h = half_ulp(tb[i]);
+        float c = (float)rho[i] * k;
+        float d = c * h;
+        out[i] = t + d;
+    }
+}
+
+/* FP16 base (10 stored mantissa bits, bias 15): ULP(theta')/2 with the same
+ * convention -- the spacing above |theta'|, zero and subnormal FP16 using the
+ * minimum-normal spacing 2^-24. */
+static float half_ulp_f16(uint16_t hb)
+{
+    int E = (hb >> 10) & 0x1F;
+    if (E < 1) E = 1;
+    return ldexpf(1.0f, E - 26);          /* 2^(E-15) * 2^-10 / 2, exact */
+}
+
+void orc_split_f16_q(const float* theta, int64_t n, int32_t qmax, uint16_t* hb, int32_t* rho)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float x = theta[i];
+        uint16_t b = orc_f16_rne(x);
+        float t = orc_f16_to_f32(b);
+        hb[i] = b;
+        if (!isfinite(t)) { rho[i] = 0; continue; }
+        float h = half_ulp_f16(b);
+        float diff = x - t;               /* exact (Sterbenz; or t == 0) */
+        float e = diff / h;               /* exact: h is a power of two, |e| <= 1 */
+        rho[i] = code_of(e, qmax);
+    }
+}
+
+void orc_unsplit_f16_q(const uint16_t* hb, const int32_t* rho, int64_t n, int32_t qmax,
+                       float* out)
+{
+    float k = 1.0f / (float)qmax;         /* RN(1/qmax) */
+    for (int64_t i = 0; i < n; ++i) {
+        float t = orc_f16_to_f32(hb[i]);
+        if (!isfinite(t)) { out[i] = t; continue; }
+        float h = half_ulp_f16(hb[i]);
         float c = (float)rho[i] * k;
         float d = c * h;
         out[i] = t + d;
@@ -359,6 +407,44 @@ void orc_quant_v(const float* v, int64_t n, uint8_t* q, uint16_t* s)
 void orc_dequant_v(const uint8_t* q, const uint16_t* s, int64_t n, float* v)
 {
     for (int64_t i = 0; i < n; ++i) v[i] = dequant_v1(q[i], s[i / GROUP]);
+}
+
+/* Linear quantisers (no companding): z = m or z = v. */
+void orc_quant_lin_m(const float* m, int64_t n, int8_t* q, uint16_t* s)
+{
+    for (int64_t g = 0; g * GROUP < n; ++g) {
+        int len = group_len(n, g);
+        const float* z = m + g * GROUP;
+        uint16_t s16 = group_scale(z, len, 0x7BFF);
+        s[g] = s16;
+        float r = s16 ? 127.0f / orc_f16_to_f32(s16) : 0.0f;
+        for (int j = 0; j < len; ++j) {
+            float y = z[j] * r;
+            q[g * GROUP + j] = s16 ? (int8_t)clampf(rne_to_int(y), -127.0f, 127.0f) : 0;
+        }
+    }
+}
+
+void orc_dequant_lin_m(const int8_t* q, const uint16_t* s, int64_t n, float* m)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float d = orc_f16_to_f32(s[i / GROUP]) * K8;
+        m[i] = (float)q[i] * d;
+    }
+}
+
+void orc_quant_lin_v(const float* v, int64_t n, uint8_t* q, uint16_t* s)
+{
+    for (int64_t g = 0; g * GROUP < n; ++g)
+        quant_group_v(v + g * GROUP, group_len(n, g), q + g * GROUP, s + g);
+}
+
+void orc_dequant_lin_v(const uint8_t* q, const uint16_t* s, int64_t n, float* v)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float d = orc_f16_to_f32(s[i / GROUP]) * K255;
+        v[i] = (float)q[i] * d;
+    }
 }
 
 /* ------------------------------------------------------------------------ */

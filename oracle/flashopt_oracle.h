@@ -28,6 +28,12 @@ void orc_unsplit(const uint16_t* tb, const int8_t* rho, int64_t n, float* out);
 void orc_split_q(const float* theta, int64_t n, int32_t qmax, uint16_t* tb, int32_t* rho);
 void orc_unsplit_q(const uint16_t* tb, const int32_t* rho, int64_t n, int32_t qmax, float* out);
 
+/* the same algorithm on an FP16 base weight (ablation: the weight-splitting
+ * part compares BF16 and FP16 bases, Fig. 3) */
+void orc_split_f16_q(const float* theta, int64_t n, int32_t qmax, uint16_t* hb, int32_t* rho);
+void orc_unsplit_f16_q(const uint16_t* hb, const int32_t* rho, int64_t n, int32_t qmax,
+                       float* out);
+
 float orc_phi_m(float x);
 float orc_phi_m_inv(float z);
 float orc_phi_v(float x);
@@ -37,6 +43,14 @@ void orc_quant_m(const float* m, int64_t n, int8_t* q, uint16_t* s);
 void orc_dequant_m(const int8_t* q, const uint16_t* s, int64_t n, float* m);
 void orc_quant_v(const float* v, int64_t n, uint8_t* q, uint16_t* s);
 void orc_dequant_v(const uint8_t* q, const uint16_t* s, int64_t n, float* v);
+
+/* linear group quantisers without companding (ablation, Fig. 4-5): the same
+ * group scale and codes applied to m and v themselves; both scales may reach
+ * the largest finite FP16 */
+void orc_quant_lin_m(const float* m, int64_t n, int8_t* q, uint16_t* s);
+void orc_dequant_lin_m(const int8_t* q, const uint16_t* s, int64_t n, float* m);
+void orc_quant_lin_v(const float* v, int64_t n, uint8_t* q, uint16_t* s);
+void orc_dequant_lin_v(const uint8_t* q, const uint16_t* s, int64_t n, float* v);
 
 /* out = {b1, c1, b2, c2, alpha, kappa, eps, lambda} */
 void orc_adamw_scalars(double lr, double beta1, double beta2, double eps, double wd,
