@@ -63,6 +63,12 @@ SIGNATURES = {
     "flashopt_quantize_v": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
     "flashopt_dequantize_v": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "flashopt_list_workspace_bytes": (_SZ, [_I32]),
+    "flashopt_split_ex": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "flashopt_unsplit_ex": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P]),
+    "flashopt_quantize_lin_m": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
+    "flashopt_dequantize_lin_m": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "flashopt_quantize_lin_v": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
+    "flashopt_dequantize_lin_v": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "flashopt_codes_bytes": (_SZ, [_I32, _I64]),
     "flashopt_scales_bytes": (_SZ, [_I32, _I64]),
     "flashopt_tensor_init": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32, _P, _P]),
@@ -158,6 +164,43 @@ def flashopt_quantize_v(v, q, scale, stream=None) -> None:
 def flashopt_dequantize_v(q, scale, v_out, stream=None) -> None:
     _check("flashopt_dequantize_v", lib().flashopt_dequantize_v(_ptr(q), _ptr(scale), q.numel(),
                                                                 _ptr(v_out), _stream(stream)))
+
+
+# ---- codec ablations (not used by the step) ---------------------------------
+
+BASE = {"bf16": 0, "fp16": 1}
+
+
+def flashopt_split_ex(theta, base: str, qmax: int, theta_base, rho, stream=None) -> None:
+    _check("flashopt_split_ex",
+           lib().flashopt_split_ex(_ptr(theta), theta.numel(), BASE[base], qmax, _ptr(theta_base),
+                                   _ptr(rho), _stream(stream)))
+
+
+def flashopt_unsplit_ex(theta_base, rho, base: str, qmax: int, theta_out, stream=None) -> None:
+    _check("flashopt_unsplit_ex",
+           lib().flashopt_unsplit_ex(_ptr(theta_base), _ptr(rho), theta_base.numel(), BASE[base],
+                                     qmax, _ptr(theta_out), _stream(stream)))
+
+
+def flashopt_quantize_lin_m(m, q, scale, stream=None) -> None:
+    _check("flashopt_quantize_lin_m", lib().flashopt_quantize_lin_m(
+        _ptr(m), m.numel(), _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def flashopt_dequantize_lin_m(q, scale, m_out, stream=None) -> None:
+    _check("flashopt_dequantize_lin_m", lib().flashopt_dequantize_lin_m(
+        _ptr(q), _ptr(scale), q.numel(), _ptr(m_out), _stream(stream)))
+
+
+def flashopt_quantize_lin_v(v, q, scale, stream=None) -> None:
+    _check("flashopt_quantize_lin_v", lib().flashopt_quantize_lin_v(
+        _ptr(v), v.numel(), _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def flashopt_dequantize_lin_v(q, scale, v_out, stream=None) -> None:
+    _check("flashopt_dequantize_lin_v", lib().flashopt_dequantize_lin_v(
+        _ptr(q), _ptr(scale), q.numel(), _ptr(v_out), _stream(stream)))
 
 
 # ---- tensor lists -----------------------------------------------------------

@@ -167,7 +167,7 @@ def ragged(sizes: Sequence[int], seed: int = 7, steps: int = 3, optimizer: str =
 # ---------------------------------------------------------------------------
 # seeded draws
 
-_PURPOSE = {"theta": 1, "grad": 2, "special": 3}
+_PURPOSE = {"theta": 1, "grad": 2, "special": 3, "weights": 4, "moments": 5}
 
 
 def _gen(seed: int, purpose: str, step: int, index: int, device) -> torch.Generator:
@@ -228,6 +228,28 @@ def draw_grad(w: Workload, index: int, step: int, device="cpu") -> torch.Tensor:
     else:
         raise ValueError(w.grad_dist)
     return x.to(torch.bfloat16)
+
+
+def draw_weights(n: int, seed: int, device="cpu") -> torch.Tensor:
+    """fp32 weights N(0, 0.02), the initialisation of the transformer lists."""
+    g = _gen(seed, "weights", 0, 0, device)
+    return torch.randn(n, generator=g, dtype=torch.float32, device=device) * 0.02
+
+
+def draw_moments(n: int, seed: int, scale: float, spread: float, device="cpu"):
+    """(m, v) fp32 of the kind an AdamW run holds, drawn directly.
+
+    Each element has its own gradient scale s = scale * exp(spread * z),
+    z ~ N(0, 1) (log-normal, so one group of 32 mixes scales); the first
+    moment is 0.23 * s * N(0, 1) (an exponential average with decay 0.9 of
+    white noise has 0.23 of the noise's standard deviation) and the second
+    s^2 * chi2_8 / 8 (an average of squares that still fluctuates)."""
+    g = _gen(seed, "moments", 0, 0, device)
+    s = scale * torch.exp(spread * torch.randn(n, generator=g, dtype=torch.float64, device=device))
+    m = 0.23 * s * torch.randn(n, generator=g, dtype=torch.float64, device=device)
+    c = torch.randn(8, n, generator=g, dtype=torch.float64, device=device)
+    v = s * s * (c * c).sum(0) / 8.0
+    return m.float(), v.float()
 
 
 def state_bytes(numel: int, optimizer: str = "adamw") -> dict:

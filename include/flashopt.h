@@ -169,6 +169,31 @@ int flashopt_quantize_v(const float* v, int64_t n, uint8_t* q, uint16_t* scale, 
 int flashopt_dequantize_v(const uint8_t* q, const uint16_t* scale, int64_t n, float* v,
                           void* stream);
 
+/* ---- codec ablations over flat buffers (weight-splitting section, Fig. 3:
+ * BF16 versus FP16 base and the width of the correction; companding section,
+ * Fig. 4-5: linear quantisation without companding).  Not used by the step.
+ * split_ex: base 0 = BF16, 1 = FP16 (RNE; beyond 65504 FP16 rounds to Inf);
+ * codes rho = clamp(rne(qmax*e)) in [-qmax, qmax], 1 <= qmax <= 32767, with
+ * e = (theta - theta')/h exact, h = ULP(theta')/2 above |theta'| (zero and
+ * subnormal bases: the minimum-normal spacing), the product qmax*e exact;
+ * rho = 0 where theta' is not finite.  unsplit_ex: theta' + (rho*RN(1/qmax))*h.
+ * theta_base and rho are [n] uint16 / int16 (2-byte aligned), theta [n] FP32. */
+int flashopt_split_ex(const float* theta, int64_t n, int32_t base, int32_t qmax,
+                      uint16_t* theta_base, int16_t* rho, void* stream);
+int flashopt_unsplit_ex(const uint16_t* theta_base, const int16_t* rho, int64_t n, int32_t base,
+                        int32_t qmax, float* theta_out, void* stream);
+/* Linear group quantisers: the group scale and codes of the quantisers above
+ * applied to m and v themselves (no phi); both scales capped at 0x7BFF.
+ * Dequantisation: m = q*(s*K8), v = q*(s*K255). */
+int flashopt_quantize_lin_m(const float* m, int64_t n, int8_t* q, uint16_t* scale,
+                            void* stream);
+int flashopt_dequantize_lin_m(const int8_t* q, const uint16_t* scale, int64_t n, float* m,
+                              void* stream);
+int flashopt_quantize_lin_v(const float* v, int64_t n, uint8_t* q, uint16_t* scale,
+                            void* stream);
+int flashopt_dequantize_lin_v(const uint8_t* q, const uint16_t* scale, int64_t n, float* v,
+                              void* stream);
+
 /* ---- one tensor's compressed state.
  * Sizes in bytes of the code records and the scale array for n elements
  * (0 for an unknown kind or n out of range). */

@@ -50,6 +50,13 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_unsplit(fake, fake, 5, mis, None) == -3
     assert lib.flashopt_quantize_m(fake, 5, None, fake, None) == -1
     assert lib.flashopt_dequantize_v(fake, P(0x10003), 5, fake, None) == -3
+    assert lib.flashopt_split_ex(fake, 10, 2, 127, fake, fake, None) == -4      # base
+    assert lib.flashopt_split_ex(fake, 10, 1, 0, fake, fake, None) == -4       # qmax
+    assert lib.flashopt_split_ex(fake, 10, 1, 32768, fake, fake, None) == -4
+    assert lib.flashopt_split_ex(None, 10, 1, 127, fake, fake, None) == -1
+    assert lib.flashopt_unsplit_ex(fake, P(0x10001), 10, 0, 127, fake, None) == -3
+    assert lib.flashopt_quantize_lin_v(fake, 5, None, fake, None) == -1
+    assert lib.flashopt_dequantize_lin_m(fake, fake, -1, fake, None) == -2
     assert lib.flashopt_list_workspace_bytes(0) >= 8
     assert lib.flashopt_list_workspace_bytes(291) >= 291 * 64
     out = P()
