@@ -75,6 +75,9 @@ def lib():
                                       _D, _D, _D, _D, _D, _I64, _P, _P, _P]),
             "orc_sgd_step": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _I64, _P, _P]),
             "orc_lion_step": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
+            "orc_adamw_step_fp32": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _D, _D, _I64]),
+            "orc_sgd_step_fp32": (None, [_I64, _P, _P, _P, _P, _D, _D, _D]),
+            "orc_lion_step_fp32": (None, [_I64, _P, _P, _P, _P, _D, _D, _D, _D]),
         }
         for name in ("bf16_rne_array", "f16_rne_array", "f16_to_f32_array", "phi_m_array",
                      "phi_m_inv_array", "phi_v_array", "phi_v_inv_array"):
@@ -334,6 +337,44 @@ def step(st: State, grad_bits, t: int, hp: dict, want_fp32=False):
         return lion_step(st, grad_bits, hp["lr"], hp["beta1"], hp["beta2"], hp["weight_decay"],
                          want_fp32)
     return sgd_step(st, grad_bits, t, hp["lr"], hp["momentum"], hp["weight_decay"], want_fp32)
+
+
+# -- compression disabled: FP32 master weight and moments --------------------
+
+class StateFP32:
+    """Uncompressed state of one tensor: FP32 theta, m, v (AdamW) and the
+    BF16 theta' the model computes with (host arrays, updated in place)."""
+
+    def __init__(self, theta_fp32, optimizer="adamw"):
+        self.theta = np.array(theta_fp32, np.float32).reshape(-1)
+        self.n = self.theta.size
+        self.optimizer = optimizer
+        self.m = np.zeros(self.n, np.float32)
+        self.v = np.zeros(self.n, np.float32) if optimizer == "adamw" else None
+        self.tb = bf16_rne(self.theta)
+
+    def copy(self) -> "StateFP32":
+        c = StateFP32.__new__(StateFP32)
+        c.n, c.optimizer = self.n, self.optimizer
+        for k in ("theta", "m", "v", "tb"):
+            v = getattr(self, k)
+            setattr(c, k, None if v is None else v.copy())
+        return c
+
+
+def step_fp32(st: StateFP32, grad_bits, t: int, hp: dict) -> None:
+    g = _c(grad_bits, np.uint16).reshape(-1)
+    assert g.size == st.n
+    if st.optimizer == "adamw":
+        lib().orc_adamw_step_fp32(st.n, _ptr(st.theta), _ptr(st.m), _ptr(st.v), _ptr(st.tb),
+                                  _ptr(g), hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                  hp["weight_decay"], t)
+    elif st.optimizer == "lion":
+        lib().orc_lion_step_fp32(st.n, _ptr(st.theta), _ptr(st.m), _ptr(st.tb), _ptr(g),
+                                 hp["lr"], hp["beta1"], hp["beta2"], hp["weight_decay"])
+    else:
+        lib().orc_sgd_step_fp32(st.n, _ptr(st.theta), _ptr(st.m), _ptr(st.tb), _ptr(g),
+                                hp["lr"], hp["momentum"], hp["weight_decay"])
 
 
 # -- threading helper (the oracle itself stays single-threaded) -------------

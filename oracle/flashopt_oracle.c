@@ -18,7 +18,10 @@
  *     G = 32 with one FP16 scale each, momentum INT8, variance UINT8;
  *   - the fused step, section "Core method > Fused optimizer step" (Alg. 4):
  *     dequantise, rebuild the master weight, standard AdamW (or SGD with
- *     momentum, named in the background section), requantise, re-split.
+ *     momentum, named in the background section), requantise, re-split;
+ *   - compression switched off for a layer, section "Practical advice": the
+ *     same updates over an FP32 master weight and FP32 moments, with the BF16
+ *     weight the model computes with rounded from the new master weight.
  *
  * The page prints the companding formulas but not the algorithms, so the
  * arithmetic order below is the plainest reading, one IEEE binary32 operation
@@ -469,6 +472,75 @@ void orc_adamw_scalars(double lr, double beta1, double beta2, double eps, double
 }
 
 /* ------------------------------------------------------------------------ */
+/* The updates of one element, shared by the compressed and the FP32 steps.  */
+
+/* AdamW (reading of "standard AdamW"): returns theta_n; sc from
+ * orc_adamw_scalars. */
+static float adam1(const float sc[8], float theta_hat, float m, float v, float gr,
+                   float* m_new, float* v_new, float* root)
+{
+    const float b1 = sc[0], c1 = sc[1], b2 = sc[2], c2 = sc[3];
+    const float alpha = sc[4], kappa = sc[5], epsf = sc[6], lambda = sc[7];
+    float bm = b1 * m;
+    float cg = c1 * gr;
+    float mn = bm + cg;
+    float bv = b2 * v;
+    float gg = gr * gr;
+    float cgg = c2 * gg;
+    float vn = bv + cgg;
+    float w = sqrtf(vn);
+    float denom_a = w * kappa;
+    float denom = denom_a + epsf;
+    float u = mn / denom;
+    float decayed = lambda * theta_hat;
+    float step = alpha * u;
+    *m_new = mn;
+    *v_new = vn;
+    *root = w;
+    return decayed - step;
+}
+
+/* SGD with momentum: L2 decay added to the gradient, no dampening. */
+static float sgd1(float mu, float eta, float omega, float theta_hat, float b, float gr,
+                  float* b_new)
+{
+    float decay = omega * theta_hat;
+    float g2 = gr + decay;
+    float mb = mu * b;
+    float bn = mb + g2;
+    float step = eta * bn;
+    *b_new = bn;
+    return theta_hat - step;
+}
+
+/* Lion (see orc_lion_step): lc = {b1, c1, b2, c2, eta, lambda}. */
+static float sign1(float c);
+static void lion_scalars(double lr, double beta1, double beta2, double wd, float lc[6])
+{
+    lc[0] = (float)beta1;
+    lc[1] = (float)(1.0 - beta1);
+    lc[2] = (float)beta2;
+    lc[3] = (float)(1.0 - beta2);
+    lc[4] = (float)lr;
+    lc[5] = (float)(1.0 - lr * wd);
+}
+
+static float lion1(const float lc[6], float theta_hat, float m, float gr, float* m_new)
+{
+    float bm = lc[0] * m;
+    float cg = lc[1] * gr;
+    float c = bm + cg;
+    float sgn = sign1(c);
+    if (sgn == 0.0f) sgn = 0.0f;           /* a zero direction is +0 */
+    float decayed = lc[5] * theta_hat;
+    float step = lc[4] * sgn;
+    float b2m = lc[2] * m;
+    float c2g = lc[3] * gr;
+    *m_new = b2m + c2g;
+    return decayed - step;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Fused steps over one tensor.                                              */
 
 void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
@@ -478,8 +550,6 @@ void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* 
 {
     float sc[8];
     orc_adamw_scalars(lr, beta1, beta2, eps, wd, t, sc);
-    const float b1 = sc[0], c1 = sc[1], b2 = sc[2], c2 = sc[3];
-    const float alpha = sc[4], kappa = sc[5], epsf = sc[6], lambda = sc[7];
 
     for (int64_t g = 0; g * GROUP < n; ++g) {
         int len = group_len(n, g);
@@ -490,21 +560,8 @@ void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* 
             float m = dequant_m1(qm[o + j], sm[g]);
             float v = dequant_v1(qv[o + j], sv[g]);
             float gr = orc_bf16_to_f32(grad[o + j]);
-
-            float bm = b1 * m;
-            float cg = c1 * gr;
-            float m_new = bm + cg;
-            float bv = b2 * v;
-            float gg = gr * gr;
-            float cgg = c2 * gg;
-            float v_new = bv + cgg;
-            float root = sqrtf(v_new);
-            float denom_a = root * kappa;
-            float denom = denom_a + epsf;
-            float u = m_new / denom;
-            float decayed = lambda * theta_hat;
-            float step = alpha * u;
-            float theta_new = decayed - step;
+            float m_new, v_new, root;
+            float theta_new = adam1(sc, theta_hat, m, v, gr, &m_new, &v_new, &root);
 
             mn[j] = m_new;
             w[j] = root;
@@ -536,13 +593,8 @@ void orc_sgd_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qb, uint16_t* sb
             float theta_hat = unsplit1(tb[o + j], rho[o + j]);
             float b = dequant_m1(qb[o + j], sb[g]);
             float gr = orc_bf16_to_f32(grad[o + j]);
-
-            float decay = omega * theta_hat;
-            float g2 = gr + decay;
-            float mb = mu * b;
-            float b_new = mb + g2;
-            float step = eta * b_new;
-            float theta_new = theta_hat - step;
+            float b_new;
+            float theta_new = sgd1(mu, eta, omega, theta_hat, b, gr, &b_new);
 
             bn[j] = b_new;
             tn[j] = theta_new;
@@ -574,10 +626,8 @@ void orc_lion_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* s
                    const uint16_t* grad, double lr, double beta1, double beta2, double wd,
                    float* theta_out, float* m_out)
 {
-    const float b1 = (float)beta1, c1 = (float)(1.0 - beta1);
-    const float b2 = (float)beta2, c2 = (float)(1.0 - beta2);
-    const float eta = (float)lr;
-    const float lambda = (float)(1.0 - lr * wd);
+    float lc[6];
+    lion_scalars(lr, beta1, beta2, wd, lc);
     for (int64_t g = 0; g * GROUP < n; ++g) {
         int len = group_len(n, g);
         int64_t o = g * GROUP;
@@ -586,18 +636,8 @@ void orc_lion_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* s
             float theta_hat = unsplit1(tb[o + j], rho[o + j]);
             float m = dequant_m1(qm[o + j], sm[g]);
             float gr = orc_bf16_to_f32(grad[o + j]);
-
-            float bm = b1 * m;
-            float cg = c1 * gr;
-            float c = bm + cg;
-            float sgn = sign1(c);
-            if (sgn == 0.0f) sgn = 0.0f;   /* a zero direction is +0 */
-            float decayed = lambda * theta_hat;
-            float step = eta * sgn;
-            float theta_new = decayed - step;
-            float b2m = b2 * m;
-            float c2g = c2 * gr;
-            float m_new = b2m + c2g;
+            float m_new;
+            float theta_new = lion1(lc, theta_hat, m, gr, &m_new);
 
             mn[j] = m_new;
             tn[j] = theta_new;
@@ -607,6 +647,56 @@ void orc_lion_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* s
         for (int j = 0; j < len; ++j) z[j] = orc_phi_m(mn[j]);
         quant_group_m(z, len, qm + o, sm + g);
         for (int j = 0; j < len; ++j) split1(tn[j], &tb[o + j], &rho[o + j]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compression disabled (Practical advice: compression can be switched off  */
+/* per layer).  The same updates over an FP32 master weight and FP32        */
+/* moments, in place; tb receives theta' = bf16_rne(theta_n), the weight    */
+/* the model computes with.                                                 */
+
+void orc_adamw_step_fp32(int64_t n, float* theta, float* m, float* v, uint16_t* tb,
+                         const uint16_t* grad, double lr, double beta1, double beta2,
+                         double eps, double wd, int64_t t)
+{
+    float sc[8];
+    orc_adamw_scalars(lr, beta1, beta2, eps, wd, t, sc);
+    for (int64_t i = 0; i < n; ++i) {
+        float m_new, v_new, root;
+        float theta_new = adam1(sc, theta[i], m[i], v[i], orc_bf16_to_f32(grad[i]), &m_new,
+                                &v_new, &root);
+        theta[i] = theta_new;
+        m[i] = m_new;
+        v[i] = v_new;
+        tb[i] = orc_bf16_rne(theta_new);
+    }
+}
+
+void orc_sgd_step_fp32(int64_t n, float* theta, float* b, uint16_t* tb, const uint16_t* grad,
+                       double lr, double momentum, double wd)
+{
+    const float mu = (float)momentum, eta = (float)lr, omega = (float)wd;
+    for (int64_t i = 0; i < n; ++i) {
+        float b_new;
+        float theta_new = sgd1(mu, eta, omega, theta[i], b[i], orc_bf16_to_f32(grad[i]), &b_new);
+        theta[i] = theta_new;
+        b[i] = b_new;
+        tb[i] = orc_bf16_rne(theta_new);
+    }
+}
+
+void orc_lion_step_fp32(int64_t n, float* theta, float* m, uint16_t* tb, const uint16_t* grad,
+                        double lr, double beta1, double beta2, double wd)
+{
+    float lc[6];
+    lion_scalars(lr, beta1, beta2, wd, lc);
+    for (int64_t i = 0; i < n; ++i) {
+        float m_new;
+        float theta_new = lion1(lc, theta[i], m[i], orc_bf16_to_f32(grad[i]), &m_new);
+        theta[i] = theta_new;
+        m[i] = m_new;
+        tb[i] = orc_bf16_rne(theta_new);
     }
 }
 

@@ -81,6 +81,16 @@ void orc_phi_m_inv_array(const float* z, int64_t n, float* out);
 void orc_phi_v_array(const float* x, int64_t n, float* out);
 void orc_phi_v_inv_array(const float* z, int64_t n, float* out);
 
+/* Compression disabled for a tensor: FP32 master weight and moments, the
+ * same updates, theta' = bf16_rne(theta_n) written to tb. */
+void orc_adamw_step_fp32(int64_t n, float* theta, float* m, float* v, uint16_t* tb,
+                         const uint16_t* grad, double lr, double beta1, double beta2,
+                         double eps, double wd, int64_t t);
+void orc_sgd_step_fp32(int64_t n, float* theta, float* b, uint16_t* tb, const uint16_t* grad,
+                       double lr, double momentum, double wd);
+void orc_lion_step_fp32(int64_t n, float* theta, float* m, uint16_t* tb, const uint16_t* grad,
+                        double lr, double beta1, double beta2, double wd);
+
 #ifdef __cplusplus
 }
 #endif
