@@ -49,8 +49,13 @@ def source_hash() -> str:
 
 def algorithmic_bytes(w: W.Workload) -> int:
     """Bytes the method must move per step: read theta', rho, m, v codes, both
-    scales and the BF16 grad; write everything but the grad."""
+    scales and the BF16 grad; write everything but the grad.  Uncompressed
+    (_fp32) state: read the FP32 master weight and moments and the grad, write
+    them back and theta'."""
     total = 0
+    if w.optimizer.endswith("_fp32"):
+        per = 14 if w.optimizer == "adamw_fp32" else 10       # bytes read = bytes written
+        return sum(2 * per * t.numel for t in w.tensors)
     for t in w.tensors:
         n, g = t.numel, (t.numel + 31) // 32
         rd = 2 * n + n + n + 2 * g + 2 * n
@@ -379,6 +384,7 @@ def main():
     torch.cuda.synchronize()
     if not args.no_other_optimizers:
         out["other_optimizers"] = [other_optimizer("llama31_8b_lion", 10, stream),
+                                   other_optimizer("llama31_8b_adamw_fp32", 5, stream),
                                    other_optimizer("resnet50", 10, stream),
                                    other_optimizer("flat1m", 10, stream),
                                    other_optimizer("gpt2_small", 10, stream),

@@ -219,14 +219,66 @@ __device__ __forceinline__ void load_lane(const GTensor& T, int64_t e, Lane8& L)
     if (kOpt == kAdamW) L.vs = gok ? T.scales[g * Layout<kOpt>::kScl + 1] : 0u;
 }
 
+// ---- the update of one element ---------------------------------------------
+//
+// The optimizer arithmetic on FP32 values, one IEEE binary32 operation per
+// line with the division and square root correctly rounded: the compressed
+// step's general path applies it to the rebuilt weight and dequantised
+// moments, the uncompressed (_FP32) step to the stored FP32 values.
+struct Upd {
+    float theta, m, v, root;        // new weight, momentum, variance, sqrt(variance)
+};
+
+template <int kOpt>
+__device__ __forceinline__ Upd update(float theta_hat, float m, float v, float g,
+                                      const StepScalars& P) {
+    Upd r;
+    r.v = 0.0f;
+    r.root = 0.0f;
+    if (kOpt == kAdamW) {
+        const AdamScalars& a = P.a;
+        const float bm = a.b1 * m;
+        const float cg = a.c1 * g;
+        r.m = bm + cg;
+        const float bv = a.b2 * v;
+        const float gg = g * g;
+        const float cgg = a.c2 * gg;
+        r.v = bv + cgg;
+        r.root = __builtin_sqrtf(r.v);
+        const float den0 = r.root * a.kappa;
+        const float den = den0 + a.eps;
+        const float u = r.m / den;
+        const float decayed = a.lambda * theta_hat;
+        const float stp = a.alpha * u;
+        r.theta = decayed - stp;
+    } else if (kOpt == kSgd) {
+        const SgdScalars& s = P.s;
+        const float decay = s.omega * theta_hat;
+        const float g2 = g + decay;
+        const float mb = s.mu * m;
+        r.m = mb + g2;
+        const float stp = s.eta * r.m;
+        r.theta = theta_hat - stp;
+    } else {
+        const LionScalars& l = P.l;
+        const float bm = l.b1 * m;
+        const float cg = l.c1 * g;
+        const float c = bm + cg;
+        const float decayed = l.lambda * theta_hat;
+        const float stp = l.eta * lion_sign(c);
+        r.theta = decayed - stp;
+        const float b2m = l.b2 * m;
+        const float c2g = l.c2 * g;
+        r.m = b2m + c2g;
+    }
+    return r;
+}
+
 // ---- the fused step on one sub-tile of one lane ----------------------------
 
 template <int kOpt>
 __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
                                           const Lane8& L, const StepScalars& P) {
-    const AdamScalars& a = P.a;
-    const SgdScalars& s = P.s;
-    const LionScalars& l = P.l;
     float z[8], w[8], tn[8];
     uint32_t amax_m = 0, amax_v = 0;
     const float dm = m_step(L.ms);
@@ -236,45 +288,14 @@ __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
         const float theta_hat = unsplit(L.th[j], L.rho[j]);
         const float m = dequant_m(L.qm[j], dm);
         const float g = bf16_to_f32(L.gr[j]);
-        float m_new, theta_new;
+        const float v = (kOpt == kAdamW) ? dequant_v(L.qv[j], dv) : 0.0f;
+        const Upd u = update<kOpt>(theta_hat, m, v, g, P);
         if (kOpt == kAdamW) {
-            const float v = dequant_v(L.qv[j], dv);
-            const float bm = a.b1 * m;
-            const float cg = a.c1 * g;
-            m_new = bm + cg;
-            const float bv = a.b2 * v;
-            const float gg = g * g;
-            const float cgg = a.c2 * gg;
-            const float v_new = bv + cgg;
-            const float root = __builtin_sqrtf(v_new);
-            const float den0 = root * a.kappa;
-            const float den = den0 + a.eps;
-            const float u = m_new / den;
-            const float decayed = a.lambda * theta_hat;
-            const float stp = a.alpha * u;
-            theta_new = decayed - stp;
-            w[j] = root;
-            amax_v = max(amax_v, as_u32(root));
-        } else if (kOpt == kSgd) {
-            const float decay = s.omega * theta_hat;
-            const float g2 = g + decay;
-            const float mb = s.mu * m;
-            m_new = mb + g2;
-            const float stp = s.eta * m_new;
-            theta_new = theta_hat - stp;
-        } else {
-            const float bm = l.b1 * m;
-            const float cg = l.c1 * g;
-            const float c = bm + cg;
-            const float decayed = l.lambda * theta_hat;
-            const float stp = l.eta * lion_sign(c);
-            theta_new = decayed - stp;
-            const float b2m = l.b2 * m;
-            const float c2g = l.c2 * g;
-            m_new = b2m + c2g;
+            w[j] = u.root;
+            amax_v = max(amax_v, as_u32(u.root));
         }
-        z[j] = phi_m(m_new);
-        tn[j] = theta_new;
+        z[j] = phi_m(u.m);
+        tn[j] = u.theta;
         amax_m = max(amax_m, as_u32(z[j]) & 0x7FFFFFFFu);
     }
     // group scales: every lane of the quad computes the same value
@@ -559,6 +580,117 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
         const int64_t e0 = (tile - cur.begin) * kTile;
         if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true>(cur.T, e0, lane, P);
         else step_tile<kOpt, false>(cur.T, e0, lane, P);
+    }
+}
+
+// ---- the uncompressed step (_FP32 kinds) -------------------------------------
+//
+// Compression switched off for a layer: FP32 records of 8 elements [theta[8] |
+// m[8] | v[8]] (96 bytes, AdamW) or [theta[8] | m[8]] (64 bytes), the update
+// above on the stored values, theta' = bf16_rne(theta_n) for the model.  The
+// same tiles and launch shape as the compressed step; each lane moves 8
+// elements per sub-tile as 16-byte accesses.
+template <int kOpt> struct LayoutF {
+    static constexpr int kRec = kOpt == kAdamW ? 96 : 64;   // bytes per 8-element record
+};
+constexpr int kThOffF = 0, kMOffF = 32, kVOffF = 64;        // field byte offsets
+
+struct RawF {
+    uint4 th[2], m[2], v[2], gr;
+};
+
+template <int kOpt>
+__device__ __forceinline__ void load_raw_f(const GTensor& T, int64_t e, RawF& R) {
+    const GLOBAL uint8_t* rec = T.codes + (e >> 3) * LayoutF<kOpt>::kRec;
+    R.gr = ld4(T.grad + e);
+    R.th[0] = ld4(rec + kThOffF);
+    R.th[1] = ld4(rec + kThOffF + 16);
+    R.m[0] = ld4(rec + kMOffF);
+    R.m[1] = ld4(rec + kMOffF + 16);
+    if (kOpt == kAdamW) {
+        R.v[0] = ld4(rec + kVOffF);
+        R.v[1] = ld4(rec + kVOffF + 16);
+    }
+}
+
+__device__ __forceinline__ float f_at(const uint4* v, int j) { return as_f32(word(v[j >> 2], j & 3)); }
+
+template <int kOpt>
+__device__ __forceinline__ void step_f(const GTensor& T, int64_t e, const RawF& R,
+                                       const StepScalars& P) {
+    uint32_t th[8], mo[8], vo[8], tb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float v = (kOpt == kAdamW) ? f_at(R.v, j) : 0.0f;
+        const Upd u = update<kOpt>(f_at(R.th, j), f_at(R.m, j), v, as_f32(bf16_bits(R.gr, j)), P);
+        th[j] = as_u32(u.theta);
+        mo[j] = as_u32(u.m);
+        vo[j] = as_u32(u.v);
+        tb[j] = f32_to_bf16(u.theta);
+    }
+    GLOBAL uint8_t* rec = T.codes + (e >> 3) * LayoutF<kOpt>::kRec;
+    st4(T.theta + e, pack_u16x8(tb));
+    st4(rec + kThOffF, make_uint4(th[0], th[1], th[2], th[3]));
+    st4(rec + kThOffF + 16, make_uint4(th[4], th[5], th[6], th[7]));
+    st4(rec + kMOffF, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+    st4(rec + kMOffF + 16, make_uint4(mo[4], mo[5], mo[6], mo[7]));
+    if (kOpt == kAdamW) {
+        st4(rec + kVOffF, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+        st4(rec + kVOffF + 16, make_uint4(vo[4], vo[5], vo[6], vo[7]));
+    }
+}
+
+// element by element, for a lane whose 8 elements run past the tensor's end
+template <int kOpt>
+__device__ __forceinline__ void step_f_partial(const GTensor& T, int64_t e, const StepScalars& P) {
+    GLOBAL float* rec = (GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
+    for (int j = 0; j < 8; ++j) {
+        if (e + j >= T.numel) break;
+        const float v = (kOpt == kAdamW) ? rec[16 + j] : 0.0f;
+        const Upd u = update<kOpt>(rec[j], rec[8 + j], v, bf16_to_f32(T.grad[e + j]), P);
+        rec[j] = u.theta;
+        rec[8 + j] = u.m;
+        if (kOpt == kAdamW) rec[16 + j] = u.v;
+        T.theta[e + j] = (uint16_t)f32_to_bf16(u.theta);
+    }
+}
+
+template <int kOpt>
+__global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restrict__ table,
+                                                        const int64_t* __restrict__ tile_begin,
+                                                        int32_t count, int64_t total_tiles,
+                                                        DevTensor one, StepScalars P) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    if (wave >= total_tiles) return;
+    TileCursor cur;
+    cur.start(table, tile_begin, count, one, total_tiles, wave);
+    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+        cur.seek(table, tile_begin, tile);
+        const GTensor& T = cur.T;
+        const int64_t e0 = (tile - cur.begin) * kTile + lane * kLaneElems;
+        if ((tile - cur.begin) * kTile + kTile <= T.numel) {
+            RawF R[2];
+            load_raw_f<kOpt>(T, e0, R[0]);
+            if (kSubTiles > 1) load_raw_f<kOpt>(T, e0 + kSubTile, R[1]);
+#pragma unroll
+            for (int k = 0; k < kSubTiles; ++k) {
+                step_f<kOpt>(T, e0 + k * kSubTile, R[k & 1], P);
+                if (k + 2 < kSubTiles) load_raw_f<kOpt>(T, e0 + (k + 2) * kSubTile, R[k & 1]);
+            }
+        } else {
+            for (int k = 0; k < kSubTiles; ++k) {
+                const int64_t e = e0 + k * kSubTile;
+                if (e + kLaneElems <= T.numel) {
+                    RawF R;
+                    load_raw_f<kOpt>(T, e, R);
+                    step_f<kOpt>(T, e, R, P);
+                } else if (e < T.numel) {
+                    step_f_partial<kOpt>(T, e, P);
+                }
+            }
+        }
     }
 }
 
@@ -877,6 +1009,69 @@ __global__ __launch_bounds__(256) void export_kernel(DevTensor d, float* theta_o
     }
 }
 
+// _FP32 kinds: master weight = x, theta' = bf16_rne(x), m = v = 0.
+template <int kOpt>
+__global__ __launch_bounds__(256) void init_fp32_kernel(DevTensor d, const float* x) {
+    const GTensor T = view(d);
+    const int64_t n = T.numel;
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        GLOBAL float* rec = (GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
+        for (int j = 0; j < 8; ++j) {
+            if (e + j >= n) break;
+            const float v = x[e + j];
+            rec[j] = v;
+            rec[8 + j] = 0.0f;
+            if (kOpt == kAdamW) rec[16 + j] = 0.0f;
+            T.theta[e + j] = (uint16_t)f32_to_bf16(v);
+        }
+    }
+}
+
+template <int kOpt>
+__global__ __launch_bounds__(256) void export_fp32_kernel(DevTensor d, float* theta_out,
+                                                          float* m_out, float* v_out) {
+    const GTensor T = view(d);
+    const int64_t n = T.numel;
+    FLAT_LOOP(n) {
+        const int64_t e = c * kSubTile + lane * kLaneElems;
+        const GLOBAL float* rec = (const GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
+        for (int j = 0; j < 8; ++j) {
+            if (e + j >= n) break;
+            if (theta_out) theta_out[e + j] = rec[j];
+            if (m_out) m_out[e + j] = rec[8 + j];
+            if (kOpt == kAdamW && v_out) v_out[e + j] = rec[16 + j];
+        }
+    }
+}
+
+// m = v = 0 over a list of _FP32 tensors (master weights kept), one tile per wave.
+template <int kOpt>
+__global__ __launch_bounds__(256) void zero_fp32_kernel(const DevTensor* __restrict__ table,
+                                                        const int64_t* __restrict__ tile_begin,
+                                                        int32_t count, int64_t total_tiles) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    if (wave >= total_tiles) return;
+    TileCursor cur;
+    cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
+    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+        cur.seek(table, tile_begin, tile);
+        const GTensor& T = cur.T;
+        const int64_t e0 = (tile - cur.begin) * kTile;
+        for (int k = 0; k < kSubTiles; ++k) {
+            const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
+            GLOBAL float* rec = (GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
+            for (int j = 0; j < 8; ++j) {
+                if (e + j >= T.numel) break;
+                rec[8 + j] = 0.0f;
+                if (kOpt == kAdamW) rec[16 + j] = 0.0f;
+            }
+        }
+    }
+}
+
 // ---- bandwidth probe ---------------------------------------------------------
 //
 // The AdamW step's memory traffic with the arithmetic taken out: the same
@@ -1031,8 +1226,12 @@ static int check_sgd(const flashopt_sgd_hparams* hp, int64_t step) {
 }
 
 static bool valid_kind(int32_t kind) {
-    return kind == FLASHOPT_KIND_ADAMW || kind == FLASHOPT_KIND_SGD || kind == FLASHOPT_KIND_LION;
+    return kind >= FLASHOPT_KIND_ADAMW && kind <= FLASHOPT_KIND_LION_FP32;
 }
+
+// the optimizer of a kind (kAdamW, kSgd, kLion) and whether its state is FP32
+static int opt_of(int32_t kind) { return kind % 3; }
+static bool is_fp32(int32_t kind) { return kind >= FLASHOPT_KIND_ADAMW_FP32; }
 
 static int check_lion(const flashopt_lion_hparams* hp, int64_t step) {
     if (!hp) return FLASHOPT_ERR_NULL;
@@ -1062,6 +1261,12 @@ static LionScalars lion_scalars(const flashopt_lion_hparams& hp) {
 static int check_tensor(const flashopt_tensor& t, int32_t kind) {
     if (t.numel < 0 || t.numel > kMaxNumel) return FLASHOPT_ERR_SIZE;
     if (t.numel == 0) return FLASHOPT_OK;
+    if (is_fp32(kind)) {                         // FP32 records, no scales
+        if (!t.theta || !t.codes) return FLASHOPT_ERR_NULL;
+        if (!aligned(t.theta, 16) || !aligned(t.codes, 16) || (t.grad && !aligned(t.grad, 16)))
+            return FLASHOPT_ERR_ALIGN;
+        return FLASHOPT_OK;
+    }
     if (!t.theta || !t.codes || !t.scales) return FLASHOPT_ERR_NULL;
     if (!aligned(t.theta, 16) || !aligned(t.codes, 8) ||
         !aligned(t.scales, kind == FLASHOPT_KIND_ADAMW ? 4 : 2) || (t.grad && !aligned(t.grad, 16)))
@@ -1280,11 +1485,13 @@ size_t flashopt_list_workspace_bytes(int32_t count) {
 
 size_t flashopt_codes_bytes(int32_t kind, int64_t numel) {
     if (!valid_kind(kind) || numel < 0 || numel > kMaxNumel) return 0;
-    return (size_t)((numel + 7) / 8) * (kind == FLASHOPT_KIND_ADAMW ? 24 : 16);
+    const bool adam = opt_of(kind) == kAdamW;
+    const size_t rec = is_fp32(kind) ? (adam ? 96 : 64) : (adam ? 24 : 16);
+    return (size_t)((numel + 7) / 8) * rec;
 }
 
 size_t flashopt_scales_bytes(int32_t kind, int64_t numel) {
-    if (!valid_kind(kind) || numel < 0 || numel > kMaxNumel) return 0;
+    if (!valid_kind(kind) || is_fp32(kind) || numel < 0 || numel > kMaxNumel) return 0;
     return (size_t)((numel + 31) / 32) * (kind == FLASHOPT_KIND_ADAMW ? 4 : 2);
 }
 
@@ -1297,12 +1504,16 @@ int flashopt_tensor_init(const flashopt_tensor* t, int32_t kind, const float* th
     if (t->numel == 0) return FLASHOPT_OK;
     if (!theta) return FLASHOPT_ERR_NULL;
     const int64_t chunks = (t->numel + kSubTile - 1) / kSubTile;
+    const dim3 grid(grid_for(chunks));
+    hipStream_t s = (hipStream_t)stream;
     if (kind == FLASHOPT_KIND_ADAMW)
-        hipLaunchKernelGGL(init_kernel<kAdamW>, dim3(grid_for(chunks)), dim3(kBlock), 0,
-                           (hipStream_t)stream, to_dev(*t), theta);
+        hipLaunchKernelGGL(init_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t), theta);
+    else if (kind == FLASHOPT_KIND_ADAMW_FP32)
+        hipLaunchKernelGGL(init_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t), theta);
+    else if (is_fp32(kind))
+        hipLaunchKernelGGL(init_fp32_kernel<kSgd>, grid, dim3(kBlock), 0, s, to_dev(*t), theta);
     else
-        hipLaunchKernelGGL(init_kernel<kSgd>, dim3(grid_for(chunks)), dim3(kBlock), 0,
-                           (hipStream_t)stream, to_dev(*t), theta);
+        hipLaunchKernelGGL(init_kernel<kSgd>, grid, dim3(kBlock), 0, s, to_dev(*t), theta);
     return launch_status();
 }
 
@@ -1312,15 +1523,23 @@ int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta,
     if (!valid_kind(kind)) return FLASHOPT_ERR_ARG;
     const int st = check_tensor(*t, kind);
     if (st != FLASHOPT_OK) return st;
-    if (kind != FLASHOPT_KIND_ADAMW) v = nullptr;           // one-momentum layouts have no v
+    if (opt_of(kind) != kAdamW) v = nullptr;                // one-momentum layouts have no v
     if (t->numel == 0 || (!theta && !m && !v)) return FLASHOPT_OK;
     const int64_t chunks = (t->numel + kSubTile - 1) / kSubTile;
+    const dim3 grid(grid_for(chunks));
+    hipStream_t s = (hipStream_t)stream;
     if (kind == FLASHOPT_KIND_ADAMW)
-        hipLaunchKernelGGL(export_kernel<kAdamW>, dim3(grid_for(chunks)), dim3(kBlock), 0,
-                           (hipStream_t)stream, to_dev(*t), theta, m, v);
+        hipLaunchKernelGGL(export_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t), theta, m,
+                           v);
+    else if (kind == FLASHOPT_KIND_ADAMW_FP32)
+        hipLaunchKernelGGL(export_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t),
+                           theta, m, v);
+    else if (is_fp32(kind))
+        hipLaunchKernelGGL(export_fp32_kernel<kSgd>, grid, dim3(kBlock), 0, s, to_dev(*t), theta,
+                           m, v);
     else
-        hipLaunchKernelGGL(export_kernel<kSgd>, dim3(grid_for(chunks)), dim3(kBlock), 0,
-                           (hipStream_t)stream, to_dev(*t), theta, m, v);
+        hipLaunchKernelGGL(export_kernel<kSgd>, grid, dim3(kBlock), 0, s, to_dev(*t), theta, m,
+                           v);
     return launch_status();
 }
 
@@ -1409,14 +1628,22 @@ int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void
 int flashopt_state_zero(const flashopt_list* L, void* stream) {
     if (!L) return FLASHOPT_ERR_NULL;
     if (L->total_tiles == 0) return FLASHOPT_OK;
+    const dim3 grid(grid_for(L->total_tiles));
+    hipStream_t s = (hipStream_t)stream;
+    const DevTensor* tab = L->d_table;
+    const int64_t* tb = L->d_tile_begin;
     if (L->kind == FLASHOPT_KIND_ADAMW)
-        hipLaunchKernelGGL(zero_kernel<kAdamW>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                           (hipStream_t)stream, (const DevTensor*)L->d_table,
-                           (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+        hipLaunchKernelGGL(zero_kernel<kAdamW>, grid, dim3(kBlock), 0, s, tab, tb, L->count,
+                           L->total_tiles);
+    else if (L->kind == FLASHOPT_KIND_ADAMW_FP32)
+        hipLaunchKernelGGL(zero_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, s, tab, tb, L->count,
+                           L->total_tiles);
+    else if (is_fp32(L->kind))
+        hipLaunchKernelGGL(zero_fp32_kernel<kSgd>, grid, dim3(kBlock), 0, s, tab, tb, L->count,
+                           L->total_tiles);
     else
-        hipLaunchKernelGGL(zero_kernel<kSgd>, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                           (hipStream_t)stream, (const DevTensor*)L->d_table,
-                           (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+        hipLaunchKernelGGL(zero_kernel<kSgd>, grid, dim3(kBlock), 0, s, tab, tb, L->count,
+                           L->total_tiles);
     return launch_status();
 }
 
@@ -1431,12 +1658,24 @@ int flashopt_stream_probe(const flashopt_list* L, void* stream) {
     return launch_status();
 }
 
-static int launch_step(int opt, const DevTensor* table, const int64_t* tile_begin, int32_t count,
-                       int64_t total_tiles, const DevTensor& one, const StepScalars& P,
-                       void* stream) {
+static int launch_step(int opt, bool fp32, const DevTensor* table, const int64_t* tile_begin,
+                       int32_t count, int64_t total_tiles, const DevTensor& one,
+                       const StepScalars& P, void* stream) {
     if (total_tiles == 0) return FLASHOPT_OK;
     const dim3 grid(grid_for(total_tiles));
     hipStream_t st = (hipStream_t)stream;
+    if (fp32) {
+        if (opt == kAdamW)
+            hipLaunchKernelGGL(step_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table,
+                               tile_begin, count, total_tiles, one, P);
+        else if (opt == kSgd)
+            hipLaunchKernelGGL(step_fp32_kernel<kSgd>, grid, dim3(kBlock), 0, st, table,
+                               tile_begin, count, total_tiles, one, P);
+        else
+            hipLaunchKernelGGL(step_fp32_kernel<kLion>, grid, dim3(kBlock), 0, st, table,
+                               tile_begin, count, total_tiles, one, P);
+        return launch_status();
+    }
     if (opt == kAdamW)
         hipLaunchKernelGGL(step_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table, tile_begin,
                            count, total_tiles, one, P);
@@ -1450,8 +1689,8 @@ static int launch_step(int opt, const DevTensor* table, const int64_t* tile_begi
 }
 
 static int launch_list(int opt, const flashopt_list* L, const StepScalars& P, void* stream) {
-    return launch_step(opt, L->d_table, L->d_tile_begin, L->count, L->total_tiles, DevTensor{},
-                       P, stream);
+    return launch_step(opt, is_fp32(L->kind), L->d_table, L->d_tile_begin, L->count,
+                       L->total_tiles, DevTensor{}, P, stream);
 }
 
 static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint16_t* grad,
@@ -1460,7 +1699,8 @@ static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint
     if (t.numel == 0) return FLASHOPT_OK;
     DevTensor one = to_dev(t);
     one.grad = (uint64_t)grad;
-    return launch_step(opt, nullptr, nullptr, 1, tiles_of(t.numel), one, P, stream);
+    return launch_step(opt, is_fp32(L->kind), nullptr, nullptr, 1, tiles_of(t.numel), one, P,
+                       stream);
 }
 
 static int check_one(const flashopt_list* L, int32_t index, const uint16_t* grad) {
@@ -1477,7 +1717,7 @@ int flashopt_adamw_step(const flashopt_list* L, const flashopt_adamw_hparams* hp
     if (!L) return FLASHOPT_ERR_NULL;
     int st = check_adam(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
+    if (opt_of(L->kind) != kAdamW) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     flashopt_list* M = const_cast<flashopt_list*>(L);   // only the scalar cache changes
     StepScalars P{};
@@ -1490,7 +1730,7 @@ int flashopt_sgd_step(const flashopt_list* L, const flashopt_sgd_hparams* hp, in
     if (!L) return FLASHOPT_ERR_NULL;
     int st = check_sgd(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
+    if (opt_of(L->kind) != kSgd) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     StepScalars P{};
     P.s = sgd_scalars(*hp);
@@ -1502,7 +1742,7 @@ int flashopt_lion_step(const flashopt_list* L, const flashopt_lion_hparams* hp, 
     if (!L) return FLASHOPT_ERR_NULL;
     int st = check_lion(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (L->kind != FLASHOPT_KIND_LION) return FLASHOPT_ERR_ARG;
+    if (opt_of(L->kind) != kLion) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     StepScalars P{};
     P.l = lion_scalars(*hp);
@@ -1515,7 +1755,7 @@ int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_
     if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
     int st = check_adam(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
+    if (opt_of(L->kind) != kAdamW) return FLASHOPT_ERR_ARG;
     st = check_one(L, index, grad);
     if (st != FLASHOPT_OK) return st;
     flashopt_list* M = const_cast<flashopt_list*>(L);
@@ -1530,7 +1770,7 @@ int flashopt_sgd_step_one(const flashopt_list* L, int32_t index, const uint16_t*
     if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
     int st = check_sgd(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
+    if (opt_of(L->kind) != kSgd) return FLASHOPT_ERR_ARG;
     st = check_one(L, index, grad);
     if (st != FLASHOPT_OK) return st;
     StepScalars P{};
@@ -1544,7 +1784,7 @@ int flashopt_lion_step_one(const flashopt_list* L, int32_t index, const uint16_t
     if (index < 0 || index >= L->count) return FLASHOPT_ERR_INDEX;
     int st = check_lion(hp, step);
     if (st != FLASHOPT_OK) return st;
-    if (L->kind != FLASHOPT_KIND_LION) return FLASHOPT_ERR_ARG;
+    if (opt_of(L->kind) != kLion) return FLASHOPT_ERR_ARG;
     st = check_one(L, index, grad);
     if (st != FLASHOPT_OK) return st;
     StepScalars P{};

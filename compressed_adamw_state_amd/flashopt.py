@@ -28,9 +28,18 @@ class FlashoptError(RuntimeError):
         self.status = status
 
 
-KIND = {"adamw": 0, "sgd": 1, "lion": 2}          # flashopt_kind
-RECORD = {"adamw": 24, "sgd": 16, "lion": 16}     # code-record bytes per 8 elements
-SCALES = {"adamw": 2, "sgd": 1, "lion": 1}        # FP16 scales per 32-element group
+# flashopt_kind; "<opt>_fp32" is the optimizer with compression switched off
+# (FP32 master weight and moments, no scales)
+KIND = {"adamw": 0, "sgd": 1, "lion": 2, "adamw_fp32": 3, "sgd_fp32": 4, "lion_fp32": 5}
+RECORD = {"adamw": 24, "sgd": 16, "lion": 16,     # state-record bytes per 8 elements
+          "adamw_fp32": 96, "sgd_fp32": 64, "lion_fp32": 64}
+SCALES = {"adamw": 2, "sgd": 1, "lion": 1,        # FP16 scales per 32-element group
+          "adamw_fp32": 0, "sgd_fp32": 0, "lion_fp32": 0}
+
+
+def base_optimizer(kind: str) -> str:
+    """The optimizer of a state kind: "adamw_fp32" -> "adamw"."""
+    return kind[:-5] if kind.endswith("_fp32") else kind
 
 
 class Tensor(ctypes.Structure):
@@ -206,9 +215,10 @@ def flashopt_dequantize_lin_v(q, scale, v_out, stream=None) -> None:
 # ---- tensor lists -----------------------------------------------------------
 
 class TensorState:
-    """Device arrays of one tensor's compressed state (allocated with torch):
-    BF16 theta', the interleaved code records and the FP16 scales, in the
-    layout of include/flashopt.h."""
+    """Device arrays of one tensor's state (allocated with torch): BF16
+    theta', the interleaved code records and the FP16 scales in the layout of
+    include/flashopt.h -- or, for the "_fp32" kinds, the FP32 records and no
+    scales."""
 
     def __init__(self, numel: int, optimizer: str, device, theta: Optional[torch.Tensor] = None):
         """theta: an existing contiguous BF16 tensor of numel elements to use as
@@ -227,8 +237,8 @@ class TensorState:
                                   dtype=torch.int16, device=device)
 
     def descriptor(self, grad: Optional[torch.Tensor] = None) -> Tensor:
-        return Tensor(self.numel, _ptr(self.theta), _ptr(self.codes), _ptr(self.scales),
-                      _ptr(grad))
+        scales = _ptr(self.scales) if self.scales.numel() else None
+        return Tensor(self.numel, _ptr(self.theta), _ptr(self.codes), scales, _ptr(grad))
 
 
 def flashopt_tensor_init(st: TensorState, theta_fp32: torch.Tensor, stream=None) -> None:
@@ -357,14 +367,15 @@ def flashopt_lion_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: 
 
 
 def step(lst: FlashoptList, optimizer: str, hp: dict, t: int, stream=None) -> None:
+    """optimizer: "adamw", "sgd", "lion" (either state kind of that optimizer)."""
     {"adamw": flashopt_adamw_step, "sgd": flashopt_sgd_step,
-     "lion": flashopt_lion_step}[optimizer](lst, hp, t, stream)
+     "lion": flashopt_lion_step}[base_optimizer(optimizer)](lst, hp, t, stream)
 
 
 def step_one(lst: FlashoptList, optimizer: str, index: int, grad, hp: dict, t: int,
              stream=None) -> None:
     {"adamw": flashopt_adamw_step_one, "sgd": flashopt_sgd_step_one,
-     "lion": flashopt_lion_step_one}[optimizer](lst, index, grad, hp, t, stream)
+     "lion": flashopt_lion_step_one}[base_optimizer(optimizer)](lst, index, grad, hp, t, stream)
 
 
 def build_list(theta_fp32: List[torch.Tensor], optimizer: str,

@@ -16,6 +16,12 @@ for SGD and Lion) plus the step counter; with theta' saved as the model's
 own BF16 weights, an AdamW checkpoint is 5.125 B/param (the page's 12 -> 5
 B/param).  Loading it into a fresh optimizer resumes bit for bit.
 
+A parameter group with "compress": False (the page's practical advice:
+compression can be switched off for layers that are sensitive to it) keeps
+an FP32 master weight and FP32 moments instead (the library's _fp32 state
+kinds, 14 B/param for AdamW); its parameters still compute in BF16, and the
+group is stepped by the same kind of launch.
+
 This module only marshals: every arithmetic operation of the update runs in
 the HIP library, and there is no fallback.
 """
@@ -46,17 +52,20 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._hooks = []
         for group in self.param_groups:
             for p in group["params"]:
-                self._init_param(p)
+                self._init_param(p, self._state_kind(group))
         self._build_lists()
         if gradient_release:
             self._install_release_hooks()
 
     # -- state -----------------------------------------------------------------
-    def _init_param(self, p: torch.Tensor) -> None:
+    def _state_kind(self, group) -> str:
+        return self.kind if group.get("compress", True) else self.kind + "_fp32"
+
+    def _init_param(self, p: torch.Tensor, kind: str) -> None:
         if not p.is_cuda:
             raise ValueError("FlashOptim parameters must live on the GPU")
         if p.dtype == torch.float32:
-            st = F.TensorState(p.numel(), self.kind, p.device)
+            st = F.TensorState(p.numel(), kind, p.device)
             F.flashopt_tensor_init(st, p.detach().reshape(-1).contiguous())
             p.data = st.theta.view(p.shape)      # the model now computes with theta'
         elif p.dtype == torch.bfloat16:
@@ -64,7 +73,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 raise ValueError("BF16 parameters must be contiguous")
             # theta' is the parameter's own storage; the split of its exact FP32
             # value rewrites the same BF16 bits and gives rho = 0
-            st = F.TensorState(p.numel(), self.kind, p.device, theta=p.data.view(-1))
+            st = F.TensorState(p.numel(), kind, p.device, theta=p.data.view(-1))
             F.flashopt_tensor_init(st, p.detach().reshape(-1).float())
         else:
             raise ValueError(f"unsupported parameter dtype {p.dtype}")
@@ -75,7 +84,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         for group in self.param_groups:
             states = [self.state[p]["flash"] for p in group["params"]]
             grads = [None] * len(states)
-            self._lists.append(F.FlashoptList(states, grads, optimizer=self.kind)
+            self._lists.append(F.FlashoptList(states, grads, optimizer=self._state_kind(group))
                                if states else None)
 
     def _hp(self, group) -> dict:
@@ -157,6 +166,8 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 len(a["params"]) != len(b["params"]) for a, b in zip(saved, self.param_groups)):
             raise ValueError("checkpoint has a different parameter layout")
         for group, sgroup in zip(self.param_groups, saved):
+            if sgroup.get("compress", True) != group.get("compress", True):
+                raise ValueError("checkpoint has a different compressed / uncompressed split")
             for k, v in sgroup.items():
                 if k != "params":
                     group[k] = v
@@ -186,9 +197,10 @@ class FlashAdamW(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
                  weight_decay: float = 1e-2, gradient_release: bool = False,
-                 release_streams: int = 1):
+                 release_streams: int = 1, compress: bool = True):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), eps=eps,
-                                      weight_decay=weight_decay), gradient_release, release_streams)
+                                      weight_decay=weight_decay, compress=compress),
+                         gradient_release, release_streams)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],
@@ -202,9 +214,9 @@ class FlashSGD(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 0.1, momentum: float = 0.9,
                  weight_decay: float = 0.0, gradient_release: bool = False,
-                 release_streams: int = 1):
-        super().__init__(params, dict(lr=lr, momentum=momentum, weight_decay=weight_decay),
-                         gradient_release, release_streams)
+                 release_streams: int = 1, compress: bool = True):
+        super().__init__(params, dict(lr=lr, momentum=momentum, weight_decay=weight_decay,
+                                      compress=compress), gradient_release, release_streams)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], momentum=group["momentum"],
@@ -217,9 +229,9 @@ class FlashLion(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-4, betas=(0.9, 0.99),
                  weight_decay: float = 0.0, gradient_release: bool = False,
-                 release_streams: int = 1):
-        super().__init__(params, dict(lr=lr, betas=tuple(betas), weight_decay=weight_decay),
-                         gradient_release, release_streams)
+                 release_streams: int = 1, compress: bool = True):
+        super().__init__(params, dict(lr=lr, betas=tuple(betas), weight_decay=weight_decay,
+                                      compress=compress), gradient_release, release_streams)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],

@@ -41,7 +41,7 @@ class TensorSpec:
 class Workload:
     name: str
     tensors: tuple
-    optimizer: str          # "adamw" | "sgd"
+    optimizer: str          # state kind: "adamw" | "sgd" | "lion", or "<one of them>_fp32"
     steps: int
     seed: int
     grad_dist: str          # see draw_grad
@@ -153,6 +153,9 @@ WORKLOADS = {
     # FlashLion at the Llama-3.1-8B shapes (the one-momentum layout, 10.125 B/param)
     "llama31_8b_lion": Workload("llama31_8b_lion", tuple(llama31_8b()), "lion", 20, 5, "normal",
                                 1e-4, LION_HP),
+    # compression switched off for every layer: FP32 master weight and moments
+    "llama31_8b_adamw_fp32": Workload("llama31_8b_adamw_fp32", tuple(llama31_8b()), "adamw_fp32",
+                                      20, 6, "normal", 1e-3, ADAMW_HP),
 }
 
 

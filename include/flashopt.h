@@ -88,11 +88,17 @@ typedef enum flashopt_status {
     FLASHOPT_ERR_INDEX = -8      /* tensor index out of range                          */
 } flashopt_status;
 
-/* Optimizer kind of a tensor's state layout (and of a list). */
+/* Optimizer kind of a tensor's state layout (and of a list).  The _FP32
+ * kinds are the same optimizers with compression switched off (practical-
+ * advice section: compression can be disabled per layer): an FP32 master
+ * weight and FP32 moments, no codes, no scales. */
 typedef enum flashopt_kind {
     FLASHOPT_KIND_ADAMW = 0,     /* rho, momentum and variance codes; two scales per group */
     FLASHOPT_KIND_SGD = 1,       /* rho and momentum codes; one scale per group            */
-    FLASHOPT_KIND_LION = 2       /* the SGD layout, holding Lion's momentum                */
+    FLASHOPT_KIND_LION = 2,      /* the SGD layout, holding Lion's momentum                */
+    FLASHOPT_KIND_ADAMW_FP32 = 3,/* FP32 theta, m, v records; no scales                    */
+    FLASHOPT_KIND_SGD_FP32 = 4,  /* FP32 theta, momentum-buffer records; no scales         */
+    FLASHOPT_KIND_LION_FP32 = 5  /* FP32 theta, momentum records; no scales                */
 } flashopt_kind;
 
 /* One parameter tensor and its compressed state (all DEVICE pointers).
@@ -110,7 +116,15 @@ typedef enum flashopt_kind {
  *   scales[g]                = FP16 momentum scale of group g (SGD, Lion)
  * for g < ceil(n/32).  flashopt_codes_bytes / flashopt_scales_bytes give the
  * sizes.  The values are exactly those of the flat arrays the quantisers and
- * split below produce, only their placement differs. */
+ * split below produce, only their placement differs.
+ *
+ * _FP32 kinds: `codes` holds FP32 records of 8 elements (16-byte aligned),
+ *   ((float*)codes)[r*F + 0 + j]  = master weight theta of element 8r+j
+ *   ((float*)codes)[r*F + 8 + j]  = momentum (SGD: momentum buffer)
+ *   ((float*)codes)[r*F + 16 + j] = variance (AdamW only)
+ * with F = 24 (AdamW) or 16 (SGD, Lion) floats; `scales` is not used (may be
+ * NULL) and theta' is written by every step as bf16_rne(theta), the weight
+ * the model computes with (it is never read). */
 typedef struct flashopt_tensor {
     int64_t numel;           /* n >= 0                                                   */
     uint16_t* theta;         /* [n] BF16 theta'; the model weight the forward pass reads */
@@ -201,12 +215,14 @@ size_t flashopt_codes_bytes(int32_t kind, int64_t numel);
 size_t flashopt_scales_bytes(int32_t kind, int64_t numel);
 /* Initialise from FP32 master weights (device [n]): theta' and rho by the split
  * (weight-splitting section, Eq. 1-2), momentum and variance codes and all
- * scales zero (m = v = 0).  t->grad is not used. */
+ * scales zero (m = v = 0).  _FP32 kinds: the master weight is theta itself,
+ * theta' = bf16_rne(theta), m = v = 0.  t->grad is not used. */
 int flashopt_tensor_init(const flashopt_tensor* t, int32_t kind, const float* theta,
                          void* stream);
-/* Export to FP32 (device [n] each; any may be NULL, v ignored for SGD): the
- * rebuilt master weight theta' + (rho*K8)*h, and the dequantised momentum and
- * variance (companding section, Alg. 2-3) -- checkpoint conversion. */
+/* Export to FP32 (device [n] each; any may be NULL, v ignored for SGD and
+ * Lion): the rebuilt master weight theta' + (rho*K8)*h, and the dequantised
+ * momentum and variance (companding section, Alg. 2-3) -- checkpoint
+ * conversion.  _FP32 kinds: copies of the stored values. */
 int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta, float* m,
                            float* v, void* stream);
 
@@ -218,9 +234,11 @@ int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta,
  * (it is a set-up call); afterwards the descriptors' pointers are fixed,
  * except the gradients (flashopt_list_set_grads).  count may be 0. */
 size_t flashopt_list_workspace_bytes(int32_t count);
-/* kind: FLASHOPT_KIND_ADAMW (steps with flashopt_adamw_step*),
- * FLASHOPT_KIND_SGD (flashopt_sgd_step*) or FLASHOPT_KIND_LION
- * (flashopt_lion_step*); a step of another kind returns FLASHOPT_ERR_ARG. */
+/* kind: FLASHOPT_KIND_ADAMW[_FP32] (steps with flashopt_adamw_step*),
+ * FLASHOPT_KIND_SGD[_FP32] (flashopt_sgd_step*) or FLASHOPT_KIND_LION[_FP32]
+ * (flashopt_lion_step*); a step of another optimizer returns FLASHOPT_ERR_ARG.
+ * Every tensor of a list has the list's kind: a model with some layers left
+ * uncompressed keeps two lists and steps both. */
 int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, int32_t kind,
                          void* workspace, size_t workspace_bytes, void* stream,
                          flashopt_list** out);
@@ -231,12 +249,14 @@ int64_t flashopt_list_numel(const flashopt_list* list);
  * arguments, no host staging buffer), so steps enqueued later see them. */
 int flashopt_list_set_grads(flashopt_list* list, const uint16_t* const* grads, void* stream);
 /* Zero the momentum and variance codes and every scale of the list (m = v = 0;
- * theta' and rho are kept). */
+ * theta' and rho, or the FP32 master weight, are kept). */
 int flashopt_state_zero(const flashopt_list* list, void* stream);
 
 /* ---- the fused step (fused-step section, Alg. 4): ONE launch over the whole
  * list.  step is the 1-based AdamW counter t shared by all tensors of one
- * optimizer step.  The list's kind must match the step. */
+ * optimizer step.  The list's kind must match the step.  On an _FP32 list
+ * the same update runs on the FP32 values (no dequantisation, requantisation
+ * or split) and theta' = bf16_rne(theta_n) is written. */
 int flashopt_adamw_step(const flashopt_list* list, const flashopt_adamw_hparams* hp,
                         int64_t step, void* stream);
 int flashopt_sgd_step(const flashopt_list* list, const flashopt_sgd_hparams* hp,

@@ -70,7 +70,7 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_create(arr, 1, A, ws, need - 1, None, ctypes.byref(out)) == -6
     assert lib.flashopt_list_create(arr, 1, A, P(0x100010), need, None, ctypes.byref(out)) == -6
     assert lib.flashopt_list_create(arr, -1, A, ws, need, None, ctypes.byref(out)) == -2
-    assert lib.flashopt_list_create(arr, 1, 5, ws, need, None, ctypes.byref(out)) == -4
+    assert lib.flashopt_list_create(arr, 1, 6, ws, need, None, ctypes.byref(out)) == -4
     nul = (F.Tensor * 1)(F.Tensor(10, fake, None, fake, fake))
     assert lib.flashopt_list_create(nul, 1, A, ws, need, None, ctypes.byref(out)) == -1
     mis_t = (F.Tensor * 1)(F.Tensor(10, P(0x10008), fake, fake, fake))
@@ -79,7 +79,7 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_create(mis_s, 1, A, ws, need, None, ctypes.byref(out)) == -3
     neg = (F.Tensor * 1)(F.Tensor(-5, fake, fake, fake, fake))
     assert lib.flashopt_list_create(neg, 1, A, ws, need, None, ctypes.byref(out)) == -2
-    assert lib.flashopt_tensor_init(arr, 3, fake, None) == -4
+    assert lib.flashopt_tensor_init(arr, 6, fake, None) == -4
     assert lib.flashopt_tensor_init(arr, A, None, None) == -1
     assert lib.flashopt_tensor_init(mis_t, A, fake, None) == -3
     assert lib.flashopt_tensor_export(None, A, fake, None, None, None) == -1
@@ -119,4 +119,21 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_lion_step(L, ctypes.byref(lion), 1, None) == 0      # nothing to launch
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == -4      # Lion list
     assert lib.flashopt_codes_bytes(2, 17) == 3 * 16 and lib.flashopt_scales_bytes(2, 33) == 4
+    assert lib.flashopt_list_destroy(L) == 0
+    # uncompressed kinds: FP32 records of 96 / 64 bytes per 8 elements, no scales
+    AF, SF, LF = 3, 4, 5
+    assert lib.flashopt_codes_bytes(AF, 17) == 3 * 96 and lib.flashopt_codes_bytes(SF, 17) == 3 * 64
+    assert lib.flashopt_codes_bytes(LF, 8) == 64
+    assert all(lib.flashopt_scales_bytes(k, 33) == 0 for k in (AF, SF, LF))
+    no_codes = (F.Tensor * 1)(F.Tensor(10, fake, None, None, fake))
+    assert lib.flashopt_list_create(no_codes, 1, AF, ws, need, None, ctypes.byref(out)) == -1
+    mis_c = (F.Tensor * 1)(F.Tensor(10, fake, P(0x10008), None, fake))   # records need 16 B
+    assert lib.flashopt_list_create(mis_c, 1, AF, ws, need, None, ctypes.byref(out)) == -3
+    assert lib.flashopt_tensor_init(mis_c, LF, fake, None) == -3
+    assert lib.flashopt_list_create(None, 0, AF, None, 0, None, ctypes.byref(out)) == 0
+    L = out
+    assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == 0       # nothing to launch
+    assert lib.flashopt_sgd_step(L, ctypes.byref(sgd), 1, None) == -4       # AdamW list
+    assert lib.flashopt_stream_probe(L, None) == -4                         # compressed only
+    assert lib.flashopt_state_zero(L, None) == 0
     assert lib.flashopt_list_destroy(L) == 0
