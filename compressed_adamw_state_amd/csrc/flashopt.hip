@@ -585,73 +585,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
 
 // ---- the uncompressed step (_FP32 kinds) -------------------------------------
 //
-// Compression switched off for a layer: FP32 records of 8 elements [theta[8] |
-// m[8] | v[8]] (96 bytes, AdamW) or [theta[8] | m[8]] (64 bytes), the update
-// above on the stored values, theta' = bf16_rne(theta_n) for the model.  The
-// same tiles and launch shape as the compressed step; each lane moves 8
-// elements per sub-tile as 16-byte accesses.
+// Compression switched off for a layer: the FP32 master weight and moments in
+// blocks of 512 elements [theta[512] | m[512] | v[512]] (6 KB, AdamW) or
+// [theta[512] | m[512]] (4 KB), the update above on the stored values, and
+// theta' = bf16_rne(theta_n) for the model.  The same tiles and launch shape
+// as the compressed step; in a 512-element sub-tile lane l owns elements
+// [4l, 4l+4) and [256+4l, 256+4l+4), so every 16-byte load and store of a
+// wave covers one contiguous kilobyte of a field (a per-lane record of 8
+// elements would spread each access over 96-byte strides).
 template <int kOpt> struct LayoutF {
-    static constexpr int kRec = kOpt == kAdamW ? 96 : 64;   // bytes per 8-element record
+    static constexpr int kFields = kOpt == kAdamW ? 3 : 2;
+    static constexpr int kBlock = kSubTile * 4 * kFields;   // bytes per 512-element block
 };
-constexpr int kThOffF = 0, kMOffF = 32, kVOffF = 64;        // field byte offsets
+
+// field f (0 theta, 1 m, 2 v) of element i
+template <int kOpt>
+__device__ __forceinline__ GLOBAL float* f32_at(const GTensor& T, int64_t i, int f) {
+    return (GLOBAL float*)(T.codes + (i >> 9) * LayoutF<kOpt>::kBlock) + f * kSubTile + (i & 511);
+}
 
 struct RawF {
-    uint4 th[2], m[2], v[2], gr;
+    uint4 th[2], m[2], v[2];        // a lane's 2 x 4 FP32 values of each field
+    uint2 gr[2];                    // and its 2 x 4 BF16 gradients
 };
 
+// e: a sub-tile's first element (a multiple of 512)
 template <int kOpt>
-__device__ __forceinline__ void load_raw_f(const GTensor& T, int64_t e, RawF& R) {
-    const GLOBAL uint8_t* rec = T.codes + (e >> 3) * LayoutF<kOpt>::kRec;
-    R.gr = ld4(T.grad + e);
-    R.th[0] = ld4(rec + kThOffF);
-    R.th[1] = ld4(rec + kThOffF + 16);
-    R.m[0] = ld4(rec + kMOffF);
-    R.m[1] = ld4(rec + kMOffF + 16);
+__device__ __forceinline__ void load_raw_f(const GTensor& T, int64_t e, int lane, RawF& R) {
+    const GLOBAL uint8_t* blk = T.codes + (e >> 9) * LayoutF<kOpt>::kBlock + 16 * lane;
+    R.gr[0] = ld2(T.grad + e + 4 * lane);
+    R.gr[1] = ld2(T.grad + e + 256 + 4 * lane);
+    R.th[0] = ld4(blk);
+    R.th[1] = ld4(blk + 1024);
+    R.m[0] = ld4(blk + 2048);
+    R.m[1] = ld4(blk + 3072);
     if (kOpt == kAdamW) {
-        R.v[0] = ld4(rec + kVOffF);
-        R.v[1] = ld4(rec + kVOffF + 16);
+        R.v[0] = ld4(blk + 4096);
+        R.v[1] = ld4(blk + 5120);
     }
 }
 
 __device__ __forceinline__ float f_at(const uint4* v, int j) { return as_f32(word(v[j >> 2], j & 3)); }
 
+__device__ __forceinline__ float g_at(const uint2* v, int j) {
+    const uint32_t w = word(v[j >> 2], (j & 3) >> 1);
+    return as_f32((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
 template <int kOpt>
-__device__ __forceinline__ void step_f(const GTensor& T, int64_t e, const RawF& R,
+__device__ __forceinline__ void step_f(const GTensor& T, int64_t e, int lane, const RawF& R,
                                        const StepScalars& P) {
     uint32_t th[8], mo[8], vo[8], tb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float v = (kOpt == kAdamW) ? f_at(R.v, j) : 0.0f;
-        const Upd u = update<kOpt>(f_at(R.th, j), f_at(R.m, j), v, as_f32(bf16_bits(R.gr, j)), P);
+        const Upd u = update<kOpt>(f_at(R.th, j), f_at(R.m, j), v, g_at(R.gr, j), P);
         th[j] = as_u32(u.theta);
         mo[j] = as_u32(u.m);
         vo[j] = as_u32(u.v);
         tb[j] = f32_to_bf16(u.theta);
     }
-    GLOBAL uint8_t* rec = T.codes + (e >> 3) * LayoutF<kOpt>::kRec;
-    st4(T.theta + e, pack_u16x8(tb));
-    st4(rec + kThOffF, make_uint4(th[0], th[1], th[2], th[3]));
-    st4(rec + kThOffF + 16, make_uint4(th[4], th[5], th[6], th[7]));
-    st4(rec + kMOffF, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-    st4(rec + kMOffF + 16, make_uint4(mo[4], mo[5], mo[6], mo[7]));
+    GLOBAL uint8_t* blk = T.codes + (e >> 9) * LayoutF<kOpt>::kBlock + 16 * lane;
+    st2(T.theta + e + 4 * lane, make_uint2(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16)));
+    st2(T.theta + e + 256 + 4 * lane, make_uint2(tb[4] | (tb[5] << 16), tb[6] | (tb[7] << 16)));
+    st4(blk, make_uint4(th[0], th[1], th[2], th[3]));
+    st4(blk + 1024, make_uint4(th[4], th[5], th[6], th[7]));
+    st4(blk + 2048, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+    st4(blk + 3072, make_uint4(mo[4], mo[5], mo[6], mo[7]));
     if (kOpt == kAdamW) {
-        st4(rec + kVOffF, make_uint4(vo[0], vo[1], vo[2], vo[3]));
-        st4(rec + kVOffF + 16, make_uint4(vo[4], vo[5], vo[6], vo[7]));
+        st4(blk + 4096, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+        st4(blk + 5120, make_uint4(vo[4], vo[5], vo[6], vo[7]));
     }
 }
 
-// element by element, for a lane whose 8 elements run past the tensor's end
+// a sub-tile that runs past the tensor's end: the lane's 8 elements one by one
 template <int kOpt>
-__device__ __forceinline__ void step_f_partial(const GTensor& T, int64_t e, const StepScalars& P) {
-    GLOBAL float* rec = (GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
+__device__ __forceinline__ void step_f_partial(const GTensor& T, int64_t e, int lane,
+                                               const StepScalars& P) {
     for (int j = 0; j < 8; ++j) {
-        if (e + j >= T.numel) break;
-        const float v = (kOpt == kAdamW) ? rec[16 + j] : 0.0f;
-        const Upd u = update<kOpt>(rec[j], rec[8 + j], v, bf16_to_f32(T.grad[e + j]), P);
-        rec[j] = u.theta;
-        rec[8 + j] = u.m;
-        if (kOpt == kAdamW) rec[16 + j] = u.v;
-        T.theta[e + j] = (uint16_t)f32_to_bf16(u.theta);
+        const int64_t i = e + (j >> 2) * 256 + 4 * lane + (j & 3);
+        if (i >= T.numel) continue;
+        GLOBAL float* th = f32_at<kOpt>(T, i, 0);
+        const float v = (kOpt == kAdamW) ? th[2 * kSubTile] : 0.0f;
+        const Upd u = update<kOpt>(th[0], th[kSubTile], v, bf16_to_f32(T.grad[i]), P);
+        th[0] = u.theta;
+        th[kSubTile] = u.m;
+        if (kOpt == kAdamW) th[2 * kSubTile] = u.v;
+        T.theta[i] = (uint16_t)f32_to_bf16(u.theta);
     }
 }
 
@@ -669,25 +689,26 @@ __global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restr
     for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const GTensor& T = cur.T;
-        const int64_t e0 = (tile - cur.begin) * kTile + lane * kLaneElems;
-        if ((tile - cur.begin) * kTile + kTile <= T.numel) {
+        const int64_t e0 = (tile - cur.begin) * kTile;
+        if (e0 + kTile <= T.numel) {
             RawF R[2];
-            load_raw_f<kOpt>(T, e0, R[0]);
-            if (kSubTiles > 1) load_raw_f<kOpt>(T, e0 + kSubTile, R[1]);
+            load_raw_f<kOpt>(T, e0, lane, R[0]);
+            if (kSubTiles > 1) load_raw_f<kOpt>(T, e0 + kSubTile, lane, R[1]);
 #pragma unroll
             for (int k = 0; k < kSubTiles; ++k) {
-                step_f<kOpt>(T, e0 + k * kSubTile, R[k & 1], P);
-                if (k + 2 < kSubTiles) load_raw_f<kOpt>(T, e0 + (k + 2) * kSubTile, R[k & 1]);
+                step_f<kOpt>(T, e0 + k * kSubTile, lane, R[k & 1], P);
+                if (k + 2 < kSubTiles)
+                    load_raw_f<kOpt>(T, e0 + (k + 2) * kSubTile, lane, R[k & 1]);
             }
         } else {
             for (int k = 0; k < kSubTiles; ++k) {
                 const int64_t e = e0 + k * kSubTile;
-                if (e + kLaneElems <= T.numel) {
+                if (e + kSubTile <= T.numel) {
                     RawF R;
-                    load_raw_f<kOpt>(T, e, R);
-                    step_f<kOpt>(T, e, R, P);
+                    load_raw_f<kOpt>(T, e, lane, R);
+                    step_f<kOpt>(T, e, lane, R, P);
                 } else if (e < T.numel) {
-                    step_f_partial<kOpt>(T, e, P);
+                    step_f_partial<kOpt>(T, e, lane, P);
                 }
             }
         }
@@ -1016,13 +1037,13 @@ __global__ __launch_bounds__(256) void init_fp32_kernel(DevTensor d, const float
     const int64_t n = T.numel;
     FLAT_LOOP(n) {
         const int64_t e = c * kSubTile + lane * kLaneElems;
-        GLOBAL float* rec = (GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
         for (int j = 0; j < 8; ++j) {
             if (e + j >= n) break;
+            GLOBAL float* th = f32_at<kOpt>(T, e + j, 0);
             const float v = x[e + j];
-            rec[j] = v;
-            rec[8 + j] = 0.0f;
-            if (kOpt == kAdamW) rec[16 + j] = 0.0f;
+            th[0] = v;
+            th[kSubTile] = 0.0f;
+            if (kOpt == kAdamW) th[2 * kSubTile] = 0.0f;
             T.theta[e + j] = (uint16_t)f32_to_bf16(v);
         }
     }
@@ -1035,12 +1056,12 @@ __global__ __launch_bounds__(256) void export_fp32_kernel(DevTensor d, float* th
     const int64_t n = T.numel;
     FLAT_LOOP(n) {
         const int64_t e = c * kSubTile + lane * kLaneElems;
-        const GLOBAL float* rec = (const GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
         for (int j = 0; j < 8; ++j) {
             if (e + j >= n) break;
-            if (theta_out) theta_out[e + j] = rec[j];
-            if (m_out) m_out[e + j] = rec[8 + j];
-            if (kOpt == kAdamW && v_out) v_out[e + j] = rec[16 + j];
+            const GLOBAL float* th = f32_at<kOpt>(T, e + j, 0);
+            if (theta_out) theta_out[e + j] = th[0];
+            if (m_out) m_out[e + j] = th[kSubTile];
+            if (kOpt == kAdamW && v_out) v_out[e + j] = th[2 * kSubTile];
         }
     }
 }
@@ -1062,11 +1083,11 @@ __global__ __launch_bounds__(256) void zero_fp32_kernel(const DevTensor* __restr
         const int64_t e0 = (tile - cur.begin) * kTile;
         for (int k = 0; k < kSubTiles; ++k) {
             const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
-            GLOBAL float* rec = (GLOBAL float*)(T.codes + (e >> 3) * LayoutF<kOpt>::kRec);
             for (int j = 0; j < 8; ++j) {
                 if (e + j >= T.numel) break;
-                rec[8 + j] = 0.0f;
-                if (kOpt == kAdamW) rec[16 + j] = 0.0f;
+                GLOBAL float* th = f32_at<kOpt>(T, e + j, 0);
+                th[kSubTile] = 0.0f;
+                if (kOpt == kAdamW) th[2 * kSubTile] = 0.0f;
             }
         }
     }
@@ -1486,8 +1507,9 @@ size_t flashopt_list_workspace_bytes(int32_t count) {
 size_t flashopt_codes_bytes(int32_t kind, int64_t numel) {
     if (!valid_kind(kind) || numel < 0 || numel > kMaxNumel) return 0;
     const bool adam = opt_of(kind) == kAdamW;
-    const size_t rec = is_fp32(kind) ? (adam ? 96 : 64) : (adam ? 24 : 16);
-    return (size_t)((numel + 7) / 8) * rec;
+    if (is_fp32(kind))                           // whole 512-element blocks of FP32 fields
+        return (size_t)((numel + kSubTile - 1) / kSubTile) * kSubTile * 4 * (adam ? 3 : 2);
+    return (size_t)((numel + 7) / 8) * (adam ? 24 : 16);
 }
 
 size_t flashopt_scales_bytes(int32_t kind, int64_t numel) {

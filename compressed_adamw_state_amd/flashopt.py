@@ -31,10 +31,9 @@ class FlashoptError(RuntimeError):
 # flashopt_kind; "<opt>_fp32" is the optimizer with compression switched off
 # (FP32 master weight and moments, no scales)
 KIND = {"adamw": 0, "sgd": 1, "lion": 2, "adamw_fp32": 3, "sgd_fp32": 4, "lion_fp32": 5}
-RECORD = {"adamw": 24, "sgd": 16, "lion": 16,     # state-record bytes per 8 elements
-          "adamw_fp32": 96, "sgd_fp32": 64, "lion_fp32": 64}
-SCALES = {"adamw": 2, "sgd": 1, "lion": 1,        # FP16 scales per 32-element group
-          "adamw_fp32": 0, "sgd_fp32": 0, "lion_fp32": 0}
+RECORD = {"adamw": 24, "sgd": 16, "lion": 16}     # code-record bytes per 8 elements
+SCALES = {"adamw": 2, "sgd": 1, "lion": 1}        # FP16 scales per 32-element group
+FP32_FIELDS = {"adamw_fp32": 3, "sgd_fp32": 2, "lion_fp32": 2}   # per 512-element block
 
 
 def base_optimizer(kind: str) -> str:
@@ -217,7 +216,7 @@ def flashopt_dequantize_lin_v(q, scale, v_out, stream=None) -> None:
 class TensorState:
     """Device arrays of one tensor's state (allocated with torch): BF16
     theta', the interleaved code records and the FP16 scales in the layout of
-    include/flashopt.h -- or, for the "_fp32" kinds, the FP32 records and no
+    include/flashopt.h -- or, for the "_fp32" kinds, the blocks of FP32 fields and no
     scales."""
 
     def __init__(self, numel: int, optimizer: str, device, theta: Optional[torch.Tensor] = None):

@@ -96,9 +96,9 @@ typedef enum flashopt_kind {
     FLASHOPT_KIND_ADAMW = 0,     /* rho, momentum and variance codes; two scales per group */
     FLASHOPT_KIND_SGD = 1,       /* rho and momentum codes; one scale per group            */
     FLASHOPT_KIND_LION = 2,      /* the SGD layout, holding Lion's momentum                */
-    FLASHOPT_KIND_ADAMW_FP32 = 3,/* FP32 theta, m, v records; no scales                    */
-    FLASHOPT_KIND_SGD_FP32 = 4,  /* FP32 theta, momentum-buffer records; no scales         */
-    FLASHOPT_KIND_LION_FP32 = 5  /* FP32 theta, momentum records; no scales                */
+    FLASHOPT_KIND_ADAMW_FP32 = 3,/* FP32 theta, m, v in 512-element blocks; no scales      */
+    FLASHOPT_KIND_SGD_FP32 = 4,  /* FP32 theta and momentum buffer in blocks; no scales    */
+    FLASHOPT_KIND_LION_FP32 = 5  /* FP32 theta and momentum in blocks; no scales           */
 } flashopt_kind;
 
 /* One parameter tensor and its compressed state (all DEVICE pointers).
@@ -118,13 +118,15 @@ typedef enum flashopt_kind {
  * sizes.  The values are exactly those of the flat arrays the quantisers and
  * split below produce, only their placement differs.
  *
- * _FP32 kinds: `codes` holds FP32 records of 8 elements (16-byte aligned),
- *   ((float*)codes)[r*F + 0 + j]  = master weight theta of element 8r+j
- *   ((float*)codes)[r*F + 8 + j]  = momentum (SGD: momentum buffer)
- *   ((float*)codes)[r*F + 16 + j] = variance (AdamW only)
- * with F = 24 (AdamW) or 16 (SGD, Lion) floats; `scales` is not used (may be
- * NULL) and theta' is written by every step as bf16_rne(theta), the weight
- * the model computes with (it is never read). */
+ * _FP32 kinds: `codes` holds blocks of 512 elements of FP32 fields (16-byte
+ * aligned),
+ *   ((float*)codes)[b*512*F + 0 + p]    = master weight theta of element 512b+p
+ *   ((float*)codes)[b*512*F + 512 + p]  = momentum (SGD: momentum buffer)
+ *   ((float*)codes)[b*512*F + 1024 + p] = variance (AdamW only)
+ * with F = 3 (AdamW) or 2 (SGD, Lion), b < ceil(n/512), p < 512; the last
+ * block's entries past n are padding.  `scales` is not used (may be NULL) and
+ * theta' is written by every step as bf16_rne(theta), the weight the model
+ * computes with (it is never read). */
 typedef struct flashopt_tensor {
     int64_t numel;           /* n >= 0                                                   */
     uint16_t* theta;         /* [n] BF16 theta'; the model weight the forward pass reads */

@@ -120,10 +120,10 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == -4      # Lion list
     assert lib.flashopt_codes_bytes(2, 17) == 3 * 16 and lib.flashopt_scales_bytes(2, 33) == 4
     assert lib.flashopt_list_destroy(L) == 0
-    # uncompressed kinds: FP32 records of 96 / 64 bytes per 8 elements, no scales
+    # uncompressed kinds: 512-element blocks of 3 (AdamW) or 2 FP32 fields, no scales
     AF, SF, LF = 3, 4, 5
-    assert lib.flashopt_codes_bytes(AF, 17) == 3 * 96 and lib.flashopt_codes_bytes(SF, 17) == 3 * 64
-    assert lib.flashopt_codes_bytes(LF, 8) == 64
+    assert lib.flashopt_codes_bytes(AF, 17) == 6144 and lib.flashopt_codes_bytes(SF, 513) == 8192
+    assert lib.flashopt_codes_bytes(LF, 512) == 4096 and lib.flashopt_codes_bytes(AF, 0) == 0
     assert all(lib.flashopt_scales_bytes(k, 33) == 0 for k in (AF, SF, LF))
     no_codes = (F.Tensor * 1)(F.Tensor(10, fake, None, None, fake))
     assert lib.flashopt_list_create(no_codes, 1, AF, ws, need, None, ctypes.byref(out)) == -1

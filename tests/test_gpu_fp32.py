@@ -16,21 +16,22 @@ from parity import log, u16
 
 pytestmark = pytest.mark.gpu
 
-RAGGED = [1, 7, 8, 9, 31, 33, 511, 513, 2047, 2048, 2049, 4095, 4097, 6143, 32 * 777 + 5,
-          (1 << 20) + 7, 0, 64]
+RAGGED = [1, 7, 8, 9, 31, 33, 511, 512, 513, 1023, 1536, 2047, 2048, 2049, 2560, 4095, 4097,
+          6143, 32 * 777 + 5, (1 << 20) + 7, 0, 64]
 HP = W.HPARAMS
 
 
 def fp32_fields(st: F.TensorState, idx=None):
-    """theta (FP32 master), m, v (AdamW) of elements idx from the FP32 records."""
-    F_ = F.RECORD[st.optimizer] // 4                      # floats per 8-element record
-    rec = st.codes.view(torch.float32)
+    """theta (FP32 master), m, v (AdamW) of elements idx, read out of the
+    512-element blocks of FP32 fields (include/flashopt.h)."""
+    nf = F.FP32_FIELDS[st.optimizer]
+    words = st.codes.view(torch.float32)
     if idx is None:
         idx = torch.arange(st.numel, device=st.codes.device)
-    base = (idx >> 3) * F_ + (idx & 7)
-    out = {"theta": rec[base].cpu().numpy(), "m": rec[base + 8].cpu().numpy()}
+    base = (idx >> 9) * (512 * nf) + (idx & 511)
+    out = {"theta": words[base].cpu().numpy(), "m": words[base + 512].cpu().numpy()}
     if st.optimizer == "adamw_fp32":
-        out["v"] = rec[base + 16].cpu().numpy()
+        out["v"] = words[base + 1024].cpu().numpy()
     return out
 
 
@@ -128,7 +129,7 @@ def test_fp32_init_export_zero():
 
 def test_fp32_kinds_host_checks():
     st = F.TensorState(100, "adamw_fp32", "cuda")
-    assert st.scales.numel() == 0 and st.codes.numel() == 13 * 96
+    assert st.scales.numel() == 0 and st.codes.numel() == 512 * 4 * 3
     d = st.descriptor()
     assert d.scales is None
     lst = F.FlashoptList([st], [None], optimizer="adamw_fp32")
