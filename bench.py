@@ -287,6 +287,9 @@ def main():
                     help="size of the plain copy kernel timed after the steps (0: skip)")
     ap.add_argument("--no-other-optimizers", action="store_true",
                     help="skip the FlashLion (Llama-3.1-8B) and FlashSGD (ResNet-50) lines")
+    ap.add_argument("--secondary", default=None, metavar="WORKLOAD",
+                    help="time only this secondary workload (--steps steps) and print its "
+                         "record: a profiling aid, not the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -296,6 +299,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     F.lib()
+
+    if args.secondary:
+        r = other_optimizer(args.secondary, args.steps, torch.cuda.current_stream())
+        print(json.dumps(r), flush=True)
+        return
 
     w = W.WORKLOADS[args.workload]
     assert w.optimizer == "adamw" and not w.release

@@ -12,7 +12,7 @@ import torch
 import oracle
 from compressed_adamw_state_amd import optim as O
 
-from parity import state_fields, u16
+from parity import log, state_fields, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -168,3 +168,64 @@ def test_export_fp32_matches_oracle_rebuild():
                                       oracle.dequant_m(o.qm, o.sm).view(np.uint32))
         np.testing.assert_array_equal(v.cpu().numpy().view(np.uint32),
                                       oracle.dequant_v(o.qv, o.sv).view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["adamw", "lion", "sgd"])
+def test_training_tracks_the_uncompressed_optimizer(kind):
+    """Fig. 2's claim on a synthetic regression task: a small MLP trained
+    with the compressed optimizer (BF16 weights theta', compressed state)
+    follows the loss curve of torch's optimizer on FP32 weights.  The model
+    computes in FP32 (weights upcast in the forward), so no BF16 GEMM runs."""
+    torch.manual_seed(7)
+    n, d, h = 4096, 64, 256
+    X = torch.randn(n, d, device="cuda")
+    a = torch.randn(d, device="cuda") / d ** 0.5
+    y = (torch.sin(3 * X @ a) + 0.1 * torch.randn(n, device="cuda")).unsqueeze(1)
+    init = [torch.randn(h, d) / d ** 0.5, torch.zeros(h), torch.randn(1, h) / h ** 0.5,
+            torch.zeros(1)]
+
+    def loss_of(ps):
+        w1, b1, w2, b2 = (p.float() for p in ps)
+        return ((torch.relu(X @ w1.t() + b1) @ w2.t() + b2 - y) ** 2).mean()
+
+    hp = {"adamw": dict(lr=3e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01),
+          "lion": dict(lr=3e-4, betas=(0.9, 0.99), weight_decay=0.1),
+          "sgd": dict(lr=0.05, momentum=0.9, weight_decay=1e-4)}[kind]
+    flash = [torch.nn.Parameter(t.clone().cuda()) for t in init]
+    ref = [torch.nn.Parameter(t.clone().cuda()) for t in init]
+    fo = {"adamw": O.FlashAdamW, "lion": O.FlashLion, "sgd": O.FlashSGD}[kind](flash, **hp)
+    if kind == "adamw":
+        ro = torch.optim.AdamW(ref, **hp)
+    elif kind == "sgd":
+        ro = torch.optim.SGD(ref, **hp)
+    else:
+        ro = None                                        # torch has no Lion: reference below
+        m_ref = [torch.zeros_like(p) for p in ref]
+    curves = {"flash": [], "ref": []}
+    for it in range(300):
+        for ps, opt, key in ((flash, fo, "flash"), (ref, ro, "ref")):
+            loss = loss_of(ps)
+            curves[key].append(loss.item())
+            if ps is flash:
+                opt.zero_grad()
+                loss.backward()
+                opt.step()
+            else:
+                for p in ps:
+                    p.grad = None
+                loss.backward()
+                if ro is not None:
+                    ro.step()
+                else:                                    # the published Lion rule, FP32
+                    with torch.no_grad():
+                        b1, b2 = hp["betas"]
+                        for p, m in zip(ps, m_ref):
+                            c = b1 * m + (1 - b1) * p.grad
+                            p.mul_(1 - hp["lr"] * hp["weight_decay"]).sub_(hp["lr"] * torch.sign(c))
+                            m.mul_(b2).add_((1 - b2) * p.grad)
+    f, r = np.array(curves["flash"]), np.array(curves["ref"])
+    log(f"{kind}: loss {f[0]:.4f} -> flash {f[-1]:.4f}, reference {r[-1]:.4f}")
+    assert f[-1] < 0.5 * f[0] and r[-1] < 0.5 * r[0]    # both learn
+    # the curves stay together: within 10 % (plus the noise floor) at every 25th step
+    for k in range(25, 300, 25):
+        assert abs(f[k] - r[k]) <= 0.1 * r[k] + 2e-3, (k, f[k], r[k])
