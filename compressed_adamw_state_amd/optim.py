@@ -9,12 +9,16 @@ layout of include/flashopt.h.  A parameter given in FP32 is split once at
 construction: its data becomes the BF16 theta' and rho keeps the rest of the
 FP32 value.  Every step is one launch of the library's fused kernel per
 parameter group (or, with gradient release, one launch per parameter from
-its gradient hook, after which the gradient is dropped).
+its gradient hook, after which the gradient is dropped).  As in torch.optim,
+a parameter whose gradient is None is skipped and every parameter keeps its
+own step count; a group where that leaves parameters out, or where the
+counts differ, is stepped by one launch per parameter.
 
 state_dict() holds the codes and scales (3.125 B/param for AdamW, 2.0625
-for SGD and Lion) plus the step counter; with theta' saved as the model's
-own BF16 weights, an AdamW checkpoint is 5.125 B/param (the page's 12 -> 5
-B/param).  Loading it into a fresh optimizer resumes bit for bit.
+for SGD and Lion) plus each parameter's step count; with theta' saved as
+the model's own BF16 weights, an AdamW checkpoint is 5.125 B/param (the
+page's 12 -> 5 B/param).  Loading it into a fresh optimizer resumes bit for
+bit.
 
 A parameter group with "compress": False (the page's practical advice:
 compression can be switched off for layers that are sensitive to it) keeps
@@ -47,7 +51,6 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._side = [torch.cuda.Stream() for _ in range(release_streams)] \
             if gradient_release and release_streams > 1 else []
         self._rr = 0
-        self._t = 0                              # optimizer steps taken (the AdamW t)
         self._lists: List[Optional[F.FlashoptList]] = []
         self._hooks = []
         for group in self.param_groups:
@@ -78,6 +81,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         else:
             raise ValueError(f"unsupported parameter dtype {p.dtype}")
         self.state[p]["flash"] = st
+        self.state[p]["step"] = 0                # this parameter's own t (as in torch.optim)
 
     def _build_lists(self) -> None:
         self._lists = []
@@ -103,22 +107,32 @@ class _FlashOptimizer(torch.optim.Optimizer):
             cur = torch.cuda.current_stream()
             for s in self._side:
                 cur.wait_stream(s)
-            self._t += 1
             return loss
-        self._t += 1
         for group, lst in zip(self.param_groups, self._lists):
             if lst is None:
                 continue
-            grads = []
-            for p in group["params"]:
+            params = group["params"]
+            for p in params:
                 g = p.grad
-                if g is None:
-                    g = torch.zeros_like(p)      # no gradient this step: a zero gradient
-                if g.dtype != torch.bfloat16 or not g.is_contiguous():
+                if g is not None and (g.dtype != torch.bfloat16 or not g.is_contiguous()):
                     raise ValueError("FlashOptim expects contiguous BF16 gradients")
-                grads.append(g.view(-1))
-            F.flashopt_list_set_grads(lst, grads)
-            F.step(lst, self.kind, self._hp(group), self._t)
+            steps = {self.state[p]["step"] for p in params}
+            if all(p.grad is not None for p in params) and len(steps) == 1:
+                # the common case: one launch over the whole group
+                t = steps.pop() + 1
+                F.flashopt_list_set_grads(lst, [p.grad.view(-1) for p in params])
+                F.step(lst, self.kind, self._hp(group), t)
+                for p in params:
+                    self.state[p]["step"] = t
+            else:
+                # as torch.optim: a parameter without a gradient is skipped, and
+                # each parameter keeps its own step count (bias correction)
+                for i, p in enumerate(params):
+                    if p.grad is None:
+                        continue
+                    t = self.state[p]["step"] + 1
+                    F.step_one(lst, self.kind, i, p.grad.view(-1), self._hp(group), t)
+                    self.state[p]["step"] = t
         return loss
 
     def _install_release_hooks(self) -> None:
@@ -137,14 +151,16 @@ class _FlashOptimizer(torch.optim.Optimizer):
                         self._rr += 1
                         stream.wait_stream(torch.cuda.current_stream())
                         g.record_stream(stream)  # the gradient outlives its release
+                    t = self.state[param]["step"] + 1
                     F.step_one(self._lists[gi], self.kind, pi, g.view(-1),
-                               self._hp(self.param_groups[gi]), self._t + 1, stream)
+                               self._hp(self.param_groups[gi]), t, stream)
+                    self.state[param]["step"] = t
                     param.grad = None            # gradient release: 2 B/param freed early
                 self._hooks.append(p.register_post_accumulate_grad_hook(hook))
 
     # -- checkpoints -------------------------------------------------------------
     def state_dict(self) -> dict:
-        sd = {"kind": self.kind, "t": self._t, "param_groups": [], "state": {}}
+        sd = {"kind": self.kind, "param_groups": [], "state": {}}
         index = 0
         for group in self.param_groups:
             g = {k: v for k, v in group.items() if k != "params"}
@@ -152,7 +168,8 @@ class _FlashOptimizer(torch.optim.Optimizer):
             for p in group["params"]:
                 st = self.state[p]["flash"]
                 sd["state"][index] = {"numel": st.numel, "codes": st.codes.clone(),
-                                      "scales": st.scales.clone()}
+                                      "scales": st.scales.clone(),
+                                      "step": self.state[p]["step"]}
                 g["params"].append(index)
                 index += 1
             sd["param_groups"].append(g)
@@ -178,7 +195,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
                     raise ValueError("checkpoint tensor size differs")
                 st.codes.copy_(src["codes"])
                 st.scales.copy_(src["scales"])
-        self._t = int(sd["t"])
+                self.state[p]["step"] = int(src["step"])
 
     def export_fp32(self, p: torch.Tensor):
         """(theta_hat, m, v) of one parameter in FP32 (v None unless AdamW)."""

@@ -52,7 +52,8 @@
  *
  * Alignment: BF16 arrays (theta', grad) 16 bytes; code records and flat
  * INT8/UINT8 code arrays 8 bytes; AdamW scale arrays 4 bytes, SGD / Lion and
- * flat scale arrays 2 bytes; FP32 arrays 16 bytes.
+ * flat scale arrays 2 bytes; FP32 arrays and the _FP32 kinds' state blocks 16
+ * bytes (the ablation entry points, element by element: their element size).
  *
  * Errors.  Every call validates its arguments on the host before launching
  * anything and returns a flashopt_status; a failed validation launches

@@ -229,3 +229,38 @@ def test_training_tracks_the_uncompressed_optimizer(kind):
     # the curves stay together: within 10 % (plus the noise floor) at every 25th step
     for k in range(25, 300, 25):
         assert abs(f[k] - r[k]) <= 0.1 * r[k] + 2e-3, (k, f[k], r[k])
+
+
+def test_parameters_without_gradients_are_skipped():
+    """As torch.optim: a parameter whose .grad is None is left untouched
+    (weights, codes and scales), and each parameter keeps its own step count,
+    so a parameter skipped once is later stepped with its own bias
+    correction (the oracle steps it with t = 1, 2 while the others reach 3)."""
+    rng = np.random.default_rng(8)
+    init = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in SHAPES]
+    params = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
+    opt = make_opt("adamw", params)
+    orcs = [oracle.State(x.reshape(-1), "adamw") for x in init]
+    counts = [0] * len(params)
+    for it in range(3):
+        before = [(p.detach().clone(), opt.state[p]["flash"].codes.clone()) for p in params]
+        for i, (p, o) in enumerate(zip(params, orcs)):
+            if it == 1 and i == 1:
+                p.grad = None                            # skipped this step
+                continue
+            g = torch.from_numpy((rng.standard_normal(p.shape) * 1e-3).astype(np.float32))
+            g = g.to(torch.bfloat16)
+            p.grad = g.cuda()
+            counts[i] += 1
+            oracle.step(o, g.view(torch.int16).numpy().view(np.uint16).reshape(-1), counts[i],
+                        HP["adamw"])
+        opt.step()
+        torch.cuda.synchronize()
+        if it == 1:
+            assert torch.equal(params[1].view(torch.int16), before[1][0].view(torch.int16))
+            assert torch.equal(opt.state[params[1]]["flash"].codes, before[1][1])
+        compare(opt, params, orcs, f"iteration {it}")
+    assert [opt.state[p]["step"] for p in params] == counts == [3, 2, 3, 3]
+    # and the per-parameter counts survive a checkpoint
+    sd = opt.state_dict()
+    assert [sd["state"][i]["step"] for i in range(len(params))] == counts
