@@ -76,6 +76,8 @@ def lib():
             "orc_sgd_step": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _I64, _P, _P]),
             "orc_lion_step": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _D, _P, _P]),
             "orc_adamw_step_fp32": (None, [_I64, _P, _P, _P, _P, _P, _D, _D, _D, _D, _D, _I64]),
+            "orc_adamw_step_linv": (None, [_I64, _P, _P, _P, _P, _P, _P, _P,
+                                           _D, _D, _D, _D, _D, _I64, _P, _P, _P]),
             "orc_sgd_step_fp32": (None, [_I64, _P, _P, _P, _P, _D, _D, _D]),
             "orc_lion_step_fp32": (None, [_I64, _P, _P, _P, _P, _D, _D, _D, _D]),
         }
@@ -282,7 +284,7 @@ class State:
         self.tb, self.rho = split(np.asarray(theta_fp32, np.float32).reshape(-1))
         self.qm = np.zeros(n, np.int8)
         self.sm = np.zeros(groups(n), np.uint16)
-        if optimizer == "adamw":
+        if optimizer in ("adamw", "adamw_linv"):
             self.qv = np.zeros(n, np.uint8)
             self.sv = np.zeros(groups(n), np.uint16)
         else:
@@ -299,13 +301,15 @@ class State:
 
 def adamw_step(st: State, grad_bits, t: int, lr, beta1, beta2, eps, weight_decay,
                want_fp32: bool = False):
+    """The AdamW step; for a State of optimizer "adamw_linv", the ablation
+    with linearly quantised variance."""
     g = _c(grad_bits, np.uint16).reshape(-1)
     assert g.size == st.n
     outs = [np.empty(st.n, np.float32) for _ in range(3)] if want_fp32 else [None] * 3
     ptrs = [None if o is None else _ptr(o) for o in outs]
-    lib().orc_adamw_step(st.n, _ptr(st.tb), _ptr(st.rho), _ptr(st.qm), _ptr(st.sm),
-                         _ptr(st.qv), _ptr(st.sv), _ptr(g), lr, beta1, beta2, eps,
-                         weight_decay, t, *ptrs)
+    fn = lib().orc_adamw_step_linv if st.optimizer == "adamw_linv" else lib().orc_adamw_step
+    fn(st.n, _ptr(st.tb), _ptr(st.rho), _ptr(st.qm), _ptr(st.sm), _ptr(st.qv), _ptr(st.sv),
+       _ptr(g), lr, beta1, beta2, eps, weight_decay, t, *ptrs)
     return outs if want_fp32 else None
 
 
@@ -330,7 +334,7 @@ def lion_step(st: State, grad_bits, lr, beta1, beta2, weight_decay, want_fp32=Fa
 
 
 def step(st: State, grad_bits, t: int, hp: dict, want_fp32=False):
-    if st.optimizer == "adamw":
+    if st.optimizer in ("adamw", "adamw_linv"):
         return adamw_step(st, grad_bits, t, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                           hp["weight_decay"], want_fp32)
     if st.optimizer == "lion":

@@ -543,10 +543,13 @@ static float lion1(const float lc[6], float theta_hat, float m, float gr, float*
 /* ------------------------------------------------------------------------ */
 /* Fused steps over one tensor.                                              */
 
-void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
-                    uint8_t* qv, uint16_t* sv, const uint16_t* grad,
-                    double lr, double beta1, double beta2, double eps, double wd, int64_t t,
-                    float* theta_out, float* m_out, float* v_out)
+/* linear_v = 0: the method.  linear_v = 1: the Fig. 5 ablation, the variance
+ * stored by the linear quantiser (read as q*RN(s*K255); written as the
+ * group scale and codes of v' itself, no square root). */
+static void adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
+                       uint8_t* qv, uint16_t* sv, const uint16_t* grad,
+                       double lr, double beta1, double beta2, double eps, double wd, int64_t t,
+                       float* theta_out, float* m_out, float* v_out, int linear_v)
 {
     float sc[8];
     orc_adamw_scalars(lr, beta1, beta2, eps, wd, t, sc);
@@ -558,13 +561,14 @@ void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* 
         for (int j = 0; j < len; ++j) {
             float theta_hat = unsplit1(tb[o + j], rho[o + j]);
             float m = dequant_m1(qm[o + j], sm[g]);
-            float v = dequant_v1(qv[o + j], sv[g]);
+            float v = linear_v ? (float)qv[o + j] * (orc_f16_to_f32(sv[g]) * K255)
+                               : dequant_v1(qv[o + j], sv[g]);
             float gr = orc_bf16_to_f32(grad[o + j]);
             float m_new, v_new, root;
             float theta_new = adam1(sc, theta_hat, m, v, gr, &m_new, &v_new, &root);
 
             mn[j] = m_new;
-            w[j] = root;
+            w[j] = linear_v ? v_new : root;    /* what the variance codes quantise */
             tn[j] = theta_new;
             if (theta_out) theta_out[o + j] = theta_new;
             if (m_out) m_out[o + j] = m_new;
@@ -575,6 +579,24 @@ void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* 
         quant_group_v(w, len, qv + o, sv + g);
         for (int j = 0; j < len; ++j) split1(tn[j], &tb[o + j], &rho[o + j]);
     }
+}
+
+void orc_adamw_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
+                    uint8_t* qv, uint16_t* sv, const uint16_t* grad,
+                    double lr, double beta1, double beta2, double eps, double wd, int64_t t,
+                    float* theta_out, float* m_out, float* v_out)
+{
+    adamw_step(n, tb, rho, qm, sm, qv, sv, grad, lr, beta1, beta2, eps, wd, t, theta_out, m_out,
+               v_out, 0);
+}
+
+void orc_adamw_step_linv(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
+                         uint8_t* qv, uint16_t* sv, const uint16_t* grad,
+                         double lr, double beta1, double beta2, double eps, double wd, int64_t t,
+                         float* theta_out, float* m_out, float* v_out)
+{
+    adamw_step(n, tb, rho, qm, sm, qv, sv, grad, lr, beta1, beta2, eps, wd, t, theta_out, m_out,
+               v_out, 1);
 }
 
 void orc_sgd_step(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qb, uint16_t* sb,

@@ -81,6 +81,13 @@ void orc_phi_m_inv_array(const float* z, int64_t n, float* out);
 void orc_phi_v_array(const float* x, int64_t n, float* out);
 void orc_phi_v_inv_array(const float* z, int64_t n, float* out);
 
+/* The AdamW step with the variance stored by the linear quantiser (no
+ * companding; the ablation of the companding section, Fig. 5). */
+void orc_adamw_step_linv(int64_t n, uint16_t* tb, int8_t* rho, int8_t* qm, uint16_t* sm,
+                         uint8_t* qv, uint16_t* sv, const uint16_t* grad,
+                         double lr, double beta1, double beta2, double eps, double wd, int64_t t,
+                         float* theta_out, float* m_out, float* v_out);
+
 /* Compression disabled for a tensor: FP32 master weight and moments, the
  * same updates, theta' = bf16_rne(theta_n) written to tb. */
 void orc_adamw_step_fp32(int64_t n, float* theta, float* m, float* v, uint16_t* tb,

@@ -190,3 +190,72 @@ def test_companding_shrinks_the_variance_error_tail(orc):
     nmse_l = ((bl - v64) ** 2).sum() / (v64 ** 2).sum()
     nmse_c = ((bc - v64) ** 2).sum() / (v64 ** 2).sum()
     assert nmse_l > 3 * nmse_c
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _bf16_bits(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _warm(orc, kind, n, steps, seed, gscale=1e-3):
+    rng = np.random.default_rng(seed)
+    st = orc.State((rng.standard_normal(n) * 0.02).astype(np.float32), kind)
+    for t in range(1, steps + 1):
+        orc.step(st, _bf16_bits(rng.standard_normal(n) * gscale), t, HP)
+    return st, rng
+
+
+def test_linear_variance_step_is_the_codec_composition(orc):
+    """The Fig. 5 ablation step (variance without companding): its codes are
+    the linear quantiser of its FP32 v', the method's quantiser of m', and
+    the split of theta_n; its update equals the pinned FP32 step fed the
+    same rebuilt weight and dequantised moments."""
+    n = 32 * 300 + 13
+    st, rng = _warm(orc, "adamw_linv", n, 3, seed=24)
+    f = orc.StateFP32(orc.unsplit(st.tb, st.rho), "adamw")
+    f.m[:] = orc.dequant_m(st.qm, st.sm)
+    f.v[:] = orc.dequant_lin_v(st.qv, st.sv)
+    g = _bf16_bits(rng.standard_normal(n) * 1e-3)
+    th, m, v = orc.step(st, g, 4, HP, want_fp32=True)
+    orc.step_fp32(f, g, 4, HP)
+    for a, b in ((th, f.theta), (m, f.m), (v, f.v)):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    qv, sv = orc.quant_lin_v(v)
+    qm, sm = orc.quant_m(m)
+    tb, rho = orc.split(th)
+    for a, b in ((st.qv, qv), (st.sv, sv), (st.qm, qm), (st.sm, sm), (st.tb, tb), (st.rho, rho)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_linear_variance_sends_small_variances_to_zero_and_steps_explode(orc):
+    """Fig. 5's failure: in groups where four elements see gradients 30 times
+    larger than the other 28, the linear codes store the quiet elements'
+    variance (900 times smaller) as 0 while their momentum survives; on a
+    step where those gradients are 0 the update is alpha*m'/eps, thousands
+    of times lr.  With square-root companding the variance survives and the
+    step stays below ~lr."""
+    n = 32 * 256
+    rng = np.random.default_rng(25)
+    scale = np.where(np.arange(n) % 32 < 4, 1e-2, 1e-2 / 30)
+    quiet = scale < 1e-2
+    steps = {}
+    for kind in ("adamw", "adamw_linv"):
+        st = orc.State((rng.standard_normal(n) * 0.02).astype(np.float32), kind)
+        r = np.random.default_rng(26)
+        for t in range(1, 10):
+            orc.step(st, _bf16_bits(r.standard_normal(n) * scale), t, HP)
+        v = (orc.dequant_lin_v if kind == "adamw_linv" else orc.dequant_v)(st.qv, st.sv)
+        lost = (v[quiet] == 0).mean()
+        assert (lost > 0.9) if kind == "adamw_linv" else (lost == 0)
+        assert (orc.dequant_m(st.qm, st.sm)[quiet] != 0).mean() > 0.8   # momentum kept
+        before = orc.unsplit(st.tb, st.rho).astype(np.float64)
+        g = r.standard_normal(n) * scale
+        g[quiet] = 0.0
+        orc.step(st, _bf16_bits(g), 10, HP)
+        steps[kind] = np.abs(orc.unsplit(st.tb, st.rho).astype(np.float64) - before)[quiet]
+    assert np.quantile(steps["adamw"], 0.99) < 2 * HP["lr"]
+    assert np.median(steps["adamw_linv"]) > 1000 * HP["lr"]
