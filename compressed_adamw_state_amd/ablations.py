@@ -14,6 +14,12 @@ Training"), measured on the GPU through the C ABI.
   its distribution over groups of 32, and the share of nonzero values that
   come back as 0.
 
+* Training without companding (Fig. 5): a small MLP on a synthetic
+  regression task trained with torch's AdamW on FP32 weights (the
+  reference), with FlashAdamW, and with FlashAdamW whose variance is stored
+  by linear codes (the fused step's ablation kind); the page reports that
+  the last diverges.
+
 Every codec operation runs in the library's kernels; the error statistics
 are plain torch reductions over their outputs, and the BF16 + BF16 baseline
 is two torch casts.  python -m compressed_adamw_state_amd.ablations prints
@@ -134,6 +140,55 @@ def run(n: int = 1 << 22, seed: int = 0, device: str = "cuda", binades=BINADES) 
     return out
 
 
+def _mlp_task(seed: int, device: str):
+    """Synthetic regression: y = sin(3 x.a) + noise, x in R^64, 4096 samples;
+    a 64-256-1 ReLU MLP.  Drawn on the host (seeded) and copied."""
+    g = torch.Generator().manual_seed(seed)
+    n, d, h = 4096, 64, 256
+    X = torch.randn(n, d, generator=g)
+    a = torch.randn(d, generator=g) / d ** 0.5
+    y = (torch.sin(3 * X @ a) + 0.1 * torch.randn(n, generator=g)).unsqueeze(1)
+    init = [torch.randn(h, d, generator=g) / d ** 0.5, torch.zeros(h),
+            torch.randn(1, h, generator=g) / h ** 0.5, torch.zeros(1)]
+    return X.to(device), y.to(device), init
+
+
+def training_study(steps: int = 300, seed: int = 7, device: str = "cuda",
+                   every: int = 10) -> dict:
+    """Loss curves (every `every` steps; None once non-finite) of the three
+    runs.  The model computes in FP32 (the BF16 weights theta' are upcast)."""
+    from . import optim as O
+    X, y, init = _mlp_task(seed, device)
+    hp = dict(lr=3e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+
+    def loss_of(ps):
+        w1, b1, w2, b2 = (p.float() for p in ps)
+        return ((torch.relu(X @ w1.t() + b1) @ w2.t() + b2 - y) ** 2).mean()
+
+    runs = {}
+    for name in ("reference", "companded", "linear"):
+        ps = [torch.nn.Parameter(t.clone().to(device)) for t in init]
+        if name == "reference":
+            opt = torch.optim.AdamW(ps, **hp)
+        else:
+            opt = O.FlashAdamW([{"params": ps, "linear_variance": name == "linear"}], **hp)
+        curve = []
+        for it in range(steps):
+            loss = loss_of(ps)
+            val = loss.item()
+            finite = val == val and abs(val) != float("inf")
+            if it % every == 0 or it == steps - 1 or not finite:
+                curve.append(val if finite else None)
+            if not finite:                               # diverged: stop feeding NaN back
+                break
+            opt.zero_grad()
+            loss.backward()
+            opt.step()
+        runs[name] = curve
+    return {"steps": steps, "every": every, "hparams": {k: list(v) if isinstance(v, tuple) else v
+                                                         for k, v in hp.items()}, "loss": runs}
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--n", type=int, default=1 << 22)
@@ -141,6 +196,7 @@ def main() -> None:
     ap.add_argument("--out", default=None, help="write the JSON here as well")
     a = ap.parse_args()
     r = run(a.n, a.seed)
+    r["training"] = training_study()
     text = json.dumps(r, indent=1)
     if a.out:
         with open(a.out, "w") as f:

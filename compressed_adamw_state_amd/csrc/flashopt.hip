@@ -276,7 +276,9 @@ __device__ __forceinline__ Upd update(float theta_hat, float m, float v, float g
 
 // ---- the fused step on one sub-tile of one lane ----------------------------
 
-template <int kOpt>
+// kLinV (AdamW only): the variance codes are the linear quantiser of v'
+// itself (the companding ablation), read back as q * RN(s*K255).
+template <int kOpt, bool kLinV = false>
 __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
                                           const Lane8& L, const StepScalars& P) {
     float z[8], w[8], tn[8];
@@ -288,11 +290,12 @@ __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
         const float theta_hat = unsplit(L.th[j], L.rho[j]);
         const float m = dequant_m(L.qm[j], dm);
         const float g = bf16_to_f32(L.gr[j]);
-        const float v = (kOpt == kAdamW) ? dequant_v(L.qv[j], dv) : 0.0f;
+        const float v = (kOpt != kAdamW) ? 0.0f
+                        : kLinV ? (float)L.qv[j] * dv : dequant_v(L.qv[j], dv);
         const Upd u = update<kOpt>(theta_hat, m, v, g, P);
         if (kOpt == kAdamW) {
-            w[j] = u.root;
-            amax_v = max(amax_v, as_u32(u.root));
+            w[j] = kLinV ? u.v : u.root;              // what the variance codes quantise
+            amax_v = max(amax_v, as_u32(w[j]));
         }
         z[j] = phi_m(u.m);
         tn[j] = u.theta;
@@ -383,7 +386,7 @@ __device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32
     return __builtin_amdgcn_perm(cd, ab, 0x05040100u);                 // a0 b0 c0 d0
 }
 
-template <int kOpt>
+template <int kOpt, bool kLinV = false>
 __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane, const Raw& R,
                                           const StepScalars& P) {
     const AdamScalars& a = P.a;
@@ -406,7 +409,7 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
         const float g = as_f32(bf16_bits(R.gr, j));
         if (kOpt == kAdamW) {
             const float zv = (float)u8(R.qv, j) * dv;
-            const float v = zv * zv;
+            const float v = kLinV ? zv : zv * zv;
             const float bm = a.b1 * m;
             const float cg = a.c1 * g;
             m_new[j] = bm + cg;
@@ -473,6 +476,7 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
             const float decayed = a.lambda * theta_hat[j];
             const float stp = a.alpha * u[j];
             tn[j] = decayed - stp;
+            if (kLinV) w[j] = v_new[j];                // the codes quantise v' itself
             amax_v = fmaxf(amax_v, w[j]);
         }
     }
@@ -540,7 +544,7 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
 // of sub-tile k+2 are issued as soon as sub-tile k is done, so one sub-tile's
 // loads are always in flight behind the arithmetic.  The partial last tile of
 // a tensor goes one bounds-checked sub-tile at a time.
-template <int kOpt, bool kFull>
+template <int kOpt, bool kFull, bool kLinV>
 __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane,
                                           const StepScalars& P) {
     if (kFull) {
@@ -549,7 +553,7 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
         if (kSubTiles > 1) load_raw<kOpt>(T, e0 + kSubTile + lane * kLaneElems, R[1]);
 #pragma unroll
         for (int k = 0; k < kSubTiles; ++k) {
-            step_fast<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1], P);
+            step_fast<kOpt, kLinV>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1], P);
             if (k + 2 < kSubTiles)
                 load_raw<kOpt>(T, e0 + (k + 2) * kSubTile + lane * kLaneElems, R[k & 1]);
         }
@@ -557,14 +561,14 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
         for (int k = 0; k < kSubTiles; ++k) {
             Lane8 L;
             load_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, L);
-            step_lane<kOpt>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, P);
+            step_lane<kOpt, kLinV>(T, e0 + k * kSubTile + lane * kLaneElems, lane, L, P);
         }
     }
 }
 
 // Five waves per SIMD: the AdamW instantiation fits in 96 VGPRs without
 // spilling, and the fifth wave covers more memory latency (measured ~0.5 %).
-template <int kOpt>
+template <int kOpt, bool kLinV = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
                                                    const int64_t* __restrict__ tile_begin,
                                                    int32_t count, int64_t total_tiles,
@@ -578,8 +582,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
     for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const int64_t e0 = (tile - cur.begin) * kTile;
-        if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true>(cur.T, e0, lane, P);
-        else step_tile<kOpt, false>(cur.T, e0, lane, P);
+        if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true, kLinV>(cur.T, e0, lane, P);
+        else step_tile<kOpt, false, kLinV>(cur.T, e0, lane, P);
     }
 }
 
@@ -1008,7 +1012,7 @@ __global__ __launch_bounds__(256) void init_kernel(DevTensor d, const float* x) 
 
 // The rebuilt FP32 master weight, momentum and (AdamW) variance; any output
 // pointer may be null.
-template <int kOpt>
+template <int kOpt, bool kLinV = false>
 __global__ __launch_bounds__(256) void export_kernel(DevTensor d, float* theta_out, float* m_out,
                                                      float* v_out) {
     const GTensor T = view(d);
@@ -1025,7 +1029,10 @@ __global__ __launch_bounds__(256) void export_kernel(DevTensor d, float* theta_o
             if (theta_out)
                 theta_out[i] = unsplit(T.theta[i], (int8_t)*code_at<kOpt>(T, i, kRhoOff));
             if (m_out) m_out[i] = dequant_m((int8_t)*code_at<kOpt>(T, i, kMOff), dm);
-            if (kOpt == kAdamW && v_out) v_out[i] = dequant_v(*code_at<kOpt>(T, i, kVOff), dv);
+            if (kOpt == kAdamW && v_out) {
+                const uint32_t q = *code_at<kOpt>(T, i, kVOff);
+                v_out[i] = kLinV ? (float)q * dv : dequant_v(q, dv);
+            }
         }
     }
 }
@@ -1247,12 +1254,18 @@ static int check_sgd(const flashopt_sgd_hparams* hp, int64_t step) {
 }
 
 static bool valid_kind(int32_t kind) {
-    return kind >= FLASHOPT_KIND_ADAMW && kind <= FLASHOPT_KIND_LION_FP32;
+    return kind >= FLASHOPT_KIND_ADAMW && kind <= FLASHOPT_KIND_ADAMW_LINEAR_V;
 }
 
-// the optimizer of a kind (kAdamW, kSgd, kLion) and whether its state is FP32
-static int opt_of(int32_t kind) { return kind % 3; }
-static bool is_fp32(int32_t kind) { return kind >= FLASHOPT_KIND_ADAMW_FP32; }
+// the optimizer of a kind (kAdamW, kSgd, kLion), whether its state is FP32,
+// and whether its variance codes are linear (the companding ablation)
+static int opt_of(int32_t kind) {
+    return kind == FLASHOPT_KIND_ADAMW_LINEAR_V ? kAdamW : kind % 3;
+}
+static bool is_fp32(int32_t kind) {
+    return kind >= FLASHOPT_KIND_ADAMW_FP32 && kind <= FLASHOPT_KIND_LION_FP32;
+}
+static bool is_linv(int32_t kind) { return kind == FLASHOPT_KIND_ADAMW_LINEAR_V; }
 
 static int check_lion(const flashopt_lion_hparams* hp, int64_t step) {
     if (!hp) return FLASHOPT_ERR_NULL;
@@ -1290,7 +1303,7 @@ static int check_tensor(const flashopt_tensor& t, int32_t kind) {
     }
     if (!t.theta || !t.codes || !t.scales) return FLASHOPT_ERR_NULL;
     if (!aligned(t.theta, 16) || !aligned(t.codes, 8) ||
-        !aligned(t.scales, kind == FLASHOPT_KIND_ADAMW ? 4 : 2) || (t.grad && !aligned(t.grad, 16)))
+        !aligned(t.scales, opt_of(kind) == kAdamW ? 4 : 2) || (t.grad && !aligned(t.grad, 16)))
         return FLASHOPT_ERR_ALIGN;
     return FLASHOPT_OK;
 }
@@ -1514,7 +1527,7 @@ size_t flashopt_codes_bytes(int32_t kind, int64_t numel) {
 
 size_t flashopt_scales_bytes(int32_t kind, int64_t numel) {
     if (!valid_kind(kind) || is_fp32(kind) || numel < 0 || numel > kMaxNumel) return 0;
-    return (size_t)((numel + 31) / 32) * (kind == FLASHOPT_KIND_ADAMW ? 4 : 2);
+    return (size_t)((numel + 31) / 32) * (opt_of(kind) == kAdamW ? 4 : 2);
 }
 
 int flashopt_tensor_init(const flashopt_tensor* t, int32_t kind, const float* theta,
@@ -1528,7 +1541,7 @@ int flashopt_tensor_init(const flashopt_tensor* t, int32_t kind, const float* th
     const int64_t chunks = (t->numel + kSubTile - 1) / kSubTile;
     const dim3 grid(grid_for(chunks));
     hipStream_t s = (hipStream_t)stream;
-    if (kind == FLASHOPT_KIND_ADAMW)
+    if (kind == FLASHOPT_KIND_ADAMW || is_linv(kind))          // same layout, all codes zero
         hipLaunchKernelGGL(init_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t), theta);
     else if (kind == FLASHOPT_KIND_ADAMW_FP32)
         hipLaunchKernelGGL(init_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t), theta);
@@ -1553,6 +1566,9 @@ int flashopt_tensor_export(const flashopt_tensor* t, int32_t kind, float* theta,
     if (kind == FLASHOPT_KIND_ADAMW)
         hipLaunchKernelGGL(export_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t), theta, m,
                            v);
+    else if (is_linv(kind))
+        hipLaunchKernelGGL((export_kernel<kAdamW, true>), grid, dim3(kBlock), 0, s, to_dev(*t),
+                           theta, m, v);
     else if (kind == FLASHOPT_KIND_ADAMW_FP32)
         hipLaunchKernelGGL(export_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, s, to_dev(*t),
                            theta, m, v);
@@ -1654,7 +1670,7 @@ int flashopt_state_zero(const flashopt_list* L, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     const DevTensor* tab = L->d_table;
     const int64_t* tb = L->d_tile_begin;
-    if (L->kind == FLASHOPT_KIND_ADAMW)
+    if (L->kind == FLASHOPT_KIND_ADAMW || is_linv(L->kind))
         hipLaunchKernelGGL(zero_kernel<kAdamW>, grid, dim3(kBlock), 0, s, tab, tb, L->count,
                            L->total_tiles);
     else if (L->kind == FLASHOPT_KIND_ADAMW_FP32)
@@ -1680,13 +1696,18 @@ int flashopt_stream_probe(const flashopt_list* L, void* stream) {
     return launch_status();
 }
 
-static int launch_step(int opt, bool fp32, const DevTensor* table, const int64_t* tile_begin,
+static int launch_step(int opt, int32_t kind, const DevTensor* table, const int64_t* tile_begin,
                        int32_t count, int64_t total_tiles, const DevTensor& one,
                        const StepScalars& P, void* stream) {
     if (total_tiles == 0) return FLASHOPT_OK;
     const dim3 grid(grid_for(total_tiles));
     hipStream_t st = (hipStream_t)stream;
-    if (fp32) {
+    if (is_linv(kind)) {
+        hipLaunchKernelGGL((step_kernel<kAdamW, true>), grid, dim3(kBlock), 0, st, table,
+                           tile_begin, count, total_tiles, one, P);
+        return launch_status();
+    }
+    if (is_fp32(kind)) {
         if (opt == kAdamW)
             hipLaunchKernelGGL(step_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table,
                                tile_begin, count, total_tiles, one, P);
@@ -1711,8 +1732,8 @@ static int launch_step(int opt, bool fp32, const DevTensor* table, const int64_t
 }
 
 static int launch_list(int opt, const flashopt_list* L, const StepScalars& P, void* stream) {
-    return launch_step(opt, is_fp32(L->kind), L->d_table, L->d_tile_begin, L->count,
-                       L->total_tiles, DevTensor{}, P, stream);
+    return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, L->total_tiles,
+                       DevTensor{}, P, stream);
 }
 
 static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint16_t* grad,
@@ -1721,8 +1742,7 @@ static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint
     if (t.numel == 0) return FLASHOPT_OK;
     DevTensor one = to_dev(t);
     one.grad = (uint64_t)grad;
-    return launch_step(opt, is_fp32(L->kind), nullptr, nullptr, 1, tiles_of(t.numel), one, P,
-                       stream);
+    return launch_step(opt, L->kind, nullptr, nullptr, 1, tiles_of(t.numel), one, P, stream);
 }
 
 static int check_one(const flashopt_list* L, int32_t index, const uint16_t* grad) {

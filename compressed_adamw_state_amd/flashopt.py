@@ -29,16 +29,20 @@ class FlashoptError(RuntimeError):
 
 
 # flashopt_kind; "<opt>_fp32" is the optimizer with compression switched off
-# (FP32 master weight and moments, no scales)
-KIND = {"adamw": 0, "sgd": 1, "lion": 2, "adamw_fp32": 3, "sgd_fp32": 4, "lion_fp32": 5}
-RECORD = {"adamw": 24, "sgd": 16, "lion": 16}     # code-record bytes per 8 elements
-SCALES = {"adamw": 2, "sgd": 1, "lion": 1}        # FP16 scales per 32-element group
+# (FP32 master weight and moments, no scales); "adamw_linv" the ablation with
+# linear variance codes (experiments only)
+KIND = {"adamw": 0, "sgd": 1, "lion": 2, "adamw_fp32": 3, "sgd_fp32": 4, "lion_fp32": 5,
+        "adamw_linv": 6}
+RECORD = {"adamw": 24, "sgd": 16, "lion": 16,     # code-record bytes per 8 elements
+          "adamw_linv": 24}
+SCALES = {"adamw": 2, "sgd": 1, "lion": 1,        # FP16 scales per 32-element group
+          "adamw_linv": 2}
 FP32_FIELDS = {"adamw_fp32": 3, "sgd_fp32": 2, "lion_fp32": 2}   # per 512-element block
 
 
 def base_optimizer(kind: str) -> str:
-    """The optimizer of a state kind: "adamw_fp32" -> "adamw"."""
-    return kind[:-5] if kind.endswith("_fp32") else kind
+    """The optimizer of a state kind: "adamw_fp32", "adamw_linv" -> "adamw"."""
+    return kind.split("_")[0]
 
 
 class Tensor(ctypes.Structure):

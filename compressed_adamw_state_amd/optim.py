@@ -24,7 +24,10 @@ A parameter group with "compress": False (the page's practical advice:
 compression can be switched off for layers that are sensitive to it) keeps
 an FP32 master weight and FP32 moments instead (the library's _fp32 state
 kinds, 14 B/param for AdamW); its parameters still compute in BF16, and the
-group is stepped by the same kind of launch.
+group is stepped by the same kind of launch.  "linear_variance": True (AdamW
+only) stores the variance with linear codes instead of square-root
+companding -- the ablation of the page's Fig. 5, for experiments, not for
+training.
 
 This module only marshals: every arithmetic operation of the update runs in
 the HIP library, and there is no fallback.
@@ -62,7 +65,13 @@ class _FlashOptimizer(torch.optim.Optimizer):
 
     # -- state -----------------------------------------------------------------
     def _state_kind(self, group) -> str:
-        return self.kind if group.get("compress", True) else self.kind + "_fp32"
+        if not group.get("compress", True):
+            return self.kind + "_fp32"
+        if group.get("linear_variance", False):
+            if self.kind != "adamw":
+                raise ValueError("linear_variance applies to FlashAdamW only")
+            return "adamw_linv"
+        return self.kind
 
     def _init_param(self, p: torch.Tensor, kind: str) -> None:
         if not p.is_cuda:
@@ -183,8 +192,8 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 len(a["params"]) != len(b["params"]) for a, b in zip(saved, self.param_groups)):
             raise ValueError("checkpoint has a different parameter layout")
         for group, sgroup in zip(self.param_groups, saved):
-            if sgroup.get("compress", True) != group.get("compress", True):
-                raise ValueError("checkpoint has a different compressed / uncompressed split")
+            if self._state_kind(sgroup) != self._state_kind(group):
+                raise ValueError("checkpoint has a different state layout for a parameter group")
             for k, v in sgroup.items():
                 if k != "params":
                     group[k] = v

@@ -63,7 +63,7 @@ ADAMW_HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 SGD_HP = dict(lr=0.1, momentum=0.9, weight_decay=1e-4)
 # Lion: the published rule's usual setting (a smaller lr and a larger decay than AdamW)
 LION_HP = dict(lr=1e-4, beta1=0.9, beta2=0.99, weight_decay=0.1)
-HPARAMS = {"adamw": ADAMW_HP, "sgd": SGD_HP, "lion": LION_HP}
+HPARAMS = {"adamw": ADAMW_HP, "sgd": SGD_HP, "lion": LION_HP, "adamw_linv": ADAMW_HP}
 
 
 def gpt2_small() -> List[TensorSpec]:

@@ -99,7 +99,9 @@ typedef enum flashopt_kind {
     FLASHOPT_KIND_LION = 2,      /* the SGD layout, holding Lion's momentum                */
     FLASHOPT_KIND_ADAMW_FP32 = 3,/* FP32 theta, m, v in 512-element blocks; no scales      */
     FLASHOPT_KIND_SGD_FP32 = 4,  /* FP32 theta and momentum buffer in blocks; no scales    */
-    FLASHOPT_KIND_LION_FP32 = 5  /* FP32 theta and momentum in blocks; no scales           */
+    FLASHOPT_KIND_LION_FP32 = 5, /* FP32 theta and momentum in blocks; no scales           */
+    FLASHOPT_KIND_ADAMW_LINEAR_V = 6 /* ablation only: the AdamW layout with linear variance
+                                        codes (no square root; companding section, Fig. 5) */
 } flashopt_kind;
 
 /* One parameter tensor and its compressed state (all DEVICE pointers).
@@ -118,6 +120,11 @@ typedef enum flashopt_kind {
  * for g < ceil(n/32).  flashopt_codes_bytes / flashopt_scales_bytes give the
  * sizes.  The values are exactly those of the flat arrays the quantisers and
  * split below produce, only their placement differs.
+ *
+ * FLASHOPT_KIND_ADAMW_LINEAR_V has the AdamW layout, but its variance codes
+ * are the linear quantiser of v' itself (scale f16_rne(max v'), codes
+ * clamp(rne(v' * RN(255/s)), 0, 255), read back as q * RN(s*K255)): the
+ * no-companding ablation, for experiments only.
  *
  * _FP32 kinds: `codes` holds blocks of 512 elements of FP32 fields (16-byte
  * aligned),

@@ -50,7 +50,7 @@ def state_fields(st: F.TensorState, idx=None, gidx=None) -> dict:
     base = (idx >> 3) * R + (idx & 7)
     out = {"theta": u16(st.theta[idx]), "rho": i8(st.codes[base]),
            "m_code": i8(st.codes[base + 8]), "m_scale": u16(st.scales[gidx * S])}
-    if st.optimizer == "adamw":
+    if S == 2:                                             # AdamW layouts
         out["v_code"] = u8(st.codes[base + 16])
         out["v_scale"] = u16(st.scales[gidx * S + 1])
     return out
@@ -142,7 +142,7 @@ class Run:
         for i, st in enumerate(self.states):
             name = self.w.tensors[i].name
             keys = [("theta", "tb"), ("rho", "rho"), ("m_code", "qm"), ("m_scale", "sm")]
-            if st.optimizer == "adamw":
+            if st.optimizer in ("adamw", "adamw_linv"):
                 keys += [("v_code", "qv"), ("v_scale", "sv")]
             if self.mode == "full":
                 o = self.orc[i]

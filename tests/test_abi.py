@@ -70,16 +70,19 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_create(arr, 1, A, ws, need - 1, None, ctypes.byref(out)) == -6
     assert lib.flashopt_list_create(arr, 1, A, P(0x100010), need, None, ctypes.byref(out)) == -6
     assert lib.flashopt_list_create(arr, -1, A, ws, need, None, ctypes.byref(out)) == -2
-    assert lib.flashopt_list_create(arr, 1, 6, ws, need, None, ctypes.byref(out)) == -4
+    assert lib.flashopt_list_create(arr, 1, 7, ws, need, None, ctypes.byref(out)) == -4
     nul = (F.Tensor * 1)(F.Tensor(10, fake, None, fake, fake))
     assert lib.flashopt_list_create(nul, 1, A, ws, need, None, ctypes.byref(out)) == -1
     mis_t = (F.Tensor * 1)(F.Tensor(10, P(0x10008), fake, fake, fake))
     assert lib.flashopt_list_create(mis_t, 1, A, ws, need, None, ctypes.byref(out)) == -3
     mis_s = (F.Tensor * 1)(F.Tensor(10, fake, fake, P(0x10002), fake))  # AdamW scales need 4 B
     assert lib.flashopt_list_create(mis_s, 1, A, ws, need, None, ctypes.byref(out)) == -3
+    assert lib.flashopt_list_create(mis_s, 1, 6, ws, need, None, ctypes.byref(out)) == -3
+    # the linear-variance ablation kind has the AdamW layout
+    assert lib.flashopt_codes_bytes(6, 17) == 3 * 24 and lib.flashopt_scales_bytes(6, 33) == 8
     neg = (F.Tensor * 1)(F.Tensor(-5, fake, fake, fake, fake))
     assert lib.flashopt_list_create(neg, 1, A, ws, need, None, ctypes.byref(out)) == -2
-    assert lib.flashopt_tensor_init(arr, 6, fake, None) == -4
+    assert lib.flashopt_tensor_init(arr, 7, fake, None) == -4
     assert lib.flashopt_tensor_init(arr, A, None, None) == -1
     assert lib.flashopt_tensor_init(mis_t, A, fake, None) == -3
     assert lib.flashopt_tensor_export(None, A, fake, None, None, None) == -1

@@ -129,3 +129,18 @@ def test_ablation_study_orderings():
     assert l["nmse"] > 10 * c["nmse"] and l["zeroed"] > 0.1 and c["zeroed"] < 1e-3
     c, l = q["v_small"]["companded"], q["v_small"]["linear"]
     assert l["zeroed"] > 0.999 and l["nmse"] > 0.9 and c["zeroed"] < 0.01
+
+
+def test_training_without_companding_diverges():
+    """Fig. 5 on a synthetic task: FlashAdamW follows torch's AdamW, and the
+    same fused step with linear variance codes blows up."""
+    r = A.training_study(steps=300)
+    log("training study: " + json.dumps(r["loss"]))
+    ref, comp, lin = (r["loss"][k] for k in ("reference", "companded", "linear"))
+    assert all(v is not None for v in ref + comp)
+    assert comp[-1] < 0.01 and ref[-1] < 0.01                # both fit the task
+    for c, f in zip(comp, ref):                              # and together while the
+        if f > 0.01:                                         # loss is above its noise
+            assert abs(c - f) <= 0.1 * f, (c, f)
+    # linear codes: non-finite, or far above the start, at some point
+    assert any(v is None or v > 10 * lin[0] for v in lin)

@@ -141,7 +141,28 @@ def test_ragged_list_every_step(opt):
         r.compare(f"step {t}")
 
 
-@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion"])
+@pytest.mark.parametrize("grad_dist", ["normal", "mixed"])
+def test_linear_variance_kind_every_step(grad_dist):
+    """The fused step's ablation kind (variance with linear codes) against
+    the oracle, every code and scale: with mixed gradients (exact zeros,
+    outliers, subnormals) many variances code to 0 and their quotients leave
+    the short sequence's window, so the general fallback runs too."""
+    base = W.ragged(RAGGED, seed=15, steps=4, optimizer="adamw_linv")
+    w = W.Workload(base.name, base.tensors, "adamw_linv", 4, base.seed, grad_dist,
+                   base.grad_scale, base.hparams)
+    r = Run(w, "full")
+    for t in range(1, w.steps + 1):
+        r.step(t)
+        r.compare(f"linear variance {grad_dist} step {t}")
+    st = r.states[RAGGED.index(32 * 777 + 5)]
+    th, m, v = (torch.empty(st.numel, device="cuda") for _ in range(3))
+    F.flashopt_tensor_export(st, th, m, v)
+    o = r.orc[RAGGED.index(32 * 777 + 5)]
+    np.testing.assert_array_equal(v.cpu().numpy().view(np.uint32),
+                                  oracle.dequant_lin_v(o.qv, o.sv).view(np.uint32))
+
+
+@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion", "adamw_linv"])
 def test_release_mode_matches_list_mode(opt):
     base = W.ragged(RAGGED[:12], seed=12, steps=3, optimizer=opt)
     rel = W.Workload(base.name, base.tensors, opt, 3, base.seed, base.grad_dist, base.grad_scale,
