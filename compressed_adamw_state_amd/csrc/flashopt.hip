@@ -1350,6 +1350,7 @@ const char* flashopt_status_string(int s) {
         case FLASHOPT_ERR_WORKSPACE: return "device workspace too small or misaligned";
         case FLASHOPT_ERR_HIP: return "HIP runtime error";
         case FLASHOPT_ERR_INDEX: return "tensor index out of range";
+        case FLASHOPT_ERR_HOST_MEMORY: return "host memory allocation failed";
         default: return "unknown status";
     }
 }
@@ -1594,17 +1595,25 @@ int flashopt_list_create(const flashopt_tensor* tensors, int32_t count, int32_t 
         if (!workspace) return FLASHOPT_ERR_NULL;
         if (workspace_bytes < need || !aligned(workspace, 256)) return FLASHOPT_ERR_WORKSPACE;
     }
-    flashopt_list* L = new (std::nothrow) flashopt_list();
-    if (!L) return FLASHOPT_ERR_ARG;
-    L->count = count;
-    L->kind = kind;
-    L->host.assign(tensors, tensors + count);
-    L->tile_begin.resize((size_t)count + 1);
-    int64_t tiles = 0;
-    std::vector<DevTensor> dev((size_t)count);
     for (int32_t i = 0; i < count; ++i) {
         const int st = check_tensor(tensors[i], kind);
-        if (st != FLASHOPT_OK) { delete L; return st; }
+        if (st != FLASHOPT_OK) return st;
+    }
+    flashopt_list* L = new (std::nothrow) flashopt_list();
+    if (!L) return FLASHOPT_ERR_HOST_MEMORY;
+    std::vector<DevTensor> dev;
+    try {                                        // no exception crosses the C interface
+        L->host.assign(tensors, tensors + count);
+        L->tile_begin.resize((size_t)count + 1);
+        dev.resize((size_t)count);
+    } catch (...) {
+        delete L;
+        return FLASHOPT_ERR_HOST_MEMORY;
+    }
+    L->count = count;
+    L->kind = kind;
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) {
         L->tile_begin[i] = tiles;
         tiles += tiles_of(tensors[i].numel);
         L->numel += tensors[i].numel;

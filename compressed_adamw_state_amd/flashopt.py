@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libflashopt.so")
 GROUP = 32
 
 STATUS = {0: "ok", -1: "null pointer", -2: "size", -3: "alignment", -4: "argument",
-          -5: "step", -6: "workspace", -7: "HIP error", -8: "index"}
+          -5: "step", -6: "workspace", -7: "HIP error", -8: "index", -9: "host memory"}
 
 
 class FlashoptError(RuntimeError):

@@ -86,7 +86,8 @@ typedef enum flashopt_status {
     FLASHOPT_ERR_STEP = -5,      /* step counter t < 1                                 */
     FLASHOPT_ERR_WORKSPACE = -6, /* device workspace too small                         */
     FLASHOPT_ERR_HIP = -7,       /* HIP runtime error (launch, copy, device query)     */
-    FLASHOPT_ERR_INDEX = -8      /* tensor index out of range                          */
+    FLASHOPT_ERR_INDEX = -8,     /* tensor index out of range                          */
+    FLASHOPT_ERR_HOST_MEMORY = -9 /* host allocation for a list handle failed          */
 } flashopt_status;
 
 /* Optimizer kind of a tensor's state layout (and of a list).  The _FP32

@@ -33,9 +33,11 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = F.lib()
-    for s in range(-8, 1):
-        assert lib.flashopt_status_string(s)
+    for s in range(-9, 1):
+        assert lib.flashopt_status_string(s) != b"unknown status"
+        assert s in F.STATUS
     assert lib.flashopt_status_string(0) == b"ok"
+    assert lib.flashopt_status_string(-10) == b"unknown status"
 
 
 def test_host_validation_without_gpu():
