@@ -1,0 +1,25 @@
+"""bench.py's command-line contract that needs no GPU: more than one GPU is
+refused with a message (this build measures one GPU's share; sharding is a
+design note), and the algorithmic byte counts per parameter."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_bytes_per_parameter():
+    sys.path.insert(0, ROOT)
+    import bench
+    from compressed_adamw_state_amd import workloads as W
+    w = W.WORKLOADS["llama31_8b"]
+    assert bench.algorithmic_bytes(w) == 98_370_700_288          # 12.25 B/param
+    assert bench.algorithmic_bytes(W.WORKLOADS["llama31_8b_lion"]) == 10.125 * w.numel
+    assert bench.algorithmic_bytes(W.WORKLOADS["llama31_8b_adamw_fp32"]) == 28 * w.numel
