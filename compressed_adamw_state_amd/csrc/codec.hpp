@@ -341,6 +341,28 @@ struct AdamScalars {
     float b1, c1, b2, c2, alpha, kappa, eps, lambda;
     uint32_t quot_neg_lo2, quot_span;
 };
+static_assert(sizeof(AdamScalars) == 40, "ten 32-bit words");
+
+// The binary32 AdamW scalars of step t from the double hyper-parameters and
+// p1 = beta1^t, p2 = beta2^t: each value formed in binary64 (correctly
+// rounded division and square root) and rounded once.  The host call and the
+// device-scheduled call both use this one definition.
+__host__ __device__ inline AdamScalars adam_scalars_from(double lr, double beta1, double beta2,
+                                                         double eps, double wd, double p1,
+                                                         double p2) {
+    AdamScalars a;
+    a.b1 = (float)beta1;
+    a.c1 = (float)(1.0 - beta1);
+    a.b2 = (float)beta2;
+    a.c2 = (float)(1.0 - beta2);
+    a.alpha = (float)(lr / (1.0 - p1));
+    a.kappa = (float)(1.0 / sqrt(1.0 - p2));
+    a.eps = (float)eps;
+    a.lambda = (float)(1.0 - lr * wd);
+    quot_window(a.eps, a.quot_neg_lo2, a.quot_span);
+    return a;
+}
+
 struct SgdScalars { float mu, eta, omega; };
 // Lion: b1, c1 = 1-beta1 (direction), b2, c2 = 1-beta2 (momentum), eta = lr,
 // lambda = 1 - lr*wd.

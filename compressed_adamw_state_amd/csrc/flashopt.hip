@@ -568,11 +568,11 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
 
 // Five waves per SIMD: the AdamW instantiation fits in 96 VGPRs without
 // spilling, and the fifth wave covers more memory latency (measured ~0.5 %).
-template <int kOpt, bool kLinV = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
-                                                   const int64_t* __restrict__ tile_begin,
-                                                   int32_t count, int64_t total_tiles,
-                                                   DevTensor one, StepScalars P) {
+template <int kOpt, bool kLinV>
+__device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
+                                          const int64_t* __restrict__ tile_begin, int32_t count,
+                                          int64_t total_tiles, const DevTensor& one,
+                                          const StepScalars& P) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
@@ -585,6 +585,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
         if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true, kLinV>(cur.T, e0, lane, P);
         else step_tile<kOpt, false, kLinV>(cur.T, e0, lane, P);
     }
+}
+
+template <int kOpt, bool kLinV = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
+                                                   const int64_t* __restrict__ tile_begin,
+                                                   int32_t count, int64_t total_tiles,
+                                                   DevTensor one, StepScalars P) {
+    step_body<kOpt, kLinV>(table, tile_begin, count, total_tiles, one, P);
+}
+
+// ---- graph-capturable AdamW: the step's scalars from a device schedule -------
+
+// Advances the schedule by one step (t + 1, p1 * beta1, p2 * beta2: the same
+// successive multiplications as the host) and writes the step's scalars.
+__global__ void schedule_advance_kernel(flashopt_adamw_schedule* S) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const double p1 = S->p1 * S->beta1;
+    const double p2 = S->p2 * S->beta2;
+    S->t = S->t + 1;
+    S->p1 = p1;
+    S->p2 = p2;
+    const AdamScalars a =
+        adam_scalars_from(S->lr, S->beta1, S->beta2, S->eps, S->weight_decay, p1, p2);
+    uint32_t w[10];
+    __builtin_memcpy(w, &a, sizeof a);
+    for (int i = 0; i < 10; ++i) S->scalars[i] = w[i];
+}
+
+__global__ void schedule_init_kernel(flashopt_adamw_schedule* S, flashopt_adamw_hparams hp,
+                                     int64_t t, double p1, double p2) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    S->lr = hp.lr;
+    S->eps = hp.eps;
+    S->weight_decay = hp.weight_decay;
+    S->beta1 = hp.beta1;
+    S->beta2 = hp.beta2;
+    S->t = t;
+    S->p1 = p1;
+    S->p2 = p2;
+    for (int i = 0; i < 10; ++i) S->scalars[i] = 0u;
+    S->pad[0] = S->pad[1] = 0u;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel_scheduled(
+    const DevTensor* __restrict__ table, const int64_t* __restrict__ tile_begin, int32_t count,
+    int64_t total_tiles, const flashopt_adamw_schedule* __restrict__ S) {
+    StepScalars P{};
+    __builtin_memcpy(&P.a, S->scalars, sizeof P.a);    // uniform: scalar loads
+    step_body<kAdamW, false>(table, tile_begin, count, total_tiles, DevTensor{}, P);
 }
 
 // ---- the uncompressed step (_FP32 kinds) -------------------------------------
@@ -1220,17 +1269,7 @@ static AdamScalars adam_scalars(const flashopt_adamw_hparams& hp, int64_t t, dou
         p2 = p2 * hp.beta2;
     }
     *p1c = p1; *p2c = p2; *tc = t; *b1c = hp.beta1; *b2c = hp.beta2;
-    AdamScalars a;
-    a.b1 = (float)hp.beta1;
-    a.c1 = (float)(1.0 - hp.beta1);
-    a.b2 = (float)hp.beta2;
-    a.c2 = (float)(1.0 - hp.beta2);
-    a.alpha = (float)(hp.lr / (1.0 - p1));
-    a.kappa = (float)(1.0 / std::sqrt(1.0 - p2));
-    a.eps = (float)hp.eps;
-    a.lambda = (float)(1.0 - hp.lr * hp.weight_decay);
-    quot_window(a.eps, a.quot_neg_lo2, a.quot_span);
-    return a;
+    return adam_scalars_from(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, p1, p2);
 }
 
 static int check_adam(const flashopt_adamw_hparams* hp, int64_t step) {
@@ -1798,6 +1837,40 @@ int flashopt_lion_step(const flashopt_list* L, const flashopt_lion_hparams* hp, 
     StepScalars P{};
     P.l = lion_scalars(*hp);
     return launch_list(kLion, L, P, stream);
+}
+
+int flashopt_adamw_schedule_init(flashopt_adamw_schedule* S, const flashopt_adamw_hparams* hp,
+                                 int64_t t, void* stream) {
+    if (!S) return FLASHOPT_ERR_NULL;
+    if (!aligned(S, 8)) return FLASHOPT_ERR_ALIGN;
+    if (t < 0) return FLASHOPT_ERR_STEP;
+    const int st = check_adam(hp, t + 1);
+    if (st != FLASHOPT_OK) return st;
+    // beta^t by t successive multiplications, as every host step computes it
+    double p1 = 1.0, p2 = 1.0;
+    for (int64_t k = 0; k < t && !(p1 == 0.0 && p2 == 0.0); ++k) {
+        p1 = p1 * hp->beta1;
+        p2 = p2 * hp->beta2;
+    }
+    hipLaunchKernelGGL(schedule_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, S, *hp, t,
+                       p1, p2);
+    return launch_status();
+}
+
+int flashopt_adamw_step_scheduled(const flashopt_list* L, flashopt_adamw_schedule* S,
+                                  void* stream) {
+    if (!L || !S) return FLASHOPT_ERR_NULL;
+    if (!aligned(S, 8)) return FLASHOPT_ERR_ALIGN;
+    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
+    int r = launch_status();
+    if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
+    hipLaunchKernelGGL(step_kernel_scheduled, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0, st,
+                       (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin, L->count,
+                       L->total_tiles, (const flashopt_adamw_schedule*)S);
+    return launch_status();
 }
 
 int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,

@@ -65,6 +65,15 @@ class LionHparams(ctypes.Structure):
                 ("weight_decay", ctypes.c_double)]
 
 
+class AdamWSchedule(ctypes.Structure):
+    """flashopt_adamw_schedule (lives in device memory; see DeviceSchedule)."""
+    _fields_ = [("lr", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("t", ctypes.c_int64), ("p1", ctypes.c_double),
+                ("p2", ctypes.c_double), ("scalars", ctypes.c_uint32 * 10),
+                ("pad", ctypes.c_uint32 * 2)]
+
+
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 SIGNATURES = {
     "flashopt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -99,6 +108,8 @@ SIGNATURES = {
                                              _P]),
     "flashopt_stream_probe": (ctypes.c_int, [_P, _P]),
     "flashopt_lion_step": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
+    "flashopt_adamw_schedule_init": (ctypes.c_int, [_P, ctypes.POINTER(AdamWHparams), _I64, _P]),
+    "flashopt_adamw_step_scheduled": (ctypes.c_int, [_P, _P, _P]),
     "flashopt_lion_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(LionHparams),
                                               _I64, _P]),
 }
@@ -367,6 +378,37 @@ def flashopt_lion_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: 
     _check("flashopt_lion_step_one",
            lib().flashopt_lion_step_one(lst.handle, index, _ptr(grad), ctypes.byref(h), step,
                                         _stream(stream)))
+
+
+class DeviceSchedule:
+    """A flashopt_adamw_schedule in device memory (a torch byte tensor): the
+    step counter, bias-correction powers and schedulable hyper-parameters of
+    flashopt_adamw_step_scheduled, which a captured HIP graph can replay."""
+
+    SIZE = ctypes.sizeof(AdamWSchedule)
+    _OFF = {name: getattr(AdamWSchedule, name).offset for name in ("lr", "eps", "weight_decay")}
+
+    def __init__(self, hp: dict, t: int = 0, device="cuda", stream=None):
+        self.buf = torch.zeros(self.SIZE, dtype=torch.uint8, device=device)
+        h = _adam(hp)
+        _check("flashopt_adamw_schedule_init",
+               lib().flashopt_adamw_schedule_init(_ptr(self.buf), ctypes.byref(h), t,
+                                                  _stream(stream)))
+
+    def set(self, name: str, value: float) -> None:
+        """Write lr, eps or weight_decay on the device (stream-ordered: takes
+        effect from the next step call or replay)."""
+        o = self._OFF[name]
+        self.buf[o:o + 8].view(torch.float64).fill_(value)
+
+    def read(self) -> AdamWSchedule:
+        return AdamWSchedule.from_buffer_copy(self.buf.cpu().numpy().tobytes())
+
+
+def flashopt_adamw_step_scheduled(lst: FlashoptList, schedule: DeviceSchedule,
+                                  stream=None) -> None:
+    _check("flashopt_adamw_step_scheduled",
+           lib().flashopt_adamw_step_scheduled(lst.handle, _ptr(schedule.buf), _stream(stream)))
 
 
 def step(lst: FlashoptList, optimizer: str, hp: dict, t: int, stream=None) -> None:

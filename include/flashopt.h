@@ -276,6 +276,36 @@ int flashopt_sgd_step(const flashopt_list* list, const flashopt_sgd_hparams* hp,
 int flashopt_lion_step(const flashopt_list* list, const flashopt_lion_hparams* hp,
                        int64_t step, void* stream);
 
+/* ---- graph-capturable AdamW.  The step counter, the bias-correction powers
+ * and the schedulable hyper-parameters live in a DEVICE struct that each call
+ * advances on the stream, so the launches of one call depend on no host value
+ * that changes from step to step: capture them once (HIP graphs,
+ * torch.cuda.graphs) and replay every step.  Each call gives exactly the
+ * results of flashopt_adamw_step with the advanced t and the struct's
+ * hyper-parameters. */
+typedef struct flashopt_adamw_schedule {
+    double lr, eps, weight_decay;  /* read on the device by every call: write new values
+                                      between calls or replays (an lr schedule); not
+                                      validated there -- keep them in the ranges of
+                                      flashopt_adamw_hparams                          */
+    double beta1, beta2;           /* fixed at init (p1 and p2 depend on them)        */
+    int64_t t;                     /* steps taken; each call first adds one           */
+    double p1, p2;                 /* beta1^t, beta2^t by t successive multiplications */
+    uint32_t scalars[10];          /* the step's binary32 scalars, written by each call */
+    uint32_t pad[2];
+} flashopt_adamw_schedule;
+
+/* Set up a schedule (DEVICE pointer, 8-byte aligned) for a state that has taken
+ * t >= 0 steps: hp validated as for flashopt_adamw_step, p1 and p2 computed on
+ * the host; written by a one-thread kernel on `stream` (no copy, no wait). */
+int flashopt_adamw_schedule_init(flashopt_adamw_schedule* schedule,
+                                 const flashopt_adamw_hparams* hp, int64_t t, void* stream);
+/* One fused AdamW step over a FLASHOPT_KIND_ADAMW list: a one-thread kernel
+ * advances the schedule and forms the scalars (adam_scalars_from, the host's
+ * own definition), then the step launch reads them from device memory. */
+int flashopt_adamw_step_scheduled(const flashopt_list* list,
+                                  flashopt_adamw_schedule* schedule, void* stream);
+
 /* ---- gradient release (fused-step section): step tensor `index` of the list
  * now, reading `grad` (device BF16 [numel], overriding the descriptor's
  * pointer); the caller may free or reuse grad once this launch has run.

@@ -112,6 +112,16 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_lion_step(L, ctypes.byref(lion), 1, None) == -4     # AdamW list
     assert lib.flashopt_lion_step_one(L, 0, fake, ctypes.byref(lion), 1, None) == -8
     assert lib.flashopt_state_zero(L, None) == 0
+    # the device schedule: validated on the host, nothing launched on failure
+    assert ctypes.sizeof(F.AdamWSchedule) == 112
+    assert lib.flashopt_adamw_schedule_init(None, ctypes.byref(hp), 0, None) == -1
+    assert lib.flashopt_adamw_schedule_init(P(0x10004), ctypes.byref(hp), 0, None) == -3
+    assert lib.flashopt_adamw_schedule_init(fake, ctypes.byref(hp), -1, None) == -5
+    bad = F.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0)
+    assert lib.flashopt_adamw_schedule_init(fake, ctypes.byref(bad), 0, None) == -4
+    assert lib.flashopt_adamw_step_scheduled(L, None, None) == -1
+    assert lib.flashopt_adamw_step_scheduled(None, fake, None) == -1
+    assert lib.flashopt_adamw_step_scheduled(L, P(0x10004), None) == -3
     assert lib.flashopt_list_destroy(L) == 0
     # an empty Lion list: hyper-parameter and step checks
     assert lib.flashopt_list_create(None, 0, 2, None, 0, None, ctypes.byref(out)) == 0
@@ -123,6 +133,7 @@ def test_host_validation_without_gpu():
         assert lib.flashopt_lion_step(L, ctypes.byref(bad_l), 1, None) == -4
     assert lib.flashopt_lion_step(L, ctypes.byref(lion), 1, None) == 0      # nothing to launch
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == -4      # Lion list
+    assert lib.flashopt_adamw_step_scheduled(L, fake, None) == -4           # Lion list
     assert lib.flashopt_codes_bytes(2, 17) == 3 * 16 and lib.flashopt_scales_bytes(2, 33) == 4
     assert lib.flashopt_list_destroy(L) == 0
     # uncompressed kinds: 512-element blocks of 3 (AdamW) or 2 FP32 fields, no scales
