@@ -20,6 +20,11 @@ the model's own BF16 weights, an AdamW checkpoint is 5.125 B/param (the
 page's 12 -> 5 B/param).  Loading it into a fresh optimizer resumes bit for
 bit.
 
+FlashAdamW(capturable=True) keeps each group's step counter and lr, eps
+and weight decay in a device schedule (flashopt_adamw_step_scheduled), so
+step() can be captured in a HIP graph (torch.cuda.graph) and replayed;
+update_schedules() pushes changed hyper-parameters between replays.
+
 A parameter group with "compress": False (the page's practical advice:
 compression can be switched off for layers that are sensitive to it) keeps
 an FP32 master weight and FP32 moments instead (the library's _fp32 state
@@ -45,9 +50,12 @@ class _FlashOptimizer(torch.optim.Optimizer):
     kind = ""                                    # "adamw" | "sgd" | "lion"
 
     def __init__(self, params, defaults: dict, gradient_release: bool = False,
-                 release_streams: int = 1):
+                 release_streams: int = 1, capturable: bool = False):
         super().__init__(params, defaults)
         self.gradient_release = gradient_release
+        self.capturable = capturable
+        if capturable and (self.kind != "adamw" or gradient_release):
+            raise ValueError("capturable applies to FlashAdamW without gradient release")
         # with release_streams > 1 the per-parameter launches from the gradient
         # hooks go round-robin over that many side streams (default priority):
         # each overlaps the rest of backward and the tail of the previous one
@@ -60,6 +68,17 @@ class _FlashOptimizer(torch.optim.Optimizer):
             for p in group["params"]:
                 self._init_param(p, self._state_kind(group))
         self._build_lists()
+        # capturable: per group, the step counter and hyper-parameters in a
+        # device schedule, so step() launches nothing that depends on host
+        # values and can be captured in a HIP graph
+        self._sched: List[Optional[F.DeviceSchedule]] = []
+        self._sched_hp: List[dict] = []
+        if capturable:
+            for group, lst in zip(self.param_groups, self._lists):
+                if self._state_kind(group) != "adamw":
+                    raise ValueError("capturable needs compressed AdamW state in every group")
+                self._sched.append(F.DeviceSchedule(self._hp(group), t=0) if lst else None)
+                self._sched_hp.append(self._hp(group))
         if gradient_release:
             self._install_release_hooks()
 
@@ -117,6 +136,9 @@ class _FlashOptimizer(torch.optim.Optimizer):
             for s in self._side:
                 cur.wait_stream(s)
             return loss
+        if self.capturable:
+            self._step_scheduled()
+            return loss
         for group, lst in zip(self.param_groups, self._lists):
             if lst is None:
                 continue
@@ -144,6 +166,40 @@ class _FlashOptimizer(torch.optim.Optimizer):
                     self.state[p]["step"] = t
         return loss
 
+    def update_schedules(self) -> None:
+        """capturable: write changed lr / eps / weight_decay of the param
+        groups into their device schedules.  step() does this itself when it
+        runs eagerly; a replayed graph does not run step()'s host code, so
+        call this (outside the graph) after changing hyper-parameters."""
+        for i, (group, sched) in enumerate(zip(self.param_groups, self._sched)):
+            if sched is None:
+                continue
+            hp = self._hp(group)
+            if (hp["beta1"], hp["beta2"]) != (self._sched_hp[i]["beta1"],
+                                              self._sched_hp[i]["beta2"]):
+                raise ValueError("betas are fixed in a capturable optimizer's schedule")
+            for k in ("lr", "eps", "weight_decay"):
+                if hp[k] != self._sched_hp[i][k]:
+                    sched.set(k, hp[k])
+            self._sched_hp[i] = hp
+
+    def _step_scheduled(self) -> None:
+        if not torch.cuda.is_current_stream_capturing():
+            self.update_schedules()
+        for group, lst, sched in zip(self.param_groups, self._lists, self._sched):
+            if lst is None:
+                continue
+            grads = []
+            for p in group["params"]:
+                g = p.grad
+                if g is None:
+                    raise ValueError("capturable: every parameter needs a gradient at each step")
+                if g.dtype != torch.bfloat16 or not g.is_contiguous():
+                    raise ValueError("FlashOptim expects contiguous BF16 gradients")
+                grads.append(g.view(-1))
+            F.flashopt_list_set_grads(lst, grads)
+            F.flashopt_adamw_step_scheduled(lst, sched)
+
     def _install_release_hooks(self) -> None:
         for gi, group in enumerate(self.param_groups):
             for pi, p in enumerate(group["params"]):
@@ -168,7 +224,17 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 self._hooks.append(p.register_post_accumulate_grad_hook(hook))
 
     # -- checkpoints -------------------------------------------------------------
+    def _sync_steps(self) -> None:
+        """capturable: the step counts live in the device schedules."""
+        for group, sched in zip(self.param_groups, self._sched):
+            if sched is not None:
+                t = sched.read().t
+                for p in group["params"]:
+                    self.state[p]["step"] = t
+
     def state_dict(self) -> dict:
+        if self.capturable:
+            self._sync_steps()
         sd = {"kind": self.kind, "param_groups": [], "state": {}}
         index = 0
         for group in self.param_groups:
@@ -205,6 +271,15 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 st.codes.copy_(src["codes"])
                 st.scales.copy_(src["scales"])
                 self.state[p]["step"] = int(src["step"])
+        if self.capturable:
+            for i, (group, sched) in enumerate(zip(self.param_groups, self._sched)):
+                if sched is None:
+                    continue
+                steps = {self.state[p]["step"] for p in group["params"]}
+                if len(steps) != 1:
+                    raise ValueError("capturable: a group's parameters need equal step counts")
+                self._sched[i] = F.DeviceSchedule(self._hp(group), t=steps.pop())
+                self._sched_hp[i] = self._hp(group)
 
     def export_fp32(self, p: torch.Tensor):
         """(theta_hat, m, v) of one parameter in FP32 (v None unless AdamW)."""
@@ -223,10 +298,10 @@ class FlashAdamW(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
                  weight_decay: float = 1e-2, gradient_release: bool = False,
-                 release_streams: int = 1, compress: bool = True):
+                 release_streams: int = 1, compress: bool = True, capturable: bool = False):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), eps=eps,
                                       weight_decay=weight_decay, compress=compress),
-                         gradient_release, release_streams)
+                         gradient_release, release_streams, capturable)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],

@@ -108,3 +108,49 @@ def test_device_scalars_equal_the_host_definition(hp):
         host = oracle.adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                                     hp["weight_decay"], t)
         np.testing.assert_array_equal(dev.view(np.uint32), host.view(np.uint32), err_msg=str(t))
+
+
+def test_capturable_flash_adamw_in_a_graph():
+    """FlashAdamW(capturable=True): opt.step() captured once with static
+    gradients, replayed every step (an lr change pushed between replays with
+    update_schedules), equals the eager optimizer bit for bit; its
+    checkpoint carries the device step count."""
+    from compressed_adamw_state_amd import optim as O
+    rng = np.random.default_rng(43)
+    shapes = [(4097,), (33, 64), (2048,), (7,)]
+    init = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    ref = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
+    cap = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
+    kw = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    ro = O.FlashAdamW(ref, **kw)
+    co = O.FlashAdamW(cap, capturable=True, **kw)
+    static = [torch.zeros_like(p) for p in cap]            # BF16, like the parameters
+    for p, g in zip(cap, static):
+        p.grad = g
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            co.step()
+    torch.cuda.synchronize()
+    for t in range(1, 6):
+        if t == 3:
+            for o in (ro, co):
+                o.param_groups[0]["lr"] = 5e-4
+            co.update_schedules()
+        gs = [torch.from_numpy((rng.standard_normal(s) * 1e-3).astype(np.float32))
+              .to(torch.bfloat16).cuda() for s in shapes]
+        for p, g, sg in zip(ref, gs, static):
+            p.grad = g.view(p.shape)
+            sg.copy_(g.view(sg.shape))
+        ro.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, cap):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), t
+            sa, sb = ro.state[a]["flash"], co.state[b]["flash"]
+            assert torch.equal(sa.codes, sb.codes) and torch.equal(sa.scales, sb.scales), t
+    sd = co.state_dict()
+    assert all(sd["state"][i]["step"] == 5 for i in range(len(cap)))
