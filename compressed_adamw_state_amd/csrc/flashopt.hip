@@ -36,6 +36,11 @@ namespace flashopt {
 
 enum Opt { kAdamW = 0, kSgd = 1, kLion = 2 };
 
+// Every tiled kernel runs blocks of kBlock threads (the launch bounds below and
+// every launch say so); kernels use the constant, not blockDim.
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
 // State layout of one tensor (see include/flashopt.h): a code record per 8
 // elements -- rho[8], m_code[8] and, for AdamW, v_code[8] -- and per 32-element
 // group the FP16 m scale followed, for AdamW, by the v scale.  SGD and Lion
@@ -574,8 +579,8 @@ __device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
                                           int64_t total_tiles, const DevTensor& one,
                                           const StepScalars& P) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, one, total_tiles, wave);
@@ -734,8 +739,8 @@ __global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restr
                                                         int32_t count, int64_t total_tiles,
                                                         DevTensor one, StepScalars P) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, one, total_tiles, wave);
@@ -773,9 +778,9 @@ __global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restr
 // Each wave walks 512-element chunks; lane l owns chunk elements [8l, 8l+8).
 #define FLAT_LOOP(n)                                                                   \
     const int lane = threadIdx.x & (kWave - 1);                                          \
-    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) +            \
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock +            \
                                  (threadIdx.x / kWave));                                 \
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);                    \
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;                    \
     for (int64_t c = wave; c * kSubTile < (n); c += nwaves)
 
 __global__ __launch_bounds__(256) void split_kernel(const float* x, int64_t n, uint16_t* tb,
@@ -1008,8 +1013,8 @@ __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__
                                                    const int64_t* __restrict__ tile_begin,
                                                    int32_t count, int64_t total_tiles) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
@@ -1128,8 +1133,8 @@ __global__ __launch_bounds__(256) void zero_fp32_kernel(const DevTensor* __restr
                                                         const int64_t* __restrict__ tile_begin,
                                                         int32_t count, int64_t total_tiles) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
@@ -1171,8 +1176,8 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
                                                     const int64_t* __restrict__ tile_begin,
                                                     int32_t count, int64_t total_tiles) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
@@ -1228,8 +1233,6 @@ __global__ void set_grads_kernel(DevTensor* table, GradBatch b) {
 
 // ---- host side -------------------------------------------------------------
 
-constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / kWave;
 // One wave per work item (tile or chunk) up to kMaxBlocks blocks; the kernels
 // fall back to a wave-stride loop beyond that.  Many short-lived waves let the
 // dispatcher refill a CU the moment one finishes, which keeps every SIMD busy
