@@ -222,6 +222,49 @@ def test_lion_hyperparameter_variants_and_edge_gradients():
         r.compare(f"lion hp {t}")
 
 
+@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion"])
+def test_non_finite_gradients_stay_in_their_groups(opt):
+    """Non-finite gradients are outside the contract, but they must neither
+    fault nor leak: with NaN and +-Inf gradients in a few 32-element groups,
+    every other group's codes and scales still equal the oracle's bit for
+    bit, step after step (groups are independent in the method)."""
+    n = 32 * 64 + 9
+    rng = np.random.default_rng(16)
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    st = F.TensorState(n, opt, "cuda")
+    F.flashopt_tensor_init(st, torch.from_numpy(theta).cuda())
+    o = oracle.State(theta, opt)
+    g = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    lst = F.FlashoptList([st], [g])
+    bad_groups = [3, 17, 64]                             # 64: the partial last group
+    hp = W.HPARAMS[opt]
+    for t in (1, 2, 3):
+        x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        x[3 * 32 + 5] = np.nan
+        x[17 * 32] = np.inf
+        x[17 * 32 + 31] = -np.inf
+        x[64 * 32 + 2] = np.nan
+        gb = torch.from_numpy(x).to(torch.bfloat16)
+        g.copy_(gb)
+        F.step(lst, opt, hp, t)
+        oracle.step(o, gb.view(torch.int16).numpy().view(np.uint16), t, hp)
+        torch.cuda.synchronize()
+        f = state_fields(st)
+        ok = np.ones(n, bool)
+        for b in bad_groups:
+            ok[b * 32:(b + 1) * 32] = False
+        gok = np.ones((n + 31) // 32, bool)
+        gok[bad_groups] = False
+        keys = [("theta", "tb"), ("rho", "rho"), ("m_code", "qm")]
+        if opt == "adamw":
+            keys.append(("v_code", "qv"))
+        for k, ok_name in keys:
+            np.testing.assert_array_equal(f[k][ok], getattr(o, ok_name)[ok], err_msg=f"{k} {t}")
+        np.testing.assert_array_equal(f["m_scale"][gok], o.sm[gok])
+        if opt == "adamw":
+            np.testing.assert_array_equal(f["v_scale"][gok], o.sv[gok])
+
+
 def test_set_grads_and_state_zero():
     w = W.ragged([3000, 70], seed=14, steps=2)
     r = Run(w, "full")
