@@ -43,6 +43,26 @@ def build_test_lib(verbose: bool = False) -> str:
     return TEST_LIB
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_api", "c_abi_check.cpp")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_api", "c_abi_check")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """The C++ consumer of the C ABI the GPU tests run (tests only): host code
+    linked against libflashopt.so and the oracle's liboracle.so."""
+    tmp = C_CHECK_BIN + ".tmp"
+    oracle_dir = os.path.join(ROOT, "oracle")
+    cmd = ["hipcc", "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"),
+           "-I", oracle_dir, "-o", tmp, C_CHECK_SRC, "-L", PKG, "-lflashopt", "-L", oracle_dir,
+           "-loracle", "-Wl,-rpath,$ORIGIN/../../compressed_adamw_state_amd",
+           "-Wl,-rpath,$ORIGIN/../../oracle"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, C_CHECK_BIN)
+    return C_CHECK_BIN
+
+
 def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp"
     cmd = ["hipcc", *FLAGS, *extra, "-o", tmp, SRC]
