@@ -367,6 +367,23 @@ struct SgdScalars { float mu, eta, omega; };
 // Lion: b1, c1 = 1-beta1 (direction), b2, c2 = 1-beta2 (momentum), eta = lr,
 // lambda = 1 - lr*wd.
 struct LionScalars { float b1, c1, b2, c2, eta, lambda; };
+
+// The SGD and Lion scalars from the double hyper-parameters, each rounded
+// once (one definition for the host call and the device-scheduled call).
+__host__ __device__ inline SgdScalars sgd_scalars_from(double lr, double momentum, double wd) {
+    return SgdScalars{(float)momentum, (float)lr, (float)wd};
+}
+__host__ __device__ inline LionScalars lion_scalars_from(double lr, double beta1, double beta2,
+                                                         double wd) {
+    LionScalars l;
+    l.b1 = (float)beta1;
+    l.c1 = (float)(1.0 - beta1);
+    l.b2 = (float)beta2;
+    l.c2 = (float)(1.0 - beta2);
+    l.eta = (float)lr;
+    l.lambda = (float)(1.0 - lr * wd);
+    return l;
+}
 // One kernel argument for every optimizer; each instantiation reads its own.
 struct StepScalars {
     AdamScalars a;

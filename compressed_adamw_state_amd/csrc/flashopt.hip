@@ -633,12 +633,57 @@ __global__ void schedule_init_kernel(flashopt_adamw_schedule* S, flashopt_adamw_
     S->pad[0] = S->pad[1] = 0u;
 }
 
+__global__ void sgd_schedule_advance_kernel(flashopt_sgd_schedule* S) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    S->t = S->t + 1;
+    const SgdScalars a = sgd_scalars_from(S->lr, S->momentum, S->weight_decay);
+    uint32_t w[3];
+    __builtin_memcpy(w, &a, sizeof a);
+    for (int i = 0; i < 3; ++i) S->scalars[i] = w[i];
+    S->scalars[3] = 0u;
+}
+
+__global__ void lion_schedule_advance_kernel(flashopt_lion_schedule* S) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    S->t = S->t + 1;
+    const LionScalars a = lion_scalars_from(S->lr, S->beta1, S->beta2, S->weight_decay);
+    uint32_t w[6];
+    __builtin_memcpy(w, &a, sizeof a);
+    for (int i = 0; i < 6; ++i) S->scalars[i] = w[i];
+}
+
+__global__ void sgd_schedule_init_kernel(flashopt_sgd_schedule* S, flashopt_sgd_hparams hp,
+                                         int64_t t) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    S->lr = hp.lr;
+    S->momentum = hp.momentum;
+    S->weight_decay = hp.weight_decay;
+    S->t = t;
+    for (int i = 0; i < 4; ++i) S->scalars[i] = 0u;
+}
+
+__global__ void lion_schedule_init_kernel(flashopt_lion_schedule* S, flashopt_lion_hparams hp,
+                                          int64_t t) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    S->lr = hp.lr;
+    S->beta1 = hp.beta1;
+    S->beta2 = hp.beta2;
+    S->weight_decay = hp.weight_decay;
+    S->t = t;
+    for (int i = 0; i < 6; ++i) S->scalars[i] = 0u;
+}
+
+// The step with its scalars read from a schedule's `scalars` words (written
+// by the advance kernel launched just before on the same stream).
+template <int kOpt>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel_scheduled(
     const DevTensor* __restrict__ table, const int64_t* __restrict__ tile_begin, int32_t count,
-    int64_t total_tiles, const flashopt_adamw_schedule* __restrict__ S) {
+    int64_t total_tiles, const uint32_t* __restrict__ scalars) {
     StepScalars P{};
-    __builtin_memcpy(&P.a, S->scalars, sizeof P.a);    // uniform: scalar loads
-    step_body<kAdamW, false>(table, tile_begin, count, total_tiles, DevTensor{}, P);
+    if (kOpt == kAdamW) __builtin_memcpy(&P.a, scalars, sizeof P.a);   // uniform: scalar loads
+    else if (kOpt == kSgd) __builtin_memcpy(&P.s, scalars, sizeof P.s);
+    else __builtin_memcpy(&P.l, scalars, sizeof P.l);
+    step_body<kOpt, false>(table, tile_begin, count, total_tiles, DevTensor{}, P);
 }
 
 // ---- the uncompressed step (_FP32 kinds) -------------------------------------
@@ -1320,18 +1365,11 @@ static int check_lion(const flashopt_lion_hparams* hp, int64_t step) {
 }
 
 static SgdScalars sgd_scalars(const flashopt_sgd_hparams& hp) {
-    return SgdScalars{(float)hp.momentum, (float)hp.lr, (float)hp.weight_decay};
+    return sgd_scalars_from(hp.lr, hp.momentum, hp.weight_decay);
 }
 
 static LionScalars lion_scalars(const flashopt_lion_hparams& hp) {
-    LionScalars l;
-    l.b1 = (float)hp.beta1;
-    l.c1 = (float)(1.0 - hp.beta1);
-    l.b2 = (float)hp.beta2;
-    l.c2 = (float)(1.0 - hp.beta2);
-    l.eta = (float)hp.lr;
-    l.lambda = (float)(1.0 - hp.lr * hp.weight_decay);
-    return l;
+    return lion_scalars_from(hp.lr, hp.beta1, hp.beta2, hp.weight_decay);
 }
 
 static int check_tensor(const flashopt_tensor& t, int32_t kind) {
@@ -1870,9 +1908,64 @@ int flashopt_adamw_step_scheduled(const flashopt_list* L, flashopt_adamw_schedul
     hipLaunchKernelGGL(schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
     int r = launch_status();
     if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
-    hipLaunchKernelGGL(step_kernel_scheduled, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0, st,
-                       (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin, L->count,
-                       L->total_tiles, (const flashopt_adamw_schedule*)S);
+    hipLaunchKernelGGL(step_kernel_scheduled<kAdamW>, dim3(grid_for(L->total_tiles)), dim3(kBlock),
+                       0, st, (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin,
+                       L->count, L->total_tiles, (const uint32_t*)S->scalars);
+    return launch_status();
+}
+
+int flashopt_sgd_schedule_init(flashopt_sgd_schedule* S, const flashopt_sgd_hparams* hp,
+                               int64_t t, void* stream) {
+    if (!S) return FLASHOPT_ERR_NULL;
+    if (!aligned(S, 8)) return FLASHOPT_ERR_ALIGN;
+    if (t < 0) return FLASHOPT_ERR_STEP;
+    const int st = check_sgd(hp, t + 1);
+    if (st != FLASHOPT_OK) return st;
+    hipLaunchKernelGGL(sgd_schedule_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, S,
+                       *hp, t);
+    return launch_status();
+}
+
+int flashopt_sgd_step_scheduled(const flashopt_list* L, flashopt_sgd_schedule* S, void* stream) {
+    if (!L || !S) return FLASHOPT_ERR_NULL;
+    if (!aligned(S, 8)) return FLASHOPT_ERR_ALIGN;
+    if (L->kind != FLASHOPT_KIND_SGD) return FLASHOPT_ERR_ARG;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(sgd_schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
+    int r = launch_status();
+    if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
+    hipLaunchKernelGGL(step_kernel_scheduled<kSgd>, dim3(grid_for(L->total_tiles)), dim3(kBlock),
+                       0, st, (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin,
+                       L->count, L->total_tiles, (const uint32_t*)S->scalars);
+    return launch_status();
+}
+
+int flashopt_lion_schedule_init(flashopt_lion_schedule* S, const flashopt_lion_hparams* hp,
+                                int64_t t, void* stream) {
+    if (!S) return FLASHOPT_ERR_NULL;
+    if (!aligned(S, 8)) return FLASHOPT_ERR_ALIGN;
+    if (t < 0) return FLASHOPT_ERR_STEP;
+    const int st = check_lion(hp, t + 1);
+    if (st != FLASHOPT_OK) return st;
+    hipLaunchKernelGGL(lion_schedule_init_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, S,
+                       *hp, t);
+    return launch_status();
+}
+
+int flashopt_lion_step_scheduled(const flashopt_list* L, flashopt_lion_schedule* S,
+                                 void* stream) {
+    if (!L || !S) return FLASHOPT_ERR_NULL;
+    if (!aligned(S, 8)) return FLASHOPT_ERR_ALIGN;
+    if (L->kind != FLASHOPT_KIND_LION) return FLASHOPT_ERR_ARG;
+    if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(lion_schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
+    int r = launch_status();
+    if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
+    hipLaunchKernelGGL(step_kernel_scheduled<kLion>, dim3(grid_for(L->total_tiles)), dim3(kBlock),
+                       0, st, (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin,
+                       L->count, L->total_tiles, (const uint32_t*)S->scalars);
     return launch_status();
 }
 

@@ -74,6 +74,18 @@ class AdamWSchedule(ctypes.Structure):
                 ("pad", ctypes.c_uint32 * 2)]
 
 
+class SGDSchedule(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("t", ctypes.c_int64),
+                ("scalars", ctypes.c_uint32 * 4)]
+
+
+class LionSchedule(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("t", ctypes.c_int64),
+                ("scalars", ctypes.c_uint32 * 6)]
+
+
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 SIGNATURES = {
     "flashopt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -110,6 +122,10 @@ SIGNATURES = {
     "flashopt_lion_step": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
     "flashopt_adamw_schedule_init": (ctypes.c_int, [_P, ctypes.POINTER(AdamWHparams), _I64, _P]),
     "flashopt_adamw_step_scheduled": (ctypes.c_int, [_P, _P, _P]),
+    "flashopt_sgd_schedule_init": (ctypes.c_int, [_P, ctypes.POINTER(SGDHparams), _I64, _P]),
+    "flashopt_sgd_step_scheduled": (ctypes.c_int, [_P, _P, _P]),
+    "flashopt_lion_schedule_init": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
+    "flashopt_lion_step_scheduled": (ctypes.c_int, [_P, _P, _P]),
     "flashopt_lion_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(LionHparams),
                                               _I64, _P]),
 }
@@ -381,34 +397,62 @@ def flashopt_lion_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: 
 
 
 class DeviceSchedule:
-    """A flashopt_adamw_schedule in device memory (a torch byte tensor): the
-    step counter, bias-correction powers and schedulable hyper-parameters of
-    flashopt_adamw_step_scheduled, which a captured HIP graph can replay."""
+    """A flashopt_{adamw,sgd,lion}_schedule in device memory (a torch byte
+    tensor): the step counter (and, for AdamW, the bias-correction powers)
+    and the schedulable hyper-parameters of the *_step_scheduled calls,
+    which a captured HIP graph can replay."""
 
-    SIZE = ctypes.sizeof(AdamWSchedule)
-    _OFF = {name: getattr(AdamWSchedule, name).offset for name in ("lr", "eps", "weight_decay")}
+    _STRUCT = {"adamw": AdamWSchedule, "sgd": SGDSchedule, "lion": LionSchedule}
+    _HP = {"adamw": lambda hp: _adam(hp), "sgd": lambda hp: _sgd(hp),
+           "lion": lambda hp: _lion(hp)}
+    # the hyper-parameters each call reads on the device (AdamW's betas are
+    # fixed at init because the powers depend on them)
+    SETTABLE = {"adamw": ("lr", "eps", "weight_decay"),
+                "sgd": ("lr", "momentum", "weight_decay"),
+                "lion": ("lr", "beta1", "beta2", "weight_decay")}
 
-    def __init__(self, hp: dict, t: int = 0, device="cuda", stream=None):
-        self.buf = torch.zeros(self.SIZE, dtype=torch.uint8, device=device)
-        h = _adam(hp)
-        _check("flashopt_adamw_schedule_init",
-               lib().flashopt_adamw_schedule_init(_ptr(self.buf), ctypes.byref(h), t,
-                                                  _stream(stream)))
+    def __init__(self, hp: dict, t: int = 0, device="cuda", stream=None,
+                 optimizer: str = "adamw"):
+        self.optimizer = optimizer
+        self.struct = self._STRUCT[optimizer]
+        self.buf = torch.zeros(ctypes.sizeof(self.struct), dtype=torch.uint8, device=device)
+        h = self._HP[optimizer](hp)
+        fn = "flashopt_%s_schedule_init" % optimizer
+        _check(fn, getattr(lib(), fn)(_ptr(self.buf), ctypes.byref(h), t, _stream(stream)))
 
     def set(self, name: str, value: float) -> None:
-        """Write lr, eps or weight_decay on the device (stream-ordered: takes
-        effect from the next step call or replay)."""
-        o = self._OFF[name]
+        """Write one of SETTABLE on the device (stream-ordered: takes effect
+        from the next step call or replay)."""
+        if name not in self.SETTABLE[self.optimizer]:
+            raise ValueError(f"{name} is not settable on a {self.optimizer} schedule")
+        o = getattr(self.struct, name).offset
         self.buf[o:o + 8].view(torch.float64).fill_(value)
 
-    def read(self) -> AdamWSchedule:
-        return AdamWSchedule.from_buffer_copy(self.buf.cpu().numpy().tobytes())
+    def read(self):
+        return self.struct.from_buffer_copy(self.buf.cpu().numpy().tobytes())
 
 
 def flashopt_adamw_step_scheduled(lst: FlashoptList, schedule: DeviceSchedule,
                                   stream=None) -> None:
     _check("flashopt_adamw_step_scheduled",
            lib().flashopt_adamw_step_scheduled(lst.handle, _ptr(schedule.buf), _stream(stream)))
+
+
+def flashopt_sgd_step_scheduled(lst: FlashoptList, schedule: DeviceSchedule,
+                                stream=None) -> None:
+    _check("flashopt_sgd_step_scheduled",
+           lib().flashopt_sgd_step_scheduled(lst.handle, _ptr(schedule.buf), _stream(stream)))
+
+
+def flashopt_lion_step_scheduled(lst: FlashoptList, schedule: DeviceSchedule,
+                                 stream=None) -> None:
+    _check("flashopt_lion_step_scheduled",
+           lib().flashopt_lion_step_scheduled(lst.handle, _ptr(schedule.buf), _stream(stream)))
+
+
+def step_scheduled(lst: FlashoptList, schedule: DeviceSchedule, stream=None) -> None:
+    {"adamw": flashopt_adamw_step_scheduled, "sgd": flashopt_sgd_step_scheduled,
+     "lion": flashopt_lion_step_scheduled}[schedule.optimizer](lst, schedule, stream)
 
 
 def step(lst: FlashoptList, optimizer: str, hp: dict, t: int, stream=None) -> None:

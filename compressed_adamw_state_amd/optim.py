@@ -20,10 +20,10 @@ the model's own BF16 weights, an AdamW checkpoint is 5.125 B/param (the
 page's 12 -> 5 B/param).  Loading it into a fresh optimizer resumes bit for
 bit.
 
-FlashAdamW(capturable=True) keeps each group's step counter and lr, eps
-and weight decay in a device schedule (flashopt_adamw_step_scheduled), so
-step() can be captured in a HIP graph (torch.cuda.graph) and replayed;
-update_schedules() pushes changed hyper-parameters between replays.
+capturable=True keeps each group's step counter and hyper-parameters in a
+device schedule (flashopt_*_step_scheduled), so step() can be captured in a
+HIP graph (torch.cuda.graph) and replayed; update_schedules() pushes
+changed hyper-parameters between replays (AdamW's betas stay fixed).
 
 A parameter group with "compress": False (the page's practical advice:
 compression can be switched off for layers that are sensitive to it) keeps
@@ -54,8 +54,8 @@ class _FlashOptimizer(torch.optim.Optimizer):
         super().__init__(params, defaults)
         self.gradient_release = gradient_release
         self.capturable = capturable
-        if capturable and (self.kind != "adamw" or gradient_release):
-            raise ValueError("capturable applies to FlashAdamW without gradient release")
+        if capturable and gradient_release:
+            raise ValueError("capturable and gradient_release do not combine")
         # with release_streams > 1 the per-parameter launches from the gradient
         # hooks go round-robin over that many side streams (default priority):
         # each overlaps the rest of backward and the tail of the previous one
@@ -75,9 +75,10 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._sched_hp: List[dict] = []
         if capturable:
             for group, lst in zip(self.param_groups, self._lists):
-                if self._state_kind(group) != "adamw":
-                    raise ValueError("capturable needs compressed AdamW state in every group")
-                self._sched.append(F.DeviceSchedule(self._hp(group), t=0) if lst else None)
+                if self._state_kind(group) != self.kind:
+                    raise ValueError("capturable needs the compressed state in every group")
+                self._sched.append(F.DeviceSchedule(self._hp(group), t=0, optimizer=self.kind)
+                                   if lst else None)
                 self._sched_hp.append(self._hp(group))
         if gradient_release:
             self._install_release_hooks()
@@ -167,20 +168,21 @@ class _FlashOptimizer(torch.optim.Optimizer):
         return loss
 
     def update_schedules(self) -> None:
-        """capturable: write changed lr / eps / weight_decay of the param
-        groups into their device schedules.  step() does this itself when it
+        """capturable: write changed hyper-parameters of the param groups
+        into their device schedules.  step() does this itself when it
         runs eagerly; a replayed graph does not run step()'s host code, so
         call this (outside the graph) after changing hyper-parameters."""
         for i, (group, sched) in enumerate(zip(self.param_groups, self._sched)):
             if sched is None:
                 continue
             hp = self._hp(group)
-            if (hp["beta1"], hp["beta2"]) != (self._sched_hp[i]["beta1"],
-                                              self._sched_hp[i]["beta2"]):
-                raise ValueError("betas are fixed in a capturable optimizer's schedule")
-            for k in ("lr", "eps", "weight_decay"):
-                if hp[k] != self._sched_hp[i][k]:
-                    sched.set(k, hp[k])
+            settable = F.DeviceSchedule.SETTABLE[self.kind]
+            for k, v in hp.items():
+                if v == self._sched_hp[i][k]:
+                    continue
+                if k not in settable:
+                    raise ValueError(f"{k} is fixed in a capturable {self.kind} schedule")
+                sched.set(k, v)
             self._sched_hp[i] = hp
 
     def _step_scheduled(self) -> None:
@@ -198,7 +200,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
                     raise ValueError("FlashOptim expects contiguous BF16 gradients")
                 grads.append(g.view(-1))
             F.flashopt_list_set_grads(lst, grads)
-            F.flashopt_adamw_step_scheduled(lst, sched)
+            F.step_scheduled(lst, sched)
 
     def _install_release_hooks(self) -> None:
         for gi, group in enumerate(self.param_groups):
@@ -278,7 +280,8 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 steps = {self.state[p]["step"] for p in group["params"]}
                 if len(steps) != 1:
                     raise ValueError("capturable: a group's parameters need equal step counts")
-                self._sched[i] = F.DeviceSchedule(self._hp(group), t=steps.pop())
+                self._sched[i] = F.DeviceSchedule(self._hp(group), t=steps.pop(),
+                                                  optimizer=self.kind)
                 self._sched_hp[i] = self._hp(group)
 
     def export_fp32(self, p: torch.Tensor):
@@ -315,9 +318,10 @@ class FlashSGD(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 0.1, momentum: float = 0.9,
                  weight_decay: float = 0.0, gradient_release: bool = False,
-                 release_streams: int = 1, compress: bool = True):
+                 release_streams: int = 1, compress: bool = True, capturable: bool = False):
         super().__init__(params, dict(lr=lr, momentum=momentum, weight_decay=weight_decay,
-                                      compress=compress), gradient_release, release_streams)
+                                      compress=compress), gradient_release, release_streams,
+                         capturable)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], momentum=group["momentum"],
@@ -330,9 +334,10 @@ class FlashLion(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-4, betas=(0.9, 0.99),
                  weight_decay: float = 0.0, gradient_release: bool = False,
-                 release_streams: int = 1, compress: bool = True):
+                 release_streams: int = 1, compress: bool = True, capturable: bool = False):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), weight_decay=weight_decay,
-                                      compress=compress), gradient_release, release_streams)
+                                      compress=compress), gradient_release, release_streams,
+                         capturable)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],

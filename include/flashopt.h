@@ -306,6 +306,31 @@ int flashopt_adamw_schedule_init(flashopt_adamw_schedule* schedule,
 int flashopt_adamw_step_scheduled(const flashopt_list* list,
                                   flashopt_adamw_schedule* schedule, void* stream);
 
+/* SGD and Lion have no step-dependent scalar; their schedules hold the
+ * hyper-parameters on the device so that a captured graph follows an lr (or
+ * momentum, beta, weight-decay) schedule written between replays.  t counts
+ * the calls.  Same results as flashopt_sgd_step / flashopt_lion_step. */
+typedef struct flashopt_sgd_schedule {
+    double lr, momentum, weight_decay;  /* read on the device by every call; not validated there */
+    int64_t t;
+    uint32_t scalars[4];                /* written by each call */
+} flashopt_sgd_schedule;
+
+typedef struct flashopt_lion_schedule {
+    double lr, beta1, beta2, weight_decay;  /* read on the device by every call */
+    int64_t t;
+    uint32_t scalars[6];                    /* written by each call */
+} flashopt_lion_schedule;
+
+int flashopt_sgd_schedule_init(flashopt_sgd_schedule* schedule, const flashopt_sgd_hparams* hp,
+                               int64_t t, void* stream);
+int flashopt_sgd_step_scheduled(const flashopt_list* list, flashopt_sgd_schedule* schedule,
+                                void* stream);
+int flashopt_lion_schedule_init(flashopt_lion_schedule* schedule,
+                                const flashopt_lion_hparams* hp, int64_t t, void* stream);
+int flashopt_lion_step_scheduled(const flashopt_list* list, flashopt_lion_schedule* schedule,
+                                 void* stream);
+
 /* ---- gradient release (fused-step section): step tensor `index` of the list
  * now, reading `grad` (device BF16 [numel], overriding the descriptor's
  * pointer); the caller may free or reuse grad once this launch has run.

@@ -134,6 +134,14 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_lion_step(L, ctypes.byref(lion), 1, None) == 0      # nothing to launch
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == -4      # Lion list
     assert lib.flashopt_adamw_step_scheduled(L, fake, None) == -4           # Lion list
+    assert lib.flashopt_sgd_step_scheduled(L, fake, None) == -4             # Lion list
+    assert ctypes.sizeof(F.SGDSchedule) == 48 and ctypes.sizeof(F.LionSchedule) == 64
+    assert lib.flashopt_lion_schedule_init(None, ctypes.byref(lion), 0, None) == -1
+    assert lib.flashopt_lion_schedule_init(fake, ctypes.byref(lion), -2, None) == -5
+    assert lib.flashopt_lion_schedule_init(P(0x10002), ctypes.byref(lion), 0, None) == -3
+    bad_sgd = F.SGDHparams(0.1, 1.5, 0.0)
+    assert lib.flashopt_sgd_schedule_init(fake, ctypes.byref(bad_sgd), 0, None) == -4
+    assert lib.flashopt_lion_step_scheduled(None, fake, None) == -1
     assert lib.flashopt_codes_bytes(2, 17) == 3 * 16 and lib.flashopt_scales_bytes(2, 33) == 4
     assert lib.flashopt_list_destroy(L) == 0
     # uncompressed kinds: 512-element blocks of 3 (AdamW) or 2 FP32 fields, no scales

@@ -25,11 +25,11 @@ SIZES = [4097, 33, 2048 * 3, 1, (1 << 18) + 5]
 HP = dict(W.ADAMW_HP)
 
 
-def make(seed):
-    w = W.ragged(SIZES, seed=seed, steps=6)
+def make(seed, opt="adamw"):
+    w = W.ragged(SIZES, seed=seed, steps=6, optimizer=opt)
     states = []
     for i, spec in enumerate(w.tensors):
-        st = F.TensorState(spec.numel, "adamw", "cuda")
+        st = F.TensorState(spec.numel, opt, "cuda")
         F.flashopt_tensor_init(st, W.draw_theta(w, i, "cuda"))
         states.append(st)
     grads = [torch.zeros(s.numel, dtype=torch.bfloat16, device="cuda") for s in states]
@@ -62,6 +62,31 @@ def test_scheduled_step_equals_host_step():
         same(a, b, f"step {t}")
     r = sched.read()
     assert r.t == 6 and r.lr == 3e-4
+
+
+@pytest.mark.parametrize("opt", ["sgd", "lion"])
+def test_scheduled_sgd_and_lion_equal_host_steps(opt):
+    w, a, ga, la = make(44, opt)
+    _, b, gb, lb = make(44, opt)
+    hp = dict(W.HPARAMS[opt])
+    sched = F.DeviceSchedule(hp, t=0, optimizer=opt)
+    for t in range(1, 7):
+        if t == 4:
+            hp["lr"] = hp["lr"] / 3
+            sched.set("lr", hp["lr"])
+        if t == 5:
+            k = "momentum" if opt == "sgd" else "beta1"
+            hp[k] = 0.5
+            sched.set(k, 0.5)
+        for i in range(len(SIZES)):
+            g = W.draw_grad(w, i, t, "cuda")
+            ga[i].copy_(g)
+            gb[i].copy_(g)
+        F.step(la, opt, hp, t)
+        F.step_scheduled(lb, sched)
+        torch.cuda.synchronize()
+        same(a, b, f"{opt} step {t}")
+    assert sched.read().t == 6
 
 
 def test_captured_graph_replays_equal_eager_steps():
@@ -110,9 +135,10 @@ def test_device_scalars_equal_the_host_definition(hp):
         np.testing.assert_array_equal(dev.view(np.uint32), host.view(np.uint32), err_msg=str(t))
 
 
-def test_capturable_flash_adamw_in_a_graph():
-    """FlashAdamW(capturable=True): opt.step() captured once with static
-    gradients, replayed every step (an lr change pushed between replays with
+@pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
+def test_capturable_optimizer_in_a_graph(kind):
+    """capturable=True: opt.step() captured once with static gradients,
+    replayed every step (an lr change pushed between replays with
     update_schedules), equals the eager optimizer bit for bit; its
     checkpoint carries the device step count."""
     from compressed_adamw_state_amd import optim as O
@@ -121,9 +147,12 @@ def test_capturable_flash_adamw_in_a_graph():
     init = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
     ref = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
     cap = [torch.nn.Parameter(torch.from_numpy(x).cuda()) for x in init]
-    kw = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
-    ro = O.FlashAdamW(ref, **kw)
-    co = O.FlashAdamW(cap, capturable=True, **kw)
+    cls, kw = {"adamw": (O.FlashAdamW, dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8,
+                                            weight_decay=0.01)),
+               "sgd": (O.FlashSGD, dict(lr=0.05, momentum=0.9, weight_decay=1e-4)),
+               "lion": (O.FlashLion, dict(lr=1e-4, betas=(0.9, 0.99), weight_decay=0.1))}[kind]
+    ro = cls(ref, **kw)
+    co = cls(cap, capturable=True, **kw)
     static = [torch.zeros_like(p) for p in cap]            # BF16, like the parameters
     for p, g in zip(cap, static):
         p.grad = g
@@ -138,7 +167,7 @@ def test_capturable_flash_adamw_in_a_graph():
     for t in range(1, 6):
         if t == 3:
             for o in (ro, co):
-                o.param_groups[0]["lr"] = 5e-4
+                o.param_groups[0]["lr"] = kw["lr"] / 2
             co.update_schedules()
         gs = [torch.from_numpy((rng.standard_normal(s) * 1e-3).astype(np.float32))
               .to(torch.bfloat16).cuda() for s in shapes]
