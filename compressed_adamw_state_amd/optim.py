@@ -82,6 +82,31 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 self._sched_hp.append(self._hp(group))
         if gradient_release:
             self._install_release_hooks()
+        self._ready = True
+
+    def add_param_group(self, param_group: dict) -> None:
+        """torch.optim's add_param_group; after construction the new group's
+        parameters get their compressed state, list, schedule and hooks."""
+        super().add_param_group(param_group)
+        if not getattr(self, "_ready", False):
+            return                               # during __init__: set up there
+        gi = len(self.param_groups) - 1
+        group = self.param_groups[gi]
+        kind = self._state_kind(group)
+        for p in group["params"]:
+            self._init_param(p, kind)
+        states = [self.state[p]["flash"] for p in group["params"]]
+        lst = F.FlashoptList(states, [None] * len(states), optimizer=kind) if states else None
+        self._lists.append(lst)
+        if self.capturable:
+            if kind != self.kind:
+                raise ValueError("capturable needs the compressed state in every group")
+            self._sched.append(F.DeviceSchedule(self._hp(group), t=0, optimizer=self.kind)
+                               if lst else None)
+            self._sched_hp.append(self._hp(group))
+        if self.gradient_release:
+            for pi, p in enumerate(group["params"]):
+                self._install_release_hook(gi, pi, p)
 
     # -- state -----------------------------------------------------------------
     def _state_kind(self, group) -> str:
@@ -205,25 +230,28 @@ class _FlashOptimizer(torch.optim.Optimizer):
     def _install_release_hooks(self) -> None:
         for gi, group in enumerate(self.param_groups):
             for pi, p in enumerate(group["params"]):
-                def hook(param, gi=gi, pi=pi):
-                    g = param.grad
-                    if g.dtype != torch.bfloat16 or not g.is_contiguous():
-                        raise ValueError("FlashOptim expects contiguous BF16 gradients")
-                    stream = None
-                    if self._side:
-                        # every backward node that read this parameter has run
-                        # (its gradient is complete), so updating it concurrently
-                        # with the rest of backward is safe
-                        stream = self._side[self._rr % len(self._side)]
-                        self._rr += 1
-                        stream.wait_stream(torch.cuda.current_stream())
-                        g.record_stream(stream)  # the gradient outlives its release
-                    t = self.state[param]["step"] + 1
-                    F.step_one(self._lists[gi], self.kind, pi, g.view(-1),
-                               self._hp(self.param_groups[gi]), t, stream)
-                    self.state[param]["step"] = t
-                    param.grad = None            # gradient release: 2 B/param freed early
-                self._hooks.append(p.register_post_accumulate_grad_hook(hook))
+                self._install_release_hook(gi, pi, p)
+
+    def _install_release_hook(self, gi: int, pi: int, p: torch.Tensor) -> None:
+        def hook(param, gi=gi, pi=pi):
+            g = param.grad
+            if g.dtype != torch.bfloat16 or not g.is_contiguous():
+                raise ValueError("FlashOptim expects contiguous BF16 gradients")
+            stream = None
+            if self._side:
+                # every backward node that read this parameter has run
+                # (its gradient is complete), so updating it concurrently
+                # with the rest of backward is safe
+                stream = self._side[self._rr % len(self._side)]
+                self._rr += 1
+                stream.wait_stream(torch.cuda.current_stream())
+                g.record_stream(stream)  # the gradient outlives its release
+            t = self.state[param]["step"] + 1
+            F.step_one(self._lists[gi], self.kind, pi, g.view(-1),
+                       self._hp(self.param_groups[gi]), t, stream)
+            self.state[param]["step"] = t
+            param.grad = None            # gradient release: 2 B/param freed early
+        self._hooks.append(p.register_post_accumulate_grad_hook(hook))
 
     # -- checkpoints -------------------------------------------------------------
     def _sync_steps(self) -> None:

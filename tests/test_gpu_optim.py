@@ -264,3 +264,28 @@ def test_parameters_without_gradients_are_skipped():
     # and the per-parameter counts survive a checkpoint
     sd = opt.state_dict()
     assert [sd["state"][i]["step"] for i in range(len(params))] == counts
+
+
+def test_add_param_group_after_construction():
+    """torch.optim's add_param_group after construction: the new group gets
+    its compressed state (and its own hyper-parameters) and is stepped like
+    the first, matching the oracle."""
+    rng = np.random.default_rng(9)
+    a0 = (rng.standard_normal(4097) * 0.02).astype(np.float32)
+    b0 = (rng.standard_normal((33, 64)) * 0.02).astype(np.float32)
+    pa = torch.nn.Parameter(torch.from_numpy(a0).cuda())
+    pb = torch.nn.Parameter(torch.from_numpy(b0).cuda())
+    opt = make_opt("adamw", [pa])
+    hp_b = dict(HP["adamw"], lr=3e-4)
+    opt.add_param_group({"params": [pb], "lr": hp_b["lr"]})
+    assert pb.dtype == torch.bfloat16 and "flash" in opt.state[pb]
+    oa, ob = oracle.State(a0, "adamw"), oracle.State(b0.reshape(-1), "adamw")
+    for t in (1, 2):
+        for p, o, hp in ((pa, oa, HP["adamw"]), (pb, ob, hp_b)):
+            g = torch.from_numpy((rng.standard_normal(p.shape) * 1e-3).astype(np.float32))
+            g = g.to(torch.bfloat16)
+            p.grad = g.cuda()
+            oracle.step(o, g.view(torch.int16).numpy().view(np.uint16).reshape(-1), t, hp)
+        opt.step()
+        torch.cuda.synchronize()
+        compare(opt, [pa, pb], [oa, ob], f"step {t}")
