@@ -18,6 +18,12 @@
 // with DPP, its two FP16 scales one 32-bit word.  Whole tiles take an
 // unguarded vector path; the last tile of a tensor takes a guarded
 // element-wise path.
+//
+// Also here: the uncompressed step for layers with compression switched off
+// (FP32 master weight and moments in 512-element blocks), the scheduled steps
+// whose scalars live in device memory (so a HIP graph can replay them), the
+// flat split / quantise kernels, the codec-ablation kernels, list maintenance
+// and a bandwidth probe of the step's access pattern.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
