@@ -8,8 +8,9 @@ and gradients are resident in HBM before timing starts; two gradient sets are
 drawn up front and the steps alternate between them (two list handles over
 the same state).
 
-Prints one JSON line (rank 0).  --gpus N > 1 is refused: this build runs on
-one GPU.
+Prints one JSON line (rank 0).  --gpus N > 1 is refused: the step is measured
+on one GPU (it shards with no exchange inside the step; no multi-GPU run is
+provided).
 """
 from __future__ import annotations
 
@@ -293,8 +294,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs the fused step on one GPU only; --gpus must be 1 "
-              "(sharding is described in DESIGN.md, not run)", file=sys.stderr)
+        print("bench.py: the fused step is measured on one GPU only; --gpus must be 1 "
+              "(the step shards with no exchange inside it, but no multi-GPU run is "
+              "provided)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)

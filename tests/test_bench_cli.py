@@ -1,5 +1,5 @@
 """bench.py's command-line contract that needs no GPU: more than one GPU is
-refused with a message (this build measures one GPU's share; sharding is a
+refused with a message (one GPU's share is what is measured; sharding is a
 design note), and the algorithmic byte counts per parameter."""
 import os
 import subprocess
