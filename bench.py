@@ -204,6 +204,42 @@ def wrapper_adamw(steps: int, stream) -> dict:
             "algorithmic_gb_s": algorithmic_bytes(w) / (ms * 1e-3) / 1e9}
 
 
+def graph_replay_adamw(steps: int) -> dict:
+    """The scheduled AdamW step (step counter and scalars in a device
+    schedule) captured once in a HIP graph and replayed `steps` times on the
+    Llama-3.1-8B list: the path a graph-captured training loop takes."""
+    w = W.WORKLOADS["llama31_8b"]
+    states, grads, lists = build_state(w, grad_sets=1)
+    sched = F.DeviceSchedule(w.hparams, t=0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            F.flashopt_adamw_step_scheduled(lists[0], sched)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for k in range(steps):
+        graph.replay()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
+    t_dev = sched.read().t
+    del graph, sched, states, grads, lists
+    torch.cuda.synchronize()
+    ms = float(np.median(per))
+    return {"workload": "llama31_8b", "optimizer": "adamw, scheduled step replayed from a HIP graph",
+            "params": w.numel, "replays": steps, "device_step_count": t_dev,
+            "step_ms_median": ms, "step_ms_min": float(per.min()),
+            "params_s": w.numel / (ms * 1e-3),
+            "algorithmic_gb_s": algorithmic_bytes(w) / (ms * 1e-3) / 1e9}
+
+
 def stream_probe(lst, stream, bytes_step: int, reps: int = 5):
     """The step's exact loads and stores with no arithmetic (flashopt_stream_probe):
     the practical floor of its access pattern.  Overwrites the state."""
@@ -400,7 +436,8 @@ def main():
                                    other_optimizer("gpt2_small", 10, stream),
                                    other_optimizer("llama2_13b", 5, stream),
                                    other_optimizer("llama2_13b", 5, stream, release_streams=2),
-                                   wrapper_adamw(10, stream)]
+                                   wrapper_adamw(10, stream),
+                                   graph_replay_adamw(10)]
         for o in out["other_optimizers"]:
             log(f"bench: {o['optimizer']} {o['workload']}: {o['step_ms_median']:.3f} ms/step")
     if args.copy_bytes:

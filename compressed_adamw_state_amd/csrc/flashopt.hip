@@ -679,17 +679,24 @@ __global__ void lion_schedule_init_kernel(flashopt_lion_schedule* S, flashopt_li
     for (int i = 0; i < 6; ++i) S->scalars[i] = 0u;
 }
 
+// A list's steps never read the single-tensor descriptor; this zero one gives
+// step_body an address that is not a per-wave local (which would live in
+// scratch memory).
+__device__ const DevTensor kNoTensor = {};
+
 // The step with its scalars read from a schedule's `scalars` words (written
 // by the advance kernel launched just before on the same stream).
 template <int kOpt>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel_scheduled(
     const DevTensor* __restrict__ table, const int64_t* __restrict__ tile_begin, int32_t count,
     int64_t total_tiles, const uint32_t* __restrict__ scalars) {
-    StepScalars P{};
-    if (kOpt == kAdamW) __builtin_memcpy(&P.a, scalars, sizeof P.a);   // uniform: scalar loads
-    else if (kOpt == kSgd) __builtin_memcpy(&P.s, scalars, sizeof P.s);
-    else __builtin_memcpy(&P.l, scalars, sizeof P.l);
-    step_body<kOpt, false>(table, tile_begin, count, total_tiles, DevTensor{}, P);
+    // typed loads of the kernel-argument pointer (uniform: scalar loads into
+    // registers; a copy through the address of a local would go to scratch)
+    StepScalars P;
+    if (kOpt == kAdamW) P.a = *reinterpret_cast<const AdamScalars*>(scalars);
+    else if (kOpt == kSgd) P.s = *reinterpret_cast<const SgdScalars*>(scalars);
+    else P.l = *reinterpret_cast<const LionScalars*>(scalars);
+    step_body<kOpt, false>(table, tile_begin, count, total_tiles, kNoTensor, P);
 }
 
 // ---- the uncompressed step (_FP32 kinds) -------------------------------------
