@@ -1075,7 +1075,7 @@ __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
-    cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
+    cur.start(table, tile_begin, count, kNoTensor, total_tiles, wave);
     for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const GTensor& T = cur.T;
@@ -1195,7 +1195,7 @@ __global__ __launch_bounds__(256) void zero_fp32_kernel(const DevTensor* __restr
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
-    cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
+    cur.start(table, tile_begin, count, kNoTensor, total_tiles, wave);
     for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const GTensor& T = cur.T;
@@ -1238,7 +1238,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
     if (wave >= total_tiles) return;
     TileCursor cur;
-    cur.start(table, tile_begin, count, DevTensor{}, total_tiles, wave);
+    cur.start(table, tile_begin, count, kNoTensor, total_tiles, wave);
     for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const GTensor& T = cur.T;
