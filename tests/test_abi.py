@@ -5,7 +5,6 @@ import ctypes
 import os
 import re
 
-import pytest
 
 from compressed_adamw_state_amd import flashopt as F
 
