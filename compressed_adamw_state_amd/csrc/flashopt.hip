@@ -966,8 +966,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* q, const
             const float d = m_step(s16);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int32_t c = (int32_t)(int8_t)(uint8_t)u[j];
-                o[j] = kCompand ? dequant_m(c, d) : (float)c * d;
+                const int32_t code = (int32_t)(int8_t)(uint8_t)u[j];
+                o[j] = kCompand ? dequant_m(code, d) : (float)code * d;
             }
         } else {
             const float d = v_step(s16);
