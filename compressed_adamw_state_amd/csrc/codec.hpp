@@ -82,19 +82,24 @@ __device__ __forceinline__ float unsplit_bits(uint32_t tbits, int32_t rho) {
 }
 
 // The same rebuild as one FMA: (rho*K8*2^-8) * 2^(E-127) is a power-of-two
-// scaling of the first product, exact when the clamped field E is at least 16
-// (|rho| >= 1 makes the first product at least 2^-15), so fma rounds once to
-// the same t + d.  Folds E into emin; the caller redoes the lane with
-// unsplit_bits() when emin < 16.
-__device__ __forceinline__ float unsplit_fma(uint32_t tbits, int32_t rho, uint32_t& emin) {
+// scaling of the first product, exact when the field E is at least 16 (|rho|
+// >= 1 makes the first product at least 2^-15), so fma rounds once to the same
+// t + d.  The field is taken unclamped and folded into emin / emax: for E in
+// [16, 254] the clamp of unsplit_bits() changes nothing, and the caller redoes
+// the lane with unsplit_bits() when any field falls outside.
+__device__ __forceinline__ float unsplit_fma(uint32_t tbits, int32_t rho, uint32_t& emin,
+                                             uint32_t& emax) {
     const float t = as_f32(tbits);
-    const uint32_t e = min(max(tbits & 0x7F800000u, 0x00800000u), 0x7F000000u);
+    const uint32_t e = tbits & 0x7F800000u;
     emin = min(emin, e);
+    emax = max(emax, e);
     const float c = (float)rho * as_f32(kK8Bits - 0x04000000u);   // K8 * 2^-8
     return __builtin_fmaf(c, as_f32(e), t);
 }
 
-__device__ __forceinline__ bool unsplit_fma_ok(uint32_t emin) { return emin >= (16u << 23); }
+__device__ __forceinline__ bool unsplit_fma_ok(uint32_t emin, uint32_t emax) {
+    return emin >= (16u << 23) && emax <= 0x7F000000u;             // E in [16, 254]
+}
 
 __device__ __forceinline__ float unsplit(uint32_t tb, int32_t rho) {
     return unsplit_bits(tb << 16, rho);

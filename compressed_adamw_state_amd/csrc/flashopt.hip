@@ -355,21 +355,55 @@ struct Raw {                        // one lane's packed loads of one sub-tile
     uint32_t ms, vs;                // the group's FP16 scales
 };
 
+// Addresses inside one full tile: the wave-uniform byte address of the tile's
+// first element in each array, and the lane's constant byte offsets within a
+// sub-tile.  Every access is a scalar base plus a 32-bit lane offset (the
+// global_load/store saddr form), so no per-lane 64-bit address arithmetic is
+// issued per sub-tile.
 template <int kOpt>
-__device__ __forceinline__ void load_raw(const GTensor& T, int64_t e, Raw& R) {
-    const int64_t g = e >> 5;
-    const GLOBAL uint8_t* rec = T.codes + (e >> 3) * Layout<kOpt>::kRec;
-    R.th = ld4(T.theta + e);
-    R.gr = ld4(T.grad + e);
+struct TileAddr {
+    static constexpr int kSubEl = kSubTile * 2;                               // BF16 bytes
+    static constexpr int kSubRec = kSubTile / 8 * Layout<kOpt>::kRec;
+    static constexpr int kSubScl = kSubTile / kGroup * Layout<kOpt>::kScl * 2;
+    GLOBAL uint8_t* theta;
+    const GLOBAL uint8_t* grad;
+    GLOBAL uint8_t* codes;
+    GLOBAL uint8_t* scales;
+    uint32_t el, rec, scl;          // lane offsets: 8 BF16, one record, the group's scales
+
+    __device__ __forceinline__ TileAddr(const GTensor& T, int64_t e0, int lane)
+        : theta((GLOBAL uint8_t*)(T.theta + e0)),
+          grad((const GLOBAL uint8_t*)(T.grad + e0)),
+          codes(T.codes + (e0 >> 3) * Layout<kOpt>::kRec),
+          scales((GLOBAL uint8_t*)(T.scales + (e0 >> 5) * Layout<kOpt>::kScl)),
+          el((uint32_t)lane * (kLaneElems * 2)),
+          rec((uint32_t)lane * Layout<kOpt>::kRec),
+          scl((uint32_t)(lane >> 2) * (Layout<kOpt>::kScl * 2)) {}
+
+    __device__ __forceinline__ GLOBAL uint8_t* th(int k) const { return theta + k * kSubEl + el; }
+    __device__ __forceinline__ const GLOBAL uint8_t* gr(int k) const {
+        return grad + k * kSubEl + el;
+    }
+    __device__ __forceinline__ GLOBAL uint8_t* rc(int k) const { return codes + k * kSubRec + rec; }
+    __device__ __forceinline__ GLOBAL uint8_t* sc(int k) const {
+        return scales + k * kSubScl + scl;
+    }
+};
+
+template <int kOpt>
+__device__ __forceinline__ void load_raw(const TileAddr<kOpt>& A, int k, Raw& R) {
+    const GLOBAL uint8_t* rec = A.rc(k);
+    R.th = ld4(A.th(k));
+    R.gr = ld4(A.gr(k));
     R.rho = ld2(rec + kRhoOff);
     R.qm = ld2(rec + kMOff);
     if (kOpt == kAdamW) {
         R.qv = ld2(rec + kVOff);
-        const uint32_t w = *(const GLOBAL uint32_t*)(T.scales + 2 * g);   // m | v << 16
+        const uint32_t w = *(const GLOBAL uint32_t*)A.sc(k);             // m | v << 16
         R.ms = w & 0xFFFFu;
         R.vs = w >> 16;
     } else {
-        R.ms = T.scales[g];
+        R.ms = *(const GLOBAL uint16_t*)A.sc(k);
     }
 }
 
@@ -398,7 +432,7 @@ __device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32
 }
 
 template <int kOpt, bool kLinV = false>
-__device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane, const Raw& R,
+__device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int lane, const Raw& R,
                                           const StepScalars& P) {
     const AdamScalars& a = P.a;
     const SgdScalars& s = P.s;
@@ -407,10 +441,11 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
     uint32_t vmin = 0xFFFFFFFFu;           // min over (bits(v') - 1): flags 0 < v' < 2^-96
-    uint32_t tmin = 0xFFFFFFFFu;           // min clamped exponent field of theta'
+    uint32_t tmin = 0xFFFFFFFFu, tmax = 0u;  // exponent fields of theta'
 #pragma unroll
-    for (int j = 0; j < 8; ++j) theta_hat[j] = unsplit_fma(bf16_bits(R.th, j), s8(R.rho, j), tmin);
-    if (__builtin_expect(!unsplit_fma_ok(tmin), 0)) {
+    for (int j = 0; j < 8; ++j)
+        theta_hat[j] = unsplit_fma(bf16_bits(R.th, j), s8(R.rho, j), tmin, tmax);
+    if (__builtin_expect(!unsplit_fma_ok(tmin, tmax), 0)) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) theta_hat[j] = unsplit_bits(bf16_bits(R.th, j), s8(R.rho, j));
     }
@@ -539,15 +574,15 @@ __device__ __forceinline__ void step_fast(const GTensor& T, int64_t e, int lane,
         }
     }
     const uint2 orho = make_uint2(rc[0] ^ 0x80808080u, rc[1] ^ 0x80808080u);
-    const int64_t g = e >> 5;
-    GLOBAL uint8_t* rec = T.codes + (e >> 3) * Layout<kOpt>::kRec;
-    st4(T.theta + e, make_uint4(otb[0], otb[1], otb[2], otb[3]));
+    GLOBAL uint8_t* rec = A.rc(k);
+    st4(A.th(k), make_uint4(otb[0], otb[1], otb[2], otb[3]));
     st2(rec + kRhoOff, orho);
     st2(rec + kMOff, oqm);
     if (kOpt == kAdamW) st2(rec + kVOff, make_uint2(qv0, qv1));
     if ((lane & 3) == 0) {
-        if (kOpt == kAdamW) *(GLOBAL uint32_t*)(T.scales + 2 * g) = sm16 | (sv16 << 16);
-        else T.scales[g] = (uint16_t)sm16;
+        if (kOpt == kAdamW)                          // m | v << 16 in one v_perm
+            *(GLOBAL uint32_t*)A.sc(k) = __builtin_amdgcn_perm(sv16, sm16, 0x05040100u);
+        else *(GLOBAL uint16_t*)A.sc(k) = (uint16_t)sm16;
     }
 }
 
@@ -559,14 +594,14 @@ template <int kOpt, bool kFull, bool kLinV>
 __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane,
                                           const StepScalars& P) {
     if (kFull) {
+        const TileAddr<kOpt> A(T, e0, lane);
         Raw R[2];
-        load_raw<kOpt>(T, e0 + lane * kLaneElems, R[0]);
-        if (kSubTiles > 1) load_raw<kOpt>(T, e0 + kSubTile + lane * kLaneElems, R[1]);
+        load_raw<kOpt>(A, 0, R[0]);
+        if (kSubTiles > 1) load_raw<kOpt>(A, 1, R[1]);
 #pragma unroll
         for (int k = 0; k < kSubTiles; ++k) {
-            step_fast<kOpt, kLinV>(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1], P);
-            if (k + 2 < kSubTiles)
-                load_raw<kOpt>(T, e0 + (k + 2) * kSubTile + lane * kLaneElems, R[k & 1]);
+            step_fast<kOpt, kLinV>(A, k, lane, R[k & 1], P);
+            if (k + 2 < kSubTiles) load_raw<kOpt>(A, k + 2, R[k & 1]);
         }
     } else {
         for (int k = 0; k < kSubTiles; ++k) {
@@ -1219,15 +1254,16 @@ __global__ __launch_bounds__(256) void zero_fp32_kernel(const DevTensor* __restr
 // and one XOR per word in place of the update (theta' ^= g, rho ^= q_m,
 // q_m ^= q_v, q_v ^= rho, both scales ^= 1).  Its time is the practical floor
 // of the step's access pattern on this device.
-__device__ __forceinline__ void probe_sub(const GTensor& T, int64_t e, int lane, const Raw& R) {
-    GLOBAL uint8_t* rec = T.codes + (e >> 3) * Layout<kAdamW>::kRec;
-    st4(T.theta + e, make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
-                                R.th.w ^ R.gr.w));
+__device__ __forceinline__ void probe_sub(const TileAddr<kAdamW>& A, int k, int lane,
+                                          const Raw& R) {
+    GLOBAL uint8_t* rec = A.rc(k);
+    st4(A.th(k), make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
+                            R.th.w ^ R.gr.w));
     st2(rec + kRhoOff, make_uint2(R.rho.x ^ R.qm.x, R.rho.y ^ R.qm.y));
     st2(rec + kMOff, make_uint2(R.qm.x ^ R.qv.x, R.qm.y ^ R.qv.y));
     st2(rec + kVOff, make_uint2(R.qv.x ^ R.rho.x, R.qv.y ^ R.rho.y));
     if ((lane & 3) == 0)
-        *(GLOBAL uint32_t*)(T.scales + 2 * (e >> 5)) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
+        *(GLOBAL uint32_t*)A.sc(k) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
 }
 
 __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict__ table,
@@ -1244,14 +1280,14 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
         const GTensor& T = cur.T;
         const int64_t e0 = (tile - cur.begin) * kTile;
         if (e0 + kTile <= T.numel) {
+            const TileAddr<kAdamW> A(T, e0, lane);
             Raw R[2];
-            load_raw<kAdamW>(T, e0 + lane * kLaneElems, R[0]);
-            if (kSubTiles > 1) load_raw<kAdamW>(T, e0 + kSubTile + lane * kLaneElems, R[1]);
+            load_raw<kAdamW>(A, 0, R[0]);
+            if (kSubTiles > 1) load_raw<kAdamW>(A, 1, R[1]);
 #pragma unroll
             for (int k = 0; k < kSubTiles; ++k) {
-                probe_sub(T, e0 + k * kSubTile + lane * kLaneElems, lane, R[k & 1]);
-                if (k + 2 < kSubTiles)
-                    load_raw<kAdamW>(T, e0 + (k + 2) * kSubTile + lane * kLaneElems, R[k & 1]);
+                probe_sub(A, k, lane, R[k & 1]);
+                if (k + 2 < kSubTiles) load_raw<kAdamW>(A, k + 2, R[k & 1]);
             }
         } else {
             for (int k = 0; k < kSubTiles; ++k) {

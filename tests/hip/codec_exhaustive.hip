@@ -108,16 +108,19 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
         }
         // 11: unsplit as one FMA == unsplit_bits for every BF16 theta' and code
         //     byte (first 2^24 inputs: theta' = bits >> 8, rho = low byte), when
-        //     the flag allows it; the flag is raised exactly for fields below 16
+        //     the flag allows it; the flag is raised exactly for fields outside
+        //     [16, 254]
         if (bits < (1u << 24)) {
             const uint32_t tbits = (bits >> 8) << 16;
             const int32_t rho = (int32_t)(int8_t)(uint8_t)(bits & 0xFFu);
-            uint32_t emin = 0xFFFFFFFFu;
-            const float f = unsplit_fma(tbits, rho, emin);
+            uint32_t emin = 0xFFFFFFFFu, emax = 0u;
+            const float f = unsplit_fma(tbits, rho, emin, emax);
             const float g = unsplit_bits(tbits, rho);
             const uint32_t E = (tbits >> 23) & 0xFFu;
-            const bool ok = unsplit_fma_ok(emin);
-            if ((ok && as_u32(f) != as_u32(g)) || ok != (E >= 16u)) { c[11]++; ex[11] = bits; }
+            const bool ok = unsplit_fma_ok(emin, emax);
+            if ((ok && as_u32(f) != as_u32(g)) || ok != (E >= 16u && E <= 254u)) {
+                c[11]++; ex[11] = bits;
+            }
         }
         // 6: the general path is used for 0 < x < 2^-96 only
         if (!(bits >> 31) && sqrt_fast_bad(x) != (x > 0.0f && x < 0x1p-96f)) {
