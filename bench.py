@@ -85,9 +85,10 @@ def read_profile(kind: str, workload: str, kernel_hash: str) -> dict:
 def build_state(w: W.Workload, grad_sets: int):
     dev = torch.device("cuda")
     states = []
+    arena = F.StateArena([spec.numel for spec in w.tensors], w.optimizer, dev)
     for i, spec in enumerate(w.tensors):
         theta = W.draw_theta(w, i, dev)
-        st = F.TensorState(spec.numel, w.optimizer, dev)
+        st = arena.state(i)
         F.flashopt_tensor_init(st, theta)
         del theta
         states.append(st)

@@ -357,9 +357,8 @@ struct Raw {                        // one lane's packed loads of one sub-tile
 
 // Addresses inside one full tile: the wave-uniform byte address of the tile's
 // first element in each array, and the lane's constant byte offsets within a
-// sub-tile.  Every access is a scalar base plus a 32-bit lane offset (the
-// global_load/store saddr form), so no per-lane 64-bit address arithmetic is
-// issued per sub-tile.
+// sub-tile.  Every access is a scalar base plus a 32-bit lane offset, so no
+// per-lane 64-bit address arithmetic is issued per sub-tile.
 template <int kOpt>
 struct TileAddr {
     static constexpr int kSubEl = kSubTile * 2;                               // BF16 bytes
@@ -431,6 +430,12 @@ __device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32
     return __builtin_amdgcn_perm(cd, ab, 0x05040100u);                 // a0 b0 c0 d0
 }
 
+// One lane's 8 elements of a full sub-tile.  The per-element part (rebuilt
+// weight, dequantised moments, update, the new weight's split) uses short
+// exact sequences; each one's condition of exactness is folded into a flag,
+// and a lane with a raised flag redoes that operation for its eight elements
+// with the general sequence.  The group part (maxima over the quad of lanes,
+// FP16 scales, code factors, codes) follows once the new weight is stored.
 template <int kOpt, bool kLinV = false>
 __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int lane, const Raw& R,
                                           const StepScalars& P) {
@@ -490,11 +495,6 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
             for (int j = 0; j < 8; ++j)                 // 0 < v' < 2^-96: IEEE square root
                 if (sqrt_fast_bad(v_new[j])) w[j] = __builtin_sqrtf(v_new[j]);
         }
-    }
-    // group maxima of |z| and w as floats (== the integer max of the bit patterns
-    // for every finite value)
-    float amax_m = 0.0f, amax_v = 0.0f;
-    if (kOpt == kAdamW) {
         // u = m' / (w*kappa + eps) by div_rn; a lane with any quotient outside
         // the window redoes its eight with the IEEE division
         float u[8];
@@ -523,13 +523,38 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
             const float stp = a.alpha * u[j];
             tn[j] = decayed - stp;
             if (kLinV) w[j] = v_new[j];                // the codes quantise v' itself
-            amax_v = fmaxf(amax_v, w[j]);
         }
     }
 #pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = phi_m_half_fast(m_new[j]);   // phi_m(m') / 2
+    // new theta' and rho: BF16 RNE convert and the biased code of the remainder
+    uint32_t otb[4];
+    uint32_t rc[2] = {0u, 0u};                      // rho + 128, four per word
+    uint32_t emin = 0xFFFFFFFFu, emax = 0u;         // exponent fields of the new theta'
+    otb[0] = split2_fast<0>(tn[0], tn[1], rc[0], emin, emax);
+    otb[1] = split2_fast<2>(tn[2], tn[3], rc[0], emin, emax);
+    otb[2] = split2_fast<0>(tn[4], tn[5], rc[1], emin, emax);
+    otb[3] = split2_fast<2>(tn[6], tn[7], rc[1], emin, emax);
+    if (__builtin_expect(!split_fast_ok(emin, emax), 0)) {
+        // some theta' exponent outside [14, 254] (tiny, zero or non-finite): general split
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const Split s0 = split(tn[2 * p]), s1 = split(tn[2 * p + 1]);
+            otb[p] = s0.tb | (s1.tb << 16);
+            const int sh = 16 * (p & 1);
+            const uint32_t pair = ((uint32_t)(s0.rho + 128) & 0xFFu) |
+                                  (((uint32_t)(s1.rho + 128) & 0xFFu) << 8);
+            rc[p >> 1] = (rc[p >> 1] & ~(0xFFFFu << sh)) | (pair << sh);
+        }
+    }
+    st4(A.th(k), make_uint4(otb[0], otb[1], otb[2], otb[3]));
+    // group maxima of |z| and w as floats (== the integer max of the bit patterns
+    // for every finite value)
+    float amax_m = 0.0f, amax_v = 0.0f;
+#pragma unroll
     for (int j = 0; j < 8; ++j) {
-        z[j] = phi_m_half_fast(m_new[j]);             // phi_m(m') / 2
         amax_m = fmaxf(amax_m, fabsf(z[j]));
+        if (kOpt == kAdamW) amax_v = fmaxf(amax_v, w[j]);
     }
     const uint32_t sm16 =
         group_scale(as_u32(2.0f * as_f32(quad_max_u32(as_u32(amax_m)))), 0x3FFFu);
@@ -554,28 +579,8 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
     for (int j = 0; j < 8; ++j) mb[j] = code_m_bits(z[j], rm);
     const uint2 oqm = make_uint2(pack_lo_bytes(mb[0], mb[1], mb[2], mb[3]),
                                  pack_lo_bytes(mb[4], mb[5], mb[6], mb[7]));
-    uint32_t otb[4];
-    uint32_t rc[2] = {0u, 0u};                      // rho + 128, four per word
-    uint32_t emin = 0xFFFFFFFFu, emax = 0u;         // exponent fields of the new theta'
-    otb[0] = split2_fast<0>(tn[0], tn[1], rc[0], emin, emax);
-    otb[1] = split2_fast<2>(tn[2], tn[3], rc[0], emin, emax);
-    otb[2] = split2_fast<0>(tn[4], tn[5], rc[1], emin, emax);
-    otb[3] = split2_fast<2>(tn[6], tn[7], rc[1], emin, emax);
-    if (__builtin_expect(!split_fast_ok(emin, emax), 0)) {
-        // some theta' exponent outside [14, 254] (tiny, zero or non-finite): general split
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const Split s0 = split(tn[2 * p]), s1 = split(tn[2 * p + 1]);
-            otb[p] = s0.tb | (s1.tb << 16);
-            const int sh = 16 * (p & 1);
-            const uint32_t pair = ((uint32_t)(s0.rho + 128) & 0xFFu) |
-                                  (((uint32_t)(s1.rho + 128) & 0xFFu) << 8);
-            rc[p >> 1] = (rc[p >> 1] & ~(0xFFFFu << sh)) | (pair << sh);
-        }
-    }
     const uint2 orho = make_uint2(rc[0] ^ 0x80808080u, rc[1] ^ 0x80808080u);
     GLOBAL uint8_t* rec = A.rc(k);
-    st4(A.th(k), make_uint4(otb[0], otb[1], otb[2], otb[3]));
     st2(rec + kRhoOff, orho);
     st2(rec + kMOff, oqm);
     if (kOpt == kAdamW) st2(rec + kVOff, make_uint2(qv0, qv1));
@@ -1254,14 +1259,18 @@ __global__ __launch_bounds__(256) void zero_fp32_kernel(const DevTensor* __restr
 // and one XOR per word in place of the update (theta' ^= g, rho ^= q_m,
 // q_m ^= q_v, q_v ^= rho, both scales ^= 1).  Its time is the practical floor
 // of the step's access pattern on this device.
+__device__ __forceinline__ uint2 xor2(const uint2 a, const uint2 b) {
+    return make_uint2(a.x ^ b.x, a.y ^ b.y);
+}
+
 __device__ __forceinline__ void probe_sub(const TileAddr<kAdamW>& A, int k, int lane,
                                           const Raw& R) {
     GLOBAL uint8_t* rec = A.rc(k);
     st4(A.th(k), make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
                             R.th.w ^ R.gr.w));
-    st2(rec + kRhoOff, make_uint2(R.rho.x ^ R.qm.x, R.rho.y ^ R.qm.y));
-    st2(rec + kMOff, make_uint2(R.qm.x ^ R.qv.x, R.qm.y ^ R.qv.y));
-    st2(rec + kVOff, make_uint2(R.qv.x ^ R.rho.x, R.qv.y ^ R.rho.y));
+    st2(rec + kRhoOff, xor2(R.rho, R.qm));
+    st2(rec + kMOff, xor2(R.qm, R.qv));
+    st2(rec + kVOff, xor2(R.qv, R.rho));
     if ((lane & 3) == 0)
         *(GLOBAL uint32_t*)A.sc(k) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
 }

@@ -65,8 +65,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._lists: List[Optional[F.FlashoptList]] = []
         self._hooks = []
         for group in self.param_groups:
-            for p in group["params"]:
-                self._init_param(p, self._state_kind(group))
+            self._init_params(group["params"], self._state_kind(group))
         self._build_lists()
         # capturable: per group, the step counter and hyper-parameters in a
         # device schedule, so step() launches nothing that depends on host
@@ -93,8 +92,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         gi = len(self.param_groups) - 1
         group = self.param_groups[gi]
         kind = self._state_kind(group)
-        for p in group["params"]:
-            self._init_param(p, kind)
+        self._init_params(group["params"], kind)
         states = [self.state[p]["flash"] for p in group["params"]]
         lst = F.FlashoptList(states, [None] * len(states), optimizer=kind) if states else None
         self._lists.append(lst)
@@ -118,24 +116,33 @@ class _FlashOptimizer(torch.optim.Optimizer):
             return "adamw_linv"
         return self.kind
 
-    def _init_param(self, p: torch.Tensor, kind: str) -> None:
-        if not p.is_cuda:
-            raise ValueError("FlashOptim parameters must live on the GPU")
-        if p.dtype == torch.float32:
-            st = F.TensorState(p.numel(), kind, p.device)
-            F.flashopt_tensor_init(st, p.detach().reshape(-1).contiguous())
-            p.data = st.theta.view(p.shape)      # the model now computes with theta'
-        elif p.dtype == torch.bfloat16:
-            if not p.is_contiguous():
+    def _init_params(self, params, kind: str) -> None:
+        """Compressed state for one group's parameters: per device, their code
+        records and scales are slices of one buffer each (F.StateArena)."""
+        for p in params:
+            if not p.is_cuda:
+                raise ValueError("FlashOptim parameters must live on the GPU")
+            if p.dtype not in (torch.float32, torch.bfloat16):
+                raise ValueError(f"unsupported parameter dtype {p.dtype}")
+            if p.dtype == torch.bfloat16 and not p.is_contiguous():
                 raise ValueError("BF16 parameters must be contiguous")
-            # theta' is the parameter's own storage; the split of its exact FP32
-            # value rewrites the same BF16 bits and gives rho = 0
-            st = F.TensorState(p.numel(), kind, p.device, theta=p.data.view(-1))
-            F.flashopt_tensor_init(st, p.detach().reshape(-1).float())
-        else:
-            raise ValueError(f"unsupported parameter dtype {p.dtype}")
-        self.state[p]["flash"] = st
-        self.state[p]["step"] = 0                # this parameter's own t (as in torch.optim)
+        by_device = {}
+        for p in params:
+            by_device.setdefault(p.device, []).append(p)
+        for device, ps in by_device.items():
+            arena = F.StateArena([p.numel() for p in ps], kind, device)
+            for i, p in enumerate(ps):
+                if p.dtype == torch.float32:
+                    st = arena.state(i)
+                    F.flashopt_tensor_init(st, p.detach().reshape(-1).contiguous())
+                    p.data = st.theta.view(p.shape)   # the model now computes with theta'
+                else:
+                    # theta' is the parameter's own storage; the split of its exact
+                    # FP32 value rewrites the same BF16 bits and gives rho = 0
+                    st = arena.state(i, theta=p.data.view(-1))
+                    F.flashopt_tensor_init(st, p.detach().reshape(-1).float())
+                self.state[p]["flash"] = st
+                self.state[p]["step"] = 0        # this parameter's own t (as in torch.optim)
 
     def _build_lists(self) -> None:
         self._lists = []

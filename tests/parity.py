@@ -73,10 +73,12 @@ class Run:
         opt = w.optimizer
         rng = np.random.default_rng(seed)
         self.states, self.grads, self.orc, self.samples = [], [], [], []
+        # the state in one StateArena, as bench.py lays it out
+        arena = F.StateArena([spec.numel for spec in w.tensors], opt, self.dev)
         for i, spec in enumerate(w.tensors):
             n = spec.numel
             theta = W.draw_theta(w, i, self.gen_dev)
-            st = F.TensorState(n, opt, self.dev)
+            st = arena.state(i)
             theta_d = theta.to(self.dev)
             F.flashopt_tensor_init(st, theta_d)
             self.states.append(st)

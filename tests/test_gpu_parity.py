@@ -265,6 +265,38 @@ def test_non_finite_gradients_stay_in_their_groups(opt):
             np.testing.assert_array_equal(f["v_scale"][gok], o.sv[gok])
 
 
+@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion", "adamw_fp32"])
+def test_arena_state_equals_per_tensor_state(opt):
+    """The same ragged list stepped with its state in one StateArena and with
+    one allocation per tensor: every theta', code and scale equal bit for bit
+    after each step (the layout inside each tensor's state is the same)."""
+    sizes = [4097, 0, 33, 2048 * 3, 1, (1 << 17) + 5]
+    rng = np.random.default_rng(17)
+    thetas = [torch.from_numpy((rng.standard_normal(n) * 0.02).astype(np.float32)).cuda()
+              for n in sizes]
+    arena = F.StateArena(sizes, opt, "cuda")
+    a = [arena.state(i) for i in range(len(sizes))]
+    b = [F.TensorState(n, opt, "cuda") for n in sizes]
+    for sa, sb, th in zip(a, b, thetas):
+        F.flashopt_tensor_init(sa, th)
+        F.flashopt_tensor_init(sb, th)
+    grads = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for n in sizes]
+    la, lb = F.FlashoptList(a, grads), F.FlashoptList(b, grads)
+    base = F.base_optimizer(opt)
+    hp = W.HPARAMS[base]
+    for t in (1, 2, 3):
+        for g in grads:
+            g.copy_(torch.from_numpy((rng.standard_normal(g.numel()) * 1e-3)
+                                     .astype(np.float32)).to(torch.bfloat16))
+        F.step(la, base, hp, t)
+        F.step(lb, base, hp, t)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a, b)):
+            assert torch.equal(sa.theta.view(torch.int16), sb.theta.view(torch.int16)), (t, i)
+            assert torch.equal(sa.codes, sb.codes), (t, i)
+            assert torch.equal(sa.scales, sb.scales), (t, i)
+
+
 def test_set_grads_and_state_zero():
     w = W.ragged([3000, 70], seed=14, steps=2)
     r = Run(w, "full")
