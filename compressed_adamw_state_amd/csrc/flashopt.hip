@@ -1381,8 +1381,10 @@ static AdamScalars adam_scalars(const flashopt_adamw_hparams& hp, int64_t t, dou
 static int check_adam(const flashopt_adamw_hparams* hp, int64_t step) {
     if (!hp) return FLASHOPT_ERR_NULL;
     if (step < 1) return FLASHOPT_ERR_STEP;
+    // eps is used as its binary32 rounding: it must not round to 0 (below
+    // 2^-150), or a zero second moment would divide 0 by 0
     if (!(hp->lr >= 0.0) || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
-        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps > 0.0) ||
+        !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !((float)hp->eps > 0.0f) ||
         !(hp->weight_decay >= 0.0) || !std::isfinite(hp->lr) || !std::isfinite(hp->eps) ||
         !std::isfinite(hp->weight_decay))
         return FLASHOPT_ERR_ARG;

@@ -9,9 +9,11 @@ missing or fails to load, every call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import List, Optional, Sequence
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -473,9 +475,20 @@ class DeviceSchedule:
 
     def set(self, name: str, value: float) -> None:
         """Write one of SETTABLE on the device (stream-ordered: takes effect
-        from the next step call or replay)."""
+        from the next step call or replay).  The device does not validate
+        what it reads, so the value is checked here against the ranges of the
+        hyper-parameter structs (include/flashopt.h)."""
         if name not in self.SETTABLE[self.optimizer]:
             raise ValueError(f"{name} is not settable on a {self.optimizer} schedule")
+        value = float(value)
+        if name in ("momentum", "beta1", "beta2"):
+            ok = 0.0 <= value < 1.0
+        elif name == "eps":
+            ok = math.isfinite(value) and float(np.float32(value)) > 0.0
+        else:                                    # lr, weight_decay
+            ok = math.isfinite(value) and value >= 0.0
+        if not ok:
+            raise ValueError(f"{name} = {value} is outside its range")
         o = getattr(self.struct, name).offset
         self.buf[o:o + 8].view(torch.float64).fill_(value)
 

@@ -149,7 +149,7 @@ typedef struct flashopt_adamw_hparams {
     double lr;            /* >= 0                                  */
     double beta1;         /* [0, 1)                                */
     double beta2;         /* [0, 1)                                */
-    double eps;           /* > 0                                   */
+    double eps;           /* > 0, and nonzero once rounded to binary32 (> 2^-150) */
     double weight_decay;  /* >= 0, decoupled (scaled by lr)        */
 } flashopt_adamw_hparams;
 

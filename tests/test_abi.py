@@ -5,6 +5,9 @@ import ctypes
 import os
 import re
 
+import pytest
+import torch
+
 
 from compressed_adamw_state_amd import flashopt as F
 
@@ -97,7 +100,8 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_numel(L) == 0
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 0, None) == -5
     for bad_hp in (F.AdamWHparams(-1, 0.9, 0.999, 1e-8, 0), F.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0),
-                   F.AdamWHparams(1e-3, 0.9, 0.999, 0.0, 0), F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, -1),
+                   F.AdamWHparams(1e-3, 0.9, 0.999, 0.0, 0), F.AdamWHparams(1e-3, 0.9, 0.999, 1e-46, 0),
+                   F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, -1),
                    F.AdamWHparams(float("nan"), 0.9, 0.999, 1e-8, 0)):
         assert lib.flashopt_adamw_step(L, ctypes.byref(bad_hp), 1, None) == -4
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == 0    # nothing to launch
@@ -160,3 +164,25 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_stream_probe(L, None) == -4                         # compressed only
     assert lib.flashopt_state_zero(L, None) == 0
     assert lib.flashopt_list_destroy(L) == 0
+
+
+def test_schedule_set_checks_ranges_on_the_host():
+    """DeviceSchedule.set writes device memory that no kernel validates, so it
+    checks each value first (a host buffer stands in for the device one)."""
+    for opt, good, bad in (("adamw", [("lr", 0.0), ("eps", 1e-45), ("weight_decay", 0.1)],
+                            [("lr", -1.0), ("lr", float("inf")), ("eps", 0.0), ("eps", 1e-46),
+                             ("eps", float("nan")), ("weight_decay", -0.1), ("beta1", 0.5)]),
+                           ("sgd", [("momentum", 0.0), ("lr", 0.1)],
+                            [("momentum", 1.0), ("momentum", -0.1), ("lr", float("nan"))]),
+                           ("lion", [("beta1", 0.99), ("beta2", 0.0)],
+                            [("beta2", 1.0), ("weight_decay", float("inf"))])):
+        s = F.DeviceSchedule.__new__(F.DeviceSchedule)
+        s.optimizer = opt
+        s.struct = F.DeviceSchedule._STRUCT[opt]
+        s.buf = torch.zeros(ctypes.sizeof(s.struct), dtype=torch.uint8)
+        for name, v in good:
+            s.set(name, v)
+            assert getattr(s.read(), name) == v
+        for name, v in bad:
+            with pytest.raises(ValueError):
+                s.set(name, v)
