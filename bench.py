@@ -241,6 +241,68 @@ def graph_replay_adamw(steps: int) -> dict:
             "algorithmic_gb_s": algorithmic_bytes(w) / (ms * 1e-3) / 1e9}
 
 
+def release_memory(iters: int, stream, layers: int = 32, width: int = 4096,
+                   batch: int = 8) -> dict:
+    """Gradient release end to end: forward + backward + FlashAdamW step of
+    a stack of `layers` BF16 linear layers (width x width, no bias; a small
+    batch, so the gradients are most of an iteration's transient memory),
+    with the step after backward and with gradient release on one and two
+    side streams.  Reports the peak of allocated memory during an iteration
+    above what stays resident (model + state), the saving per parameter, the
+    median time per iteration, and whether the weights after the timed
+    iterations are bit-identical across the three modes."""
+    from compressed_adamw_state_amd import optim as O
+    n = layers * width * width
+    x = torch.randn(batch, width, device="cuda", dtype=torch.bfloat16,
+                    generator=torch.Generator("cuda").manual_seed(11))
+    modes = {}
+    ref = None
+    for name, release, streams in (("step after backward", False, 1),
+                                   ("gradient release", True, 1),
+                                   ("gradient release, 2 streams", True, 2)):
+        torch.cuda.manual_seed(12)
+        model = torch.nn.Sequential(*[torch.nn.Linear(width, width, bias=False, device="cuda",
+                                                      dtype=torch.bfloat16)
+                                      for _ in range(layers)])
+        opt = O.FlashAdamW(model.parameters(), lr=1e-3, gradient_release=release,
+                           release_streams=streams)
+
+        def iteration():
+            model(x).float().pow(2).mean().backward()
+            opt.step()
+            opt.zero_grad(set_to_none=True)
+
+        iteration()
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record(stream)
+        for k in range(iters):
+            iteration()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(iters)])
+        w = torch.cat([p.detach().view(torch.int16).reshape(-1) for p in model.parameters()])
+        same = None if ref is None else bool(torch.equal(w, ref))
+        if ref is None:
+            ref = w
+        modes[name] = {"peak_transient_bytes": int(peak), "iteration_ms_median": float(np.median(per)),
+                       "weights_equal_step_after_backward": same}
+        del opt, model, w
+        torch.cuda.empty_cache()
+    base_peak = modes["step after backward"]["peak_transient_bytes"]
+    for name, m in modes.items():
+        m["saving_bytes_per_param"] = (base_peak - m["peak_transient_bytes"]) / n
+    del ref
+    torch.cuda.empty_cache()
+    return {"workload": f"{layers} x Linear({width}, {width}) BF16, batch {batch}",
+            "optimizer": "FlashAdamW, gradient release end to end", "params": n,
+            "iterations": iters, "modes": modes,
+            "step_ms_median": modes["gradient release"]["iteration_ms_median"]}
+
+
 def stream_probe(lst, stream, bytes_step: int, reps: int = 5):
     """The step's exact loads and stores with no arithmetic (flashopt_stream_probe):
     the practical floor of its access pattern.  Overwrites the state."""
@@ -438,7 +500,8 @@ def main():
                                    other_optimizer("llama2_13b", 5, stream),
                                    other_optimizer("llama2_13b", 5, stream, release_streams=2),
                                    wrapper_adamw(10, stream),
-                                   graph_replay_adamw(10)]
+                                   graph_replay_adamw(10),
+                                   release_memory(5, stream)]
         for o in out["other_optimizers"]:
             log(f"bench: {o['optimizer']} {o['workload']}: {o['step_ms_median']:.3f} ms/step")
     if args.copy_bytes:
