@@ -121,25 +121,51 @@ def copy_ceiling(nbytes: int, stream, reps: int = 5):
             "best_ms": best * 1e3, "gb_s": 8 * n / best / 1e9}
 
 
-def other_optimizer(name: str, steps: int, stream, release_streams: int = 1) -> dict:
+def release_buckets(sizes, bucket_bytes: int):
+    """Gradient-release buckets in backward order: (first, count) ranges of
+    consecutive tensors, each closed once its BF16 gradients reach
+    bucket_bytes (one tensor per bucket when bucket_bytes is 0)."""
+    out, hi = [], len(sizes) - 1
+    while hi >= 0:
+        lo, b = hi, 2 * sizes[hi]
+        while b < bucket_bytes and lo > 0:
+            lo -= 1
+            b += 2 * sizes[lo]
+        out.append((lo, hi - lo + 1))
+        hi = lo - 1
+    return out
+
+
+def other_optimizer(name: str, steps: int, stream, release_streams: int = 1,
+                    bucket_bytes: int = 0, release: bool = False) -> dict:
     """Time `steps` list steps of another optimizer's workload (after warm-up);
-    state built fresh, freed on return.  In gradient-release mode the per-tensor
-    launches go round-robin over `release_streams` streams (tensors are
-    independent, so one launch's tail can overlap the next); each step is
-    bracketed on `stream`."""
+    state built fresh, freed on return.  In gradient-release mode (the
+    workload's own, or `release`) the tensors are stepped in backward order,
+    one launch per tensor or, with bucket_bytes > 0, one range launch per
+    bucket of consecutive tensors (release_buckets); the launches go
+    round-robin over `release_streams` streams (tensors are independent, so
+    one launch's tail can overlap the next); each step is bracketed on
+    `stream`."""
     w = W.WORKLOADS[name]
+    release = release or w.release
     states, grads, lists = build_state(w, grad_sets=2)
     side = [stream] + [torch.cuda.Stream() for _ in range(release_streams - 1)]
+    buckets = release_buckets([t.numel for t in w.tensors], bucket_bytes)
 
     def one_step(k, t):
-        if w.release:            # gradient release: one launch per tensor, backward order
+        if release:              # gradient release, backward order
             start = torch.cuda.Event()
             start.record(stream)
             for s in side[1:]:
                 s.wait_event(start)
-            for j, i in enumerate(reversed(range(len(w.tensors)))):
-                F.step_one(lists[k % 2], w.optimizer, i, grads[k % 2][i], w.hparams, t,
-                           side[j % len(side)])
+            for j, (first, count) in enumerate(buckets):
+                if bucket_bytes > 0:
+                    F.step_range(lists[k % 2], w.optimizer, first,
+                                 grads[k % 2][first:first + count], w.hparams, t,
+                                 side[j % len(side)])
+                else:
+                    F.step_one(lists[k % 2], w.optimizer, first, grads[k % 2][first],
+                               w.hparams, t, side[j % len(side)])
             for s in side[1:]:
                 done = torch.cuda.Event()
                 done.record(s)
@@ -162,8 +188,9 @@ def other_optimizer(name: str, steps: int, stream, release_streams: int = 1) -> 
     ms = float(np.median(per))
     gbs = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
     return {"workload": name, "optimizer": w.optimizer, "params": w.numel,
-            "launches_per_step": len(w.tensors) if w.release else 1,
-            "streams": len(side) if w.release else 1,
+            "gradient_release": release, "bucket_bytes": bucket_bytes if release else None,
+            "launches_per_step": (len(buckets) * (2 if bucket_bytes > 0 else 1)) if release else 1,
+            "streams": len(side) if release else 1,
             "bytes_per_param": algorithmic_bytes(w) / w.numel, "step_ms_median": ms,
             "step_ms_min": float(per.min()), "params_s": w.numel / (ms * 1e-3),
             "algorithmic_gb_s": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS}
@@ -499,6 +526,13 @@ def main():
                                    other_optimizer("gpt2_small", 10, stream),
                                    other_optimizer("llama2_13b", 5, stream),
                                    other_optimizer("llama2_13b", 5, stream, release_streams=2),
+                                   other_optimizer("llama2_13b", 5, stream,
+                                                   bucket_bytes=64 << 20),
+                                   other_optimizer("llama2_13b", 5, stream, release_streams=2,
+                                                   bucket_bytes=64 << 20),
+                                   other_optimizer("gpt2_small", 10, stream, release=True),
+                                   other_optimizer("gpt2_small", 10, stream, release=True,
+                                                   bucket_bytes=16 << 20),
                                    wrapper_adamw(10, stream),
                                    graph_replay_adamw(10),
                                    release_memory(5, stream)]

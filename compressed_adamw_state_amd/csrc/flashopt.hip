@@ -619,18 +619,20 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
 
 // Five waves per SIMD: the AdamW instantiation fits in 96 VGPRs without
 // spilling, and the fifth wave covers more memory latency (measured ~0.5 %).
+// The launch covers the list's tiles [tile0, tile0 + ntiles) (a range of
+// whole tensors: the whole list, or a bucket of consecutive tensors).
 template <int kOpt, bool kLinV>
 __device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
                                           const int64_t* __restrict__ tile_begin, int32_t count,
-                                          int64_t total_tiles, const DevTensor& one,
+                                          int64_t tile0, int64_t ntiles, const DevTensor& one,
                                           const StepScalars& P) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    if (wave >= total_tiles) return;
+    if (wave >= ntiles) return;
     TileCursor cur;
-    cur.start(table, tile_begin, count, one, total_tiles, wave);
-    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+    cur.start(table, tile_begin, count, one, ntiles, tile0 + wave);
+    for (int64_t tile = tile0 + wave; tile < tile0 + ntiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const int64_t e0 = (tile - cur.begin) * kTile;
         if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true, kLinV>(cur.T, e0, lane, P);
@@ -641,9 +643,9 @@ __device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
 template <int kOpt, bool kLinV = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
                                                    const int64_t* __restrict__ tile_begin,
-                                                   int32_t count, int64_t total_tiles,
+                                                   int32_t count, int64_t tile0, int64_t ntiles,
                                                    DevTensor one, StepScalars P) {
-    step_body<kOpt, kLinV>(table, tile_begin, count, total_tiles, one, P);
+    step_body<kOpt, kLinV>(table, tile_begin, count, tile0, ntiles, one, P);
 }
 
 // ---- graph-capturable AdamW: the step's scalars from a device schedule -------
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
     if (kOpt == kAdamW) P.a = *reinterpret_cast<const AdamScalars*>(scalars);
     else if (kOpt == kSgd) P.s = *reinterpret_cast<const SgdScalars*>(scalars);
     else P.l = *reinterpret_cast<const LionScalars*>(scalars);
-    step_body<kOpt, false>(table, tile_begin, count, total_tiles, kNoTensor, P);
+    step_body<kOpt, false>(table, tile_begin, count, 0, total_tiles, kNoTensor, P);
 }
 
 // ---- the uncompressed step (_FP32 kinds) -------------------------------------
@@ -834,15 +836,16 @@ __device__ __forceinline__ void step_f_partial(const GTensor& T, int64_t e, int 
 template <int kOpt>
 __global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restrict__ table,
                                                         const int64_t* __restrict__ tile_begin,
-                                                        int32_t count, int64_t total_tiles,
-                                                        DevTensor one, StepScalars P) {
+                                                        int32_t count, int64_t tile0,
+                                                        int64_t ntiles, DevTensor one,
+                                                        StepScalars P) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-    if (wave >= total_tiles) return;
+    if (wave >= ntiles) return;
     TileCursor cur;
-    cur.start(table, tile_begin, count, one, total_tiles, wave);
-    for (int64_t tile = wave; tile < total_tiles; tile += nwaves) {
+    cur.start(table, tile_begin, count, one, ntiles, tile0 + wave);
+    for (int64_t tile = tile0 + wave; tile < tile0 + ntiles; tile += nwaves) {
         cur.seek(table, tile_begin, tile);
         const GTensor& T = cur.T;
         const int64_t e0 = (tile - cur.begin) * kTile;
@@ -1788,28 +1791,35 @@ int flashopt_list_destroy(flashopt_list* L) {
 
 int64_t flashopt_list_numel(const flashopt_list* L) { return L ? L->numel : -1; }
 
-int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void* stream) {
-    if (!L) return FLASHOPT_ERR_NULL;
-    if (L->count == 0) return FLASHOPT_OK;
-    if (!grads) return FLASHOPT_ERR_NULL;
-    bool all = true;
-    for (int32_t i = 0; i < L->count; ++i) {
+// Writes the gradient pointers of tensors [first, first + count) into the
+// device table (one small kernel per kGradBatch tensors) and the host mirror.
+static int set_grads_range(flashopt_list* L, int32_t first, int32_t count,
+                           const uint16_t* const* grads, void* stream) {
+    for (int32_t i = 0; i < count; ++i)
         if (grads[i] && !aligned(grads[i], 16)) return FLASHOPT_ERR_ALIGN;
-        if (!grads[i] && L->host[i].numel > 0) all = false;
-    }
-    for (int32_t first = 0; first < L->count; first += kGradBatch) {
+    for (int32_t off = 0; off < count; off += kGradBatch) {
         GradBatch b;
-        b.first = first;
-        b.count = std::min<int32_t>(kGradBatch, L->count - first);
-        for (int i = 0; i < b.count; ++i) b.ptr[i] = grads[first + i];
+        b.first = first + off;
+        b.count = std::min<int32_t>(kGradBatch, count - off);
+        for (int i = 0; i < b.count; ++i) b.ptr[i] = grads[off + i];
         hipLaunchKernelGGL(set_grads_kernel, dim3(1), dim3(kGradBatch), 0, (hipStream_t)stream,
                            L->d_table, b);
         const int st = launch_status();
         if (st != FLASHOPT_OK) return st;
     }
-    for (int32_t i = 0; i < L->count; ++i) L->host[i].grad = grads[i];
+    for (int32_t i = 0; i < count; ++i) L->host[first + i].grad = grads[i];
+    bool all = true;
+    for (int32_t i = 0; i < L->count; ++i)
+        if (!L->host[i].grad && L->host[i].numel > 0) all = false;
     L->all_have_grad = all;
     return FLASHOPT_OK;
+}
+
+int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void* stream) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (L->count == 0) return FLASHOPT_OK;
+    if (!grads) return FLASHOPT_ERR_NULL;
+    return set_grads_range(L, 0, L->count, grads, stream);
 }
 
 int flashopt_state_zero(const flashopt_list* L, void* stream) {
@@ -1845,43 +1855,44 @@ int flashopt_stream_probe(const flashopt_list* L, void* stream) {
     return launch_status();
 }
 
+// One launch of the step over the tiles [tile0, tile0 + ntiles) of a list
+// (table, tile_begin) or, with table == nullptr, of the single tensor `one`.
 static int launch_step(int opt, int32_t kind, const DevTensor* table, const int64_t* tile_begin,
-                       int32_t count, int64_t total_tiles, const DevTensor& one,
+                       int32_t count, int64_t tile0, int64_t ntiles, const DevTensor& one,
                        const StepScalars& P, void* stream) {
-    if (total_tiles == 0) return FLASHOPT_OK;
-    const dim3 grid(grid_for(total_tiles));
+    if (ntiles == 0) return FLASHOPT_OK;
+    const dim3 grid(grid_for(ntiles));
     hipStream_t st = (hipStream_t)stream;
     if (is_linv(kind)) {
         hipLaunchKernelGGL((step_kernel<kAdamW, true>), grid, dim3(kBlock), 0, st, table,
-                           tile_begin, count, total_tiles, one, P);
+                           tile_begin, count, tile0, ntiles, one, P);
         return launch_status();
     }
     if (is_fp32(kind)) {
         if (opt == kAdamW)
             hipLaunchKernelGGL(step_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table,
-                               tile_begin, count, total_tiles, one, P);
+                               tile_begin, count, tile0, ntiles, one, P);
         else if (opt == kSgd)
             hipLaunchKernelGGL(step_fp32_kernel<kSgd>, grid, dim3(kBlock), 0, st, table,
-                               tile_begin, count, total_tiles, one, P);
+                               tile_begin, count, tile0, ntiles, one, P);
         else
             hipLaunchKernelGGL(step_fp32_kernel<kLion>, grid, dim3(kBlock), 0, st, table,
-                               tile_begin, count, total_tiles, one, P);
+                               tile_begin, count, tile0, ntiles, one, P);
         return launch_status();
     }
     if (opt == kAdamW)
         hipLaunchKernelGGL(step_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table, tile_begin,
-                           count, total_tiles, one, P);
+                           count, tile0, ntiles, one, P);
     else if (opt == kSgd)
         hipLaunchKernelGGL(step_kernel<kSgd>, grid, dim3(kBlock), 0, st, table, tile_begin,
-                           count, total_tiles, one, P);
+                           count, tile0, ntiles, one, P);
     else
         hipLaunchKernelGGL(step_kernel<kLion>, grid, dim3(kBlock), 0, st, table, tile_begin,
-                           count, total_tiles, one, P);
+                           count, tile0, ntiles, one, P);
     return launch_status();
 }
-
 static int launch_list(int opt, const flashopt_list* L, const StepScalars& P, void* stream) {
-    return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, L->total_tiles,
+    return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, 0, L->total_tiles,
                        DevTensor{}, P, stream);
 }
 
@@ -1891,7 +1902,7 @@ static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint
     if (t.numel == 0) return FLASHOPT_OK;
     DevTensor one = to_dev(t);
     one.grad = (uint64_t)grad;
-    return launch_step(opt, L->kind, nullptr, nullptr, 1, tiles_of(t.numel), one, P, stream);
+    return launch_step(opt, L->kind, nullptr, nullptr, 1, 0, tiles_of(t.numel), one, P, stream);
 }
 
 static int check_one(const flashopt_list* L, int32_t index, const uint16_t* grad) {
@@ -2070,6 +2081,79 @@ int flashopt_lion_step_one(const flashopt_list* L, int32_t index, const uint16_t
     StepScalars P{};
     P.l = lion_scalars(*hp);
     return launch_one(kLion, L, index, grad, P, stream);
+}
+
+// ---- bucketed gradient release: one launch over consecutive tensors ----------
+
+static int check_range(const flashopt_list* L, int32_t first, int32_t count) {
+    if (!L) return FLASHOPT_ERR_NULL;
+    if (first < 0 || count < 0 || first > L->count - count) return FLASHOPT_ERR_INDEX;
+    return FLASHOPT_OK;
+}
+
+static int check_range_grads(const flashopt_list* L, int32_t first, int32_t count,
+                             const uint16_t* const* grads) {
+    if (count > 0 && !grads) return FLASHOPT_ERR_NULL;
+    for (int32_t i = 0; i < count; ++i) {
+        if (!grads[i] && L->host[first + i].numel > 0) return FLASHOPT_ERR_NULL;
+        if (grads[i] && !aligned(grads[i], 16)) return FLASHOPT_ERR_ALIGN;
+    }
+    return FLASHOPT_OK;
+}
+
+static int launch_range(int opt, flashopt_list* L, int32_t first, int32_t count,
+                        const uint16_t* const* grads, const StepScalars& P, void* stream) {
+    if (count == 0) return FLASHOPT_OK;
+    const int st = set_grads_range(L, first, count, grads, stream);
+    if (st != FLASHOPT_OK) return st;
+    const int64_t t0 = L->tile_begin[first], t1 = L->tile_begin[first + count];
+    return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, t0, t1 - t0,
+                       DevTensor{}, P, stream);
+}
+
+int flashopt_adamw_step_range(flashopt_list* L, int32_t first, int32_t count,
+                              const uint16_t* const* grads, const flashopt_adamw_hparams* hp,
+                              int64_t step, void* stream) {
+    int st = check_range(L, first, count);
+    if (st != FLASHOPT_OK) return st;
+    st = check_adam(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (opt_of(L->kind) != kAdamW) return FLASHOPT_ERR_ARG;
+    st = check_range_grads(L, first, count, grads);
+    if (st != FLASHOPT_OK) return st;
+    StepScalars P{};
+    P.a = adam_scalars(*hp, step, &L->p1, &L->p2, &L->t, &L->b1, &L->b2);
+    return launch_range(kAdamW, L, first, count, grads, P, stream);
+}
+
+int flashopt_sgd_step_range(flashopt_list* L, int32_t first, int32_t count,
+                            const uint16_t* const* grads, const flashopt_sgd_hparams* hp,
+                            int64_t step, void* stream) {
+    int st = check_range(L, first, count);
+    if (st != FLASHOPT_OK) return st;
+    st = check_sgd(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (opt_of(L->kind) != kSgd) return FLASHOPT_ERR_ARG;
+    st = check_range_grads(L, first, count, grads);
+    if (st != FLASHOPT_OK) return st;
+    StepScalars P{};
+    P.s = sgd_scalars(*hp);
+    return launch_range(kSgd, L, first, count, grads, P, stream);
+}
+
+int flashopt_lion_step_range(flashopt_list* L, int32_t first, int32_t count,
+                             const uint16_t* const* grads, const flashopt_lion_hparams* hp,
+                             int64_t step, void* stream) {
+    int st = check_range(L, first, count);
+    if (st != FLASHOPT_OK) return st;
+    st = check_lion(hp, step);
+    if (st != FLASHOPT_OK) return st;
+    if (opt_of(L->kind) != kLion) return FLASHOPT_ERR_ARG;
+    st = check_range_grads(L, first, count, grads);
+    if (st != FLASHOPT_OK) return st;
+    StepScalars P{};
+    P.l = lion_scalars(*hp);
+    return launch_range(kLion, L, first, count, grads, P, stream);
 }
 
 }  // extern "C"

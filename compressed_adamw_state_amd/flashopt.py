@@ -130,6 +130,12 @@ SIGNATURES = {
     "flashopt_lion_step_scheduled": (ctypes.c_int, [_P, _P, _P]),
     "flashopt_lion_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(LionHparams),
                                               _I64, _P]),
+    "flashopt_adamw_step_range": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P),
+                                                 ctypes.POINTER(AdamWHparams), _I64, _P]),
+    "flashopt_sgd_step_range": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P),
+                                               ctypes.POINTER(SGDHparams), _I64, _P]),
+    "flashopt_lion_step_range": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P),
+                                                ctypes.POINTER(LionHparams), _I64, _P]),
 }
 
 _lib = None
@@ -447,6 +453,19 @@ def flashopt_lion_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: 
     _check("flashopt_lion_step_one",
            lib().flashopt_lion_step_one(lst.handle, index, _ptr(grad), ctypes.byref(h), step,
                                         _stream(stream)))
+
+
+def step_range(lst: FlashoptList, optimizer: str, first: int,
+               grads: Sequence[Optional[torch.Tensor]], hp: dict, t: int, stream=None) -> None:
+    """Bucketed gradient release: one launch over the list's tensors
+    [first, first + len(grads)) with these gradients (flashopt_*_step_range)."""
+    base = base_optimizer(optimizer)
+    fn = "flashopt_%s_step_range" % base
+    h = {"adamw": _adam, "sgd": _sgd, "lion": _lion}[base](hp)
+    arr = (ctypes.c_void_p * max(len(grads), 1))(*[_ptr(g) for g in grads])
+    _check(fn, getattr(lib(), fn)(lst.handle, first, len(grads), arr, ctypes.byref(h), t,
+                                  _stream(stream)))
+    lst.grads[first:first + len(grads)] = list(grads)
 
 
 class DeviceSchedule:

@@ -9,7 +9,10 @@ layout of include/flashopt.h.  A parameter given in FP32 is split once at
 construction: its data becomes the BF16 theta' and rho keeps the rest of the
 FP32 value.  Every step is one launch of the library's fused kernel per
 parameter group (or, with gradient release, one launch per parameter from
-its gradient hook, after which the gradient is dropped).  As in torch.optim,
+its gradient hook, after which the gradient is dropped; with
+release_bucket_bytes > 0, one launch per bucket of consecutive parameters
+whose gradients arrived one after another, once the bucket holds that many
+bytes of gradients, the last bucket at step()).  As in torch.optim,
 a parameter whose gradient is None is skipped and every parameter keeps its
 own step count; a group where that leaves parameters out, or where the
 counts differ, is stepped by one launch per parameter.
@@ -50,10 +53,17 @@ class _FlashOptimizer(torch.optim.Optimizer):
     kind = ""                                    # "adamw" | "sgd" | "lion"
 
     def __init__(self, params, defaults: dict, gradient_release: bool = False,
-                 release_streams: int = 1, capturable: bool = False):
+                 release_streams: int = 1, release_bucket_bytes: int = 0,
+                 capturable: bool = False):
         super().__init__(params, defaults)
         self.gradient_release = gradient_release
         self.capturable = capturable
+        # release_bucket_bytes > 0: consecutive parameters of a group whose
+        # gradients arrive one after another are stepped by one launch
+        # (flashopt_*_step_range) once their gradients reach this many bytes;
+        # the gradients of a bucket stay alive until its launch
+        self.release_bucket_bytes = int(release_bucket_bytes)
+        self._bucket = None
         if capturable and gradient_release:
             raise ValueError("capturable and gradient_release do not combine")
         # with release_streams > 1 the per-parameter launches from the gradient
@@ -163,8 +173,10 @@ class _FlashOptimizer(torch.optim.Optimizer):
             with torch.enable_grad():
                 loss = closure()
         if self.gradient_release:
-            # the hooks already stepped every parameter of this iteration; the
-            # next forward must see their updates
+            # the hooks already stepped every parameter of this iteration (a
+            # last bucket is stepped now); the next forward must see their
+            # updates
+            self._flush_bucket()
             cur = torch.cuda.current_stream()
             for s in self._side:
                 cur.wait_stream(s)
@@ -244,21 +256,59 @@ class _FlashOptimizer(torch.optim.Optimizer):
             g = param.grad
             if g.dtype != torch.bfloat16 or not g.is_contiguous():
                 raise ValueError("FlashOptim expects contiguous BF16 gradients")
-            stream = None
-            if self._side:
-                # every backward node that read this parameter has run
-                # (its gradient is complete), so updating it concurrently
-                # with the rest of backward is safe
-                stream = self._side[self._rr % len(self._side)]
-                self._rr += 1
-                stream.wait_stream(torch.cuda.current_stream())
-                g.record_stream(stream)  # the gradient outlives its release
+            if self.release_bucket_bytes > 0:
+                self._add_to_bucket(gi, pi, param, g)
+                return
+            stream = self._release_stream([g])
             t = self.state[param]["step"] + 1
             F.step_one(self._lists[gi], self.kind, pi, g.view(-1),
                        self._hp(self.param_groups[gi]), t, stream)
             self.state[param]["step"] = t
             param.grad = None            # gradient release: 2 B/param freed early
         self._hooks.append(p.register_post_accumulate_grad_hook(hook))
+
+    def _release_stream(self, grads):
+        """The stream a release launch goes on: the current one, or the next
+        side stream (made to wait for the current one, which produced the
+        gradients; they are recorded on it so they outlive their release).
+        A hook fires once every backward node that read its parameter has
+        run, so updating the parameter concurrently with the rest of
+        backward is safe."""
+        if not self._side:
+            return None
+        stream = self._side[self._rr % len(self._side)]
+        self._rr += 1
+        stream.wait_stream(torch.cuda.current_stream())
+        for g in grads:
+            g.record_stream(stream)
+        return stream
+
+    def _add_to_bucket(self, gi: int, pi: int, param, g) -> None:
+        t = self.state[param]["step"] + 1
+        b = self._bucket
+        if b is not None and not (b["gi"] == gi and b["t"] == t and
+                                  (pi == b["lo"] - 1 or pi == b["hi"] + 1)):
+            self._flush_bucket()
+            b = None
+        if b is None:
+            b = self._bucket = {"gi": gi, "t": t, "lo": pi, "hi": pi, "grads": {}, "bytes": 0}
+        b["lo"], b["hi"] = min(b["lo"], pi), max(b["hi"], pi)
+        b["grads"][pi] = g.view(-1)
+        b["bytes"] += 2 * g.numel()
+        self.state[param]["step"] = t
+        param.grad = None                # the bucket holds the gradient until its launch
+        if b["bytes"] >= self.release_bucket_bytes:
+            self._flush_bucket()
+
+    def _flush_bucket(self) -> None:
+        b, self._bucket = self._bucket, None
+        if b is None:
+            return
+        grads = [b["grads"][i] for i in range(b["lo"], b["hi"] + 1)]
+        stream = self._release_stream(grads)
+        gi = b["gi"]
+        F.step_range(self._lists[gi], self.kind, b["lo"], grads, self._hp(self.param_groups[gi]),
+                     b["t"], stream)
 
     # -- checkpoints -------------------------------------------------------------
     def _sync_steps(self) -> None:
@@ -336,10 +386,11 @@ class FlashAdamW(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
                  weight_decay: float = 1e-2, gradient_release: bool = False,
-                 release_streams: int = 1, compress: bool = True, capturable: bool = False):
+                 release_streams: int = 1, release_bucket_bytes: int = 0,
+                 compress: bool = True, capturable: bool = False):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), eps=eps,
                                       weight_decay=weight_decay, compress=compress),
-                         gradient_release, release_streams, capturable)
+                         gradient_release, release_streams, release_bucket_bytes, capturable)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],
@@ -353,10 +404,11 @@ class FlashSGD(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 0.1, momentum: float = 0.9,
                  weight_decay: float = 0.0, gradient_release: bool = False,
-                 release_streams: int = 1, compress: bool = True, capturable: bool = False):
+                 release_streams: int = 1, release_bucket_bytes: int = 0,
+                 compress: bool = True, capturable: bool = False):
         super().__init__(params, dict(lr=lr, momentum=momentum, weight_decay=weight_decay,
                                       compress=compress), gradient_release, release_streams,
-                         capturable)
+                         release_bucket_bytes, capturable)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], momentum=group["momentum"],
@@ -369,10 +421,11 @@ class FlashLion(_FlashOptimizer):
 
     def __init__(self, params: Iterable, lr: float = 1e-4, betas=(0.9, 0.99),
                  weight_decay: float = 0.0, gradient_release: bool = False,
-                 release_streams: int = 1, compress: bool = True, capturable: bool = False):
+                 release_streams: int = 1, release_bucket_bytes: int = 0,
+                 compress: bool = True, capturable: bool = False):
         super().__init__(params, dict(lr=lr, betas=tuple(betas), weight_decay=weight_decay,
                                       compress=compress), gradient_release, release_streams,
-                         capturable)
+                         release_bucket_bytes, capturable)
 
     def _hp(self, group) -> dict:
         return dict(lr=group["lr"], beta1=group["betas"][0], beta2=group["betas"][1],

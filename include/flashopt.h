@@ -342,6 +342,26 @@ int flashopt_sgd_step_one(const flashopt_list* list, int32_t index, const uint16
 int flashopt_lion_step_one(const flashopt_list* list, int32_t index, const uint16_t* grad,
                            const flashopt_lion_hparams* hp, int64_t step, void* stream);
 
+/* Bucketed gradient release (fused-step section): one launch steps the
+ * consecutive tensors [first, first + count) of the list.  grads: HOST array
+ * of count device BF16 gradient pointers (16-byte aligned; NULL only for
+ * empty tensors), written first into the list's descriptors by a small
+ * kernel on `stream` (so a later whole-list step reads them too); the caller
+ * may free or reuse the gradients once this launch has run.  Ranges stepped
+ * from different streams must not overlap.  Same arithmetic and results as
+ * the whole-list step.  Errors: FLASHOPT_ERR_INDEX for a range outside the
+ * list, then the hyper-parameter, kind and gradient checks of the other
+ * calls; nothing is launched on error. */
+int flashopt_adamw_step_range(flashopt_list* list, int32_t first, int32_t count,
+                              const uint16_t* const* grads, const flashopt_adamw_hparams* hp,
+                              int64_t step, void* stream);
+int flashopt_sgd_step_range(flashopt_list* list, int32_t first, int32_t count,
+                            const uint16_t* const* grads, const flashopt_sgd_hparams* hp,
+                            int64_t step, void* stream);
+int flashopt_lion_step_range(flashopt_list* list, int32_t first, int32_t count,
+                             const uint16_t* const* grads, const flashopt_lion_hparams* hp,
+                             int64_t step, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

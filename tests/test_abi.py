@@ -105,6 +105,14 @@ def test_host_validation_without_gpu():
                    F.AdamWHparams(float("nan"), 0.9, 0.999, 1e-8, 0)):
         assert lib.flashopt_adamw_step(L, ctypes.byref(bad_hp), 1, None) == -4
     assert lib.flashopt_adamw_step(L, ctypes.byref(hp), 1, None) == 0    # nothing to launch
+    # bucketed release over an empty list: only the empty range is valid
+    assert lib.flashopt_adamw_step_range(None, 0, 0, None, ctypes.byref(hp), 1, None) == -1
+    assert lib.flashopt_adamw_step_range(L, 0, 0, None, ctypes.byref(hp), 1, None) == 0
+    assert lib.flashopt_adamw_step_range(L, 0, 1, None, ctypes.byref(hp), 1, None) == -8
+    assert lib.flashopt_adamw_step_range(L, -1, 0, None, ctypes.byref(hp), 1, None) == -8
+    assert lib.flashopt_adamw_step_range(L, 0, 0, None, ctypes.byref(hp), 0, None) == -5
+    assert lib.flashopt_sgd_step_range(L, 0, 0, None, ctypes.byref(F.SGDHparams(0.1, 0.9, 0.0)),
+                                       1, None) == -4                     # an AdamW list
     sgd = F.SGDHparams(0.1, 1.0, 0.0)
     assert lib.flashopt_sgd_step(L, ctypes.byref(sgd), 1, None) == -4
     sgd = F.SGDHparams(0.1, 0.9, 0.0)

@@ -333,3 +333,38 @@ def test_gradient_release_saves_the_gradient_memory_end_to_end(streams):
     assert saving >= 1.5, (peaks, saving)            # 2 B/param less the gradients in flight
     for a, b in zip(weights[False], weights[True]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
+@pytest.mark.parametrize("bucket", [1, 3 * 2 ** 20, 2 ** 40])
+def test_bucketed_gradient_release_equals_step_after_backward(kind, bucket):
+    """release_bucket_bytes: buckets of consecutive parameters stepped by one
+    range launch (a bucket of one parameter, buckets of a few MiB, and one
+    bucket left for step()) give the same weights and state as stepping after
+    backward, bit for bit, over several iterations of a small MLP with
+    parameters of mixed sizes."""
+    torch.cuda.manual_seed(7)
+    widths = [256, 1024, 64, 512, 8]
+    x = torch.randn(16, widths[0], device="cuda", dtype=torch.bfloat16,
+                    generator=torch.Generator("cuda").manual_seed(8))
+    results = []
+    for release in (False, True):
+        torch.cuda.manual_seed(9)
+        layers = []
+        for a, b in zip(widths[:-1], widths[1:]):
+            layers += [torch.nn.Linear(a, b, device="cuda", dtype=torch.bfloat16), torch.nn.Tanh()]
+        model = torch.nn.Sequential(*layers)
+        params = list(model.parameters())
+        opt = make_opt(kind, params, release=release)
+        if release:
+            opt.release_bucket_bytes = bucket
+        for _ in range(3):
+            model(x).float().pow(2).mean().backward()
+            opt.step()
+            opt.zero_grad(set_to_none=True)
+        torch.cuda.synchronize()
+        results.append([(p.detach().view(torch.int16).clone(), opt.state[p]["flash"].codes.clone(),
+                         opt.state[p]["flash"].scales.clone(), opt.state[p]["step"])
+                        for p in params])
+    for (ta, ca, sa, na), (tb, cb, sb, nb) in zip(*results):
+        assert torch.equal(ta, tb) and torch.equal(ca, cb) and torch.equal(sa, sb) and na == nb

@@ -297,6 +297,44 @@ def test_arena_state_equals_per_tensor_state(opt):
             assert torch.equal(sa.scales, sb.scales), (t, i)
 
 
+@pytest.mark.parametrize("opt", ["adamw", "sgd", "lion", "adamw_fp32", "adamw_linv"])
+def test_bucketed_range_steps_equal_the_whole_list_step(opt):
+    """flashopt_*_step_range over buckets of consecutive tensors, issued in
+    backward order with fresh gradient tensors each step (and an empty
+    range), equals the whole-list step bit for bit."""
+    sizes = [4097, 0, 33, 2048 * 3, 1, (1 << 17) + 5, 2048, 7]
+    buckets = [(6, 2), (5, 1), (2, 3), (2, 0), (0, 2)]      # (first, count), backward order
+    assert sorted(i for f, c in buckets for i in range(f, f + c)) == list(range(len(sizes)))
+    rng = np.random.default_rng(18)
+    thetas = [torch.from_numpy((rng.standard_normal(n) * 0.02).astype(np.float32)).cuda()
+              for n in sizes]
+    arena = F.StateArena(sizes, opt, "cuda")
+    a = [arena.state(i) for i in range(len(sizes))]
+    b = [F.TensorState(n, opt, "cuda") for n in sizes]
+    for sa, sb, th in zip(a, b, thetas):
+        F.flashopt_tensor_init(sa, th)
+        F.flashopt_tensor_init(sb, th)
+    ga = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for n in sizes]
+    la = F.FlashoptList(a, ga)
+    lb = F.FlashoptList(b, [None] * len(sizes))
+    base = F.base_optimizer(opt)
+    hp = W.HPARAMS[base]
+    for t in (1, 2, 3):
+        gs = [torch.from_numpy((rng.standard_normal(n) * 1e-3).astype(np.float32))
+              .to(torch.bfloat16).cuda() for n in sizes]
+        for g, d in zip(ga, gs):
+            g.copy_(d)
+        F.step(la, base, hp, t)
+        for first, count in buckets:
+            F.step_range(lb, base, first, [gs[i] if sizes[i] else None
+                                           for i in range(first, first + count)], hp, t)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a, b)):
+            assert torch.equal(sa.theta.view(torch.int16), sb.theta.view(torch.int16)), (t, i)
+            assert torch.equal(sa.codes, sb.codes), (t, i)
+            assert torch.equal(sa.scales, sb.scales), (t, i)
+
+
 def test_set_grads_and_state_zero():
     w = W.ragged([3000, 70], seed=14, steps=2)
     r = Run(w, "full")
