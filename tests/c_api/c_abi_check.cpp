@@ -1,7 +1,8 @@
 // A C++ consumer of the C ABI with no Python and no torch: device memory from
 // hipMalloc, the stream from hipStreamCreate, every call through
-// include/flashopt.h.  It steps a ragged list with AdamW (whole-list launch
-// and gradient release), Lion and SGD, and compares every theta', code and
+// include/flashopt.h.  It steps a ragged list with AdamW (whole-list launch,
+// gradient release per tensor and in buckets of consecutive tensors), Lion
+// and SGD, and compares every theta', code and
 // scale with the CPU oracle (oracle/flashopt_oracle.h, test infrastructure)
 // stepping the same inputs.  Exit status 0 when everything matches.
 //
@@ -98,12 +99,16 @@ int compare(const Host& h, const Dev& d, int32_t kind, const char* what) {
     return bad ? 1 : 0;
 }
 
-int run(int32_t kind, bool release, hipStream_t stream) {
+enum Mode { kList, kRelease, kBuckets };
+
+int run(int32_t kind, Mode mode, hipStream_t stream) {
     const int64_t sizes[] = {4101, 33, 2048, 1, 0, 70000};
     const int count = (int)(sizeof sizes / sizeof sizes[0]);
-    const char* name = kind == FLASHOPT_KIND_ADAMW ? (release ? "adamw release" : "adamw")
+    const char* name = kind == FLASHOPT_KIND_ADAMW
+                           ? (mode == kRelease ? "adamw release"
+                              : mode == kBuckets ? "adamw buckets" : "adamw")
                        : kind == FLASHOPT_KIND_LION ? "lion" : "sgd";
-    Rng rng{0x5EEDull + (uint64_t)kind * 7 + (release ? 1 : 0)};
+    Rng rng{0x5EEDull + (uint64_t)kind * 7 + (uint64_t)mode};
     std::vector<Host> host((size_t)count);
     std::vector<Dev> dev((size_t)count);
     std::vector<flashopt_tensor> desc((size_t)count);
@@ -170,9 +175,17 @@ int run(int32_t kind, bool release, hipStream_t stream) {
                 orc_sgd_step(n, h.tb.data(), h.rho.data(), h.qm.data(), h.sm.data(), g.data(),
                              sgd.lr, sgd.momentum, sgd.weight_decay, t, nullptr, nullptr);
         }
-        if (release) {
+        if (mode == kRelease) {
             for (int i = count - 1; i >= 0; --i)     // backward order, one launch per tensor
                 FO_OK(flashopt_adamw_step_one(list, i, dev[(size_t)i].grad, &adam, t, stream));
+        } else if (mode == kBuckets) {
+            // backward order, one launch per bucket of consecutive tensors
+            const int buckets[][2] = {{4, 2}, {1, 3}, {0, 1}};
+            for (const auto& b : buckets) {
+                const uint16_t* g[3];
+                for (int i = 0; i < b[1]; ++i) g[i] = dev[(size_t)(b[0] + i)].grad;
+                FO_OK(flashopt_adamw_step_range(list, b[0], b[1], g, &adam, t, stream));
+            }
         } else if (kind == FLASHOPT_KIND_ADAMW) {
             FO_OK(flashopt_adamw_step(list, &adam, t, stream));
         } else if (kind == FLASHOPT_KIND_LION) {
@@ -208,10 +221,11 @@ int main() {
     HIP_OK(hipSetDevice(0));
     HIP_OK(hipStreamCreate(&stream));
     int rc = 0;
-    if (!rc) rc = run(FLASHOPT_KIND_ADAMW, false, stream);
-    if (!rc) rc = run(FLASHOPT_KIND_ADAMW, true, stream);
-    if (!rc) rc = run(FLASHOPT_KIND_LION, false, stream);
-    if (!rc) rc = run(FLASHOPT_KIND_SGD, false, stream);
+    if (!rc) rc = run(FLASHOPT_KIND_ADAMW, kList, stream);
+    if (!rc) rc = run(FLASHOPT_KIND_ADAMW, kRelease, stream);
+    if (!rc) rc = run(FLASHOPT_KIND_ADAMW, kBuckets, stream);
+    if (!rc) rc = run(FLASHOPT_KIND_LION, kList, stream);
+    if (!rc) rc = run(FLASHOPT_KIND_SGD, kList, stream);
     HIP_OK(hipStreamDestroy(stream));
     return rc;
 }

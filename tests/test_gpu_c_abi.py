@@ -1,6 +1,7 @@
 """The C ABI used from C++ with no Python and no torch (tests/c_api/
 c_abi_check.cpp, built by __graft_entry__.build()): hipMalloc'd buffers, a
-HIP stream, AdamW (whole list and gradient release), Lion and SGD steps over
+HIP stream, AdamW (whole list, gradient release per tensor and in buckets), Lion
+and SGD steps over
 a ragged list, every code and scale compared with the oracle."""
 import os
 import subprocess
@@ -17,4 +18,4 @@ def test_c_consumer_matches_oracle():
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.count("match the oracle") == 4
+    assert r.stdout.count("match the oracle") == 5
