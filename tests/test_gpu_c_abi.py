@@ -1,8 +1,8 @@
 """The C ABI used from C++ with no Python and no torch (tests/c_api/
 c_abi_check.cpp, built by __graft_entry__.build()): hipMalloc'd buffers, a
-HIP stream, AdamW (whole list, gradient release per tensor and in buckets), Lion
-and SGD steps over
-a ragged list, every code and scale compared with the oracle."""
+HIP stream, AdamW (whole list, gradient release per tensor and in buckets),
+Lion and SGD steps over a ragged list, every code and scale compared with the
+oracle."""
 import os
 import subprocess
 
