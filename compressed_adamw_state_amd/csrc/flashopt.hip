@@ -619,9 +619,31 @@ __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane
 
 // Five waves per SIMD: the AdamW instantiation fits in 96 VGPRs without
 // spilling, and the fifth wave covers more memory latency (measured ~0.5 %).
-// The launch covers the list's tiles [tile0, tile0 + ntiles) (a range of
-// whole tensors: the whole list, or a bucket of consecutive tensors).
+// Sub-tile k of the tile at e0, alone: the full fast path with its own
+// loads, or the bounds-checked path for the part of a tensor's last tile
+// that holds elements.
 template <int kOpt, bool kLinV>
+__device__ __forceinline__ void step_sub(const GTensor& T, int64_t e0, int k, int lane,
+                                         const StepScalars& P) {
+    const int64_t e = e0 + (int64_t)k * kSubTile;
+    if (e + kSubTile <= T.numel) {
+        const TileAddr<kOpt> A(T, e0, lane);
+        Raw R;
+        load_raw<kOpt>(A, k, R);
+        step_fast<kOpt, kLinV>(A, k, lane, R, P);
+    } else if (e < T.numel) {
+        Lane8 L;
+        load_lane<kOpt>(T, e + lane * kLaneElems, L);
+        step_lane<kOpt, kLinV>(T, e + lane * kLaneElems, lane, L, P);
+    }
+}
+
+// The launch covers the list's tiles [tile0, tile0 + ntiles) (a range of
+// whole tensors: the whole list, or a bucket of consecutive tensors).  kSplit
+// (launches of few tiles): one wave per 512-element sub-tile instead of one
+// per tile, so a small launch spreads over four times as many waves; the
+// arithmetic per element is the same.
+template <int kOpt, bool kLinV, bool kSplit>
 __device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
                                           const int64_t* __restrict__ tile_begin, int32_t count,
                                           int64_t tile0, int64_t ntiles, const DevTensor& one,
@@ -629,6 +651,19 @@ __device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    if (kSplit) {
+        const int64_t nitems = ntiles * kSubTiles;
+        if (wave >= nitems) return;
+        TileCursor cur;
+        cur.start(table, tile_begin, count, one, ntiles, tile0 + wave / kSubTiles);
+        for (int64_t item = wave; item < nitems; item += nwaves) {
+            const int64_t tile = tile0 + item / kSubTiles;
+            cur.seek(table, tile_begin, tile);
+            step_sub<kOpt, kLinV>(cur.T, (tile - cur.begin) * kTile, (int)(item % kSubTiles),
+                                  lane, P);
+        }
+        return;
+    }
     if (wave >= ntiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, one, ntiles, tile0 + wave);
@@ -640,12 +675,12 @@ __device__ __forceinline__ void step_body(const DevTensor* __restrict__ table,
     }
 }
 
-template <int kOpt, bool kLinV = false>
+template <int kOpt, bool kLinV, bool kSplit>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel(const DevTensor* __restrict__ table,
                                                    const int64_t* __restrict__ tile_begin,
                                                    int32_t count, int64_t tile0, int64_t ntiles,
                                                    DevTensor one, StepScalars P) {
-    step_body<kOpt, kLinV>(table, tile_begin, count, tile0, ntiles, one, P);
+    step_body<kOpt, kLinV, kSplit>(table, tile_begin, count, tile0, ntiles, one, P);
 }
 
 // ---- graph-capturable AdamW: the step's scalars from a device schedule -------
@@ -728,7 +763,7 @@ __device__ const DevTensor kNoTensor = {};
 
 // The step with its scalars read from a schedule's `scalars` words (written
 // by the advance kernel launched just before on the same stream).
-template <int kOpt>
+template <int kOpt, bool kSplit>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel_scheduled(
     const DevTensor* __restrict__ table, const int64_t* __restrict__ tile_begin, int32_t count,
     int64_t total_tiles, const uint32_t* __restrict__ scalars) {
@@ -738,7 +773,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
     if (kOpt == kAdamW) P.a = *reinterpret_cast<const AdamScalars*>(scalars);
     else if (kOpt == kSgd) P.s = *reinterpret_cast<const SgdScalars*>(scalars);
     else P.l = *reinterpret_cast<const LionScalars*>(scalars);
-    step_body<kOpt, false>(table, tile_begin, count, 0, total_tiles, kNoTensor, P);
+    step_body<kOpt, false, kSplit>(table, tile_begin, count, 0, total_tiles, kNoTensor, P);
 }
 
 // ---- the uncompressed step (_FP32 kinds) -------------------------------------
@@ -1855,20 +1890,40 @@ int flashopt_stream_probe(const flashopt_list* L, void* stream) {
     return launch_status();
 }
 
+// Launches of fewer tiles than this run one wave per 512-element sub-tile
+// (the kSplit form of the step kernels).  Measured on MI355X (AdamW, one
+// tensor): the split form takes 6.4 instead of 9.2 us at 64 tiles, 11.8
+// instead of 14.9 at 1279, 42.4 instead of 43.9 at 8192 (and 63 instead of
+// 66 us on the 161-tensor ResNet-50 list); the two are even around 16K-32K
+// tiles, and from 64K tiles on one wave per tile is ~2 % faster.
+constexpr int64_t kSplitTiles = 16384;
+
+extern "C++" {   // templates, inside the C-linkage block
+template <int kOpt, bool kLinV>
+static int launch_fused(const DevTensor* table, const int64_t* tile_begin, int32_t count,
+                        int64_t tile0, int64_t ntiles, const DevTensor& one, const StepScalars& P,
+                        hipStream_t st) {
+    if (ntiles < kSplitTiles)
+        hipLaunchKernelGGL((step_kernel<kOpt, kLinV, true>), dim3(grid_for(ntiles * kSubTiles)),
+                           dim3(kBlock), 0, st, table, tile_begin, count, tile0, ntiles, one, P);
+    else
+        hipLaunchKernelGGL((step_kernel<kOpt, kLinV, false>), dim3(grid_for(ntiles)),
+                           dim3(kBlock), 0, st, table, tile_begin, count, tile0, ntiles, one, P);
+    return launch_status();
+}
+}  // extern "C++"
+
 // One launch of the step over the tiles [tile0, tile0 + ntiles) of a list
 // (table, tile_begin) or, with table == nullptr, of the single tensor `one`.
 static int launch_step(int opt, int32_t kind, const DevTensor* table, const int64_t* tile_begin,
                        int32_t count, int64_t tile0, int64_t ntiles, const DevTensor& one,
                        const StepScalars& P, void* stream) {
     if (ntiles == 0) return FLASHOPT_OK;
-    const dim3 grid(grid_for(ntiles));
     hipStream_t st = (hipStream_t)stream;
-    if (is_linv(kind)) {
-        hipLaunchKernelGGL((step_kernel<kAdamW, true>), grid, dim3(kBlock), 0, st, table,
-                           tile_begin, count, tile0, ntiles, one, P);
-        return launch_status();
-    }
+    if (is_linv(kind))
+        return launch_fused<kAdamW, true>(table, tile_begin, count, tile0, ntiles, one, P, st);
     if (is_fp32(kind)) {
+        const dim3 grid(grid_for(ntiles));
         if (opt == kAdamW)
             hipLaunchKernelGGL(step_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table,
                                tile_begin, count, tile0, ntiles, one, P);
@@ -1881,16 +1936,30 @@ static int launch_step(int opt, int32_t kind, const DevTensor* table, const int6
         return launch_status();
     }
     if (opt == kAdamW)
-        hipLaunchKernelGGL(step_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table, tile_begin,
-                           count, tile0, ntiles, one, P);
-    else if (opt == kSgd)
-        hipLaunchKernelGGL(step_kernel<kSgd>, grid, dim3(kBlock), 0, st, table, tile_begin,
-                           count, tile0, ntiles, one, P);
+        return launch_fused<kAdamW, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
+    if (opt == kSgd)
+        return launch_fused<kSgd, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
+    return launch_fused<kLion, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
+}
+// The scheduled step kernel over a whole list, in the same launch form as
+// launch_fused chooses.
+extern "C++" {
+template <int kOpt>
+static int launch_scheduled(const flashopt_list* L, const uint32_t* scalars, hipStream_t st) {
+    const DevTensor* table = (const DevTensor*)L->d_table;
+    const int64_t* tile_begin = (const int64_t*)L->d_tile_begin;
+    if (L->total_tiles < kSplitTiles)
+        hipLaunchKernelGGL((step_kernel_scheduled<kOpt, true>),
+                           dim3(grid_for(L->total_tiles * kSubTiles)), dim3(kBlock), 0, st, table,
+                           tile_begin, L->count, L->total_tiles, scalars);
     else
-        hipLaunchKernelGGL(step_kernel<kLion>, grid, dim3(kBlock), 0, st, table, tile_begin,
-                           count, tile0, ntiles, one, P);
+        hipLaunchKernelGGL((step_kernel_scheduled<kOpt, false>), dim3(grid_for(L->total_tiles)),
+                           dim3(kBlock), 0, st, table, tile_begin, L->count, L->total_tiles,
+                           scalars);
     return launch_status();
 }
+}  // extern "C++"
+
 static int launch_list(int opt, const flashopt_list* L, const StepScalars& P, void* stream) {
     return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, 0, L->total_tiles,
                        DevTensor{}, P, stream);
@@ -1979,10 +2048,7 @@ int flashopt_adamw_step_scheduled(const flashopt_list* L, flashopt_adamw_schedul
     hipLaunchKernelGGL(schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
     int r = launch_status();
     if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
-    hipLaunchKernelGGL(step_kernel_scheduled<kAdamW>, dim3(grid_for(L->total_tiles)), dim3(kBlock),
-                       0, st, (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin,
-                       L->count, L->total_tiles, (const uint32_t*)S->scalars);
-    return launch_status();
+    return launch_scheduled<kAdamW>(L, (const uint32_t*)S->scalars, st);
 }
 
 int flashopt_sgd_schedule_init(flashopt_sgd_schedule* S, const flashopt_sgd_hparams* hp,
@@ -2006,10 +2072,7 @@ int flashopt_sgd_step_scheduled(const flashopt_list* L, flashopt_sgd_schedule* S
     hipLaunchKernelGGL(sgd_schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
     int r = launch_status();
     if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
-    hipLaunchKernelGGL(step_kernel_scheduled<kSgd>, dim3(grid_for(L->total_tiles)), dim3(kBlock),
-                       0, st, (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin,
-                       L->count, L->total_tiles, (const uint32_t*)S->scalars);
-    return launch_status();
+    return launch_scheduled<kSgd>(L, (const uint32_t*)S->scalars, st);
 }
 
 int flashopt_lion_schedule_init(flashopt_lion_schedule* S, const flashopt_lion_hparams* hp,
@@ -2034,10 +2097,7 @@ int flashopt_lion_step_scheduled(const flashopt_list* L, flashopt_lion_schedule*
     hipLaunchKernelGGL(lion_schedule_advance_kernel, dim3(1), dim3(64), 0, st, S);
     int r = launch_status();
     if (r != FLASHOPT_OK || L->total_tiles == 0) return r;
-    hipLaunchKernelGGL(step_kernel_scheduled<kLion>, dim3(grid_for(L->total_tiles)), dim3(kBlock),
-                       0, st, (const DevTensor*)L->d_table, (const int64_t*)L->d_tile_begin,
-                       L->count, L->total_tiles, (const uint32_t*)S->scalars);
-    return launch_status();
+    return launch_scheduled<kLion>(L, (const uint32_t*)S->scalars, st);
 }
 
 int flashopt_adamw_step_one(const flashopt_list* L, int32_t index, const uint16_t* grad,
