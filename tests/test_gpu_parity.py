@@ -371,6 +371,50 @@ def test_tensor_beyond_2_to_31_elements(opt):
     log(f"{opt} tensor of {n} elements: {n_cmp} sampled elements compared")
 
 
+def test_range_launch_of_a_large_tensor_after_a_small_one():
+    """A range launch whose first tile is not 0 in the one-wave-per-tile form
+    (the range holds 16384 tiles): equal to the whole-list step bit for bit."""
+    sizes = [1000, 16384 * 2048 - 3]
+    rng = np.random.default_rng(20)
+    thetas = [torch.from_numpy((rng.standard_normal(n) * 0.02).astype(np.float32)).cuda()
+              for n in sizes]
+    a = [F.TensorState(n, "adamw", "cuda") for n in sizes]
+    b = [F.TensorState(n, "adamw", "cuda") for n in sizes]
+    for sa, sb, th in zip(a, b, thetas):
+        F.flashopt_tensor_init(sa, th)
+        F.flashopt_tensor_init(sb, th)
+    del thetas
+    gs = [torch.from_numpy((rng.standard_normal(n) * 1e-3).astype(np.float32))
+          .to(torch.bfloat16).cuda() for n in sizes]
+    la, lb = F.FlashoptList(a, gs), F.FlashoptList(b, [None, None])
+    for t in (1, 2):
+        F.step(la, "adamw", W.ADAMW_HP, t)
+        F.step_range(lb, "adamw", 1, [gs[1]], W.ADAMW_HP, t)
+        F.step_range(lb, "adamw", 0, [gs[0]], W.ADAMW_HP, t)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(a[i].theta.view(torch.int16), b[i].theta.view(torch.int16)), (t, i)
+            assert torch.equal(a[i].codes, b[i].codes) and torch.equal(a[i].scales, b[i].scales)
+
+
+@pytest.mark.parametrize("extra_tiles", [0, 1])
+def test_both_sides_of_the_split_launch_threshold(extra_tiles):
+    """Lists of 16383 tiles (the split form: one wave per 512-element
+    sub-tile) and 16384 tiles (one wave per tile), with a partial last tile in
+    each tensor, against the oracle on sampled groups (including groups of
+    the last, partial tile of every tensor) for two steps."""
+    tile = 2048
+    sizes = [16000 * tile - 7, 381 * tile + 100 + extra_tiles * tile, 1000]
+    assert sum(-(-n // tile) for n in sizes) == 16383 + extra_tiles
+    w = W.ragged(sizes, seed=19, steps=2)
+    last = [(n - 1) // 32 for n in sizes]
+    r = Run(w, "sampled", samples_per_tensor=6, seed=19,
+            extra_groups=[g - k for g in last for k in (1, 5, 17, 40)])
+    for t in (1, 2):
+        r.step(t)
+        r.compare(f"{16383 + extra_tiles} tiles, step {t}")
+
+
 def test_config1_flat1m_all_steps():
     w = W.WORKLOADS["flat1m"]
     r = Run(w, "full")
