@@ -66,9 +66,10 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._bucket = None
         if capturable and gradient_release:
             raise ValueError("capturable and gradient_release do not combine")
-        # with release_streams > 1 the per-parameter launches from the gradient
-        # hooks go round-robin over that many side streams (default priority):
-        # each overlaps the rest of backward and the tail of the previous one
+        # with release_streams > 1 the launches from the gradient hooks (per
+        # parameter or per bucket) go round-robin over that many side streams
+        # (default priority): each overlaps the rest of backward and the tail
+        # of the previous one
         self._side = [torch.cuda.Stream() for _ in range(release_streams)] \
             if gradient_release and release_streams > 1 else []
         self._rr = 0
