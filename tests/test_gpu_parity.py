@@ -335,6 +335,26 @@ def test_bucketed_range_steps_equal_the_whole_list_step(opt):
             assert torch.equal(sa.scales, sb.scales), (t, i)
 
 
+@pytest.mark.parametrize("opt", ["adamw", "sgd"])
+def test_list_of_three_thousand_small_tensors(opt):
+    """A list of 3000 tensors with sizes around the group, sub-tile and tile
+    boundaries (and many empty ones): the tile table's search, gradient
+    pointers replaced in 15 batches between steps, every code and scale
+    against the oracle."""
+    cycle = [0, 1, 31, 32, 33, 0, 511, 512, 513, 2047, 2048, 2049, 5000, 0, 7]
+    sizes = [cycle[i % len(cycle)] for i in range(3000)]
+    w = W.ragged(sizes, seed=21, steps=3, optimizer=opt)
+    r = Run(w, "full")
+    r.step(1)
+    r.compare("step 1")
+    new = [torch.zeros(st.numel, dtype=torch.bfloat16, device="cuda") for st in r.states]
+    F.flashopt_list_set_grads(r.lst, new)
+    r.grads = new
+    for t in (2, 3):
+        r.step(t)
+        r.compare(f"step {t}")
+
+
 def test_set_grads_and_state_zero():
     w = W.ragged([3000, 70], seed=14, steps=2)
     r = Run(w, "full")
