@@ -868,7 +868,9 @@ __device__ __forceinline__ void step_f_partial(const GTensor& T, int64_t e, int 
     }
 }
 
-template <int kOpt>
+// kSplit: one wave per 512-element sub-tile (small launches), as in the
+// compressed step.
+template <int kOpt, bool kSplit>
 __global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restrict__ table,
                                                         const int64_t* __restrict__ tile_begin,
                                                         int32_t count, int64_t tile0,
@@ -877,6 +879,26 @@ __global__ __launch_bounds__(256) void step_fp32_kernel(const DevTensor* __restr
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
     const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+    if (kSplit) {
+        const int64_t nitems = ntiles * kSubTiles;
+        if (wave >= nitems) return;
+        TileCursor cur;
+        cur.start(table, tile_begin, count, one, ntiles, tile0 + wave / kSubTiles);
+        for (int64_t item = wave; item < nitems; item += nwaves) {
+            const int64_t tile = tile0 + item / kSubTiles;
+            cur.seek(table, tile_begin, tile);
+            const GTensor& T = cur.T;
+            const int64_t e = (tile - cur.begin) * kTile + (item % kSubTiles) * kSubTile;
+            if (e + kSubTile <= T.numel) {
+                RawF R;
+                load_raw_f<kOpt>(T, e, lane, R);
+                step_f<kOpt>(T, e, lane, R, P);
+            } else if (e < T.numel) {
+                step_f_partial<kOpt>(T, e, lane, P);
+            }
+        }
+        return;
+    }
     if (wave >= ntiles) return;
     TileCursor cur;
     cur.start(table, tile_begin, count, one, ntiles, tile0 + wave);
@@ -1911,6 +1933,19 @@ static int launch_fused(const DevTensor* table, const int64_t* tile_begin, int32
                            dim3(kBlock), 0, st, table, tile_begin, count, tile0, ntiles, one, P);
     return launch_status();
 }
+
+template <int kOpt>
+static int launch_fp32(const DevTensor* table, const int64_t* tile_begin, int32_t count,
+                       int64_t tile0, int64_t ntiles, const DevTensor& one, const StepScalars& P,
+                       hipStream_t st) {
+    if (ntiles < kSplitTiles)
+        hipLaunchKernelGGL((step_fp32_kernel<kOpt, true>), dim3(grid_for(ntiles * kSubTiles)),
+                           dim3(kBlock), 0, st, table, tile_begin, count, tile0, ntiles, one, P);
+    else
+        hipLaunchKernelGGL((step_fp32_kernel<kOpt, false>), dim3(grid_for(ntiles)),
+                           dim3(kBlock), 0, st, table, tile_begin, count, tile0, ntiles, one, P);
+    return launch_status();
+}
 }  // extern "C++"
 
 // One launch of the step over the tiles [tile0, tile0 + ntiles) of a list
@@ -1923,17 +1958,11 @@ static int launch_step(int opt, int32_t kind, const DevTensor* table, const int6
     if (is_linv(kind))
         return launch_fused<kAdamW, true>(table, tile_begin, count, tile0, ntiles, one, P, st);
     if (is_fp32(kind)) {
-        const dim3 grid(grid_for(ntiles));
         if (opt == kAdamW)
-            hipLaunchKernelGGL(step_fp32_kernel<kAdamW>, grid, dim3(kBlock), 0, st, table,
-                               tile_begin, count, tile0, ntiles, one, P);
-        else if (opt == kSgd)
-            hipLaunchKernelGGL(step_fp32_kernel<kSgd>, grid, dim3(kBlock), 0, st, table,
-                               tile_begin, count, tile0, ntiles, one, P);
-        else
-            hipLaunchKernelGGL(step_fp32_kernel<kLion>, grid, dim3(kBlock), 0, st, table,
-                               tile_begin, count, tile0, ntiles, one, P);
-        return launch_status();
+            return launch_fp32<kAdamW>(table, tile_begin, count, tile0, ntiles, one, P, st);
+        if (opt == kSgd)
+            return launch_fp32<kSgd>(table, tile_begin, count, tile0, ntiles, one, P, st);
+        return launch_fp32<kLion>(table, tile_begin, count, tile0, ntiles, one, P, st);
     }
     if (opt == kAdamW)
         return launch_fused<kAdamW, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
