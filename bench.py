@@ -273,8 +273,8 @@ def release_memory(iters: int, stream, layers: int = 32, width: int = 4096,
     """Gradient release end to end: forward + backward + FlashAdamW step of
     a stack of `layers` BF16 linear layers (width x width, no bias; a small
     batch, so the gradients are most of an iteration's transient memory),
-    with the step after backward and with gradient release on one and two
-    side streams.  Reports the peak of allocated memory during an iteration
+    with the step after backward, with gradient release on one and two
+    side streams, and with release in 64 MiB buckets.  Reports the peak of allocated memory during an iteration
     above what stays resident (model + state), the saving per parameter, the
     median time per iteration, and whether the weights after the timed
     iterations are bit-identical across the three modes."""
@@ -284,15 +284,16 @@ def release_memory(iters: int, stream, layers: int = 32, width: int = 4096,
                     generator=torch.Generator("cuda").manual_seed(11))
     modes = {}
     ref = None
-    for name, release, streams in (("step after backward", False, 1),
-                                   ("gradient release", True, 1),
-                                   ("gradient release, 2 streams", True, 2)):
+    for name, release, streams, bucket in (("step after backward", False, 1, 0),
+                                           ("gradient release", True, 1, 0),
+                                           ("gradient release, 2 streams", True, 2, 0),
+                                           ("gradient release, 64 MiB buckets", True, 1, 64 << 20)):
         torch.cuda.manual_seed(12)
         model = torch.nn.Sequential(*[torch.nn.Linear(width, width, bias=False, device="cuda",
                                                       dtype=torch.bfloat16)
                                       for _ in range(layers)])
         opt = O.FlashAdamW(model.parameters(), lr=1e-3, gradient_release=release,
-                           release_streams=streams)
+                           release_streams=streams, release_bucket_bytes=bucket)
 
         def iteration():
             model(x).float().pow(2).mean().backward()

@@ -2190,14 +2190,21 @@ static int check_range_grads(const flashopt_list* L, int32_t first, int32_t coun
     return FLASHOPT_OK;
 }
 
+// The gradients of a range launch serve that launch only (the caller may
+// free them once it has run): afterwards the list holds no gradient for
+// those tensors, so a whole-list step needs flashopt_list_set_grads first.
 static int launch_range(int opt, flashopt_list* L, int32_t first, int32_t count,
                         const uint16_t* const* grads, const StepScalars& P, void* stream) {
     if (count == 0) return FLASHOPT_OK;
-    const int st = set_grads_range(L, first, count, grads, stream);
+    int st = set_grads_range(L, first, count, grads, stream);
     if (st != FLASHOPT_OK) return st;
     const int64_t t0 = L->tile_begin[first], t1 = L->tile_begin[first + count];
-    return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, t0, t1 - t0,
-                       DevTensor{}, P, stream);
+    st = launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, t0, t1 - t0,
+                     DevTensor{}, P, stream);
+    for (int32_t i = 0; i < count; ++i) L->host[first + i].grad = nullptr;
+    for (int32_t i = 0; i < count; ++i)
+        if (L->host[first + i].numel > 0) L->all_have_grad = false;
+    return st;
 }
 
 int flashopt_adamw_step_range(flashopt_list* L, int32_t first, int32_t count,

@@ -458,14 +458,17 @@ def flashopt_lion_step_one(lst: FlashoptList, index: int, grad, hp: dict, step: 
 def step_range(lst: FlashoptList, optimizer: str, first: int,
                grads: Sequence[Optional[torch.Tensor]], hp: dict, t: int, stream=None) -> None:
     """Bucketed gradient release: one launch over the list's tensors
-    [first, first + len(grads)) with these gradients (flashopt_*_step_range)."""
+    [first, first + len(grads)) with these gradients (flashopt_*_step_range).
+    The gradients serve this launch only: the list keeps no reference to
+    them (so released gradients are freed), and holds no gradient for these
+    tensors afterwards."""
     base = base_optimizer(optimizer)
     fn = "flashopt_%s_step_range" % base
     h = {"adamw": _adam, "sgd": _sgd, "lion": _lion}[base](hp)
     arr = (ctypes.c_void_p * max(len(grads), 1))(*[_ptr(g) for g in grads])
     _check(fn, getattr(lib(), fn)(lst.handle, first, len(grads), arr, ctypes.byref(h), t,
                                   _stream(stream)))
-    lst.grads[first:first + len(grads)] = list(grads)
+    lst.grads[first:first + len(grads)] = [None] * len(grads)
 
 
 class DeviceSchedule:

@@ -346,9 +346,11 @@ int flashopt_lion_step_one(const flashopt_list* list, int32_t index, const uint1
  * consecutive tensors [first, first + count) of the list.  grads: HOST array
  * of count device BF16 gradient pointers (16-byte aligned; NULL only for
  * empty tensors), written first into the list's descriptors by a small
- * kernel on `stream` (so a later whole-list step reads them too); the caller
- * may free or reuse the gradients once this launch has run.  Ranges stepped
- * from different streams must not overlap.  Same arithmetic and results as
+ * kernel on `stream`.  They serve this launch only: the caller may free or
+ * reuse the gradients once it has run, and afterwards the list holds no
+ * gradient for these tensors (a whole-list step returns FLASHOPT_ERR_NULL
+ * until flashopt_list_set_grads gives them again).  Ranges stepped from
+ * different streams must not overlap.  Same arithmetic and results as
  * the whole-list step.  Errors: FLASHOPT_ERR_INDEX for a range outside the
  * list, then the hyper-parameter, kind and gradient checks of the other
  * calls; nothing is launched on error. */

@@ -292,13 +292,13 @@ def test_add_param_group_after_construction():
         compare(opt, [pa, pb], [oa, ob], f"step {t}")
 
 
-@pytest.mark.parametrize("streams", [1, 2])
-def test_gradient_release_saves_the_gradient_memory_end_to_end(streams):
+@pytest.mark.parametrize("streams,bucket", [(1, 0), (2, 0), (1, 4 << 20)])
+def test_gradient_release_saves_the_gradient_memory_end_to_end(streams, bucket):
     """Forward + backward + step of a stack of BF16 linear layers: with
     gradient release the peak of allocated memory during an iteration is lower
-    by about the gradients' 2 B/param (all but the few gradients in flight),
-    and the weights after two iterations equal stepping after backward bit for
-    bit."""
+    by about the gradients' 2 B/param (all but the few gradients in flight, or
+    in the open bucket), and the weights after two iterations equal stepping
+    after backward bit for bit."""
     layers, width, batch = 8, 1024, 4
     n = layers * width * width
     x = torch.randn(batch, width, device="cuda", dtype=torch.bfloat16,
@@ -310,7 +310,7 @@ def test_gradient_release_saves_the_gradient_memory_end_to_end(streams):
                                                       dtype=torch.bfloat16)
                                       for _ in range(layers)])
         opt = O.FlashAdamW(model.parameters(), lr=1e-3, gradient_release=release,
-                           release_streams=streams)
+                           release_streams=streams, release_bucket_bytes=bucket)
 
         def iteration():
             model(x).float().pow(2).mean().backward()
@@ -328,9 +328,11 @@ def test_gradient_release_saves_the_gradient_memory_end_to_end(streams):
         del opt, model
         torch.cuda.empty_cache()
     saving = (peaks[False] - peaks[True]) / n
-    log(f"release ({streams} stream(s)): peak {peaks[False] / 2**20:.1f} MiB -> "
+    log(f"release ({streams} stream(s), bucket {bucket}): peak {peaks[False] / 2**20:.1f} MiB -> "
         f"{peaks[True] / 2**20:.1f} MiB, {saving:.3f} B/param saved")
-    assert saving >= 1.5, (peaks, saving)            # 2 B/param less the gradients in flight
+    grad = 2 * width * width                           # one layer's gradient
+    assert peaks[False] >= 2 * n                       # every gradient alive at the step
+    assert peaks[True] <= max(bucket, grad) + 2 * grad + (1 << 20), (peaks, saving)
     for a, b in zip(weights[False], weights[True]):
         assert torch.equal(a, b)
 

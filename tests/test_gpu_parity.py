@@ -391,6 +391,28 @@ def test_tensor_beyond_2_to_31_elements(opt):
     log(f"{opt} tensor of {n} elements: {n_cmp} sampled elements compared")
 
 
+def test_range_launch_gradients_serve_that_launch_only():
+    """After a range launch the list holds no gradient for those tensors: a
+    whole-list step is refused (FLASHOPT_ERR_NULL) until set_grads gives them
+    again, and the binding keeps no reference to the released gradients."""
+    sizes = [4097, 33]
+    states = [F.TensorState(n, "adamw", "cuda") for n in sizes]
+    for st in states:
+        F.flashopt_tensor_init(st, torch.zeros(st.numel, device="cuda"))
+    gs = [torch.ones(n, dtype=torch.bfloat16, device="cuda") * 1e-3 for n in sizes]
+    lst = F.FlashoptList(states, gs)
+    F.step(lst, "adamw", W.ADAMW_HP, 1)                  # the list's own gradients
+    g0 = torch.ones(sizes[0], dtype=torch.bfloat16, device="cuda")
+    F.step_range(lst, "adamw", 0, [g0], W.ADAMW_HP, 2)
+    assert lst.grads[0] is None and lst.grads[1] is gs[1]
+    with pytest.raises(F.FlashoptError) as e:
+        F.step(lst, "adamw", W.ADAMW_HP, 3)
+    assert e.value.status == -1                          # FLASHOPT_ERR_NULL
+    F.flashopt_list_set_grads(lst, gs)
+    F.step(lst, "adamw", W.ADAMW_HP, 3)
+    torch.cuda.synchronize()
+
+
 def test_range_launch_of_a_large_tensor_after_a_small_one():
     """A range launch whose first tile is not 0 in the one-wave-per-tile form
     (the range holds 16384 tiles): equal to the whole-list step bit for bit."""
