@@ -199,6 +199,10 @@ class _FlashOptimizer(torch.optim.Optimizer):
                 t = steps.pop() + 1
                 F.flashopt_list_set_grads(lst, [p.grad.view(-1) for p in params])
                 F.step(lst, self.kind, self._hp(group), t)
+                # the list keeps no gradient after the launch, so zero_grad()
+                # frees them as with any torch optimizer (stream-ordered: the
+                # memory is reused only after the launch has run)
+                F.flashopt_list_set_grads(lst, [None] * len(params))
                 for p in params:
                     self.state[p]["step"] = t
             else:

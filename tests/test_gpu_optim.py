@@ -370,3 +370,31 @@ def test_bucketed_gradient_release_equals_step_after_backward(kind, bucket):
                         for p in params])
     for (ta, ca, sa, na), (tb, cb, sb, nb) in zip(*results):
         assert torch.equal(ta, tb) and torch.equal(ca, cb) and torch.equal(sa, sb) and na == nb
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
+def test_step_keeps_no_gradient_alive(kind):
+    """As with torch's optimizers, step() followed by zero_grad() leaves no
+    gradient allocated: between iterations the allocated memory is the
+    parameters and the optimizer state only (a list that kept the last
+    gradients would hold 2 B/param more through the next forward and
+    backward)."""
+    width, layers = 1024, 4
+    torch.cuda.manual_seed(10)
+    model = torch.nn.Sequential(*[torch.nn.Linear(width, width, bias=False, device="cuda",
+                                                  dtype=torch.bfloat16) for _ in range(layers)])
+    x = torch.randn(8, width, device="cuda", dtype=torch.bfloat16,
+                    generator=torch.Generator("cuda").manual_seed(11))
+    # one forward and backward first: the BLAS library's workspace is
+    # allocated on a process's first products and stays
+    model(x).float().pow(2).mean().backward()
+    model.zero_grad(set_to_none=True)
+    opt = make_opt(kind, list(model.parameters()))
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    for _ in range(2):
+        model(x).float().pow(2).mean().backward()
+        opt.step()
+        opt.zero_grad(set_to_none=True)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == base
