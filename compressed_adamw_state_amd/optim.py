@@ -12,7 +12,9 @@ parameter group (or, with gradient release, one launch per parameter from
 its gradient hook, after which the gradient is dropped; with
 release_bucket_bytes > 0, one launch per bucket of consecutive parameters
 whose gradients arrived one after another, once the bucket holds that many
-bytes of gradients, the last bucket at step()).  As in torch.optim,
+bytes of gradients, the last bucket at step()).  Gradient release steps at
+every backward pass, so it is for training without gradient accumulation
+over micro-batches (as the page's practical advice puts it).  As in torch.optim,
 a parameter whose gradient is None is skipped and every parameter keeps its
 own step count; a group where that leaves parameters out, or where the
 counts differ, is stepped by one launch per parameter.
