@@ -327,6 +327,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
                     self.state[p]["step"] = t
 
     def state_dict(self) -> dict:
+        self._flush_bucket()             # an open release bucket belongs to this state
         if self.capturable:
             self._sync_steps()
         sd = {"kind": self.kind, "param_groups": [], "state": {}}
@@ -345,6 +346,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         return sd
 
     def load_state_dict(self, sd: dict) -> None:
+        self._flush_bucket()             # stepped, then overwritten below
         if sd.get("kind") != self.kind:
             raise ValueError(f"checkpoint is for {sd.get('kind')}, not {self.kind}")
         saved = sd["param_groups"]

@@ -398,3 +398,25 @@ def test_step_keeps_no_gradient_alive(kind):
         opt.zero_grad(set_to_none=True)
     torch.cuda.synchronize()
     assert torch.cuda.memory_allocated() == base
+
+
+def test_checkpoint_during_bucketed_release_includes_the_open_bucket():
+    """state_dict() taken after backward but before step() with a bucket
+    still open steps that bucket first: the checkpoint equals the one taken
+    after step(), codes, scales and step counts."""
+    torch.cuda.manual_seed(12)
+    model = torch.nn.Sequential(*[torch.nn.Linear(256, 256, device="cuda", dtype=torch.bfloat16)
+                                  for _ in range(3)])
+    x = torch.randn(4, 256, device="cuda", dtype=torch.bfloat16,
+                    generator=torch.Generator("cuda").manual_seed(13))
+    opt = make_opt("adamw", list(model.parameters()), release=True)
+    opt.release_bucket_bytes = 1 << 40                   # one bucket, open until step()
+    model(x).float().pow(2).mean().backward()
+    assert opt._bucket is not None
+    early = opt.state_dict()
+    opt.step()
+    late = opt.state_dict()
+    for i in late["state"]:
+        a, b = early["state"][i], late["state"][i]
+        assert a["step"] == b["step"] == 1
+        assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["scales"], b["scales"])
