@@ -222,6 +222,25 @@ def test_lion_hyperparameter_variants_and_edge_gradients():
         r.compare(f"lion hp {t}")
 
 
+def test_sgd_hyperparameter_variants_and_edge_gradients():
+    # zero, subnormal and outlier gradients, special weights (zeros,
+    # subnormals, powers of two), and settings that isolate each coefficient:
+    # no momentum (the closed form theta - lr*(g + wd*theta)), no decay, a
+    # frozen step (lr = 0), heavy momentum and a large rate
+    base = W.ragged([4097, 1000, 33, 2048 * 2], seed=22, steps=1, optimizer="sgd")
+    w = W.Workload("sgd_edges", base.tensors, "sgd", 6, 22, "mixed", 1e-2, W.SGD_HP,
+                   special_theta=True)
+    r = Run(w, "full")
+    for t, hp in enumerate([W.SGD_HP,
+                            dict(lr=0.1, momentum=0.0, weight_decay=1e-4),
+                            dict(lr=0.05, momentum=0.9, weight_decay=0.0),
+                            dict(lr=0.0, momentum=0.9, weight_decay=1e-4),
+                            dict(lr=0.01, momentum=0.99, weight_decay=5e-4),
+                            dict(lr=3.0, momentum=0.5, weight_decay=1e-2)], 1):
+        r.step(t, hp)
+        r.compare(f"sgd hp {t}")
+
+
 @pytest.mark.parametrize("opt", ["adamw", "sgd", "lion"])
 def test_non_finite_gradients_stay_in_their_groups(opt):
     """Non-finite gradients are outside the contract, but they must neither
