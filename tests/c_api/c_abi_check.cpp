@@ -186,6 +186,12 @@ int run(int32_t kind, Mode mode, hipStream_t stream) {
                 for (int i = 0; i < b[1]; ++i) g[i] = dev[(size_t)(b[0] + i)].grad;
                 FO_OK(flashopt_adamw_step_range(list, b[0], b[1], g, &adam, t, stream));
             }
+            // the ranges' gradients served those launches only: a whole-list
+            // step is refused until the gradients are given again
+            if (flashopt_adamw_step(list, &adam, t + 1, stream) != FLASHOPT_ERR_NULL) {
+                std::fprintf(stderr, "%s: whole-list step accepted after range launches\n", name);
+                return 1;
+            }
         } else if (kind == FLASHOPT_KIND_ADAMW) {
             FO_OK(flashopt_adamw_step(list, &adam, t, stream));
         } else if (kind == FLASHOPT_KIND_LION) {
