@@ -28,7 +28,9 @@ bit.
 capturable=True keeps each group's step counter and hyper-parameters in a
 device schedule (flashopt_*_step_scheduled), so step() can be captured in a
 HIP graph (torch.cuda.graph) and replayed; update_schedules() pushes
-changed hyper-parameters between replays (AdamW's betas stay fixed).
+changed hyper-parameters between replays (AdamW's betas stay fixed).  A
+replay reads the gradients at the addresses captured, so they must stay
+static (zero_grad(set_to_none=False)).
 
 A parameter group with "compress": False (the page's practical advice:
 compression can be switched off for layers that are sensitive to it) keeps
