@@ -14,12 +14,20 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "flashopt.hip")
+CSRC = os.path.join(PKG, "csrc")
+# translation units of libflashopt.so: the fused step (hot path), the
+# uncompressed kinds, one tensor's codec and state, the codec ablations, the
+# measurement probes, the device schedules, and the C ABI of tensor lists
+UNITS = ["step.hip", "step_fp32.hip", "tensor.hip", "ablation.hip", "probe.hip", "schedule.hip",
+         "list.hip"]
+SOURCES = [os.path.join(CSRC, u) for u in UNITS] + [
+    os.path.join(CSRC, h) for h in ("codec.hpp", "device.hpp", "host.hpp", "quant.hpp")]
+BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashopt.so")
 ARCH = os.environ.get("FLASHOPT_ARCH", "gfx950")
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -35,7 +43,7 @@ TEST_LIB = os.path.join(ROOT, "tests", "hip", "libcodec_exhaustive.so")
 def build_test_lib(verbose: bool = False) -> str:
     """The exhaustive device check of the codec's short sequences (tests only)."""
     tmp = TEST_LIB + ".tmp"
-    cmd = ["hipcc", *FLAGS, "-o", tmp, TEST_SRC]
+    cmd = ["hipcc", *FLAGS, "-shared", "-o", tmp, TEST_SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -64,8 +72,21 @@ def build_c_check(verbose: bool = False) -> str:
 
 
 def build(verbose: bool = False, extra=()) -> str:
+    """Compile every translation unit (in parallel) and link libflashopt.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(u)[0] + ".o") for u in UNITS]
+
+    def compile_one(k):
+        cmd = ["hipcc", *FLAGS, *extra, "-c", "-o", objs[k], os.path.join(CSRC, UNITS[k])]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+
+    with ThreadPoolExecutor(min(len(UNITS), os.cpu_count() or 1)) as ex:
+        list(ex.map(compile_one, range(len(UNITS))))
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", *FLAGS, *extra, "-o", tmp, SRC]
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
