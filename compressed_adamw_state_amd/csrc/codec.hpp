@@ -237,20 +237,25 @@ __device__ __forceinline__ float code_factor_fast(uint32_t s16, float qmax) {
     return s16 == 0u ? 0.0f : r;
 }
 
-// Square root from the hardware reciprocal square root: q = rsq(x), g = x*q,
-// the residual x - g*g in one FMA, and the correction g + residual*(q/2) in
-// one more.  Exact for x = 0 (the max keeps q finite) and for every finite
-// x >= 2^-96; sqrt_fast_bad() flags the inputs in between, and Inf or NaN x
-// give NaN (the fused step's quotient guard catches those lanes).
+// Square root from the hardware reciprocal square root y = rsq(x) by one
+// correction in the coupled form of the Newton-Raphson iteration for sqrt(x)
+// and 1/(2 sqrt(x)) (the final step of Markstein's square root: P. Markstein,
+// "IA-64 and Elementary Functions: Speed and Precision", 2000, chapter on
+// square root): g = x*y approximates sqrt(x), the residual x - g*g is exact
+// in one FMA, and g + residual*(y/2) in one more FMA rounds once.  Checked
+// exhaustively to return the correctly rounded root for every finite x >=
+// 2^-96; sqrt_fast_bad() flags 0 <= x < 2^-96 (x = 0 gives 0 * Inf = NaN,
+// tiny x lose bits in the residual), and Inf or NaN x give NaN (the fused
+// step's quotient guard catches those lanes).
 __device__ __forceinline__ float sqrt_fast(float x) {
-    const float q = __builtin_amdgcn_rsqf(fmaxf(x, 0x1p-96f));
+    const float q = __builtin_amdgcn_rsqf(x);
     const float g = x * q;
     const float d = __builtin_fmaf(-g, g, x);
     return __builtin_fmaf(d, 0.5f * q, g);
 }
 
 __device__ __forceinline__ bool sqrt_fast_bad(float x) {
-    return as_u32(x) - 1u < 0x0F7FFFFFu;          // 0 < x < 2^-96 (x >= 0)
+    return as_u32(x) < 0x0F800000u;               // +0 <= x < 2^-96 (x >= +0)
 }
 
 // Re-split of two weights with the gfx950 BF16 convert (RNE).  For theta'

@@ -100,7 +100,7 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
     float z[8], w[8], tn[8], m_new[8], v_new[8], theta_hat[8];
     const float dm = m_step(R.ms);
     const float dv = (kOpt == kAdamW) ? v_step(R.vs) : 0.0f;
-    uint32_t vmin = 0xFFFFFFFFu;           // min over (bits(v') - 1): flags 0 < v' < 2^-96
+    uint32_t vmin = 0xFFFFFFFFu;           // min over bits(v') >= +0: flags v' < 2^-96
     uint32_t tmin = 0xFFFFFFFFu, tmax = 0u;  // exponent fields of theta'
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -124,7 +124,7 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
             const float cgg = a.c2 * gg;
             v_new[j] = bv + cgg;
             w[j] = sqrt_fast(v_new[j]);
-            vmin = min(vmin, as_u32(v_new[j]) - 1u);
+            vmin = min(vmin, as_u32(v_new[j]));
         } else if (kOpt == kSgd) {
             const float decay = s.omega * theta_hat[j];
             const float g2 = g + decay;
@@ -145,9 +145,9 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
         }
     }
     if (kOpt == kAdamW) {
-        if (__builtin_expect(vmin < 0x0F7FFFFFu, 0)) {
+        if (__builtin_expect(vmin < 0x0F800000u, 0)) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)                 // 0 < v' < 2^-96: IEEE square root
+            for (int j = 0; j < 8; ++j)                 // v' < 2^-96 (or 0): IEEE square root
                 if (sqrt_fast_bad(v_new[j])) w[j] = __builtin_sqrtf(v_new[j]);
         }
         // u = m' / (w*kappa + eps) by div_rn; a lane with any quotient outside

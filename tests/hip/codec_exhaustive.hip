@@ -122,8 +122,8 @@ __global__ void __launch_bounds__(256) all_inputs(uint32_t* count, uint32_t* exa
                 c[11]++; ex[11] = bits;
             }
         }
-        // 6: the general path is used for 0 < x < 2^-96 only
-        if (!(bits >> 31) && sqrt_fast_bad(x) != (x > 0.0f && x < 0x1p-96f)) {
+        // 6: the general path is used for +0 <= x < 2^-96 only
+        if (!(bits >> 31) && sqrt_fast_bad(x) != (x >= 0.0f && x < 0x1p-96f)) {
             c[6]++; ex[6] = bits;
         }
     }
