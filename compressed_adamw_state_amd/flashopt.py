@@ -121,6 +121,11 @@ SIGNATURES = {
     "flashopt_sgd_step_one": (ctypes.c_int, [_P, _I32, _P, ctypes.POINTER(SGDHparams), _I64,
                                              _P]),
     "flashopt_stream_probe": (ctypes.c_int, [_P, _P]),
+    "flashopt_mix_ceiling": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
+    "flashopt_adamw_step_noalloc": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32,
+                                                   ctypes.POINTER(AdamWHparams), _I64, _P]),
+    "flashopt_stream_sweep": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                             _I32, _I64, _P]),
     "flashopt_lion_step": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
     "flashopt_adamw_schedule_init": (ctypes.c_int, [_P, ctypes.POINTER(AdamWHparams), _I64, _P]),
     "flashopt_adamw_step_scheduled": (ctypes.c_int, [_P, _P, _P]),
@@ -399,6 +404,48 @@ def flashopt_stream_probe(lst: FlashoptList, stream=None) -> None:
     loads and stores with one XOR per word instead of the update.  Overwrites
     the state."""
     _check("flashopt_stream_probe", lib().flashopt_stream_probe(lst.handle, _stream(stream)))
+
+
+NOALLOC_MAX_TENSORS = 4096
+
+
+def flashopt_adamw_step_noalloc(states: Sequence[TensorState], grads: Sequence[torch.Tensor],
+                                hp: dict, step: int, stream=None) -> None:
+    """The whole-list AdamW step without a handle or workspace
+    (include/flashopt.h): the descriptor table lives in the library's own
+    device array, so the call allocates nothing on the device."""
+    arr = (Tensor * max(len(states), 1))()
+    for i, (st, g) in enumerate(zip(states, grads)):
+        arr[i] = st.descriptor(g)
+    h = _adam(hp)
+    _check("flashopt_adamw_step_noalloc", lib().flashopt_adamw_step_noalloc(
+        arr, len(states), ctypes.byref(h), step, _stream(stream)))
+
+
+def flashopt_mix_ceiling(theta: torch.Tensor, grad: torch.Tensor, codes: torch.Tensor,
+                         scales: torch.Tensor, n: int, stream=None) -> None:
+    """Ceiling of the step's byte mix (include/flashopt_probe.h) over flat
+    buffers of n parameters: theta, grad 2n bytes, codes 3n, scales n/8.
+    Overwrites theta, codes and scales."""
+    for t, need in ((theta, 2 * n), (grad, 2 * n), (codes, 3 * n), (scales, n // 8)):
+        assert t.is_contiguous() and t.numel() * t.element_size() >= need
+    _check("flashopt_mix_ceiling", lib().flashopt_mix_ceiling(
+        _ptr(theta), _ptr(grad), _ptr(codes), _ptr(scales), n, _stream(stream)))
+
+
+def flashopt_stream_sweep(reads: Sequence[torch.Tensor], writes: Sequence[torch.Tensor],
+                          nbytes: int, in_place: bool = False, stream=None) -> None:
+    """Stream-count sweep (include/flashopt_probe.h): len(reads) buffers read,
+    len(writes) written, nbytes each; in place, `writes` must be the first
+    len(writes) of `reads`."""
+    if in_place and any(a is not b for a, b in zip(writes, reads[:len(writes)])):
+        raise ValueError("in place: writes must be reads[:len(writes)]")
+    for t in list(reads) + list(writes):
+        assert t.is_contiguous() and t.numel() * t.element_size() >= nbytes
+    r = (ctypes.c_void_p * max(len(reads), 1))(*[_ptr(t) for t in reads])
+    w = (ctypes.c_void_p * max(len(writes), 1))(*[_ptr(t) for t in writes])
+    _check("flashopt_stream_sweep", lib().flashopt_stream_sweep(
+        len(reads), len(writes), r, w, int(in_place), nbytes, _stream(stream)))
 
 
 def _adam(hp: dict) -> AdamWHparams:

@@ -5,7 +5,8 @@
  * Training" (digest page, "Core method > Fused optimizer step", Alg. 4) fuses
  * the whole update into one pass so that it costs no more memory traffic than
  * a standard optimizer step: the step is meant to be bound by HBM bandwidth.
- * This probe measures that bound for the step's own access pattern.
+ * These probes measure that bound: for the step's own access pattern, for
+ * the best pattern of the step's byte mix, and for plain streams.
  */
 #ifndef FLASHOPT_PROBE_H
 #define FLASHOPT_PROBE_H
@@ -27,6 +28,37 @@ extern "C" {
  * tensor: FLASHOPT_ERR_ARG / FLASHOPT_ERR_NULL otherwise); one launch on
  * `stream`, nothing allocated, no synchronisation. */
 int flashopt_stream_probe(const flashopt_list* list, void* stream);
+
+/* The practical ceiling of the AdamW step's traffic: the same bytes per
+ * parameter (read 7.125, write 5.125) over the same four read and three
+ * written streams, in place like the step, but over flat buffers with the
+ * best access pattern the byte mix allows (every load and store a fully
+ * coalesced 16 bytes per lane; a wave loads one 2048-parameter tile, then
+ * stores it).  Over n parameters (n a multiple of 2048):
+ *   theta   uint16[n]           theta ^= grad            (read and written)
+ *   grad    uint16[n]           read only
+ *   codes   uint8[3n]           every byte ^= 0x5A       (read and written)
+ *   scales  uint16[n/16]        every 16-bit word ^= 1   (read and written)
+ * (3n code bytes: rho, m and v codes; n/16 scale words: two FP16 per group
+ * of 32).  DESTRUCTIVE.  Errors: FLASHOPT_ERR_SIZE (n < 0 or not a multiple
+ * of 2048), FLASHOPT_ERR_NULL, FLASHOPT_ERR_ALIGN (any pointer not 16-byte
+ * aligned).  One launch on `stream`, nothing allocated, no synchronisation. */
+int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, uint16_t* scales,
+                         int64_t n, void* stream);
+
+/* Stream-count sweep: `nread` device buffers read and `nwrite` written, each
+ * of `bytes` bytes (a multiple of 16), one 16-byte unit of each per thread.
+ * Written value: the XOR of the units read, its first word XORed with the
+ * written buffer's index w (so buffer w holds the XOR of the read buffers
+ * with w in every fourth word); with nwrite = 0 nothing is written.
+ * in_place != 0: the written buffers are reads[0 .. nwrite-1] (nwrite <=
+ * nread) and `writes` is ignored; else writes[0 .. nwrite-1].  (nread,
+ * nwrite) must be one of (1,0) (0,1) (1,1) (2,1) (1,2) (2,2) (3,2) (4,3)
+ * (7,5) (4,0) (0,4), else FLASHOPT_ERR_ARG.  Host arrays of device
+ * pointers; buffers 16-byte aligned (FLASHOPT_ERR_ALIGN) and non-NULL
+ * (FLASHOPT_ERR_NULL).  One launch on `stream`, nothing allocated. */
+int flashopt_stream_sweep(int32_t nread, int32_t nwrite, const void* const* reads,
+                          void* const* writes, int32_t in_place, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,3 +40,54 @@ def test_stream_probe_touches_every_byte():
         np.testing.assert_array_equal(f["v_code"], b["v_code"] ^ b["rho"].view(np.uint8))
         np.testing.assert_array_equal(f["m_scale"], b["m_scale"] ^ 1)
         np.testing.assert_array_equal(f["v_scale"], b["v_scale"] ^ 1)
+
+
+def test_mix_ceiling_touches_every_byte():
+    """flashopt_mix_ceiling: theta ^= grad, every code byte ^= 0x5A, every
+    scale word ^= 1, over 5 tiles of 2048 parameters (and nothing beyond)."""
+    gen = torch.Generator().manual_seed(8)
+    n = 2048 * 5
+    pad = 64
+    theta = torch.randint(-2 ** 15, 2 ** 15, (n + pad,), generator=gen, dtype=torch.int16)
+    grad = torch.randint(-2 ** 15, 2 ** 15, (n + pad,), generator=gen, dtype=torch.int16)
+    codes = torch.randint(0, 256, (3 * n + pad,), generator=gen, dtype=torch.uint8)
+    scales = torch.randint(-2 ** 15, 2 ** 15, (n // 16 + pad,), generator=gen, dtype=torch.int16)
+    d = [t.cuda() for t in (theta, grad, codes, scales)]
+    F.flashopt_mix_ceiling(d[0], d[1], d[2], d[3], n)
+    torch.cuda.synchronize()
+    th, gr, cd, sc = (t.cpu() for t in d)
+    assert torch.equal(th[:n], theta[:n] ^ grad[:n]) and torch.equal(th[n:], theta[n:])
+    assert torch.equal(gr, grad)
+    assert torch.equal(cd[:3 * n], codes[:3 * n] ^ 0x5A) and torch.equal(cd[3 * n:], codes[3 * n:])
+    assert torch.equal(sc[:n // 16], scales[:n // 16] ^ 1)
+    assert torch.equal(sc[n // 16:], scales[n // 16:])
+
+
+@pytest.mark.parametrize("rw", [(1, 0), (0, 1), (1, 1), (2, 1), (1, 2), (2, 2), (3, 2), (4, 3),
+                                (7, 5), (4, 0), (0, 4)])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_stream_sweep_values(rw, in_place):
+    """flashopt_stream_sweep writes the XOR of the buffers read into every
+    written buffer, with the written buffer's index in every fourth word."""
+    r, w = rw
+    if in_place and w > r:
+        pytest.skip("in place needs nwrite <= nread")
+    gen = torch.Generator().manual_seed(9)
+    words = 4 * 1000 + 4            # 1001 units of 16 bytes: a partial block
+    reads = [torch.randint(-2 ** 31, 2 ** 31 - 1, (words,), generator=gen, dtype=torch.int32)
+             for _ in range(r)]
+    writes = [] if in_place else [torch.zeros(words, dtype=torch.int32) for _ in range(w)]
+    dr = [t.cuda() for t in reads]
+    dw = dr[:w] if in_place else [t.cuda() for t in writes]
+    F.flashopt_stream_sweep(dr, dw, 4 * words, in_place=in_place)
+    torch.cuda.synchronize()
+    acc = torch.zeros(words, dtype=torch.int32)
+    for t in reads:
+        acc ^= t
+    outs = dr[:w] if in_place else dw
+    for k, o in enumerate(outs):
+        exp = acc.clone()
+        exp[0::4] ^= k
+        assert torch.equal(o.cpu(), exp), (rw, in_place, k)
+    for k in range(w if in_place else 0, r):
+        assert torch.equal(dr[k].cpu(), reads[k])
