@@ -181,10 +181,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
             # the hooks already stepped every parameter of this iteration (a
             # last bucket is stepped now); the next forward must see their
             # updates
-            self._flush_bucket()
-            cur = torch.cuda.current_stream()
-            for s in self._side:
-                cur.wait_stream(s)
+            self._join_release()
             return loss
         if self.capturable:
             self._step_scheduled()
@@ -309,6 +306,17 @@ class _FlashOptimizer(torch.optim.Optimizer):
         if b["bytes"] >= self.release_bucket_bytes:
             self._flush_bucket()
 
+    def _join_release(self) -> None:
+        """Step a release bucket still open, then make the current stream
+        wait for every release launch issued so far (on the side streams
+        too): work queued on the current stream afterwards -- the next
+        forward, a checkpoint's copies, an export -- sees the updated state,
+        and no release launch still running can overwrite what it writes."""
+        self._flush_bucket()
+        cur = torch.cuda.current_stream()
+        for s in self._side:
+            cur.wait_stream(s)
+
     def _flush_bucket(self) -> None:
         b, self._bucket = self._bucket, None
         if b is None:
@@ -329,7 +337,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
                     self.state[p]["step"] = t
 
     def state_dict(self) -> dict:
-        self._flush_bucket()             # an open release bucket belongs to this state
+        self._join_release()             # an open release bucket belongs to this state
         if self.capturable:
             self._sync_steps()
         sd = {"kind": self.kind, "param_groups": [], "state": {}}
@@ -348,7 +356,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         return sd
 
     def load_state_dict(self, sd: dict) -> None:
-        self._flush_bucket()             # stepped, then overwritten below
+        self._join_release()             # stepped and finished, then overwritten below
         if sd.get("kind") != self.kind:
             raise ValueError(f"checkpoint is for {sd.get('kind')}, not {self.kind}")
         saved = sd["param_groups"]
@@ -382,6 +390,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
 
     def export_fp32(self, p: torch.Tensor):
         """(theta_hat, m, v) of one parameter in FP32 (v None unless AdamW)."""
+        self._join_release()
         st = self.state[p]["flash"]
         th = torch.empty(st.numel, dtype=torch.float32, device=st.theta.device)
         m = torch.empty_like(th)

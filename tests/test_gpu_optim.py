@@ -420,3 +420,55 @@ def test_checkpoint_during_bucketed_release_includes_the_open_bucket():
         a, b = early["state"][i], late["state"][i]
         assert a["step"] == b["step"] == 1
         assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["scales"], b["scales"])
+
+
+@pytest.mark.parametrize("what", ["state_dict", "load_state_dict", "export_fp32"])
+def test_checkpoint_and_export_wait_for_side_stream_release(what):
+    """With release_streams=2 the release launches run on side streams:
+    state_dict(), load_state_dict() and export_fp32() taken after backward
+    with a bucket still open step it and wait for every release launch
+    before touching the state, so they read (or overwrite) the state after
+    the step, equal to the single-stream optimizer's.  The layers are large
+    enough (4 x 4096 x 4096) that a range launch still runs when the copies
+    are queued."""
+    width, layers = 4096, 4
+    x = torch.randn(4, width, device="cuda", dtype=torch.bfloat16,
+                    generator=torch.Generator("cuda").manual_seed(15))
+    runs = []
+    for streams in (1, 2):
+        torch.cuda.manual_seed(14)
+        model = torch.nn.Sequential(*[torch.nn.Linear(width, width, bias=False, device="cuda",
+                                                      dtype=torch.bfloat16)
+                                      for _ in range(layers)])
+        params = list(model.parameters())
+        opt = make_opt("adamw", params, release=True, streams=streams)
+        opt.release_bucket_bytes = 3 * width * width * 2    # closes once, one bucket stays open
+        model(x).float().pow(2).mean().backward()
+        if what == "state_dict":
+            sd = opt.state_dict()
+            runs.append([(sd["state"][i]["codes"], sd["state"][i]["scales"])
+                         for i in sorted(sd["state"])])
+        elif what == "export_fp32":
+            runs.append([opt.export_fp32(p) for p in params])
+        else:
+            ckpt = {"kind": "adamw", "param_groups": [dict(opt.param_groups[0],
+                                                           params=list(range(layers)))],
+                    "state": {i: {"numel": p.numel(),
+                                  "codes": torch.full_like(opt.state[p]["flash"].codes, 7),
+                                  "scales": torch.full_like(opt.state[p]["flash"].scales, 9),
+                                  "step": 5} for i, p in enumerate(params)}}
+            opt.load_state_dict(ckpt)
+            torch.cuda.synchronize()
+            for i, p in enumerate(params):
+                st = opt.state[p]["flash"]
+                assert torch.equal(st.codes, ckpt["state"][i]["codes"]), (streams, i)
+                assert torch.equal(st.scales, ckpt["state"][i]["scales"]), (streams, i)
+            runs.append(None)
+        torch.cuda.synchronize()
+    if what == "state_dict":
+        for (ca, sa), (cb, sb) in zip(*runs):
+            assert torch.equal(ca, cb) and torch.equal(sa, sb)
+    elif what == "export_fp32":
+        for a, b in zip(*runs):
+            for ta, tb in zip(a, b):
+                assert torch.equal(ta, tb)
