@@ -195,27 +195,82 @@ def test_fp32_and_compressed_steps_share_the_update(orc, optimizer, hp):
         np.testing.assert_array_equal(f.v.view(np.uint32), outs[2].view(np.uint32))
 
 
+def _phi_inv(z):
+    return z / (2.0 - np.abs(z))
+
+
+def _adam_quotient(m, v, kappa, eps):
+    return m / (kappa * np.sqrt(np.maximum(v, 0.0)) + eps)
+
+
 @pytest.mark.parametrize("n", [64, 1024])
 def test_compressed_trajectory_stays_near_fp32_adamw(orc, n):
     """The compressed AdamW run against the uncompressed one (pinned above to
-    torch in float64) from the same weights and gradients, 10 steps: step 1
-    differs only by the split's rounding (<= h/254 + 1 ulp); afterwards the
-    quantised m and v (about 1 % each in the companded domain) move each
-    update by about 1 %, so the weights stay within a few percent of one lr
-    per step and the typical deviation is under 2 % of the distance moved."""
+    torch in float64), from the same weights and gradients, 10 steps.  The
+    two share the update bit for bit (previous test), so they differ only by
+    what the compressed state stores, and the deviation is bounded, element
+    by element and step by step, by the quantisation errors the pinned bounds
+    allow:
+
+      m:  |m_hat - m_f| <= Bm(t) = b1 Bm(t-1) + Qm(t), with Qm the momentum
+          dequantisation bound (companded error s/254, the bound pinned in
+          test_oracle_quant, carried through phi_m^-1);
+      v:  |v_hat - v_f| <= Bv(t) = b2 Bv(t-1) + Qv(t), Qv from the variance
+          bound (error s/510 of sqrt(v));
+      theta: |theta_hat - theta_f| <= B(t) = lambda B(t-1) + alpha_t du(t)
+          + h/254 + rounding, where du(t) is the largest change of the Adam
+          quotient m'/(kappa sqrt(v') + eps) over the box m' +- b1 Bm(t-1),
+          v' +- b2 Bv(t-1) around the compressed run's values (the quotient is
+          monotone in each, so its extremes are at the corners), and h/254 the
+          split's bound (h = ULP(theta')/2).
+
+    That is the sum over steps of lr-scaled quotient errors plus the split's
+    h/254, with the companding bounds as the only source.  A few float32
+    roundings per operation are added as slack; everything else is exact."""
     rng = np.random.default_rng(n)
     th0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
     st = orc.State(th0, "adamw")
     f = orc.StateFP32(orc.unsplit(st.tb, st.rho), "adamw")
+    b_theta = np.zeros(n)
+    b_m = np.zeros(n)
+    b_v = np.zeros(n)
+    group = lambda a: np.repeat(a.view(np.float16).astype(np.float64), 32)[:n]
     for t in range(1, 11):
         g = bf16_bits(rng.standard_normal(n) * 1e-3)
-        orc.step(st, g, t, HP)
+        b1, c1, b2, c2, alpha, kappa, eps, lam = (float(x) for x in orc.adamw_scalars(
+            HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], t))
+        theta_n, m_new, v_new = (x.astype(np.float64) for x in orc.step(st, g, t, HP,
+                                                                          want_fp32=True))
         orc.step_fp32(f, g, t, HP)
+        # the update's inputs: m' and v' of the two runs differ by at most
+        dm = b1 * b_m + 3 * ulp32(np.abs(m_new) + b1 * b_m)
+        dv = b2 * b_v + 3 * ulp32(np.abs(v_new) + b2 * b_v)
+        corners = [_adam_quotient(m_new + a * dm, v_new + b * dv, kappa, eps)
+                   for a in (-1, 1) for b in (-1, 1)]
+        u = _adam_quotient(m_new, v_new, kappa, eps)
+        du = np.maximum(np.max(corners, axis=0) - u, u - np.min(corners, axis=0)) \
+            + 6 * ulp32(np.abs(u) + 1e-30)
+        e = (st.tb.astype(np.int64) >> 7) & 0xFF                # the new theta' exponent field
+        h = 2.0 ** (np.maximum(e, 1) - 135)                     # ULP(theta')/2
+        b_theta = lam * b_theta + alpha * du + h / 254 + 4 * ulp32(np.abs(theta_n) + b_theta)
+        # the codes just written: dequantisation bounds around the stored values
+        m_hat = orc.dequant_m(st.qm, st.sm).astype(np.float64)
+        z_hat = 2 * m_hat / (1 + np.abs(m_hat))
+        dz = group(st.sm) / 254 * 1.01 + 8 * ulp32(z_hat)
+        assert np.all(np.abs(z_hat) + dz < 2)
+        q_m = np.maximum(_phi_inv(z_hat + dz) - m_hat, m_hat - _phi_inv(z_hat - dz))
+        v_hat = orc.dequant_v(st.qv, st.sv).astype(np.float64)
+        w_hat = np.sqrt(v_hat)
+        dw = group(st.sv) / 510 * 1.01 + 8 * ulp32(w_hat)
+        q_v = np.maximum((w_hat + dw) ** 2 - v_hat, v_hat - np.maximum(w_hat - dw, 0) ** 2) \
+            + ulp32(v_hat)
+        b_m = dm + q_m
+        b_v = dv + q_v
+        assert np.all(np.abs(m_hat - f.m) <= b_m), t
+        assert np.all(np.abs(v_hat - f.v) <= b_v), t
         dev = np.abs(orc.unsplit(st.tb, st.rho).astype(np.float64) - f.theta)
+        assert np.all(dev <= b_theta), (t, float((dev / b_theta).max()))
+        # not vacuous: the bound stays a few percent of the distance moved
         moved = np.abs(f.theta - th0.astype(np.float64))
-        if t == 1:
-            e = (st.tb.astype(np.int64) >> 7) & 0xFF                # theta' exponent field
-            h = 2.0 ** (np.maximum(e, 1) - 135)                     # ULP(theta')/2
-            assert np.all(dev <= h / 254 + 2 * ulp32(f.theta))
-        assert dev.max() <= 0.1 * t * HP["lr"]
+        assert np.median(b_theta / np.maximum(moved, 1e-12)) < 0.1, t
         assert np.median(dev / np.maximum(moved, 1e-12)) < 0.02
