@@ -143,15 +143,25 @@ static inline DevTensor to_dev(const flashopt_tensor& t) {
 // tiles, and from 64K tiles on one wave per tile is ~2 % faster.
 constexpr int64_t kSplitTiles = 16384;
 
+// Tiles at the end of a gradient-release launch (one tensor, or a bucket of
+// them) that run as sub-tile waves (the hybrid form): about one round of the
+// waves the GPU holds at once (256 CUs x 4 SIMDs x 5 waves = 5120).
+#ifndef FLASHOPT_RELEASE_TAIL
+#define FLASHOPT_RELEASE_TAIL 2560
+#endif
+constexpr int64_t kReleaseTail = FLASHOPT_RELEASE_TAIL;
+
 // ---- launches exported by the kernel files ----------------------------------
 
 // step.hip: one launch of the compressed step (opt kAdamW / kSgd / kLion;
 // linv: AdamW with linear variance codes) over tiles [tile0, tile0 + ntiles)
 // of a list (table, tile_begin) or, with table == nullptr, of the single
-// tensor `one`; and the scheduled step over a whole list.
+// tensor `one`; a launch of at least kSplitTiles tiles with tail > 0 takes the
+// hybrid form, its last `tail` tiles as 512-element sub-tile waves (gradient
+// release passes kReleaseTail); and the scheduled step over a whole list.
 int launch_step_compressed(int opt, bool linv, const DevTensor* table, const int64_t* tile_begin,
                            int32_t count, int64_t tile0, int64_t ntiles, const DevTensor& one,
-                           const StepScalars& P, hipStream_t st);
+                           const StepScalars& P, int64_t tail, hipStream_t st);
 int launch_step_scheduled(int opt, const DevTensor* table, const int64_t* tile_begin,
                           int32_t count, int64_t total_tiles, const uint32_t* scalars,
                           hipStream_t st);

@@ -124,21 +124,22 @@ int flashopt_list_set_grads(flashopt_list* L, const uint16_t* const* grads, void
 }
 
 // One launch of the step over the tiles [tile0, tile0 + ntiles) of a list
-// (table, tile_begin) or, with table == nullptr, of the single tensor `one`.
+// (table, tile_begin) or, with table == nullptr, of the single tensor `one`;
+// tail > 0: the compressed step's hybrid form (gradient-release launches).
 static int launch_step(int opt, int32_t kind, const DevTensor* table, const int64_t* tile_begin,
                        int32_t count, int64_t tile0, int64_t ntiles, const DevTensor& one,
-                       const StepScalars& P, void* stream) {
+                       const StepScalars& P, int64_t tail, void* stream) {
     if (ntiles == 0) return FLASHOPT_OK;
     hipStream_t st = (hipStream_t)stream;
     if (is_fp32(kind))
         return launch_step_fp32(opt, table, tile_begin, count, tile0, ntiles, one, P, st);
     return launch_step_compressed(opt, is_linv(kind), table, tile_begin, count, tile0, ntiles, one,
-                                  P, st);
+                                  P, tail, st);
 }
 
 static int launch_list(int opt, const flashopt_list* L, const StepScalars& P, void* stream) {
     return launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, 0, L->total_tiles,
-                       DevTensor{}, P, stream);
+                       DevTensor{}, P, 0, stream);
 }
 
 static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint16_t* grad,
@@ -147,7 +148,8 @@ static int launch_one(int opt, const flashopt_list* L, int32_t index, const uint
     if (t.numel == 0) return FLASHOPT_OK;
     DevTensor one = to_dev(t);
     one.grad = (uint64_t)grad;
-    return launch_step(opt, L->kind, nullptr, nullptr, 1, 0, tiles_of(t.numel), one, P, stream);
+    return launch_step(opt, L->kind, nullptr, nullptr, 1, 0, tiles_of(t.numel), one, P,
+                       kReleaseTail, stream);
 }
 
 static int check_one(const flashopt_list* L, int32_t index, const uint16_t* grad) {
@@ -267,7 +269,7 @@ static int launch_range(int opt, flashopt_list* L, int32_t first, int32_t count,
     if (st != FLASHOPT_OK) return st;
     const int64_t t0 = L->tile_begin[first], t1 = L->tile_begin[first + count];
     st = launch_step(opt, L->kind, L->d_table, L->d_tile_begin, L->count, t0, t1 - t0,
-                     DevTensor{}, P, stream);
+                     DevTensor{}, P, kReleaseTail, stream);
     for (int32_t i = 0; i < count; ++i) L->host[first + i].grad = nullptr;
     for (int32_t i = 0; i < count; ++i)
         if (L->host[first + i].numel > 0) L->all_have_grad = false;

@@ -19,6 +19,8 @@
 // with DPP, its two FP16 scales one 32-bit word.  Whole tiles take an
 // unguarded vector path; the last tile of a tensor takes a guarded
 // element-wise path.
+#include <algorithm>
+
 #include "host.hpp"
 
 namespace flashopt {
@@ -146,12 +148,22 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
     }
     if (kOpt == kAdamW) {
         if (__builtin_expect(vmin < 0x0F800000u, 0)) {
+            // v' = +0 (a zero gradient over a variance coded 0): sqrt_fast gave
+            // NaN (0 * Inf), the root is +0; 0 < v' < 2^-96: the IEEE square root
+            uint32_t tiny = 0xFFFFFFFFu;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)                 // v' < 2^-96 (or 0): IEEE square root
-                if (sqrt_fast_bad(v_new[j])) w[j] = __builtin_sqrtf(v_new[j]);
+            for (int j = 0; j < 8; ++j) {
+                if (as_u32(v_new[j]) == 0u) w[j] = 0.0f;
+                tiny = min(tiny, as_u32(v_new[j]) - 1u);
+            }
+            if (__builtin_expect(tiny < 0x0F7FFFFFu, 0)) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (as_u32(v_new[j]) - 1u < 0x0F7FFFFFu) w[j] = __builtin_sqrtf(v_new[j]);
+            }
         }
         // u = m' / (w*kappa + eps) by div_rn; a lane with any quotient outside
-        // the window redoes its eight with the IEEE division
+        // the window rechecks its eight (below)
         float u[8];
         uint32_t qkey = 0u;
 #pragma unroll
@@ -163,13 +175,26 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
             qkey = max(qkey, quot_key(q0, a.quot_neg_lo2));
         }
         if (__builtin_expect(qkey >= a.quot_span, 0)) {
-            // also where v' is Inf or NaN: sqrt_fast returned NaN there
+            // the elements whose quotient is outside the window (the same q0 as
+            // above): a zero m' over a finite denominator gives u = m' exactly
+            // (0 / den keeps the sign of m'), the others (tiny or huge
+            // quotients; v' Inf or NaN, where sqrt_fast returned NaN) the IEEE
+            // square root and division
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                w[j] = __builtin_sqrtf(v_new[j]);
                 const float den0 = w[j] * a.kappa;
                 const float den = den0 + a.eps;
-                u[j] = m_new[j] / den;
+                const float q0 = m_new[j] * rcp_rn(den);
+                if (quot_key(q0, a.quot_neg_lo2) >= a.quot_span) {
+                    if (m_new[j] == 0.0f && __builtin_isfinite(den)) {
+                        u[j] = m_new[j];
+                    } else {
+                        w[j] = __builtin_sqrtf(v_new[j]);
+                        const float d0 = w[j] * a.kappa;
+                        const float d = d0 + a.eps;
+                        u[j] = m_new[j] / d;
+                    }
+                }
             }
         }
 #pragma unroll
@@ -338,6 +363,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
     step_body<kOpt, kLinV, kSplit>(table, tile_begin, count, tile0, ntiles, one, P);
 }
 
+// The hybrid form of a launch (gradient release: one launch per tensor or per
+// bucket): waves [0, nbulk) take one whole tile each, as in step_body, and
+// the last ntiles - nbulk tiles go to one wave per 512-element sub-tile.
+// Waves are dispatched in order, so the launch ends on short waves: its tail
+// (the time the last waves run while SIMDs fall idle) is about a quarter of a
+// whole tile's.  The grid covers every wave (no stride loop).
+template <int kOpt, bool kLinV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void step_kernel_hybrid(
+    const DevTensor* __restrict__ table, const int64_t* __restrict__ tile_begin, int32_t count,
+    int64_t tile0, int64_t ntiles, int64_t nbulk, DevTensor one, StepScalars P) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    TileCursor cur;
+    if (wave < nbulk) {
+        cur.start(table, tile_begin, count, one, ntiles, tile0 + wave);
+        const int64_t e0 = (tile0 + wave - cur.begin) * kTile;
+        if (e0 + kTile <= cur.T.numel) step_tile<kOpt, true, kLinV>(cur.T, e0, lane, P);
+        else step_tile<kOpt, false, kLinV>(cur.T, e0, lane, P);
+        return;
+    }
+    const int64_t item = wave - nbulk;
+    if (item >= (ntiles - nbulk) * kSubTiles) return;
+    const int64_t tile = tile0 + nbulk + item / kSubTiles;
+    cur.start(table, tile_begin, count, one, ntiles, tile);
+    step_sub<kOpt, kLinV>(cur.T, (tile - cur.begin) * kTile, (int)(item % kSubTiles), lane, P);
+}
+
 // The step with its scalars read from a schedule's `scalars` words (written
 // by the advance kernel launched just before on the same stream).
 template <int kOpt, bool kSplit>
@@ -356,7 +408,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
 template <int kOpt, bool kLinV>
 static int launch_fused(const DevTensor* table, const int64_t* tile_begin, int32_t count,
                         int64_t tile0, int64_t ntiles, const DevTensor& one, const StepScalars& P,
-                        hipStream_t st) {
+                        int64_t tail, hipStream_t st) {
+    const int64_t nbulk = ntiles - std::min(tail, ntiles);
+    if (ntiles >= kSplitTiles && tail > 0 &&
+        nbulk + (ntiles - nbulk) * kSubTiles <= kMaxBlocks * kWavesPerBlock) {
+        hipLaunchKernelGGL((step_kernel_hybrid<kOpt, kLinV>),
+                           dim3(grid_for(nbulk + (ntiles - nbulk) * kSubTiles)), dim3(kBlock), 0,
+                           st, table, tile_begin, count, tile0, ntiles, nbulk, one, P);
+        return launch_status();
+    }
     if (ntiles < kSplitTiles)
         hipLaunchKernelGGL((step_kernel<kOpt, kLinV, true>), dim3(grid_for(ntiles * kSubTiles)),
                            dim3(kBlock), 0, st, table, tile_begin, count, tile0, ntiles, one, P);
@@ -369,14 +429,17 @@ static int launch_fused(const DevTensor* table, const int64_t* tile_begin, int32
 // One launch of the compressed step (see host.hpp).
 int launch_step_compressed(int opt, bool linv, const DevTensor* table, const int64_t* tile_begin,
                            int32_t count, int64_t tile0, int64_t ntiles, const DevTensor& one,
-                           const StepScalars& P, hipStream_t st) {
+                           const StepScalars& P, int64_t tail, hipStream_t st) {
     if (linv)
-        return launch_fused<kAdamW, true>(table, tile_begin, count, tile0, ntiles, one, P, st);
+        return launch_fused<kAdamW, true>(table, tile_begin, count, tile0, ntiles, one, P, tail,
+                                          st);
     if (opt == kAdamW)
-        return launch_fused<kAdamW, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
+        return launch_fused<kAdamW, false>(table, tile_begin, count, tile0, ntiles, one, P, tail,
+                                           st);
     if (opt == kSgd)
-        return launch_fused<kSgd, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
-    return launch_fused<kLion, false>(table, tile_begin, count, tile0, ntiles, one, P, st);
+        return launch_fused<kSgd, false>(table, tile_begin, count, tile0, ntiles, one, P, tail,
+                                         st);
+    return launch_fused<kLion, false>(table, tile_begin, count, tile0, ntiles, one, P, tail, st);
 }
 
 // The scheduled step kernel over a whole list, in the same launch form as
