@@ -86,9 +86,13 @@ def read_profile(kind: str, workload: str, kernel_hash: str) -> dict:
 
 
 def build_state(w: W.Workload, grad_sets: int):
+    """The workload's state and `grad_sets` gradient sets, all in one
+    StateArena (theta', gradients, code records and scales each in a region
+    of their own), and one list handle per gradient set."""
     dev = torch.device("cuda")
     states = []
-    arena = F.StateArena([spec.numel for spec in w.tensors], w.optimizer, dev)
+    arena = F.StateArena([spec.numel for spec in w.tensors], w.optimizer, dev, theta=True,
+                         grad_sets=grad_sets)
     for i, spec in enumerate(w.tensors):
         theta = W.draw_theta(w, i, dev)
         st = arena.state(i)
@@ -97,7 +101,8 @@ def build_state(w: W.Workload, grad_sets: int):
         states.append(st)
     grads = []
     for k in range(grad_sets):
-        grads.append([W.draw_grad(w, i, k + 1, dev) for i in range(len(w.tensors))])
+        grads.append([arena.grad(k, i).copy_(W.draw_grad(w, i, k + 1, dev))
+                      for i in range(len(w.tensors))])
     lists = [F.FlashoptList(states, g) for g in grads]
     F.flashopt_state_zero(lists[0])
     torch.cuda.synchronize()
@@ -377,32 +382,195 @@ def cpu_single_thread_flat1m(seconds: float = 3.0) -> float:
     return n * steps / (time.perf_counter() - t0)
 
 
-def cpu_baseline(seconds: float, threads: int):
-    """The oracle as it stands, on a bounded sample of the workload: a
-    2^25-parameter group-aligned slice with the Llama workload's
-    distributions (theta ~ N(0, 0.02), grads N(0, 1e-4)), stepped on
-    `threads` host threads (chunks of whole groups) until `seconds` pass."""
+def cpu_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most
+    16 (the CPU share of one GPU on the benchmark's hosts)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
+def host_fields(st: F.TensorState) -> dict:
+    """theta', rho, momentum and variance codes, both scales of one tensor as
+    contiguous host arrays (unpacked from the interleaved records on the
+    device, then copied)."""
+    n = st.numel
+    nrec, ng = (n + 7) // 8, (n + 31) // 32
+    rec = st.codes[:nrec * 24].view(nrec, 3, 8)
+    sc = st.scales[:ng * 2].view(ng, 2)
+    host = lambda t: t.contiguous().cpu().numpy()
+    return {"tb": host(st.theta.view(torch.int16)).view(np.uint16),
+            "rho": host(rec[:, 0].reshape(-1)[:n]).view(np.int8),
+            "qm": host(rec[:, 1].reshape(-1)[:n]).view(np.int8),
+            "qv": host(rec[:, 2].reshape(-1)[:n]),
+            "sm": host(sc[:, 0]).view(np.uint16), "sv": host(sc[:, 1]).view(np.uint16)}
+
+
+def cpu_baseline(states, grads, t: int, hp: dict, threads: int) -> dict:
+    """The oracle as it stands, timed on one full step of the benchmark's
+    workload: every tensor of the list, from the state the GPU holds after
+    the timed steps and with the gradient set of step t, copied to the host
+    tensor by tensor (the copies and unpacking are not timed) and stepped by
+    the oracle on `threads` host threads over whole 32-element groups."""
     import oracle
-    n = 1 << 25
-    g = torch.Generator().manual_seed(1234)
-    theta = (torch.randn(n, generator=g) * 0.02).numpy()
-    st = oracle.State(theta, "adamw")
-    hp = W.ADAMW_HP
-    grads = [(torch.randn(n, generator=g) * 1e-4).to(torch.bfloat16).view(torch.int16).numpy()
-             .view(np.uint16) for _ in range(2)]
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.step_chunked(st, grads[steps % 2], steps + 1, hp, nthreads=threads)
-        steps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": n * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} AdamW steps over a {n}-parameter slice (Llama-3.1-8B "
-                      f"distributions), {threads} threads, {dt:.1f} s",
+    spent, n = 0.0, 0
+    for st, g in zip(states, grads):
+        f = host_fields(st)
+        o = oracle.State.__new__(oracle.State)
+        o.n, o.optimizer = st.numel, "adamw"
+        for k, v in f.items():
+            setattr(o, k, v)
+        gb = g.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.step_chunked(o, gb, t, hp, nthreads=threads)
+        spent += time.perf_counter() - t0
+        n += st.numel
+        del f, o, gb
+    return {"value": n / spent, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full AdamW step of the benchmark's list ({len(states)} tensors, {n} "
+                      f"params) from the GPU's state after the timed steps, tensor by tensor, "
+                      f"host copies not timed; {threads} threads over whole 32-element groups, "
+                      f"{spent:.1f} s",
+            "oracle_seconds": spent, "params": n,
+            "host_cpus": os.cpu_count(), "host_cpus_available": len(os.sched_getaffinity(0)),
             "cpu_model": cpu_model(),
             "single_thread_flat1m_params_s": cpu_single_thread_flat1m()}
+
+
+def mix_ceiling(n: int, stream, reps: int = 5) -> dict:
+    """flashopt_mix_ceiling over flat buffers of n parameters: the step's own
+    byte mix (7.125 B read, 5.125 B written per parameter, four streams read
+    and three written, in place) with every access a coalesced 16 bytes per
+    lane -- the practical ceiling for the step's traffic."""
+    th = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
+    gr = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
+    cd = torch.randint(0, 255, (3 * n,), dtype=torch.uint8, device="cuda")
+    sc = torch.randint(-2 ** 15, 2 ** 15 - 1, (n // 16,), dtype=torch.int16, device="cuda")
+    F.flashopt_mix_ceiling(th, gr, cd, sc, n, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        F.flashopt_mix_ceiling(th, gr, cd, sc, n, stream)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    best = min(ev[r].elapsed_time(ev[r + 1]) for r in range(reps)) / 1e3
+    nbytes = int(12.25 * n)
+    del th, gr, cd, sc
+    torch.cuda.empty_cache()
+    return {"kernel": "mix_ceiling_kernel (flashopt_mix_ceiling)", "params": n,
+            "bytes_read_per_param": 7.125, "bytes_written_per_param": 5.125,
+            "best_ms": best * 1e3, "gb_s": nbytes / best / 1e9}
+
+
+def pattern_variants(n: int, stream, reps: int = 5, rounds: int = 2) -> list:
+    """flashopt_pattern_probe variants 0-3 and flashopt_mix_ceiling over the
+    same flat buffers of n parameters, alternating, best of `reps` launches
+    per round: the step's traffic under each access pattern."""
+    th = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
+    gr = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
+    cd = torch.randint(0, 255, (3 * n,), dtype=torch.uint8, device="cuda")
+    sc = torch.randint(-2 ** 15, 2 ** 15 - 1, (n // 16,), dtype=torch.int16, device="cuda")
+    names = {0: "records 24 B as 3 x 8 B, 2 buffers (the fused kernel's)",
+             1: "codes as 16-B units", 2: "16-B units by global-to-LDS DMA",
+             3: "records 24 B, 3 buffers (loads before stores)", 4: "mix ceiling (all 16-B, flat)"}
+    rows = {}
+    for _ in range(rounds):
+        for v in range(5):
+            f = (lambda: F.flashopt_mix_ceiling(th, gr, cd, sc, n, stream)) if v == 4 else \
+                (lambda v=v: F.flashopt_pattern_probe(v, th, gr, cd, sc, n, stream))
+            f()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(stream)
+            for k in range(reps):
+                f()
+                ev[k + 1].record(stream)
+            torch.cuda.synchronize()
+            rows.setdefault(v, []).append(min(ev[k].elapsed_time(ev[k + 1]) for k in range(reps)))
+    del th, gr, cd, sc
+    torch.cuda.empty_cache()
+    return [{"variant": v, "pattern": names[v], "best_ms": min(t),
+             "gb_s": 12.25 * n / (min(t) * 1e-3) / 1e9} for v, t in rows.items()]
+
+
+def layouts(w: W.Workload, stream, steps: int = 10) -> list:
+    """The fused step and its probe over the workload in two placements: the
+    StateArena with theta', the gradients, the codes and the scales each in a
+    region of their own (build_state), and theta' and the gradients allocated
+    tensor by tensor beside an arena of codes and scales."""
+    out = []
+    for name in ("arena regions", "theta' and gradients per tensor"):
+        if name == "arena regions":
+            states, grads, lists = build_state(w, grad_sets=1)
+            lst = lists[0]
+        else:
+            dev = torch.device("cuda")
+            arena = F.StateArena([t.numel for t in w.tensors], w.optimizer, dev)
+            states = []
+            for i in range(len(w.tensors)):
+                theta = W.draw_theta(w, i, dev)
+                st = arena.state(i)
+                F.flashopt_tensor_init(st, theta)
+                del theta
+                states.append(st)
+            grads = [[W.draw_grad(w, i, 1, dev) for i in range(len(w.tensors))]]
+            lst = F.FlashoptList(states, grads[0])
+            lists = [lst]
+        t = 0
+        for _ in range(2):
+            t += 1
+            F.flashopt_adamw_step(lst, w.hparams, t, stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for k in range(steps):
+            t += 1
+            F.flashopt_adamw_step(lst, w.hparams, t, stream)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+        probe = stream_probe(lst, stream, algorithmic_bytes(w))
+        out.append({"layout": name, "step_ms_median": float(np.median(per)),
+                    "probe_ms": probe["best_ms"], "probe_gb_s": probe["gb_s"]})
+        del states, grads, lists, lst
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+SWEEP = [(1, 0, False), (0, 1, False), (4, 0, False), (0, 4, False), (1, 1, False),
+         (1, 1, True), (2, 1, False), (2, 1, True), (1, 2, False), (2, 2, False), (2, 2, True),
+         (3, 2, False), (3, 2, True), (4, 3, False), (4, 3, True), (7, 5, False)]
+
+
+def stream_sweep(nbytes: int, stream, reps: int = 5, rounds: int = 2) -> list:
+    """flashopt_stream_sweep: plain 16-byte-per-lane streams over separate
+    buffers of nbytes each, R read and W written (in place: the written
+    buffers are read ones), best of `reps` launches, `rounds` rounds."""
+    bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+            for _ in range(12)]
+    rows = {}
+    for _ in range(rounds):
+        for r, w, ip in SWEEP:
+            reads = bufs[:r]
+            writes = bufs[:w] if ip else bufs[r:r + w]
+            F.flashopt_stream_sweep(reads, writes, nbytes, ip, stream)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(stream)
+            for k in range(reps):
+                F.flashopt_stream_sweep(reads, writes, nbytes, ip, stream)
+                ev[k + 1].record(stream)
+            torch.cuda.synchronize()
+            best = min(ev[k].elapsed_time(ev[k + 1]) for k in range(reps)) / 1e3
+            rows.setdefault((r, w, ip), []).append((r + w) * nbytes / best / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    return [{"read": r, "written": w, "in_place": ip, "gb_s": v}
+            for (r, w, ip), v in rows.items()]
 
 
 def main():
@@ -411,13 +579,18 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama31_8b")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads for cpu_baseline (0: the CPUs available, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=1 << 32,
                     help="size of the plain copy kernel timed after the steps (0: skip)")
     ap.add_argument("--no-other-optimizers", action="store_true",
                     help="skip the FlashLion (Llama-3.1-8B) and FlashSGD (ResNet-50) lines")
+    ap.add_argument("--access-patterns", action="store_true",
+                    help="time only the access-pattern evidence and print it as JSON: the plain "
+                         "stream-count sweep (12 buffers of 2 GiB), the step's traffic over flat "
+                         "buffers under each pattern variant and the byte-mix ceiling, and the "
+                         "step and its probe in two placements")
     ap.add_argument("--secondary", default=None, metavar="WORKLOAD",
                     help="time only this secondary workload (--steps steps) and print its "
                          "record: a profiling aid, not the benchmark line")
@@ -434,6 +607,14 @@ def main():
 
     if args.secondary:
         r = other_optimizer(args.secondary, args.steps, torch.cuda.current_stream())
+        print(json.dumps(r), flush=True)
+        return
+    if args.access_patterns:
+        stream = torch.cuda.current_stream()
+        w = W.WORKLOADS["llama31_8b"]
+        r = {"stream_sweep_2GiB": stream_sweep(2 << 30, stream),
+             "flat_patterns": pattern_variants(w.numel, stream),
+             "layouts": layouts(w, stream)}
         print(json.dumps(r), flush=True)
         return
 
@@ -513,15 +694,29 @@ def main():
                      "avg_launch_ms": avg * 1e3, "source_sha256_16": khash,
                      "valu_instructions_per_param":
                          float(sq["valu_instructions_per_param"]) if sq else None,
-                     "valu_busy": (float(sq["valu_time_ms_at_measured_clock"]) /
-                                   float(sq["kernel_time_ms"])) if sq else None},
+                     # VALU issue time per launch (the SQ counters' instruction count at
+                     # the shader clock measured in that profiled run) over this run's
+                     # average launch time
+                     "valu_busy": (float(sq["valu_time_ms_at_measured_clock"]) / (avg * 1e3))
+                     if sq else None,
+                     "valu_busy_in_profiled_run": (float(sq["valu_time_ms_at_measured_clock"]) /
+                                                   float(sq["kernel_time_ms"])) if sq else None},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or cpu_threads()
+        log(f"bench: timing the CPU oracle on one full step ({threads} threads)")
+        out["cpu_baseline"] = cpu_baseline(states, grads[(t + 1) % 2], t + 1, hp, threads)
+        log(f"bench: oracle {out['cpu_baseline']['value'] / 1e9:.3f} G params/s")
     out["stream_probe"] = stream_probe(lists[0], stream, bytes_step)
     out["stream_probe"]["step_over_probe"] = avg * 1e3 / out["stream_probe"]["best_ms"]
     log(f"bench: stream probe {out['stream_probe']['gb_s']:.0f} GB/s")
     del states, grads, lists
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    out["mix_ceiling"] = mix_ceiling(nparams, stream)
+    out["mix_ceiling"]["step_over_ceiling"] = avg * 1e3 / out["mix_ceiling"]["best_ms"]
+    log(f"bench: byte-mix ceiling {out['mix_ceiling']['gb_s']:.0f} GB/s")
     if not args.no_other_optimizers:
         out["other_optimizers"] = [other_optimizer("llama31_8b_lion", 10, stream),
                                    other_optimizer("llama31_8b_adamw_fp32", 5, stream),
@@ -545,9 +740,6 @@ def main():
     if args.copy_bytes:
         out["copy_ceiling"] = copy_ceiling(args.copy_bytes, stream)
         log(f"bench: plain copy {out['copy_ceiling']['gb_s']:.0f} GB/s")
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.cpu_threads)
     print(json.dumps(out), flush=True)
 
 

@@ -5,6 +5,8 @@
 
 namespace flashopt {
 
+#define LDS __attribute__((address_space(3)))
+
 // ---- bandwidth probe ---------------------------------------------------------
 //
 // The AdamW step's memory traffic with the arithmetic taken out: the same
@@ -128,6 +130,180 @@ __global__ __launch_bounds__(256) void mix_ceiling_kernel(GLOBAL uint8_t* theta,
     }
 }
 
+// ---- access-pattern variants over the same flat buffers --------------------------
+//
+// The step's traffic (same bytes, streams and 2048-parameter tiles as the
+// ceiling above) with the access patterns the fused kernel could use, to
+// isolate the pattern from the byte mix.  Per tile, four 512-parameter
+// sub-tiles; lane l owns parameters [8l, 8l+8) of a sub-tile.
+//   0: the fused kernel's own pattern: theta' and the gradient 16 bytes per
+//      lane, the code record of the lane's 8 parameters (24 bytes) as three
+//      8-byte accesses, a quad leader's 4-byte scale pair; sub-tile k+2
+//      loaded once sub-tile k is stored (two register buffers).
+//   1: as 0, but the 1536 code bytes of a sub-tile as 16-byte units (lane l
+//      unit l, lanes 0-31 also unit 64 + l) and the 64 scale bytes as 16
+//      lanes x 4 bytes.
+//   2: the units of 1, loaded by global-to-LDS DMA (global_load_lds_dwordx4)
+//      into a two-slot ring per wave and read back from LDS: no VGPR holds a
+//      load in flight.
+//   3: as 0 with three register buffers: the loads of sub-tile k+2 are issued
+//      before sub-tile k is stored.
+// Results: theta' ^= grad in every variant; codes: variants 0 and 3 replace
+// each 8-parameter record's three 8-byte words (a, b, c) with (a^b, b^c,
+// c^a), variants 1 and 2 XOR every code byte with 0x5A; every scale word
+// (the pair of a 32-parameter group) ^= 0x00010001.
+struct PatternPtrs {
+    GLOBAL uint8_t* th;
+    const GLOBAL uint8_t* gr;
+    GLOBAL uint8_t* rec;
+    GLOBAL uint8_t* sc;
+    int64_t ntiles;
+};
+
+struct PRec { u32x4 th, gr; u32x2 a, b, c; uint32_t s; };
+
+__device__ __forceinline__ void prec_load(const PatternPtrs& p, int64_t w, int k, int lane,
+                                          PRec& r) {
+    r.th = *(const GLOBAL u32x4*)(p.th + w * 4096 + k * 1024 + lane * 16);
+    r.gr = *(const GLOBAL u32x4*)(p.gr + w * 4096 + k * 1024 + lane * 16);
+    const GLOBAL uint8_t* c = p.rec + w * 6144 + k * 1536 + lane * 24;
+    r.a = *(const GLOBAL u32x2*)c;
+    r.b = *(const GLOBAL u32x2*)(c + 8);
+    r.c = *(const GLOBAL u32x2*)(c + 16);
+    r.s = *(const GLOBAL uint32_t*)(p.sc + w * 256 + k * 64 + (lane >> 2) * 4);
+}
+
+__device__ __forceinline__ void prec_store(const PatternPtrs& p, int64_t w, int k, int lane,
+                                           const PRec& r) {
+    *(GLOBAL u32x4*)(p.th + w * 4096 + k * 1024 + lane * 16) = r.th ^ r.gr;
+    GLOBAL uint8_t* c = p.rec + w * 6144 + k * 1536 + lane * 24;
+    *(GLOBAL u32x2*)c = r.a ^ r.b;
+    *(GLOBAL u32x2*)(c + 8) = r.b ^ r.c;
+    *(GLOBAL u32x2*)(c + 16) = r.c ^ r.a;
+    if ((lane & 3) == 0)
+        *(GLOBAL uint32_t*)(p.sc + w * 256 + k * 64 + (lane >> 2) * 4) = r.s ^ 0x00010001u;
+}
+
+template <int kBuffers>
+__global__ __launch_bounds__(256) void pattern_records_kernel(PatternPtrs p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    if (w >= p.ntiles) return;
+    PRec r[kBuffers];
+    prec_load(p, w, 0, lane, r[0]);
+    prec_load(p, w, 1, lane, r[1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (kBuffers == 3 && k + 2 < 4) prec_load(p, w, k + 2, lane, r[(k + 2) % kBuffers]);
+        prec_store(p, w, k, lane, r[k % kBuffers]);
+        if (kBuffers == 2 && k + 2 < 4) prec_load(p, w, k + 2, lane, r[k % kBuffers]);
+    }
+}
+
+struct PUnits { u32x4 th, gr, c0, c1; uint32_t s; };
+
+__global__ __launch_bounds__(256) void pattern_units_kernel(PatternPtrs p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    if (w >= p.ntiles) return;
+    GLOBAL uint8_t* th = p.th + w * 4096;
+    const GLOBAL uint8_t* gr = p.gr + w * 4096;
+    GLOBAL uint8_t* rec = p.rec + w * 6144;
+    GLOBAL uint8_t* sc = p.sc + w * 256;
+    auto ld = [&](int k, PUnits& r) {
+        r.th = *(const GLOBAL u32x4*)(th + k * 1024 + lane * 16);
+        r.gr = *(const GLOBAL u32x4*)(gr + k * 1024 + lane * 16);
+        r.c0 = *(const GLOBAL u32x4*)(rec + k * 1536 + lane * 16);
+        if (lane < 32) r.c1 = *(const GLOBAL u32x4*)(rec + k * 1536 + 1024 + lane * 16);
+        if (lane < 16) r.s = *(const GLOBAL uint32_t*)(sc + k * 64 + lane * 4);
+    };
+    auto st = [&](int k, const PUnits& r) {
+        *(GLOBAL u32x4*)(th + k * 1024 + lane * 16) = r.th ^ r.gr;
+        *(GLOBAL u32x4*)(rec + k * 1536 + lane * 16) = r.c0 ^ 0x5A5A5A5Au;
+        if (lane < 32) *(GLOBAL u32x4*)(rec + k * 1536 + 1024 + lane * 16) = r.c1 ^ 0x5A5A5A5Au;
+        if (lane < 16) *(GLOBAL uint32_t*)(sc + k * 64 + lane * 4) = r.s ^ 0x00010001u;
+    };
+    PUnits r[2];
+    ld(0, r[0]);
+    ld(1, r[1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        st(k, r[k & 1]);
+        if (k + 2 < 4) ld(k + 2, r[k & 1]);
+    }
+}
+
+// Variant 2.  Per wave a ring of two LDS slots of 3648 bytes (theta' 1024,
+// gradient 1024, codes 1536, scales 64); one batch of DMA loads is five
+// instructions (theta', gradient, codes in two, scales), the stores of a
+// sub-tile four.  The vmcnt waits below count the memory instructions
+// issued after the batch being consumed (vmcnt counts loads and stores of a
+// wave in issue order on this architecture).
+constexpr int kSlot = 3648;
+#define FLASHOPT_VMCNT(N) \
+    __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (0x7 << 4) | (0xF << 8) | (((N) >> 4) << 14))
+#define FLASHOPT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+__device__ __forceinline__ void dma16(const GLOBAL uint8_t* src, LDS uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds((const GLOBAL uint32_t*)src, (LDS uint32_t*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const GLOBAL uint8_t* src, LDS uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds((const GLOBAL uint32_t*)src, (LDS uint32_t*)dst, 4, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void pattern_dma_kernel(PatternPtrs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerBlock * 2 * kSlot];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    if (w >= p.ntiles) return;
+    GLOBAL uint8_t* th = p.th + w * 4096;
+    const GLOBAL uint8_t* gr = p.gr + w * 4096;
+    GLOBAL uint8_t* rec = p.rec + w * 6144;
+    GLOBAL uint8_t* sc = p.sc + w * 256;
+    LDS uint8_t* base = (LDS uint8_t*)lds + (threadIdx.x / kWave) * 2 * kSlot;
+    auto issue = [&](int k) {
+        LDS uint8_t* s = base + (k & 1) * kSlot;
+        dma16(th + k * 1024 + lane * 16, s);
+        dma16(gr + k * 1024 + lane * 16, s + 1024);
+        dma16(rec + k * 1536 + lane * 16, s + 2048);
+        if (lane < 32) dma16(rec + k * 1536 + 1024 + lane * 16, s + 3072);
+        if (lane < 16) dma4(sc + k * 64 + lane * 4, s + 3584);
+    };
+    auto consume = [&](int k) {
+        LDS uint8_t* s = base + (k & 1) * kSlot;
+        const u32x4 t = *(LDS u32x4*)(s + lane * 16);
+        const u32x4 g = *(LDS u32x4*)(s + 1024 + lane * 16);
+        const u32x4 c0 = *(LDS u32x4*)(s + 2048 + lane * 16);
+        u32x4 c1 = {0u, 0u, 0u, 0u};
+        uint32_t sv = 0u;
+        if (lane < 32) c1 = *(LDS u32x4*)(s + 3072 + lane * 16);
+        if (lane < 16) sv = *(LDS uint32_t*)(s + 3584 + lane * 4);
+        FLASHOPT_LGKMCNT0();              // the slot's data is in registers: it may be refilled
+        return [=]() {
+            *(GLOBAL u32x4*)(th + k * 1024 + lane * 16) = t ^ g;
+            *(GLOBAL u32x4*)(rec + k * 1536 + lane * 16) = c0 ^ 0x5A5A5A5Au;
+            if (lane < 32) *(GLOBAL u32x4*)(rec + k * 1536 + 1024 + lane * 16) = c1 ^ 0x5A5A5A5Au;
+            if (lane < 16) *(GLOBAL uint32_t*)(sc + k * 64 + lane * 4) = sv ^ 0x00010001u;
+        };
+    };
+    issue(0);
+    issue(1);
+    FLASHOPT_VMCNT(5);                    // batch 0 landed (batch 1 may be in flight)
+    auto s0 = consume(0);
+    issue(2);
+    s0();
+    FLASHOPT_VMCNT(5 + 4);                // batch 1 (then batch 2, stores 0)
+    auto s1 = consume(1);
+    issue(3);
+    s1();
+    FLASHOPT_VMCNT(4 + 5 + 4);            // batch 2 (then stores 0, batch 3, stores 1)
+    auto s2 = consume(2);
+    s2();
+    FLASHOPT_VMCNT(4 + 4);                // batch 3 (then stores 1, stores 2)
+    auto s3 = consume(3);
+    s3();
+}
+
 // ---- stream-count sweep ---------------------------------------------------------
 //
 // R buffers read and W buffers written, all of the same size, one 16-byte
@@ -194,6 +370,26 @@ int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, 
     hipLaunchKernelGGL(mix_ceiling_kernel, dim3(grid_for(ntiles)), dim3(kBlock), 0,
                        (hipStream_t)stream, (GLOBAL uint8_t*)theta, (const GLOBAL uint8_t*)grad,
                        (GLOBAL uint8_t*)codes, (GLOBAL uint8_t*)scales, ntiles);
+    return launch_status();
+}
+
+int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* grad,
+                           uint8_t* codes, uint16_t* scales, int64_t n, void* stream) {
+    if (variant < 0 || variant > 3) return FLASHOPT_ERR_ARG;
+    if (n < 0 || n > kMaxNumel || n % kMixTile != 0) return FLASHOPT_ERR_SIZE;
+    if (n == 0) return FLASHOPT_OK;
+    if (!theta || !grad || !codes || !scales) return FLASHOPT_ERR_NULL;
+    if (!aligned(theta, 16) || !aligned(grad, 16) || !aligned(codes, 16) || !aligned(scales, 16))
+        return FLASHOPT_ERR_ALIGN;
+    PatternPtrs p{(GLOBAL uint8_t*)theta, (const GLOBAL uint8_t*)grad, (GLOBAL uint8_t*)codes,
+                  (GLOBAL uint8_t*)scales, n / kMixTile};
+    const dim3 grid(grid_for(p.ntiles)), block(kBlock);
+    if (p.ntiles > kMaxBlocks * kWavesPerBlock) return FLASHOPT_ERR_SIZE;   // one wave per tile
+    hipStream_t s = (hipStream_t)stream;
+    if (variant == 0) hipLaunchKernelGGL(pattern_records_kernel<2>, grid, block, 0, s, p);
+    else if (variant == 1) hipLaunchKernelGGL(pattern_units_kernel, grid, block, 0, s, p);
+    else if (variant == 2) hipLaunchKernelGGL(pattern_dma_kernel, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(pattern_records_kernel<3>, grid, block, 0, s, p);
     return launch_status();
 }
 

@@ -122,8 +122,7 @@ SIGNATURES = {
                                              _P]),
     "flashopt_stream_probe": (ctypes.c_int, [_P, _P]),
     "flashopt_mix_ceiling": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
-    "flashopt_adamw_step_noalloc": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32,
-                                                   ctypes.POINTER(AdamWHparams), _I64, _P]),
+    "flashopt_pattern_probe": (ctypes.c_int, [_I32, _P, _P, _P, _P, _I64, _P]),
     "flashopt_stream_sweep": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                              _I32, _I64, _P]),
     "flashopt_lion_step": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
@@ -296,32 +295,53 @@ class TensorState:
 
 
 class StateArena:
-    """The compressed state of a list of tensors in two device buffers: every
-    tensor's code records are a slice of one zeroed uint8 buffer and its
-    scales a slice of one zeroed int16 buffer, each slice starting on a
-    4096-byte boundary.  On one MI355X the fused step over state laid out this
-    way measured about 2 % faster than over one allocation per tensor (the
-    same kernel; the placement of its streams in HBM differs).  state(i)
-    builds tensor i's TensorState on its slices, so theta' can be allocated
-    (or taken from a parameter) one tensor at a time."""
+    """The state of a list of tensors in one device buffer with one region per
+    stream the fused step reads or writes: optionally theta' (theta=True),
+    optionally `grad_sets` sets of BF16 gradients, then the code records,
+    then the FP16 scales.  Each region starts on a 2 MiB boundary and each
+    tensor's slice within it on a 4096-byte boundary; code records and scales
+    are zeroed.  state(i) builds tensor i's TensorState on its slices (theta'
+    from the arena, or a given tensor such as a parameter's own storage);
+    grad(j, i) is tensor i's gradient of set j.
+
+    Why: the step's bandwidth depends on where its streams sit in HBM.  On
+    MI355X, over the Llama-3.1-8B list, the step's loads and stores with no
+    arithmetic (flashopt_stream_probe) measured 16.2-16.9 ms with this layout
+    against 17.4-18.8 ms with theta' and gradients allocated per tensor and
+    18.5-18.9 ms with each tensor's four arrays side by side; the step itself
+    18.35-18.48 ms against 18.5-19.1 ms (one box, one process)."""
 
     ALIGN = 4096
+    REGION = 1 << 21
 
-    def __init__(self, numels: Sequence[int], optimizer: str, device):
+    def __init__(self, numels: Sequence[int], optimizer: str, device, theta: bool = False,
+                 grad_sets: int = 0):
         self.numels = [int(n) for n in numels]
         self.optimizer = optimizer
         kind = KIND[optimizer]
         cb = [lib().flashopt_codes_bytes(kind, n) for n in self.numels]
         sb = [lib().flashopt_scales_bytes(kind, n) for n in self.numels]
-        self._cs, ct = self._slices(cb)
-        self._ss, st = self._slices(sb)
-        self.codes = torch.zeros(max(ct, 1), dtype=torch.uint8, device=device)
-        self.scales = torch.zeros(max(st // 2, 1), dtype=torch.int16, device=device)
-        self.device = self.codes.device
+        bb = [2 * n for n in self.numels]
+        start = 0
+        self._ts = None
+        if theta:
+            self._ts, start = self._slices(bb, start)
+        self._gs = []
+        for _ in range(grad_sets):
+            gs, start = self._slices(bb, start)
+            self._gs.append(gs)
+        self._cs, start = self._slices(cb, start)
+        self._ss, end = self._slices(sb, start)
+        self.buffer = torch.empty(max(end, 1), dtype=torch.uint8, device=device)
+        self.device = self.buffer.device
+        c0 = min([o for o, _ in self._cs] + [end])
+        self.buffer[c0:end].zero_()                            # code records and scales
 
     @classmethod
-    def _slices(cls, sizes):
-        out, o = [], 0
+    def _slices(cls, sizes, start):
+        """slices of `sizes` bytes from the next region boundary at or after start"""
+        o = -(-start // cls.REGION) * cls.REGION
+        out = []
         for b in sizes:
             out.append((o, b))
             o += -(-b // cls.ALIGN) * cls.ALIGN
@@ -330,9 +350,17 @@ class StateArena:
     def state(self, i: int, theta: Optional[torch.Tensor] = None) -> TensorState:
         co, cb = self._cs[i]
         so, sb = self._ss[i]
+        if theta is None and self._ts is not None:
+            to, tb = self._ts[i]
+            theta = self.buffer[to:to + tb].view(torch.bfloat16)
         return TensorState(self.numels[i], self.optimizer, self.device, theta=theta,
-                           codes=self.codes[co:co + cb],
-                           scales=self.scales[so // 2:(so + sb) // 2])
+                           codes=self.buffer[co:co + cb],
+                           scales=self.buffer[so:so + sb].view(torch.int16))
+
+    def grad(self, j: int, i: int) -> torch.Tensor:
+        """Tensor i's BF16 gradient buffer of set j (contents undefined)."""
+        go, gb = self._gs[j][i]
+        return self.buffer[go:go + gb].view(torch.bfloat16)
 
 
 def flashopt_tensor_init(st: TensorState, theta_fp32: torch.Tensor, stream=None) -> None:
@@ -406,22 +434,6 @@ def flashopt_stream_probe(lst: FlashoptList, stream=None) -> None:
     _check("flashopt_stream_probe", lib().flashopt_stream_probe(lst.handle, _stream(stream)))
 
 
-NOALLOC_MAX_TENSORS = 4096
-
-
-def flashopt_adamw_step_noalloc(states: Sequence[TensorState], grads: Sequence[torch.Tensor],
-                                hp: dict, step: int, stream=None) -> None:
-    """The whole-list AdamW step without a handle or workspace
-    (include/flashopt.h): the descriptor table lives in the library's own
-    device array, so the call allocates nothing on the device."""
-    arr = (Tensor * max(len(states), 1))()
-    for i, (st, g) in enumerate(zip(states, grads)):
-        arr[i] = st.descriptor(g)
-    h = _adam(hp)
-    _check("flashopt_adamw_step_noalloc", lib().flashopt_adamw_step_noalloc(
-        arr, len(states), ctypes.byref(h), step, _stream(stream)))
-
-
 def flashopt_mix_ceiling(theta: torch.Tensor, grad: torch.Tensor, codes: torch.Tensor,
                          scales: torch.Tensor, n: int, stream=None) -> None:
     """Ceiling of the step's byte mix (include/flashopt_probe.h) over flat
@@ -431,6 +443,17 @@ def flashopt_mix_ceiling(theta: torch.Tensor, grad: torch.Tensor, codes: torch.T
         assert t.is_contiguous() and t.numel() * t.element_size() >= need
     _check("flashopt_mix_ceiling", lib().flashopt_mix_ceiling(
         _ptr(theta), _ptr(grad), _ptr(codes), _ptr(scales), n, _stream(stream)))
+
+
+def flashopt_pattern_probe(variant: int, theta: torch.Tensor, grad: torch.Tensor,
+                           codes: torch.Tensor, scales: torch.Tensor, n: int, stream=None) -> None:
+    """The step's traffic with access pattern `variant` (include/flashopt_probe.h)
+    over the flat buffers of flashopt_mix_ceiling.  Overwrites theta, codes and
+    scales."""
+    for t, need in ((theta, 2 * n), (grad, 2 * n), (codes, 3 * n), (scales, n // 8)):
+        assert t.is_contiguous() and t.numel() * t.element_size() >= need
+    _check("flashopt_pattern_probe", lib().flashopt_pattern_probe(
+        variant, _ptr(theta), _ptr(grad), _ptr(codes), _ptr(scales), n, _stream(stream)))
 
 
 def flashopt_stream_sweep(reads: Sequence[torch.Tensor], writes: Sequence[torch.Tensor],
@@ -606,7 +629,7 @@ def build_list(theta_fp32: List[torch.Tensor], optimizer: str,
     optimizer state); returns (states, list handle)."""
     states = []
     arena = StateArena([th.numel() for th in theta_fp32], optimizer,
-                       theta_fp32[0].device) if theta_fp32 else None
+                       theta_fp32[0].device, theta=True) if theta_fp32 else None
     for i, th in enumerate(theta_fp32):
         st = arena.state(i)
         flashopt_tensor_init(st, th.reshape(-1).contiguous(), stream)

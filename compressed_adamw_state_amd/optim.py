@@ -145,7 +145,11 @@ class _FlashOptimizer(torch.optim.Optimizer):
         for p in params:
             by_device.setdefault(p.device, []).append(p)
         for device, ps in by_device.items():
-            arena = F.StateArena([p.numel() for p in ps], kind, device)
+            # FP32 parameters get their BF16 theta' from the arena (one region for
+            # theta', one for the codes, one for the scales); BF16 parameters
+            # keep their own storage as theta'
+            arena = F.StateArena([p.numel() for p in ps], kind, device,
+                                 theta=all(p.dtype == torch.float32 for p in ps))
             for i, p in enumerate(ps):
                 if p.dtype == torch.float32:
                     st = arena.state(i)

@@ -46,6 +46,29 @@ int flashopt_stream_probe(const flashopt_list* list, void* stream);
 int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, uint16_t* scales,
                          int64_t n, void* stream);
 
+/* The step's traffic over the same flat buffers as flashopt_mix_ceiling
+ * (theta 2n, grad 2n, codes 3n, scales n/8 bytes; n a multiple of 2048; one
+ * wave per 2048-parameter tile of four 512-parameter sub-tiles, lane l owning
+ * parameters [8l, 8l+8) of a sub-tile), with one of the access patterns the
+ * fused kernel could use -- to tell the pattern's cost from the byte mix's:
+ *   variant 0: the fused kernel's own: theta' and gradient 16 bytes per lane,
+ *              the code record of a lane's 8 parameters (24 bytes) as three
+ *              8-byte accesses, the group's 4-byte scale pair from one lane of
+ *              four, two register buffers (sub-tile k+2 loaded once k is stored);
+ *   variant 1: as 0 with the 1536 code bytes of a sub-tile as 16-byte units
+ *              and the 64 scale bytes as 16 lanes x 4 bytes;
+ *   variant 2: the units of 1 loaded by global-to-LDS DMA into a two-slot ring
+ *              per wave (no register holds a load in flight);
+ *   variant 3: as 0 with three register buffers (the loads of sub-tile k+2
+ *              issued before sub-tile k is stored).
+ * Results: theta ^= grad; codes: variants 0 and 3 replace each 24-byte record's
+ * 8-byte words (a, b, c) with (a^b, b^c, c^a), variants 1 and 2 XOR every code
+ * byte with 0x5A; every 32-bit scale word ^= 0x00010001.  DESTRUCTIVE.  Errors:
+ * FLASHOPT_ERR_ARG (variant outside 0-3) and those of flashopt_mix_ceiling.
+ * One launch on `stream`, nothing allocated. */
+int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* grad,
+                           uint8_t* codes, uint16_t* scales, int64_t n, void* stream);
+
 /* Stream-count sweep: `nread` device buffers read and `nwrite` written, each
  * of `bytes` bytes (a multiple of 16), one 16-byte unit of each per thread.
  * Written value: the XOR of the units read, its first word XORed with the

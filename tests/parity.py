@@ -9,6 +9,10 @@ Two comparison modes:
              ones) the initial weights and each step's gradients are copied
              back, the oracle steps just those groups (groups are independent),
              and the device state at those groups is compared.
+In sampled mode, step(t, every_element=True) also checks every element of
+that step: the device state before the step is copied aside, and after the
+GPU step the oracle steps each tensor from that copy with the step's
+gradient, on the host, and every byte of the result is compared.
 """
 from __future__ import annotations
 
@@ -56,6 +60,32 @@ def state_fields(st: F.TensorState, idx=None, gidx=None) -> dict:
     return out
 
 
+def record_fields(theta: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int,
+                  optimizer: str) -> dict:
+    """theta', rho, m_code, v_code, m_scale, v_scale of one tensor from its
+    device arrays (live state or a copy), unpacked from the interleaved
+    records on the device and returned as contiguous host arrays."""
+    R, S = F.RECORD[optimizer], F.SCALES[optimizer]
+    nrec, ng = (n + 7) // 8, (n + GROUP - 1) // GROUP
+    rec = codes[:nrec * R].view(nrec, R // 8, 8)
+    sc = scales[:ng * S].view(ng, S)
+    out = {"theta": u16(theta[:n]), "rho": i8(rec[:, 0].reshape(-1)[:n]),
+           "m_code": i8(rec[:, 1].reshape(-1)[:n]), "m_scale": u16(sc[:, 0])}
+    if S == 2:
+        out["v_code"] = u8(rec[:, 2].reshape(-1)[:n])
+        out["v_scale"] = u16(sc[:, 1])
+    return out
+
+
+def oracle_state(fields: dict, n: int, optimizer: str) -> oracle.State:
+    """An oracle State holding the given fields (host arrays, stepped in place)."""
+    o = oracle.State.__new__(oracle.State)
+    o.n, o.optimizer = n, optimizer
+    o.tb, o.rho, o.qm, o.sm = fields["theta"], fields["rho"], fields["m_code"], fields["m_scale"]
+    o.qv, o.sv = fields.get("v_code"), fields.get("v_scale")
+    return o
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -73,8 +103,9 @@ class Run:
         opt = w.optimizer
         rng = np.random.default_rng(seed)
         self.states, self.grads, self.orc, self.samples = [], [], [], []
-        # the state in one StateArena, as bench.py lays it out
-        arena = F.StateArena([spec.numel for spec in w.tensors], opt, self.dev)
+        # the state and one gradient set in one StateArena, as bench.py lays them out
+        arena = F.StateArena([spec.numel for spec in w.tensors], opt, self.dev, theta=True,
+                             grad_sets=1)
         for i, spec in enumerate(w.tensors):
             n = spec.numel
             theta = W.draw_theta(w, i, self.gen_dev)
@@ -82,8 +113,7 @@ class Run:
             theta_d = theta.to(self.dev)
             F.flashopt_tensor_init(st, theta_d)
             self.states.append(st)
-            self.grads.append(None if w.release else
-                              torch.zeros(n, dtype=torch.bfloat16, device=self.dev))
+            self.grads.append(arena.grad(0, i))
             if mode == "full":
                 self.orc.append(oracle.State(theta.numpy(), opt))
             else:
@@ -112,17 +142,22 @@ class Run:
         return torch.cat([torch.arange(g * GROUP, min(n, g * GROUP + GROUP))
                           for g in self.samples[i]]).to(self.dev)
 
-    def step(self, t: int, hp: dict | None = None, threads: int | None = None):
+    def step(self, t: int, hp: dict | None = None, threads: int | None = None,
+             every_element: bool = False) -> int:
+        """GPU step t (and the oracle on the compared groups); with
+        every_element, also the every-element check of this step (returns the
+        number of elements it compared)."""
         w = self.w
         hp = hp or w.hparams
+        snap = None
+        if every_element:
+            assert self.mode == "sampled"
+            snap = [(st.theta.clone(), st.codes.clone(), st.scales.clone()) for st in self.states]
         grads = []
         for i in range(len(w.tensors)):
             g = W.draw_grad(w, i, t, self.gen_dev)
-            if w.release:
-                grads.append(g.to(self.dev))
-            else:
-                self.grads[i].copy_(g)
-                grads.append(self.grads[i])
+            self.grads[i].copy_(g)
+            grads.append(self.grads[i])
             if self.mode == "full":
                 oracle.step_chunked(self.orc[i], u16(g), t, hp, nthreads=threads)
             else:
@@ -137,6 +172,39 @@ class Run:
         else:
             F.step(self.lst, w.optimizer, hp, t)
         torch.cuda.synchronize()
+        self.t = t
+        if snap is None:
+            return 0
+        checked = 0
+        for i, st in enumerate(self.states):
+            n = st.numel
+            pre = record_fields(*snap[i], n, st.optimizer)
+            snap[i] = None                                   # free the device copy
+            o = oracle_state(pre, n, st.optimizer)
+            oracle.step_chunked(o, u16(grads[i]), t, hp, nthreads=threads)
+            post = record_fields(st.theta, st.codes, st.scales, n, st.optimizer)
+            keys = [("theta", "tb"), ("rho", "rho"), ("m_code", "qm"), ("m_scale", "sm")]
+            if "v_code" in post:
+                keys += [("v_code", "qv"), ("v_scale", "sv")]
+            for k, ok in keys:
+                got, exp = post[k], getattr(o, ok)
+                if not np.array_equal(got, exp):
+                    bad = np.nonzero(got != exp)[0]
+                    raise AssertionError(
+                        f"every element, step {t}: tensor {i} ({w.tensors[i].name}) {k}: "
+                        f"{bad.size} mismatches, first at {bad[:5].tolist()}: gpu "
+                        f"{got[bad[:5]].tolist()} oracle {exp[bad[:5]].tolist()}")
+            checked += n
+        return checked
+
+    def advance_to(self, t: int, compare_every: int = 0, label: str = "") -> None:
+        """Steps self.t + 1 .. t (sampled comparisons every compare_every
+        steps when it is positive)."""
+        for k in range(getattr(self, "t", 0) + 1, t + 1):
+            self.step(k)
+            if compare_every and k % compare_every == 0:
+                n = self.compare(f"{label} step {k}")
+                log(f"{label} step {k}: {n} sampled elements compared")
 
     def compare(self, label: str = "") -> int:
         """Assert bit equality of every compared code and scale; return #elements."""

@@ -1,6 +1,7 @@
 """StateArena's slicing on the host (CPU tensors; no GPU call): each tensor's
-code records and scales are views of the two shared buffers, of exactly the
-layout's sizes, starting on 4096-byte boundaries, in order and disjoint."""
+code records, scales and (when asked) theta' and gradient buffers are views
+of the one shared buffer, of exactly the layout's sizes, starting on
+4096-byte boundaries, disjoint, one region per stream in a fixed order."""
 import pytest
 import torch
 
@@ -10,31 +11,49 @@ SIZES = [4097, 0, 33, 2048 * 3, 1, (1 << 17) + 5, 32]
 
 
 @pytest.mark.parametrize("opt", ["adamw", "sgd", "lion", "adamw_linv", "adamw_fp32", "sgd_fp32"])
-def test_slices(opt):
-    arena = F.StateArena(SIZES, opt, "cpu")
+@pytest.mark.parametrize("theta,grad_sets", [(False, 0), (True, 2)])
+def test_slices(opt, theta, grad_sets):
+    arena = F.StateArena(SIZES, opt, "cpu", theta=theta, grad_sets=grad_sets)
     lib = F.lib()
     kind = F.KIND[opt]
-    cbase = arena.codes.data_ptr()
-    sbase = arena.scales.data_ptr()
-    prev_c = prev_s = 0
+    base = arena.buffer.data_ptr()
+    end = base + arena.buffer.numel()
+    views = []                                    # (stream, start, bytes)
     for i, n in enumerate(SIZES):
         st = arena.state(i)
         assert st.numel == n and st.theta.numel() == n and st.theta.dtype == torch.bfloat16
         assert st.codes.numel() == lib.flashopt_codes_bytes(kind, n)
         assert 2 * st.scales.numel() == lib.flashopt_scales_bytes(kind, n)
-        assert st.codes.untyped_storage().data_ptr() == cbase          # views, not copies
-        assert st.scales.untyped_storage().data_ptr() == sbase
+        for t in [st.codes, st.scales] + ([st.theta] if theta else []):
+            assert t.untyped_storage().data_ptr() == base            # views, not copies
         if n == 0:
             continue                      # an empty view's data_ptr is 0, as for any empty tensor
-        co = st.codes.data_ptr() - cbase
-        assert co % F.StateArena.ALIGN == 0 and co >= prev_c           # aligned, in order, disjoint
-        prev_c = co + st.codes.numel()
-        if st.scales.numel():                                           # the FP32 kinds have none
-            so = st.scales.data_ptr() - sbase
-            assert so % F.StateArena.ALIGN == 0 and so >= prev_s
-            prev_s = so + 2 * st.scales.numel()
+        arrays = [("codes", st.codes)] + ([("scales", st.scales)] if st.scales.numel() else [])
+        if theta:
+            arrays.append(("theta", st.theta))
+        for j in range(grad_sets):
+            g = arena.grad(j, i)
+            assert g.dtype == torch.bfloat16 and g.numel() == n
+            assert g.untyped_storage().data_ptr() == base
+            arrays.append((f"grad{j}", g))
+        for name, t in arrays:
+            views.append((name, t.data_ptr(), t.numel() * t.element_size()))
         assert not st.codes.any() and not st.scales.any()               # zeroed
-    assert prev_c <= arena.codes.numel() and prev_s <= 2 * arena.scales.numel()
+    # aligned, inside the buffer, disjoint; each stream's slices in tensor order
+    # within one region, regions in the order theta, grads, codes, scales
+    for name, p, b in views:
+        assert (p - base) % F.StateArena.ALIGN == 0 and base <= p and p + b <= end
+    iv = sorted((p, p + b) for _, p, b in views)
+    assert all(a[1] <= c[0] for a, c in zip(iv, iv[1:]))
+    order = ["theta"] + [f"grad{j}" for j in range(grad_sets)] + ["codes", "scales"]
+    first = {}
+    for name, p, b in views:
+        first.setdefault(name, p)
+        assert p >= first[name]
+    present = [o for o in order if o in first]
+    assert [first[o] for o in present] == sorted(first[o] for o in present)
+    for o in present:
+        assert (first[o] - base) % F.StateArena.REGION == 0
 
 
 def test_theta_taken_and_checked():
@@ -51,5 +70,5 @@ def test_theta_taken_and_checked():
 
 
 def test_empty_list():
-    arena = F.StateArena([], "adamw", "cpu")
-    assert arena.codes.numel() >= 1 and arena.scales.numel() >= 1
+    arena = F.StateArena([], "adamw", "cpu", theta=True, grad_sets=1)
+    assert arena.buffer.numel() >= 1

@@ -91,3 +91,33 @@ def test_stream_sweep_values(rw, in_place):
         assert torch.equal(o.cpu(), exp), (rw, in_place, k)
     for k in range(w if in_place else 0, r):
         assert torch.equal(dr[k].cpu(), reads[k])
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_pattern_probe_variants(variant):
+    """flashopt_pattern_probe: theta ^= grad; codes per record (a^b, b^c, c^a)
+    for variants 0 and 3, every byte ^= 0x5A for 1 and 2; every scale word ^=
+    0x00010001; over 7 tiles and nothing beyond."""
+    gen = torch.Generator().manual_seed(10 + variant)
+    n = 2048 * 7
+    pad = 64
+    theta = torch.randint(-2 ** 15, 2 ** 15, (n + pad,), generator=gen, dtype=torch.int16)
+    grad = torch.randint(-2 ** 15, 2 ** 15, (n + pad,), generator=gen, dtype=torch.int16)
+    codes = torch.randint(0, 256, (3 * n + pad,), generator=gen, dtype=torch.uint8)
+    scales = torch.randint(-2 ** 15, 2 ** 15, (n // 16 + pad,), generator=gen, dtype=torch.int16)
+    d = [t.cuda() for t in (theta, grad, codes, scales)]
+    F.flashopt_pattern_probe(variant, d[0], d[1], d[2], d[3], n)
+    torch.cuda.synchronize()
+    th, gr, cd, sc = (t.cpu() for t in d)
+    assert torch.equal(th[:n], theta[:n] ^ grad[:n]) and torch.equal(th[n:], theta[n:])
+    assert torch.equal(gr, grad)
+    if variant in (0, 3):
+        w = codes[:3 * n].view(torch.int64).view(-1, 3)
+        exp = torch.stack([w[:, 0] ^ w[:, 1], w[:, 1] ^ w[:, 2], w[:, 2] ^ w[:, 0]], 1)
+        assert torch.equal(cd[:3 * n].view(torch.int64).view(-1, 3), exp)
+    else:
+        assert torch.equal(cd[:3 * n], codes[:3 * n] ^ 0x5A)
+    assert torch.equal(cd[3 * n:], codes[3 * n:])
+    s32 = scales[:n // 16].view(torch.int32)
+    assert torch.equal(sc[:n // 16].view(torch.int32), s32 ^ 0x00010001)
+    assert torch.equal(sc[n // 16:], scales[n // 16:])
