@@ -17,9 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 # translation units of libflashopt.so: the fused step (hot path), the
 # uncompressed kinds, one tensor's codec and state, the codec ablations, the
-# measurement probes, the device schedules, and the C ABI of tensor lists
+# measurement probes, the device schedules, the C ABI of tensor lists, and the
+# step that allocates nothing
 UNITS = ["step.hip", "step_fp32.hip", "tensor.hip", "ablation.hip", "probe.hip", "schedule.hip",
-         "list.hip"]
+         "list.hip", "noalloc.hip"]
 SOURCES = [os.path.join(CSRC, u) for u in UNITS] + [
     os.path.join(CSRC, h) for h in ("codec.hpp", "device.hpp", "host.hpp", "quant.hpp")]
 BUILD_DIR = os.path.join(PKG, "_build")

@@ -123,6 +123,8 @@ SIGNATURES = {
     "flashopt_stream_probe": (ctypes.c_int, [_P, _P]),
     "flashopt_mix_ceiling": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
     "flashopt_pattern_probe": (ctypes.c_int, [_I32, _P, _P, _P, _P, _I64, _P]),
+    "flashopt_adamw_step_noalloc": (ctypes.c_int, [ctypes.POINTER(Tensor), _I32,
+                                                   ctypes.POINTER(AdamWHparams), _I64, _P]),
     "flashopt_stream_sweep": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                              _I32, _I64, _P]),
     "flashopt_lion_step": (ctypes.c_int, [_P, ctypes.POINTER(LionHparams), _I64, _P]),
@@ -432,6 +434,22 @@ def flashopt_stream_probe(lst: FlashoptList, stream=None) -> None:
     loads and stores with one XOR per word instead of the update.  Overwrites
     the state."""
     _check("flashopt_stream_probe", lib().flashopt_stream_probe(lst.handle, _stream(stream)))
+
+
+NOALLOC_MAX_TENSORS = 4096
+
+
+def flashopt_adamw_step_noalloc(states: Sequence[TensorState], grads: Sequence[torch.Tensor],
+                                hp: dict, step: int, stream=None) -> None:
+    """The whole-list AdamW step without a handle or workspace
+    (include/flashopt.h): the descriptor table lives in the library's own
+    device array, so the call allocates nothing on the device."""
+    arr = (Tensor * max(len(states), 1))()
+    for i, (st, g) in enumerate(zip(states, grads)):
+        arr[i] = st.descriptor(g)
+    h = _adam(hp)
+    _check("flashopt_adamw_step_noalloc", lib().flashopt_adamw_step_noalloc(
+        arr, len(states), ctypes.byref(h), step, _stream(stream)))
 
 
 def flashopt_mix_ceiling(theta: torch.Tensor, grad: torch.Tensor, codes: torch.Tensor,

@@ -276,6 +276,27 @@ int flashopt_sgd_step(const flashopt_list* list, const flashopt_sgd_hparams* hp,
 int flashopt_lion_step(const flashopt_list* list, const flashopt_lion_hparams* hp,
                        int64_t step, void* stream);
 
+/* ---- the whole-list AdamW step for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same result as flashopt_list_create over `tensors`
+ * (kind FLASHOPT_KIND_ADAMW, every numel > 0 tensor with a gradient) followed
+ * by flashopt_adamw_step, bit for bit, with the same kernel and launch shape,
+ * but no handle and no workspace: the descriptor table and tile offsets live
+ * in a fixed array of the library's own device memory (each GPU the library
+ * runs on holds one, about 290 KB, until the process ends), written by a few
+ * small kernels on `stream` (the descriptors travel as kernel arguments) and
+ * then read by the step.  Calls on one stream are ordered; calls that overlap
+ * on one GPU (other streams, other host threads) share that array and race.
+ * Nothing is allocated, nothing synchronises.  tensors: HOST array of `count`
+ * descriptors.  Errors: FLASHOPT_ERR_SIZE (count < 0 or above
+ * FLASHOPT_NOALLOC_MAX_TENSORS), FLASHOPT_ERR_NULL (tensors NULL with count > 0,
+ * a missing gradient), the checks of flashopt_list_create and
+ * flashopt_adamw_step, FLASHOPT_ERR_HIP (no current device, the array's address
+ * not found, a launch failure). */
+#define FLASHOPT_NOALLOC_MAX_TENSORS 4096
+int flashopt_adamw_step_noalloc(const flashopt_tensor* tensors, int32_t count,
+                                const flashopt_adamw_hparams* hp, int64_t step, void* stream);
+
 /* ---- graph-capturable AdamW.  The step counter, the bias-correction powers
  * and the schedulable hyper-parameters live in a DEVICE struct that each call
  * advances on the stream, so the launches of one call depend on no host value

@@ -58,6 +58,23 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_split_ex(fake, 10, 1, 0, fake, fake, None) == -4       # qmax
     assert lib.flashopt_split_ex(fake, 10, 1, 32768, fake, fake, None) == -4
     assert lib.flashopt_split_ex(None, 10, 1, 127, fake, fake, None) == -1
+    # the step that allocates nothing: count range, NULL array, hyper-parameters,
+    # and the list checks of every descriptor, all before any HIP call
+    hp = F.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    one = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake))
+    noalloc = lib.flashopt_adamw_step_noalloc
+    assert noalloc(one, F.NOALLOC_MAX_TENSORS + 1, ctypes.byref(hp), 1, None) == -2
+    assert noalloc(one, -1, ctypes.byref(hp), 1, None) == -2
+    assert noalloc(None, 3, ctypes.byref(hp), 1, None) == -1
+    assert noalloc(one, 1, ctypes.byref(hp), 0, None) == -5
+    bad = F.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0.01)
+    assert noalloc(one, 1, ctypes.byref(bad), 1, None) == -4
+    assert noalloc((F.Tensor * 1)(F.Tensor(10, fake, fake, fake, None)), 1, ctypes.byref(hp), 1,
+                   None) == -1                                  # a gradient is required
+    assert noalloc((F.Tensor * 1)(F.Tensor(10, mis, fake, fake, fake)), 1, ctypes.byref(hp), 1,
+                   None) == -3
+    assert noalloc((F.Tensor * 1)(F.Tensor(-1, fake, fake, fake, fake)), 1, ctypes.byref(hp), 1,
+                   None) == -2
     assert lib.flashopt_unsplit_ex(fake, P(0x10001), 10, 0, 127, fake, None) == -3
     assert lib.flashopt_quantize_lin_v(fake, 5, None, fake, None) == -1
     assert lib.flashopt_dequantize_lin_m(fake, fake, -1, fake, None) == -2
