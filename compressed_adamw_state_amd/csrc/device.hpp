@@ -270,6 +270,18 @@ struct Raw {                        // one lane's packed loads of one sub-tile
     uint32_t ms, vs;                // the group's FP16 scales
 };
 
+// The lane's index in its wave, read where a tile's addresses are formed.  The
+// asm is volatile so that the compiler cannot hoist it (and the per-lane
+// offsets derived from it) out of a kernel's tile loop: hoisted, those offsets
+// stay live as 64-bit pairs across the whole loop body, and under the step's
+// register budget one of them went to scratch memory, 512 bytes written and
+// read back per wave.
+__device__ __forceinline__ uint32_t lane_here() {
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Addresses inside one full tile: the wave-uniform byte address of the tile's
 // first element in each array, and the lane's constant byte offsets within a
 // sub-tile.  Every access is a scalar base plus a 32-bit lane offset, so no
@@ -285,14 +297,16 @@ struct TileAddr {
     GLOBAL uint8_t* scales;
     uint32_t el, rec, scl;          // lane offsets: 8 BF16, one record, the group's scales
 
-    __device__ __forceinline__ TileAddr(const GTensor& T, int64_t e0, int lane)
+    __device__ __forceinline__ TileAddr(const GTensor& T, int64_t e0)
         : theta((GLOBAL uint8_t*)(T.theta + e0)),
           grad((const GLOBAL uint8_t*)(T.grad + e0)),
           codes(T.codes + (e0 >> 3) * Layout<kOpt>::kRec),
-          scales((GLOBAL uint8_t*)(T.scales + (e0 >> 5) * Layout<kOpt>::kScl)),
-          el((uint32_t)lane * (kLaneElems * 2)),
-          rec((uint32_t)lane * Layout<kOpt>::kRec),
-          scl((uint32_t)(lane >> 2) * (Layout<kOpt>::kScl * 2)) {}
+          scales((GLOBAL uint8_t*)(T.scales + (e0 >> 5) * Layout<kOpt>::kScl)) {
+        const uint32_t lane = lane_here();
+        el = lane * (kLaneElems * 2);
+        rec = lane * Layout<kOpt>::kRec;
+        scl = (lane >> 2) * (Layout<kOpt>::kScl * 2);
+    }
 
     __device__ __forceinline__ GLOBAL uint8_t* th(int k) const { return theta + k * kSubEl + el; }
     __device__ __forceinline__ const GLOBAL uint8_t* gr(int k) const {

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
         const GTensor& T = cur.T;
         const int64_t e0 = (tile - cur.begin) * kTile;
         if (e0 + kTile <= T.numel) {
-            const TileAddr<kAdamW> A(T, e0, lane);
+            const TileAddr<kAdamW> A(T, e0);
             Raw R[2];
             load_raw<kAdamW>(A, 0, R[0]);
             if (kSubTiles > 1) load_raw<kAdamW>(A, 1, R[1]);

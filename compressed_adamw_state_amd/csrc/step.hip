@@ -279,7 +279,7 @@ template <int kOpt, bool kFull, bool kLinV>
 __device__ __forceinline__ void step_tile(const GTensor& T, int64_t e0, int lane,
                                           const StepScalars& P) {
     if (kFull) {
-        const TileAddr<kOpt> A(T, e0, lane);
+        const TileAddr<kOpt> A(T, e0);
         Raw R[2];
         load_raw<kOpt>(A, 0, R[0]);
         if (kSubTiles > 1) load_raw<kOpt>(A, 1, R[1]);
@@ -307,7 +307,7 @@ __device__ __forceinline__ void step_sub(const GTensor& T, int64_t e0, int k, in
                                          const StepScalars& P) {
     const int64_t e = e0 + (int64_t)k * kSubTile;
     if (e + kSubTile <= T.numel) {
-        const TileAddr<kOpt> A(T, e0, lane);
+        const TileAddr<kOpt> A(T, e0);
         Raw R;
         load_raw<kOpt>(A, k, R);
         step_fast<kOpt, kLinV>(A, k, lane, R, P);
