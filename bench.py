@@ -594,6 +594,9 @@ def main():
     ap.add_argument("--secondary", default=None, metavar="WORKLOAD",
                     help="time only this secondary workload (--steps steps) and print its "
                          "record: a profiling aid, not the benchmark line")
+    ap.add_argument("--release", action="store_true",
+                    help="with --secondary: step the workload in gradient-release mode (one "
+                         "launch per tensor, backward order)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -606,7 +609,8 @@ def main():
     F.lib()
 
     if args.secondary:
-        r = other_optimizer(args.secondary, args.steps, torch.cuda.current_stream())
+        r = other_optimizer(args.secondary, args.steps, torch.cuda.current_stream(),
+                            release=args.release)
         print(json.dumps(r), flush=True)
         return
     if args.access_patterns:
@@ -664,6 +668,7 @@ def main():
     traffic = float(traffic_kv["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in traffic_kv \
         else None
     sq = read_profile("sq", w.name, khash)
+    valu_cycles = float(sq["SQ_INSTS_VALU"]) * 4 / 1024 if "SQ_INSTS_VALU" in sq else None
     out = {
         "metric": METRIC,
         "value": nparams * args.steps / wall,
@@ -694,13 +699,13 @@ def main():
                      "avg_launch_ms": avg * 1e3, "source_sha256_16": khash,
                      "valu_instructions_per_param":
                          float(sq["valu_instructions_per_param"]) if sq else None,
-                     # VALU issue time per launch (the SQ counters' instruction count at
-                     # the shader clock measured in that profiled run) over this run's
-                     # average launch time
-                     "valu_busy": (float(sq["valu_time_ms_at_measured_clock"]) / (avg * 1e3))
-                     if sq else None,
-                     "valu_busy_in_profiled_run": (float(sq["valu_time_ms_at_measured_clock"]) /
-                                                   float(sq["kernel_time_ms"])) if sq else None},
+                     # VALU issue cycles per SIMD per launch (SQ_INSTS_VALU of the profiled
+                     # run, one wave64 instruction per SIMD every 4 cycles on 1024 SIMDs), and
+                     # the shader clock at which that issue alone fills this run's launch
+                     "valu_cycles_per_simd": valu_cycles,
+                     "valu_bound_clock_ghz": (valu_cycles / (avg * 1e9)) if valu_cycles else None,
+                     "shader_clock_ghz_in_profiled_run":
+                         float(sq["shader_clock_ghz"]) if "shader_clock_ghz" in sq else None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
