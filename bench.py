@@ -465,8 +465,63 @@ def mix_ceiling(n: int, stream, reps: int = 5) -> dict:
             "best_ms": best * 1e3, "gb_s": nbytes / best / 1e9}
 
 
+def best_of(f, reps: int, stream) -> float:
+    """Best of `reps` launches of f (ms, HIP events on `stream`), after one
+    untimed launch."""
+    f()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for k in range(reps):
+        f()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    return min(ev[k].elapsed_time(ev[k + 1]) for k in range(reps))
+
+
+def placement(n: int, stream, sets: int = 3, rounds: int = 3, reps: int = 3) -> dict:
+    """Where the buffers lie: `sets` allocations of the byte-mix buffers
+    (theta', grad, codes, scales of n parameters) alive at once, each timed
+    with flashopt_mix_ceiling in alternation over `rounds` rounds; pattern
+    variants 0 and 4 (hashed tile order) on each; then set 0 with one array of
+    set 1 swapped in at a time, and each array alone (read, write, in-place
+    read+write over its whole size by flashopt_stream_sweep)."""
+    def alloc():
+        return [torch.empty(2 * n, dtype=torch.uint8, device="cuda"),
+                torch.empty(2 * n, dtype=torch.uint8, device="cuda"),
+                torch.empty(3 * n, dtype=torch.uint8, device="cuda"),
+                torch.empty(n // 8, dtype=torch.uint8, device="cuda")]
+    S = [alloc() for _ in range(sets)]
+    for b in S:
+        for t in b:
+            t.zero_()
+    mix = lambda b: (lambda: F.flashopt_mix_ceiling(b[0], b[1], b[2], b[3], n, stream))
+    pat = lambda v, b: (lambda: F.flashopt_pattern_probe(v, b[0], b[1], b[2], b[3], n, stream))
+    out = {"params": n, "mix_ms_by_round": [[best_of(mix(b), reps, stream) for b in S]
+                                            for _ in range(rounds)],
+           "variant0_ms": [best_of(pat(0, b), reps, stream) for b in S],
+           "variant4_hashed_order_ms": [best_of(pat(4, b), reps, stream) for b in S]}
+    names = ["theta", "grad", "codes", "scales"]
+    out["set0_with_one_array_of_set1_ms"] = {
+        names[i]: best_of(mix([S[1][j] if j == i else S[0][j] for j in range(4)]), reps, stream)
+        for i in range(4)}
+    single = {}
+    for k, b in enumerate(S):
+        for i in range(3):
+            t, nb = b[i], b[i].numel() // 16 * 16
+            rd = best_of(lambda: F.flashopt_stream_sweep([t], [], nb, False, stream), reps, stream)
+            wr = best_of(lambda: F.flashopt_stream_sweep([], [t], nb, False, stream), reps, stream)
+            rw = best_of(lambda: F.flashopt_stream_sweep([t], [t], nb, True, stream), reps, stream)
+            single[f"set{k} {names[i]}"] = {"read_gb_s": nb / rd / 1e6, "write_gb_s": nb / wr / 1e6,
+                                            "rw_in_place_gb_s": 2 * nb / rw / 1e6}
+    out["single_array"] = single
+    del S
+    torch.cuda.empty_cache()
+    return out
+
+
 def pattern_variants(n: int, stream, reps: int = 5, rounds: int = 2) -> list:
-    """flashopt_pattern_probe variants 0-3 and flashopt_mix_ceiling over the
+    """flashopt_pattern_probe variants 0-4 and flashopt_mix_ceiling over the
     same flat buffers of n parameters, alternating, best of `reps` launches
     per round: the step's traffic under each access pattern."""
     th = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
@@ -475,21 +530,14 @@ def pattern_variants(n: int, stream, reps: int = 5, rounds: int = 2) -> list:
     sc = torch.randint(-2 ** 15, 2 ** 15 - 1, (n // 16,), dtype=torch.int16, device="cuda")
     names = {0: "records 24 B as 3 x 8 B, 2 buffers (the fused kernel's)",
              1: "codes as 16-B units", 2: "16-B units by global-to-LDS DMA",
-             3: "records 24 B, 3 buffers (loads before stores)", 4: "mix ceiling (all 16-B, flat)"}
+             3: "records 24 B, 3 buffers (loads before stores)",
+             4: "as 0, tiles in a hashed order", "mix": "mix ceiling (all 16-B, flat)"}
     rows = {}
     for _ in range(rounds):
-        for v in range(5):
-            f = (lambda: F.flashopt_mix_ceiling(th, gr, cd, sc, n, stream)) if v == 4 else \
+        for v in names:
+            f = (lambda: F.flashopt_mix_ceiling(th, gr, cd, sc, n, stream)) if v == "mix" else \
                 (lambda v=v: F.flashopt_pattern_probe(v, th, gr, cd, sc, n, stream))
-            f()
-            torch.cuda.synchronize()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-            ev[0].record(stream)
-            for k in range(reps):
-                f()
-                ev[k + 1].record(stream)
-            torch.cuda.synchronize()
-            rows.setdefault(v, []).append(min(ev[k].elapsed_time(ev[k + 1]) for k in range(reps)))
+            rows.setdefault(v, []).append(best_of(f, reps, stream))
     del th, gr, cd, sc
     torch.cuda.empty_cache()
     return [{"variant": v, "pattern": names[v], "best_ms": min(t),
@@ -591,6 +639,10 @@ def main():
                          "stream-count sweep (12 buffers of 2 GiB), the step's traffic over flat "
                          "buffers under each pattern variant and the byte-mix ceiling, and the "
                          "step and its probe in two placements")
+    ap.add_argument("--placement", action="store_true",
+                    help="time only the placement study and print it as JSON: three allocations "
+                         "of the byte-mix buffers at Llama-3.1-8B size, timed in alternation, "
+                         "in two tile orders, with arrays swapped between them and alone")
     ap.add_argument("--secondary", default=None, metavar="WORKLOAD",
                     help="time only this secondary workload (--steps steps) and print its "
                          "record: a profiling aid, not the benchmark line")
@@ -620,6 +672,10 @@ def main():
              "flat_patterns": pattern_variants(w.numel, stream),
              "layouts": layouts(w, stream)}
         print(json.dumps(r), flush=True)
+        return
+    if args.placement:
+        n = W.WORKLOADS["llama31_8b"].numel // 2048 * 2048
+        print(json.dumps(placement(n, torch.cuda.current_stream())), flush=True)
         return
 
     w = W.WORKLOADS[args.workload]

@@ -148,6 +148,11 @@ __global__ __launch_bounds__(256) void mix_ceiling_kernel(GLOBAL uint8_t* theta,
 //      load in flight.
 //   3: as 0 with three register buffers: the loads of sub-tile k+2 are issued
 //      before sub-tile k is stored.
+//   4: as 0 with the tiles in a hashed order: wave w takes tile
+//      (w * mult) mod ntiles (mult a prime not dividing ntiles, so every tile
+//      once), so the tiles in flight at any moment are spread over the whole
+//      buffers instead of one window: separates an effect of which addresses
+//      are accessed together from one of where the buffers lie.
 // Results: theta' ^= grad in every variant; codes: variants 0 and 3 replace
 // each 8-parameter record's three 8-byte words (a, b, c) with (a^b, b^c,
 // c^a), variants 1 and 2 XOR every code byte with 0x5A; every scale word
@@ -158,6 +163,7 @@ struct PatternPtrs {
     GLOBAL uint8_t* rec;
     GLOBAL uint8_t* sc;
     int64_t ntiles;
+    int64_t mult;       // variant 4's tile order; 0: tile = wave
 };
 
 struct PRec { u32x4 th, gr; u32x2 a, b, c; uint32_t s; };
@@ -187,8 +193,9 @@ __device__ __forceinline__ void prec_store(const PatternPtrs& p, int64_t w, int 
 template <int kBuffers>
 __global__ __launch_bounds__(256) void pattern_records_kernel(PatternPtrs p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
-    if (w >= p.ntiles) return;
+    const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+    if (wave >= p.ntiles) return;
+    const int64_t w = p.mult ? wave * p.mult % p.ntiles : wave;
     PRec r[kBuffers];
     prec_load(p, w, 0, lane, r[0]);
     prec_load(p, w, 1, lane, r[1]);
@@ -375,18 +382,27 @@ int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, 
 
 int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* grad,
                            uint8_t* codes, uint16_t* scales, int64_t n, void* stream) {
-    if (variant < 0 || variant > 3) return FLASHOPT_ERR_ARG;
+    if (variant < 0 || variant > 4) return FLASHOPT_ERR_ARG;
     if (n < 0 || n > kMaxNumel || n % kMixTile != 0) return FLASHOPT_ERR_SIZE;
     if (n == 0) return FLASHOPT_OK;
     if (!theta || !grad || !codes || !scales) return FLASHOPT_ERR_NULL;
     if (!aligned(theta, 16) || !aligned(grad, 16) || !aligned(codes, 16) || !aligned(scales, 16))
         return FLASHOPT_ERR_ALIGN;
     PatternPtrs p{(GLOBAL uint8_t*)theta, (const GLOBAL uint8_t*)grad, (GLOBAL uint8_t*)codes,
-                  (GLOBAL uint8_t*)scales, n / kMixTile};
+                  (GLOBAL uint8_t*)scales, n / kMixTile, 0};
+    if (variant == 4) {
+        // the first of these primes that does not divide ntiles (ntiles <= 2^25
+        // with one wave per tile, so at most one of them divides it, and
+        // wave * mult stays far below 2^63)
+        static const int64_t kPrimes[] = {1000003, 1000033, 1000037, 1000039};
+        for (int64_t q : kPrimes)
+            if (p.ntiles % q != 0) { p.mult = q; break; }
+    }
     const dim3 grid(grid_for(p.ntiles)), block(kBlock);
     if (p.ntiles > kMaxBlocks * kWavesPerBlock) return FLASHOPT_ERR_SIZE;   // one wave per tile
     hipStream_t s = (hipStream_t)stream;
-    if (variant == 0) hipLaunchKernelGGL(pattern_records_kernel<2>, grid, block, 0, s, p);
+    if (variant == 0 || variant == 4)
+        hipLaunchKernelGGL(pattern_records_kernel<2>, grid, block, 0, s, p);
     else if (variant == 1) hipLaunchKernelGGL(pattern_units_kernel, grid, block, 0, s, p);
     else if (variant == 2) hipLaunchKernelGGL(pattern_dma_kernel, grid, block, 0, s, p);
     else hipLaunchKernelGGL(pattern_records_kernel<3>, grid, block, 0, s, p);

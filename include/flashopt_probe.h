@@ -60,11 +60,14 @@ int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, 
  *   variant 2: the units of 1 loaded by global-to-LDS DMA into a two-slot ring
  *              per wave (no register holds a load in flight);
  *   variant 3: as 0 with three register buffers (the loads of sub-tile k+2
- *              issued before sub-tile k is stored).
- * Results: theta ^= grad; codes: variants 0 and 3 replace each 24-byte record's
+ *              issued before sub-tile k is stored);
+ *   variant 4: as 0 with the tiles taken in a hashed order (wave w takes tile
+ *              w * q mod ntiles, q a prime near 10^6 that does not divide
+ *              ntiles), so the tiles in flight are spread over the buffers.
+ * Results: theta ^= grad; codes: variants 0, 3 and 4 replace each 24-byte record's
  * 8-byte words (a, b, c) with (a^b, b^c, c^a), variants 1 and 2 XOR every code
  * byte with 0x5A; every 32-bit scale word ^= 0x00010001.  DESTRUCTIVE.  Errors:
- * FLASHOPT_ERR_ARG (variant outside 0-3) and those of flashopt_mix_ceiling.
+ * FLASHOPT_ERR_ARG (variant outside 0-4) and those of flashopt_mix_ceiling.
  * One launch on `stream`, nothing allocated. */
 int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* grad,
                            uint8_t* codes, uint16_t* scales, int64_t n, void* stream);

@@ -93,11 +93,12 @@ def test_stream_sweep_values(rw, in_place):
         assert torch.equal(dr[k].cpu(), reads[k])
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_pattern_probe_variants(variant):
     """flashopt_pattern_probe: theta ^= grad; codes per record (a^b, b^c, c^a)
-    for variants 0 and 3, every byte ^= 0x5A for 1 and 2; every scale word ^=
-    0x00010001; over 7 tiles and nothing beyond."""
+    for variants 0, 3 and 4, every byte ^= 0x5A for 1 and 2; every scale word ^=
+    0x00010001; over 7 tiles and nothing beyond (variant 4: every tile once,
+    in its hashed order)."""
     gen = torch.Generator().manual_seed(10 + variant)
     n = 2048 * 7
     pad = 64
@@ -111,7 +112,7 @@ def test_pattern_probe_variants(variant):
     th, gr, cd, sc = (t.cpu() for t in d)
     assert torch.equal(th[:n], theta[:n] ^ grad[:n]) and torch.equal(th[n:], theta[n:])
     assert torch.equal(gr, grad)
-    if variant in (0, 3):
+    if variant in (0, 3, 4):
         w = codes[:3 * n].view(torch.int64).view(-1, 3)
         exp = torch.stack([w[:, 0] ^ w[:, 1], w[:, 1] ^ w[:, 2], w[:, 2] ^ w[:, 0]], 1)
         assert torch.equal(cd[:3 * n].view(torch.int64).view(-1, 3), exp)
