@@ -482,8 +482,8 @@ def best_of(f, reps: int, stream) -> float:
 def placement(n: int, stream, sets: int = 3, rounds: int = 3, reps: int = 3) -> dict:
     """Where the buffers lie: `sets` allocations of the byte-mix buffers
     (theta', grad, codes, scales of n parameters) alive at once, each timed
-    with flashopt_mix_ceiling in alternation over `rounds` rounds; pattern
-    variants 0 and 4 (hashed tile order) on each; then set 0 with one array of
+    with flashopt_mix_ceiling in alternation over `rounds` rounds; every
+    pattern variant (4: hashed tile order) on each; then set 0 with one array of
     set 1 swapped in at a time, and each array alone (read, write, in-place
     read+write over its whole size by flashopt_stream_sweep)."""
     def alloc():
@@ -499,8 +499,7 @@ def placement(n: int, stream, sets: int = 3, rounds: int = 3, reps: int = 3) -> 
     pat = lambda v, b: (lambda: F.flashopt_pattern_probe(v, b[0], b[1], b[2], b[3], n, stream))
     out = {"params": n, "mix_ms_by_round": [[best_of(mix(b), reps, stream) for b in S]
                                             for _ in range(rounds)],
-           "variant0_ms": [best_of(pat(0, b), reps, stream) for b in S],
-           "variant4_hashed_order_ms": [best_of(pat(4, b), reps, stream) for b in S]}
+           "variant_ms": {v: [best_of(pat(v, b), reps, stream) for b in S] for v in range(5)}}
     names = ["theta", "grad", "codes", "scales"]
     out["set0_with_one_array_of_set1_ms"] = {
         names[i]: best_of(mix([S[1][j] if j == i else S[0][j] for j in range(4)]), reps, stream)
