@@ -306,12 +306,14 @@ class StateArena:
     from the arena, or a given tensor such as a parameter's own storage);
     grad(j, i) is tensor i's gradient of set j.
 
-    Why: the step's bandwidth depends on where its streams sit in HBM.  On
-    MI355X, over the Llama-3.1-8B list, the step's loads and stores with no
-    arithmetic (flashopt_stream_probe) measured 16.2-16.9 ms with this layout
-    against 17.4-18.8 ms with theta' and gradients allocated per tensor and
-    18.5-18.9 ms with each tensor's four arrays side by side; the step itself
-    18.35-18.48 ms against 18.5-19.1 ms (one box, one process)."""
+    Why one buffer with a region per stream: one allocation for the whole
+    state instead of four per tensor, and each stream the step reads or
+    writes contiguous across the list's tensors.  The step's rate on MI355X
+    does not depend on the layout inside the buffer so much as on where the
+    allocation's physical pages land: the same byte mix over different
+    allocations of the same buffers takes 16.3-19.0 ms at Llama-3.1-8B size,
+    whatever the order of the tiles or the offsets between regions, and each
+    array alone streams at the same rate in every allocation."""
 
     ALIGN = 4096
     REGION = 1 << 21
