@@ -312,7 +312,7 @@ class StateArena:
     does not depend on the layout inside the buffer so much as on where the
     allocation's physical pages land: the same byte mix over different
     allocations of the same buffers takes 16.3-19.0 ms at Llama-3.1-8B size,
-    whatever the order of the tiles or the offsets between regions, and each
+    whatever the order of the tiles, and each
     array alone streams at the same rate in every allocation."""
 
     ALIGN = 4096
