@@ -227,7 +227,7 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
             rc[p >> 1] = (rc[p >> 1] & ~(0xFFFFu << sh)) | (pair << sh);
         }
     }
-    st4(A.th(k), make_uint4(otb[0], otb[1], otb[2], otb[3]));
+    st4nt(A.th(k), make_uint4(otb[0], otb[1], otb[2], otb[3]));
     // group maxima of |z| and w as floats (== the integer max of the bit patterns
     // for every finite value)
     float amax_m = 0.0f, amax_v = 0.0f;

@@ -33,8 +33,9 @@ int flashopt_stream_probe(const flashopt_list* list, void* stream);
  * parameter (read 7.125, write 5.125) over the same four read and three
  * written streams, in place like the step, but over flat buffers with the
  * best access pattern the byte mix allows (every load and store a fully
- * coalesced 16 bytes per lane; a wave loads one 2048-parameter tile, then
- * stores it).  Over n parameters (n a multiple of 2048):
+ * coalesced 16 bytes per lane with the non-temporal hint; a wave loads one
+ * 2048-parameter tile, then stores it).  Over n parameters (n a multiple of
+ * 2048):
  *   theta   uint16[n]           theta ^= grad            (read and written)
  *   grad    uint16[n]           read only
  *   codes   uint8[3n]           every byte ^= 0x5A       (read and written)
@@ -51,6 +52,8 @@ int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, 
  * wave per 2048-parameter tile of four 512-parameter sub-tiles, lane l owning
  * parameters [8l, 8l+8) of a sub-tile), with one of the access patterns the
  * fused kernel could use -- to tell the pattern's cost from the byte mix's:
+ *   (theta' and the gradient carry the non-temporal hint in every variant, as
+ *   in the fused kernel; variant 2's DMA loads do not)
  *   variant 0: the fused kernel's own: theta' and gradient 16 bytes per lane,
  *              the code record of a lane's 8 parameters (24 bytes) as three
  *              8-byte accesses, the group's 4-byte scale pair from one lane of
