@@ -28,6 +28,18 @@ __device__ __forceinline__ GLOBAL float* f32_at(const GTensor& T, int64_t i, int
     return (GLOBAL float*)(T.codes + (i >> 9) * LayoutF<kOpt>::kBlock) + f * kSubTile + (i & 511);
 }
 
+// Every access of the uncompressed step covers whole lines, each touched once
+// per step: all carry the non-temporal hint (2.5-3.2 % faster than without on
+// the Llama-3.1-8B list; device.hpp has the 16-byte forms).
+__device__ __forceinline__ uint2 ld2nt(const GLOBAL void* p) {
+    const u32x2 v = __builtin_nontemporal_load((const GLOBAL u32x2*)p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st2nt(GLOBAL void* p, uint2 v) {
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, (GLOBAL u32x2*)p);
+}
+
 struct RawF {
     uint4 th[2], m[2], v[2];        // a lane's 2 x 4 FP32 values of each field
     uint2 gr[2];                    // and its 2 x 4 BF16 gradients
@@ -37,15 +49,15 @@ struct RawF {
 template <int kOpt>
 __device__ __forceinline__ void load_raw_f(const GTensor& T, int64_t e, int lane, RawF& R) {
     const GLOBAL uint8_t* blk = T.codes + (e >> 9) * LayoutF<kOpt>::kBlock + 16 * lane;
-    R.gr[0] = ld2(T.grad + e + 4 * lane);
-    R.gr[1] = ld2(T.grad + e + 256 + 4 * lane);
-    R.th[0] = ld4(blk);
-    R.th[1] = ld4(blk + 1024);
-    R.m[0] = ld4(blk + 2048);
-    R.m[1] = ld4(blk + 3072);
+    R.gr[0] = ld2nt(T.grad + e + 4 * lane);
+    R.gr[1] = ld2nt(T.grad + e + 256 + 4 * lane);
+    R.th[0] = ld4nt(blk);
+    R.th[1] = ld4nt(blk + 1024);
+    R.m[0] = ld4nt(blk + 2048);
+    R.m[1] = ld4nt(blk + 3072);
     if (kOpt == kAdamW) {
-        R.v[0] = ld4(blk + 4096);
-        R.v[1] = ld4(blk + 5120);
+        R.v[0] = ld4nt(blk + 4096);
+        R.v[1] = ld4nt(blk + 5120);
     }
 }
 
@@ -70,15 +82,15 @@ __device__ __forceinline__ void step_f(const GTensor& T, int64_t e, int lane, co
         tb[j] = f32_to_bf16(u.theta);
     }
     GLOBAL uint8_t* blk = T.codes + (e >> 9) * LayoutF<kOpt>::kBlock + 16 * lane;
-    st2(T.theta + e + 4 * lane, make_uint2(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16)));
-    st2(T.theta + e + 256 + 4 * lane, make_uint2(tb[4] | (tb[5] << 16), tb[6] | (tb[7] << 16)));
-    st4(blk, make_uint4(th[0], th[1], th[2], th[3]));
-    st4(blk + 1024, make_uint4(th[4], th[5], th[6], th[7]));
-    st4(blk + 2048, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-    st4(blk + 3072, make_uint4(mo[4], mo[5], mo[6], mo[7]));
+    st2nt(T.theta + e + 4 * lane, make_uint2(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16)));
+    st2nt(T.theta + e + 256 + 4 * lane, make_uint2(tb[4] | (tb[5] << 16), tb[6] | (tb[7] << 16)));
+    st4nt(blk, make_uint4(th[0], th[1], th[2], th[3]));
+    st4nt(blk + 1024, make_uint4(th[4], th[5], th[6], th[7]));
+    st4nt(blk + 2048, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+    st4nt(blk + 3072, make_uint4(mo[4], mo[5], mo[6], mo[7]));
     if (kOpt == kAdamW) {
-        st4(blk + 4096, make_uint4(vo[0], vo[1], vo[2], vo[3]));
-        st4(blk + 5120, make_uint4(vo[4], vo[5], vo[6], vo[7]));
+        st4nt(blk + 4096, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+        st4nt(blk + 5120, make_uint4(vo[4], vo[5], vo[6], vo[7]));
     }
 }
 
