@@ -261,9 +261,13 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
                                  pack_lo_bytes(mb[4], mb[5], mb[6], mb[7]));
     const uint2 orho = make_uint2(rc[0] ^ 0x80808080u, rc[1] ^ 0x80808080u);
     GLOBAL uint8_t* rec = A.rc(k);
-    st2(rec + kRhoOff, orho);
-    st2(rec + kMOff, oqm);
-    if (kOpt == kAdamW) st2(rec + kVOff, make_uint2(qv0, qv1));
+    if (Layout<kOpt>::kRec == 16) {                  // SGD, Lion: one hinted 16-byte record
+        st4nt(rec, make_uint4(orho.x, orho.y, oqm.x, oqm.y));
+    } else {
+        st2(rec + kRhoOff, orho);
+        st2(rec + kMOff, oqm);
+        if (kOpt == kAdamW) st2(rec + kVOff, make_uint2(qv0, qv1));
+    }
     if ((lane & 3) == 0) {
         if (kOpt == kAdamW)                          // m | v << 16 in one v_perm
             *(GLOBAL uint32_t*)A.sc(k) = __builtin_amdgcn_perm(sv16, sm16, 0x05040100u);
