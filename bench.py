@@ -393,18 +393,18 @@ def cpu_threads() -> int:
 
 
 def host_fields(st: F.TensorState) -> dict:
-    """theta', rho, momentum and variance codes, both scales of one tensor as
-    contiguous host arrays (unpacked from the interleaved records on the
-    device, then copied)."""
+    """theta', rho, momentum and variance codes, both scales of one AdamW
+    tensor as contiguous host arrays (the code planes of each 512-element
+    block, include/flashopt.h, unpacked on the device, then copied)."""
     n = st.numel
-    nrec, ng = (n + 7) // 8, (n + 31) // 32
-    rec = st.codes[:nrec * 24].view(nrec, 3, 8)
+    nblk, ng = (n + 511) // 512, (n + 31) // 32
+    pl = st.codes[:nblk * 1536].view(nblk, 3, 512)
     sc = st.scales[:ng * 2].view(ng, 2)
     host = lambda t: t.contiguous().cpu().numpy()
     return {"tb": host(st.theta.view(torch.int16)).view(np.uint16),
-            "rho": host(rec[:, 0].reshape(-1)[:n]).view(np.int8),
-            "qm": host(rec[:, 1].reshape(-1)[:n]).view(np.int8),
-            "qv": host(rec[:, 2].reshape(-1)[:n]),
+            "rho": host(pl[:, 0].reshape(-1)[:n]).view(np.int8),
+            "qm": host(pl[:, 1].reshape(-1)[:n]).view(np.int8),
+            "qv": host(pl[:, 2].reshape(-1)[:n]),
             "sm": host(sc[:, 0]).view(np.uint16), "sv": host(sc[:, 1]).view(np.uint16)}
 
 
@@ -499,7 +499,7 @@ def placement(n: int, stream, sets: int = 3, rounds: int = 3, reps: int = 3) -> 
     pat = lambda v, b: (lambda: F.flashopt_pattern_probe(v, b[0], b[1], b[2], b[3], n, stream))
     out = {"params": n, "mix_ms_by_round": [[best_of(mix(b), reps, stream) for b in S]
                                             for _ in range(rounds)],
-           "variant_ms": {v: [best_of(pat(v, b), reps, stream) for b in S] for v in range(5)}}
+           "variant_ms": {v: [best_of(pat(v, b), reps, stream) for b in S] for v in range(6)}}
     names = ["theta", "grad", "codes", "scales"]
     out["set0_with_one_array_of_set1_ms"] = {
         names[i]: best_of(mix([S[1][j] if j == i else S[0][j] for j in range(4)]), reps, stream)
@@ -520,17 +520,19 @@ def placement(n: int, stream, sets: int = 3, rounds: int = 3, reps: int = 3) -> 
 
 
 def pattern_variants(n: int, stream, reps: int = 5, rounds: int = 2) -> list:
-    """flashopt_pattern_probe variants 0-4 and flashopt_mix_ceiling over the
+    """flashopt_pattern_probe variants 0-5 and flashopt_mix_ceiling over the
     same flat buffers of n parameters, alternating, best of `reps` launches
     per round: the step's traffic under each access pattern."""
     th = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
     gr = torch.randint(-2 ** 15, 2 ** 15 - 1, (n,), dtype=torch.int16, device="cuda")
     cd = torch.randint(0, 255, (3 * n,), dtype=torch.uint8, device="cuda")
     sc = torch.randint(-2 ** 15, 2 ** 15 - 1, (n // 16,), dtype=torch.int16, device="cuda")
-    names = {0: "records 24 B as 3 x 8 B, 2 buffers (the fused kernel's)",
+    names = {0: "codes as 3 x 8-B plane runs, hinted, 2 buffers (the fused kernel's)",
              1: "codes as 16-B units", 2: "16-B units by global-to-LDS DMA",
-             3: "records 24 B, 3 buffers (loads before stores)",
-             4: "as 0, tiles in a hashed order", "mix": "mix ceiling (all 16-B, flat)"}
+             3: "as 0, 3 buffers (loads before stores)",
+             4: "as 0, tiles in a hashed order",
+             5: "codes as interleaved 24-B records, 3 x 8 B unhinted (the earlier layout)",
+             "mix": "mix ceiling (all 16-B, flat)"}
     rows = {}
     for _ in range(rounds):
         for v in names:
@@ -740,7 +742,7 @@ def main():
         "config": {"workload": f"{w.name}: Llama-3.1-8B-shaped list, {len(w.tensors)} tensors, "
                                f"{nparams} params, AdamW lr 1e-3 betas (0.9, 0.999) eps 1e-8 "
                                f"wd 0.01, bf16 grads N(0, 1e-4)",
-                   "state": "theta' bf16 + 24-byte code records (rho, m, v per 8 elements) + fp16 scale pair per 32",
+                   "state": "theta' bf16 + int8 rho, int8 m and uint8 v code planes per 512-element block + fp16 scale pair per 32",
                    "launches_per_step": 1},
         "hbm_gb_s": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBS,

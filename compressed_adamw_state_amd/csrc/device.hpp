@@ -24,15 +24,20 @@ enum Opt { kAdamW = 0, kSgd = 1, kLion = 2 };
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// State layout of one tensor (see include/flashopt.h): a code record per 8
-// elements -- rho[8], m_code[8] and, for AdamW, v_code[8] -- and per 32-element
-// group the FP16 m scale followed, for AdamW, by the v scale.  SGD and Lion
-// keep one momentum, so they share the 16-byte record.
+// State layout of one tensor (see include/flashopt.h).  Codes, per
+// 512-element block: AdamW keeps three 512-byte planes, rho, m_code and
+// v_code, each in element order; SGD and Lion keep 64 16-byte records, one
+// per 8-element run, rho[8] then m_code[8].  Either way a lane's codes in a
+// full sub-tile are whole accesses that, with the other lanes', cover whole
+// lines.  Scales: per 32-element group the FP16 m scale followed, for AdamW,
+// by the v scale.
+enum Field { kRho = 0, kM = 1, kV = 2 };
 template <int kOpt> struct Layout {
-    static constexpr int kRec = kOpt == kAdamW ? 24 : 16;   // bytes per 8-element record
-    static constexpr int kScl = kOpt == kAdamW ? 2 : 1;     // FP16 scales per group
+    static constexpr int kLaneCode = kOpt == kAdamW ? 8 : 16;    // bytes between 8-element runs
+    static constexpr int kField = kOpt == kAdamW ? 512 : 8;      // bytes between fields
+    static constexpr int kBlockBytes = kOpt == kAdamW ? 1536 : 1024;   // per 512 elements
+    static constexpr int kScl = kOpt == kAdamW ? 2 : 1;           // FP16 scales per group
 };
-constexpr int kRhoOff = 0, kMOff = 8, kVOff = 16;          // field offsets in a record
 
 // Device descriptor of one tensor as it sits in the table and in kernel
 // arguments: plain 64-bit addresses (64 bytes per tensor).
@@ -64,10 +69,11 @@ __device__ __forceinline__ GTensor view(const DevTensor& d) {
     return t;
 }
 
-// byte address of field `off` of element i's record entry
+// byte address of field f of element i's code
 template <int kOpt>
-__device__ __forceinline__ GLOBAL uint8_t* code_at(const GTensor& T, int64_t i, int off) {
-    return T.codes + (i >> 3) * Layout<kOpt>::kRec + off + (i & 7);
+__device__ __forceinline__ GLOBAL uint8_t* code_at(const GTensor& T, int64_t i, int f) {
+    return T.codes + (i >> 9) * Layout<kOpt>::kBlockBytes +
+           ((i & 511) >> 3) * Layout<kOpt>::kLaneCode + f * Layout<kOpt>::kField + (i & 7);
 }
 
 
@@ -92,13 +98,15 @@ __device__ __forceinline__ void st2(GLOBAL void* p, uint2 v) {
     const u32x2 w = {v.x, v.y};
     *(GLOBAL u32x2*)p = w;
 }
-// The same 16-byte accesses with the non-temporal hint (the `nt` bit), for
-// the streams a step touches once in whole lines: theta' (read and written)
-// and the gradient (read).  Measured on the Llama-3.1-8B step, against plain
-// accesses in the same process: 1.5-2.2 % faster whatever the placement of the
-// state.  AdamW's code records are not hinted: a lane's 24-byte record takes
-// two accesses over the same lines, and the hint on those made the step
-// slower; SGD's and Lion's 16-byte records, one access each, are.
+// The same accesses with the non-temporal hint (the `nt` bit), for the
+// streams a step touches once, each access covering whole lines with the
+// other lanes': theta' (read and written), the gradient (read) and the code
+// planes or records.  Measured on the Llama-3.1-8B step against plain
+// accesses in the same process: 1.5-2.2 % faster on theta' and the gradient
+// whatever the placement of the state, 2.6-3.3 % on Lion's records.  Where a
+// lane's access covers only part of each line (AdamW's earlier interleaved
+// 24-byte records, two accesses over the same lines) the hint made the step
+// slower.
 __device__ __forceinline__ uint4 ld4nt(const GLOBAL void* p) {
     const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)p);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -106,6 +114,14 @@ __device__ __forceinline__ uint4 ld4nt(const GLOBAL void* p) {
 __device__ __forceinline__ void st4nt(GLOBAL void* p, uint4 v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, (GLOBAL u32x4*)p);
+}
+__device__ __forceinline__ uint2 ld2nt(const GLOBAL void* p) {
+    const u32x2 v = __builtin_nontemporal_load((const GLOBAL u32x2*)p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st2nt(GLOBAL void* p, uint2 v) {
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, (GLOBAL u32x2*)p);
 }
 
 __device__ __forceinline__ int64_t uniform(int64_t x) {
@@ -212,9 +228,9 @@ __device__ __forceinline__ void load_lane(const GTensor& T, int64_t e, Lane8& L)
         const bool ok = e + j < n;
         L.th[j] = ok ? T.theta[e + j] : 0u;
         L.gr[j] = ok ? T.grad[e + j] : 0u;
-        L.rho[j] = ok ? (int8_t)*code_at<kOpt>(T, e + j, kRhoOff) : 0;
-        L.qm[j] = ok ? (int8_t)*code_at<kOpt>(T, e + j, kMOff) : 0;
-        if (kOpt == kAdamW) L.qv[j] = ok ? *code_at<kOpt>(T, e + j, kVOff) : 0u;
+        L.rho[j] = ok ? (int8_t)*code_at<kOpt>(T, e + j, kRho) : 0;
+        L.qm[j] = ok ? (int8_t)*code_at<kOpt>(T, e + j, kM) : 0;
+        if (kOpt == kAdamW) L.qv[j] = ok ? *code_at<kOpt>(T, e + j, kV) : 0u;
     }
     const int64_t g = e >> 5;
     const bool gok = (e & ~int64_t(31)) < n;           // the lane's group has valid elements
@@ -304,22 +320,22 @@ __device__ __forceinline__ uint32_t lane_here() {
 template <int kOpt>
 struct TileAddr {
     static constexpr int kSubEl = kSubTile * 2;                               // BF16 bytes
-    static constexpr int kSubRec = kSubTile / 8 * Layout<kOpt>::kRec;
+    static constexpr int kSubRec = Layout<kOpt>::kBlockBytes;
     static constexpr int kSubScl = kSubTile / kGroup * Layout<kOpt>::kScl * 2;
     GLOBAL uint8_t* theta;
     const GLOBAL uint8_t* grad;
     GLOBAL uint8_t* codes;
     GLOBAL uint8_t* scales;
-    uint32_t el, rec, scl;          // lane offsets: 8 BF16, one record, the group's scales
+    uint32_t el, rec, scl;          // lane offsets: 8 BF16, its code run, the group's scales
 
     __device__ __forceinline__ TileAddr(const GTensor& T, int64_t e0)
         : theta((GLOBAL uint8_t*)(T.theta + e0)),
           grad((const GLOBAL uint8_t*)(T.grad + e0)),
-          codes(T.codes + (e0 >> 3) * Layout<kOpt>::kRec),
+          codes(T.codes + (e0 >> 9) * Layout<kOpt>::kBlockBytes),
           scales((GLOBAL uint8_t*)(T.scales + (e0 >> 5) * Layout<kOpt>::kScl)) {
         const uint32_t lane = lane_here();
         el = lane * (kLaneElems * 2);
-        rec = lane * Layout<kOpt>::kRec;
+        rec = lane * Layout<kOpt>::kLaneCode;
         scl = (lane >> 2) * (Layout<kOpt>::kScl * 2);
     }
 
@@ -338,22 +354,17 @@ __device__ __forceinline__ void load_raw(const TileAddr<kOpt>& A, int k, Raw& R)
     const GLOBAL uint8_t* rec = A.rc(k);
     R.th = ld4nt(A.th(k));
     R.gr = ld4nt(A.gr(k));
-    if (Layout<kOpt>::kRec == 16) {
-        // SGD, Lion: a lane's record is one whole 16-byte access, hinted like
-        // theta' (2.6-3.3 % faster Lion steps at Llama-3.1-8B shapes)
-        const uint4 r = ld4nt(rec);
-        R.rho = make_uint2(r.x, r.y);
-        R.qm = make_uint2(r.z, r.w);
-    } else {
-        R.rho = ld2(rec + kRhoOff);
-        R.qm = ld2(rec + kMOff);
-    }
     if (kOpt == kAdamW) {
-        R.qv = ld2(rec + kVOff);
+        R.rho = ld2nt(rec);
+        R.qm = ld2nt(rec + Layout<kOpt>::kField);
+        R.qv = ld2nt(rec + 2 * Layout<kOpt>::kField);
         const uint32_t w = *(const GLOBAL uint32_t*)A.sc(k);             // m | v << 16
         R.ms = w & 0xFFFFu;
         R.vs = w >> 16;
     } else {
+        const uint4 r = ld4nt(rec);                        // one 16-byte record
+        R.rho = make_uint2(r.x, r.y);
+        R.qm = make_uint2(r.z, r.w);
         R.ms = *(const GLOBAL uint16_t*)A.sc(k);
     }
 }

@@ -23,9 +23,9 @@ __device__ __forceinline__ void probe_sub(const TileAddr<kAdamW>& A, int k, int 
     GLOBAL uint8_t* rec = A.rc(k);
     st4nt(A.th(k), make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
                               R.th.w ^ R.gr.w));
-    st2(rec + kRhoOff, xor2(R.rho, R.qm));
-    st2(rec + kMOff, xor2(R.qm, R.qv));
-    st2(rec + kVOff, xor2(R.qv, R.rho));
+    st2nt(rec, xor2(R.rho, R.qm));
+    st2nt(rec + Layout<kAdamW>::kField, xor2(R.qm, R.qv));
+    st2nt(rec + 2 * Layout<kAdamW>::kField, xor2(R.qv, R.rho));
     if ((lane & 3) == 0)
         *(GLOBAL uint32_t*)A.sc(k) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
 }
@@ -59,9 +59,9 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
                 for (int j = 0; j < 8; ++j) {
                     const int64_t i = e + j;
                     if (i < T.numel) {
-                        GLOBAL uint8_t* r = code_at<kAdamW>(T, i, kRhoOff);
-                        GLOBAL uint8_t* m = code_at<kAdamW>(T, i, kMOff);
-                        GLOBAL uint8_t* v = code_at<kAdamW>(T, i, kVOff);
+                        GLOBAL uint8_t* r = code_at<kAdamW>(T, i, kRho);
+                        GLOBAL uint8_t* m = code_at<kAdamW>(T, i, kM);
+                        GLOBAL uint8_t* v = code_at<kAdamW>(T, i, kV);
                         const uint8_t rho = *r, qm = *m, qv = *v;
                         T.theta[i] = (uint16_t)(T.theta[i] ^ T.grad[i]);
                         *r = (uint8_t)(rho ^ qm);
@@ -138,12 +138,14 @@ __global__ __launch_bounds__(256) void mix_ceiling_kernel(GLOBAL uint8_t* theta,
 // isolate the pattern from the byte mix.  Per tile, four 512-parameter
 // sub-tiles; lane l owns parameters [8l, 8l+8) of a sub-tile.
 //   0: the fused kernel's own pattern: theta' and the gradient 16 bytes per
-//      lane, the code record of the lane's 8 parameters (24 bytes) as three
-//      8-byte accesses, a quad leader's 4-byte scale pair; sub-tile k+2
-//      loaded once sub-tile k is stored (two register buffers).
+//      lane, the codes of the lane's 8 parameters as three 8-byte runs, one
+//      in each 512-byte plane of the sub-tile's 1536 code bytes, a quad
+//      leader's 4-byte scale pair; every theta', gradient and code access
+//      hinted non-temporal; sub-tile k+2 loaded once sub-tile k is stored
+//      (two register buffers).
 //   1: as 0, but the 1536 code bytes of a sub-tile as 16-byte units (lane l
 //      unit l, lanes 0-31 also unit 64 + l) and the 64 scale bytes as 16
-//      lanes x 4 bytes.
+//      lanes x 4 bytes, the codes not hinted.
 //   2: the units of 1, loaded by global-to-LDS DMA (global_load_lds_dwordx4)
 //      into a two-slot ring per wave and read back from LDS: no VGPR holds a
 //      load in flight.
@@ -154,8 +156,11 @@ __global__ __launch_bounds__(256) void mix_ceiling_kernel(GLOBAL uint8_t* theta,
 //      once), so the tiles in flight at any moment are spread over the whole
 //      buffers instead of one window: separates an effect of which addresses
 //      are accessed together from one of where the buffers lie.
-// Results: theta' ^= grad in every variant; codes: variants 0 and 3 replace
-// each 8-parameter record's three 8-byte words (a, b, c) with (a^b, b^c,
+//   5: as 0, but the lane's codes as one interleaved 24-byte record (lane l
+//      at bytes [24l, 24l+24) of the sub-tile's 1536), three 8-byte accesses
+//      without the hint: the layout the fused kernel used before the planes.
+// Results: theta' ^= grad in every variant; codes: variants 0, 3, 4 and 5
+// replace each lane's three 8-byte code words (a, b, c) with (a^b, b^c,
 // c^a), variants 1 and 2 XOR every code byte with 0x5A; every scale word
 // (the pair of a 32-parameter group) ^= 0x00010001.
 struct PatternPtrs {
@@ -169,42 +174,67 @@ struct PatternPtrs {
 
 struct PRec { u32x4 th, gr; u32x2 a, b, c; uint32_t s; };
 
+// the lane's three 8-byte code words of sub-tile k: plane runs (kPlanes) or
+// one interleaved record
+template <bool kPlanes>
+__device__ __forceinline__ GLOBAL uint8_t* prec_codes(const PatternPtrs& p, int64_t w, int k,
+                                                      int lane) {
+    return p.rec + w * 6144 + k * 1536 + lane * (kPlanes ? 8 : 24);
+}
+template <bool kPlanes> constexpr int kPrecWord = kPlanes ? 512 : 8;    // bytes between words
+
+template <bool kPlanes>
 __device__ __forceinline__ void prec_load(const PatternPtrs& p, int64_t w, int k, int lane,
                                           PRec& r) {
     r.th = __builtin_nontemporal_load((const GLOBAL u32x4*)(p.th + w * 4096 + k * 1024 + lane * 16));
     r.gr = __builtin_nontemporal_load((const GLOBAL u32x4*)(p.gr + w * 4096 + k * 1024 + lane * 16));
-    const GLOBAL uint8_t* c = p.rec + w * 6144 + k * 1536 + lane * 24;
-    r.a = *(const GLOBAL u32x2*)c;
-    r.b = *(const GLOBAL u32x2*)(c + 8);
-    r.c = *(const GLOBAL u32x2*)(c + 16);
+    const GLOBAL uint8_t* c = prec_codes<kPlanes>(p, w, k, lane);
+    constexpr int d = kPrecWord<kPlanes>;
+    if (kPlanes) {
+        r.a = __builtin_nontemporal_load((const GLOBAL u32x2*)c);
+        r.b = __builtin_nontemporal_load((const GLOBAL u32x2*)(c + d));
+        r.c = __builtin_nontemporal_load((const GLOBAL u32x2*)(c + 2 * d));
+    } else {
+        r.a = *(const GLOBAL u32x2*)c;
+        r.b = *(const GLOBAL u32x2*)(c + d);
+        r.c = *(const GLOBAL u32x2*)(c + 2 * d);
+    }
     r.s = *(const GLOBAL uint32_t*)(p.sc + w * 256 + k * 64 + (lane >> 2) * 4);
 }
 
+template <bool kPlanes>
 __device__ __forceinline__ void prec_store(const PatternPtrs& p, int64_t w, int k, int lane,
                                            const PRec& r) {
     __builtin_nontemporal_store(r.th ^ r.gr, (GLOBAL u32x4*)(p.th + w * 4096 + k * 1024 + lane * 16));
-    GLOBAL uint8_t* c = p.rec + w * 6144 + k * 1536 + lane * 24;
-    *(GLOBAL u32x2*)c = r.a ^ r.b;
-    *(GLOBAL u32x2*)(c + 8) = r.b ^ r.c;
-    *(GLOBAL u32x2*)(c + 16) = r.c ^ r.a;
+    GLOBAL uint8_t* c = prec_codes<kPlanes>(p, w, k, lane);
+    constexpr int d = kPrecWord<kPlanes>;
+    if (kPlanes) {
+        __builtin_nontemporal_store(r.a ^ r.b, (GLOBAL u32x2*)c);
+        __builtin_nontemporal_store(r.b ^ r.c, (GLOBAL u32x2*)(c + d));
+        __builtin_nontemporal_store(r.c ^ r.a, (GLOBAL u32x2*)(c + 2 * d));
+    } else {
+        *(GLOBAL u32x2*)c = r.a ^ r.b;
+        *(GLOBAL u32x2*)(c + d) = r.b ^ r.c;
+        *(GLOBAL u32x2*)(c + 2 * d) = r.c ^ r.a;
+    }
     if ((lane & 3) == 0)
         *(GLOBAL uint32_t*)(p.sc + w * 256 + k * 64 + (lane >> 2) * 4) = r.s ^ 0x00010001u;
 }
 
-template <int kBuffers>
+template <int kBuffers, bool kPlanes>
 __global__ __launch_bounds__(256) void pattern_records_kernel(PatternPtrs p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = uniform((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
     if (wave >= p.ntiles) return;
     const int64_t w = p.mult ? wave * p.mult % p.ntiles : wave;
     PRec r[kBuffers];
-    prec_load(p, w, 0, lane, r[0]);
-    prec_load(p, w, 1, lane, r[1]);
+    prec_load<kPlanes>(p, w, 0, lane, r[0]);
+    prec_load<kPlanes>(p, w, 1, lane, r[1]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        if (kBuffers == 3 && k + 2 < 4) prec_load(p, w, k + 2, lane, r[(k + 2) % kBuffers]);
-        prec_store(p, w, k, lane, r[k % kBuffers]);
-        if (kBuffers == 2 && k + 2 < 4) prec_load(p, w, k + 2, lane, r[k % kBuffers]);
+        if (kBuffers == 3 && k + 2 < 4) prec_load<kPlanes>(p, w, k + 2, lane, r[(k + 2) % kBuffers]);
+        prec_store<kPlanes>(p, w, k, lane, r[k % kBuffers]);
+        if (kBuffers == 2 && k + 2 < 4) prec_load<kPlanes>(p, w, k + 2, lane, r[k % kBuffers]);
     }
 }
 
@@ -383,7 +413,7 @@ int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, 
 
 int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* grad,
                            uint8_t* codes, uint16_t* scales, int64_t n, void* stream) {
-    if (variant < 0 || variant > 4) return FLASHOPT_ERR_ARG;
+    if (variant < 0 || variant > 5) return FLASHOPT_ERR_ARG;
     if (n < 0 || n > kMaxNumel || n % kMixTile != 0) return FLASHOPT_ERR_SIZE;
     if (n == 0) return FLASHOPT_OK;
     if (!theta || !grad || !codes || !scales) return FLASHOPT_ERR_NULL;
@@ -403,10 +433,11 @@ int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* gra
     if (p.ntiles > kMaxBlocks * kWavesPerBlock) return FLASHOPT_ERR_SIZE;   // one wave per tile
     hipStream_t s = (hipStream_t)stream;
     if (variant == 0 || variant == 4)
-        hipLaunchKernelGGL(pattern_records_kernel<2>, grid, block, 0, s, p);
+        hipLaunchKernelGGL((pattern_records_kernel<2, true>), grid, block, 0, s, p);
     else if (variant == 1) hipLaunchKernelGGL(pattern_units_kernel, grid, block, 0, s, p);
     else if (variant == 2) hipLaunchKernelGGL(pattern_dma_kernel, grid, block, 0, s, p);
-    else hipLaunchKernelGGL(pattern_records_kernel<3>, grid, block, 0, s, p);
+    else if (variant == 3) hipLaunchKernelGGL((pattern_records_kernel<3, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((pattern_records_kernel<2, false>), grid, block, 0, s, p);
     return launch_status();
 }
 

@@ -13,10 +13,11 @@
 // and the tile -> tensor lookup is a scalar binary search over per-tensor
 // tile offsets kept in a small device table.  Within a tile, lane l owns 8
 // consecutive elements of each 512-element sub-tile: one 16-byte BF16 load
-// each for theta' and the gradient, and one 8-element code record (rho, m
-// and v codes interleaved, so the state is one stream rather than three) read
-// as three 8-byte loads; a quantisation group is one quad of lanes reduced
-// with DPP, its two FP16 scales one 32-bit word.  Whole tiles take an
+// each for theta' and the gradient, and its codes: one 8-byte run in each of
+// the sub-tile's three 512-byte code planes (AdamW: rho, m, v codes; the
+// planes of a sub-tile are contiguous, so the codes stay one stream) or one
+// 16-byte record (SGD, Lion: rho and m codes); a quantisation group is one
+// quad of lanes reduced with DPP, its two FP16 scales one 32-bit word.  Whole tiles take an
 // unguarded vector path; the last tile of a tensor takes a guarded
 // element-wise path.
 #include <algorithm>
@@ -76,9 +77,9 @@ __device__ __forceinline__ void step_lane(const GTensor& T, int64_t e, int lane,
     for (int j = 0; j < 8; ++j) {
         if (e + j < n) {
             T.theta[e + j] = (uint16_t)otb[j];
-            *code_at<kOpt>(T, e + j, kRhoOff) = (uint8_t)orho[j];
-            *code_at<kOpt>(T, e + j, kMOff) = (uint8_t)oqm[j];
-            if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kVOff) = (uint8_t)oqv[j];
+            *code_at<kOpt>(T, e + j, kRho) = (uint8_t)orho[j];
+            *code_at<kOpt>(T, e + j, kM) = (uint8_t)oqm[j];
+            if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kV) = (uint8_t)oqv[j];
         }
     }
     if ((lane & 3) == 0 && e < n) {
@@ -261,12 +262,12 @@ __device__ __forceinline__ void step_fast(const TileAddr<kOpt>& A, int k, int la
                                  pack_lo_bytes(mb[4], mb[5], mb[6], mb[7]));
     const uint2 orho = make_uint2(rc[0] ^ 0x80808080u, rc[1] ^ 0x80808080u);
     GLOBAL uint8_t* rec = A.rc(k);
-    if (Layout<kOpt>::kRec == 16) {                  // SGD, Lion: one hinted 16-byte record
+    if (kOpt == kAdamW) {                            // three 8-byte plane runs
+        st2nt(rec, orho);
+        st2nt(rec + Layout<kOpt>::kField, oqm);
+        st2nt(rec + 2 * Layout<kOpt>::kField, make_uint2(qv0, qv1));
+    } else {                                         // one 16-byte record
         st4nt(rec, make_uint4(orho.x, orho.y, oqm.x, oqm.y));
-    } else {
-        st2(rec + kRhoOff, orho);
-        st2(rec + kMOff, oqm);
-        if (kOpt == kAdamW) st2(rec + kVOff, make_uint2(qv0, qv1));
     }
     if ((lane & 3) == 0) {
         if (kOpt == kAdamW)                          // m | v << 16 in one v_perm

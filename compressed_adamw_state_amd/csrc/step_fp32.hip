@@ -30,15 +30,7 @@ __device__ __forceinline__ GLOBAL float* f32_at(const GTensor& T, int64_t i, int
 
 // Every access of the uncompressed step covers whole lines, each touched once
 // per step: all carry the non-temporal hint (2.5-3.2 % faster than without on
-// the Llama-3.1-8B list; device.hpp has the 16-byte forms).
-__device__ __forceinline__ uint2 ld2nt(const GLOBAL void* p) {
-    const u32x2 v = __builtin_nontemporal_load((const GLOBAL u32x2*)p);
-    return make_uint2(v.x, v.y);
-}
-__device__ __forceinline__ void st2nt(GLOBAL void* p, uint2 v) {
-    const u32x2 w = {v.x, v.y};
-    __builtin_nontemporal_store(w, (GLOBAL u32x2*)p);
-}
+// the Llama-3.1-8B list).
 
 struct RawF {
     uint4 th[2], m[2], v[2];        // a lane's 2 x 4 FP32 values of each field

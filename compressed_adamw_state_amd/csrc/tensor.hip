@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void zero_kernel(const DevTensor* __restrict__
             const int64_t e = e0 + k * kSubTile + lane * kLaneElems;
             for (int j = 0; j < 8; ++j) {
                 if (e + j < T.numel) {
-                    *code_at<kOpt>(T, e + j, kMOff) = 0;
-                    if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kVOff) = 0;
+                    *code_at<kOpt>(T, e + j, kM) = 0;
+                    if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kV) = 0;
                 }
             }
             if ((lane & 3) == 0 && e < T.numel) {
@@ -120,9 +120,9 @@ __global__ __launch_bounds__(256) void init_kernel(DevTensor d, const float* x) 
             if (e + j < n) {
                 const Split sp = split(x[e + j]);
                 T.theta[e + j] = (uint16_t)sp.tb;
-                *code_at<kOpt>(T, e + j, kRhoOff) = (uint8_t)sp.rho;
-                *code_at<kOpt>(T, e + j, kMOff) = 0;
-                if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kVOff) = 0;
+                *code_at<kOpt>(T, e + j, kRho) = (uint8_t)sp.rho;
+                *code_at<kOpt>(T, e + j, kM) = 0;
+                if (kOpt == kAdamW) *code_at<kOpt>(T, e + j, kV) = 0;
             }
         }
         if ((lane & 3) == 0 && e < n) {
@@ -149,10 +149,10 @@ __global__ __launch_bounds__(256) void export_kernel(DevTensor d, float* theta_o
             const int64_t i = e + j;
             if (i >= n) break;
             if (theta_out)
-                theta_out[i] = unsplit(T.theta[i], (int8_t)*code_at<kOpt>(T, i, kRhoOff));
-            if (m_out) m_out[i] = dequant_m((int8_t)*code_at<kOpt>(T, i, kMOff), dm);
+                theta_out[i] = unsplit(T.theta[i], (int8_t)*code_at<kOpt>(T, i, kRho));
+            if (m_out) m_out[i] = dequant_m((int8_t)*code_at<kOpt>(T, i, kM), dm);
             if (kOpt == kAdamW && v_out) {
-                const uint32_t q = *code_at<kOpt>(T, i, kVOff);
+                const uint32_t q = *code_at<kOpt>(T, i, kV);
                 v_out[i] = kLinV ? (float)q * dv : dequant_v(q, dv);
             }
         }
@@ -268,7 +268,8 @@ size_t flashopt_codes_bytes(int32_t kind, int64_t numel) {
     const bool adam = opt_of(kind) == kAdamW;
     if (is_fp32(kind))                           // whole 512-element blocks of FP32 fields
         return (size_t)((numel + kSubTile - 1) / kSubTile) * kSubTile * 4 * (adam ? 3 : 2);
-    return (size_t)((numel + 7) / 8) * (adam ? 24 : 16);
+    if (adam) return (size_t)((numel + kSubTile - 1) / kSubTile) * 1536;   // whole blocks
+    return (size_t)((numel + 7) / 8) * 16;
 }
 
 size_t flashopt_scales_bytes(int32_t kind, int64_t numel) {

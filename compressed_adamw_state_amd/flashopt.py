@@ -35,8 +35,6 @@ class FlashoptError(RuntimeError):
 # linear variance codes (experiments only)
 KIND = {"adamw": 0, "sgd": 1, "lion": 2, "adamw_fp32": 3, "sgd_fp32": 4, "lion_fp32": 5,
         "adamw_linv": 6}
-RECORD = {"adamw": 24, "sgd": 16, "lion": 16,     # code-record bytes per 8 elements
-          "adamw_linv": 24}
 SCALES = {"adamw": 2, "sgd": 1, "lion": 1,        # FP16 scales per 32-element group
           "adamw_linv": 2}
 FP32_FIELDS = {"adamw_fp32": 3, "sgd_fp32": 2, "lion_fp32": 2}   # per 512-element block
@@ -260,9 +258,10 @@ def flashopt_dequantize_lin_v(q, scale, v_out, stream=None) -> None:
 
 class TensorState:
     """Device arrays of one tensor's state (allocated with torch): BF16
-    theta', the interleaved code records and the FP16 scales in the layout of
-    include/flashopt.h -- or, for the "_fp32" kinds, the blocks of FP32 fields and no
-    scales."""
+    theta', the codes (AdamW: 512-element blocks of rho, m and v code planes;
+    SGD, Lion: 8-element records) and the FP16 scales in the layout of
+    include/flashopt.h -- or, for the "_fp32" kinds, the blocks of FP32 fields
+    and no scales."""
 
     def __init__(self, numel: int, optimizer: str, device, theta: Optional[torch.Tensor] = None,
                  codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):

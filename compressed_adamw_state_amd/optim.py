@@ -3,9 +3,9 @@ FlashLion ("FlashOptim: Optimizers for Memory Efficient Training", Practical
 advice: replace the standard optimizer, keep the hyper-parameters).
 
 Each parameter's BF16 data is theta' -- the weight the model computes with
--- and the optimizer keeps, per parameter, the interleaved code records (rho,
-momentum and, for AdamW, variance codes) and the FP16 group scales in the
-layout of include/flashopt.h.  A parameter given in FP32 is split once at
+-- and the optimizer keeps, per parameter, the codes (rho, momentum and, for
+AdamW, variance codes) and the FP16 group scales in the layout of
+include/flashopt.h.  A parameter given in FP32 is split once at
 construction: its data becomes the BF16 theta' and rho keeps the rest of the
 FP32 value.  Every step is one launch of the library's fused kernel per
 parameter group (or, with gradient release, one launch per parameter from

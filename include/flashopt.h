@@ -107,15 +107,21 @@ typedef enum flashopt_kind {
 
 /* One parameter tensor and its compressed state (all DEVICE pointers).
  *
- * State layout.  The per-element codes are interleaved in records of 8
- * consecutive elements, so the fused step reads and writes the state as one
- * stream (HBM bandwidth on this device falls with the number of concurrent
- * streams):
- *   codes[r*R + 0 + j]  = rho of element 8r+j          (INT8, two's complement)
- *   codes[r*R + 8 + j]  = momentum code of element 8r+j (INT8; SGD: momentum buffer)
- *   codes[r*R + 16 + j] = variance code of element 8r+j (UINT8; AdamW only)
- * with R = 24 (AdamW) or 16 (SGD, Lion), r < ceil(n/8), j < 8; the last record's
- * entries past n are padding (never read as state, may be overwritten).
+ * State layout.  The per-element codes lie in blocks of 512 consecutive
+ * elements, one block after another, so the fused step reads and writes them
+ * as one stream (HBM bandwidth on this device falls with the number of
+ * concurrent streams).  AdamW: a block is three 512-byte planes,
+ *   codes[b*1536 + 0 + p]    = rho of element 512b+p             (INT8, two's complement)
+ *   codes[b*1536 + 512 + p]  = momentum code of element 512b+p   (INT8)
+ *   codes[b*1536 + 1024 + p] = variance code of element 512b+p   (UINT8)
+ * with b < ceil(n/512), p < 512, so that each of a lane's three code accesses
+ * in the step (8 bytes) covers whole lines together with its wave's other
+ * lanes.  SGD, Lion: a record of 16 bytes per 8 consecutive elements,
+ *   codes[r*16 + 0 + j] = rho of element 8r+j                    (INT8)
+ *   codes[r*16 + 8 + j] = momentum code of element 8r+j          (INT8; SGD: momentum buffer)
+ * with r < ceil(n/8), j < 8 (a lane's record is one 16-byte access).  In both
+ * layouts the entries past n are padding (never read as state, may be
+ * overwritten).
  *   scales[2g], scales[2g+1] = FP16 momentum and variance scales of group g (AdamW)
  *   scales[g]                = FP16 momentum scale of group g (SGD, Lion)
  * for g < ceil(n/32).  flashopt_codes_bytes / flashopt_scales_bytes give the

@@ -55,22 +55,30 @@ int flashopt_mix_ceiling(uint16_t* theta, const uint16_t* grad, uint8_t* codes, 
  *   (theta' and the gradient carry the non-temporal hint in every variant, as
  *   in the fused kernel; variant 2's DMA loads do not)
  *   variant 0: the fused kernel's own: theta' and gradient 16 bytes per lane,
- *              the code record of a lane's 8 parameters (24 bytes) as three
- *              8-byte accesses, the group's 4-byte scale pair from one lane of
- *              four, two register buffers (sub-tile k+2 loaded once k is stored);
+ *              the codes of a lane's 8 parameters as three 8-byte runs, one
+ *              in each 512-byte plane of the sub-tile's 1536 code bytes, all
+ *              hinted non-temporal, the group's 4-byte scale pair from one
+ *              lane of four, two register buffers (sub-tile k+2 loaded once k
+ *              is stored);
  *   variant 1: as 0 with the 1536 code bytes of a sub-tile as 16-byte units
- *              and the 64 scale bytes as 16 lanes x 4 bytes;
+ *              (not hinted) and the 64 scale bytes as 16 lanes x 4 bytes;
  *   variant 2: the units of 1 loaded by global-to-LDS DMA into a two-slot ring
  *              per wave (no register holds a load in flight);
  *   variant 3: as 0 with three register buffers (the loads of sub-tile k+2
  *              issued before sub-tile k is stored);
  *   variant 4: as 0 with the tiles taken in a hashed order (wave w takes tile
  *              w * q mod ntiles, q a prime near 10^6 that does not divide
- *              ntiles), so the tiles in flight are spread over the buffers.
- * Results: theta ^= grad; codes: variants 0, 3 and 4 replace each 24-byte record's
- * 8-byte words (a, b, c) with (a^b, b^c, c^a), variants 1 and 2 XOR every code
- * byte with 0x5A; every 32-bit scale word ^= 0x00010001.  DESTRUCTIVE.  Errors:
- * FLASHOPT_ERR_ARG (variant outside 0-4) and those of flashopt_mix_ceiling.
+ *              ntiles), so the tiles in flight are spread over the buffers;
+ *   variant 5: as 0 with a lane's codes as one interleaved 24-byte record
+ *              (bytes [24l, 24l+24) of the sub-tile's 1536) taken as three
+ *              8-byte accesses without the hint: the fused kernel's earlier
+ *              layout.
+ * Results: theta ^= grad; codes: variants 0, 3, 4 and 5 replace each lane's
+ * three 8-byte code words (a, b, c) -- at 8l, 512 + 8l and 1024 + 8l of each
+ * 1536-byte sub-tile block for 0, 3 and 4, at 24l, 24l + 8 and 24l + 16 for 5
+ * -- with (a^b, b^c, c^a), variants 1 and 2 XOR every code byte with 0x5A;
+ * every 32-bit scale word ^= 0x00010001.  DESTRUCTIVE.  Errors:
+ * FLASHOPT_ERR_ARG (variant outside 0-5) and those of flashopt_mix_ceiling.
  * One launch on `stream`, nothing allocated. */
 int flashopt_pattern_probe(int32_t variant, uint16_t* theta, const uint16_t* grad,
                            uint8_t* codes, uint16_t* scales, int64_t n, void* stream);

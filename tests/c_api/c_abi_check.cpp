@@ -69,7 +69,7 @@ struct Dev {                        // the same tensor's state on the device
     size_t codes_bytes = 0, scales_bytes = 0;
 };
 
-// compare the device state of one tensor with the oracle's, record by record
+// compare the device state of one tensor with the oracle's, element by element
 int compare(const Host& h, const Dev& d, int32_t kind, const char* what) {
     const int64_t n = h.n;
     const bool adam = kind == FLASHOPT_KIND_ADAMW;
@@ -81,14 +81,18 @@ int compare(const Host& h, const Dev& d, int32_t kind, const char* what) {
         hipMemcpy(codes.data(), d.codes, d.codes_bytes, hipMemcpyDeviceToHost) != hipSuccess ||
         hipMemcpy(scales.data(), d.scales, d.scales_bytes, hipMemcpyDeviceToHost) != hipSuccess)
         return 2;
-    const int64_t rec = adam ? 24 : 16, per_group = adam ? 2 : 1;
+    const int64_t per_group = adam ? 2 : 1;
     int64_t bad = 0;
     for (int64_t i = 0; i < n; ++i) {
-        const uint8_t* r = codes.data() + (i >> 3) * rec + (i & 7);
+        // AdamW: 512-element blocks of rho, m and v planes; SGD, Lion: 16-byte
+        // records of 8 elements (include/flashopt.h)
+        const uint8_t* r = adam ? codes.data() + (i >> 9) * 1536 + (i & 511)
+                                : codes.data() + (i >> 3) * 16 + (i & 7);
+        const int64_t field = adam ? 512 : 8;
         bad += th[i] != h.tb[i];
         bad += (int8_t)r[0] != h.rho[i];
-        bad += (int8_t)r[8] != h.qm[i];
-        if (adam) bad += r[16] != h.qv[i];
+        bad += (int8_t)r[field] != h.qm[i];
+        if (adam) bad += r[2 * field] != h.qv[i];
     }
     for (int64_t g = 0; g < (n + 31) / 32; ++g) {
         bad += scales[g * per_group] != h.sm[g];

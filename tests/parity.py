@@ -40,22 +40,31 @@ def u8(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy().view(np.uint8)
 
 
+def code_index(i: torch.Tensor, optimizer: str, field: int) -> torch.Tensor:
+    """Byte index in `codes` of field `field` (0 rho, 1 m, 2 v) of elements i
+    (include/flashopt.h): AdamW's 512-element blocks of three 512-byte
+    planes, SGD's and Lion's 16-byte records of 8 elements."""
+    if F.SCALES[optimizer] == 2:                           # AdamW layouts
+        return (i >> 9) * 1536 + field * 512 + (i & 511)
+    return (i >> 3) * 16 + field * 8 + (i & 7)
+
+
 def state_fields(st: F.TensorState, idx=None, gidx=None) -> dict:
     """theta', rho, m_code, v_code (elements idx) and m_scale, v_scale (groups
-    gidx) of a device TensorState as numpy arrays, read out of the interleaved
-    code records and scale pairs (include/flashopt.h); None selects all."""
+    gidx) of a device TensorState as numpy arrays, read out of the code
+    planes or records and the scale pairs (include/flashopt.h); None selects
+    all."""
     dev = st.codes.device
     n = st.numel
     if idx is None:
         idx = torch.arange(n, device=dev)
     if gidx is None:
         gidx = torch.arange((n + GROUP - 1) // GROUP, device=dev)
-    R, S = F.RECORD[st.optimizer], F.SCALES[st.optimizer]
-    base = (idx >> 3) * R + (idx & 7)
-    out = {"theta": u16(st.theta[idx]), "rho": i8(st.codes[base]),
-           "m_code": i8(st.codes[base + 8]), "m_scale": u16(st.scales[gidx * S])}
+    S, opt = F.SCALES[st.optimizer], st.optimizer
+    out = {"theta": u16(st.theta[idx]), "rho": i8(st.codes[code_index(idx, opt, 0)]),
+           "m_code": i8(st.codes[code_index(idx, opt, 1)]), "m_scale": u16(st.scales[gidx * S])}
     if S == 2:                                             # AdamW layouts
-        out["v_code"] = u8(st.codes[base + 16])
+        out["v_code"] = u8(st.codes[code_index(idx, opt, 2)])
         out["v_scale"] = u16(st.scales[gidx * S + 1])
     return out
 
@@ -63,16 +72,21 @@ def state_fields(st: F.TensorState, idx=None, gidx=None) -> dict:
 def record_fields(theta: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, n: int,
                   optimizer: str) -> dict:
     """theta', rho, m_code, v_code, m_scale, v_scale of one tensor from its
-    device arrays (live state or a copy), unpacked from the interleaved
+    device arrays (live state or a copy), unpacked from the code planes or
     records on the device and returned as contiguous host arrays."""
-    R, S = F.RECORD[optimizer], F.SCALES[optimizer]
-    nrec, ng = (n + 7) // 8, (n + GROUP - 1) // GROUP
-    rec = codes[:nrec * R].view(nrec, R // 8, 8)
+    S = F.SCALES[optimizer]
+    ng = (n + GROUP - 1) // GROUP
+    if S == 2:                                             # AdamW: [block][field][512]
+        nblk = (n + 511) // 512
+        fld = codes[:nblk * 1536].view(nblk, 3, 512)
+    else:                                                  # SGD, Lion: [record][field][8]
+        nrec = (n + 7) // 8
+        fld = codes[:nrec * 16].view(nrec, 2, 8)
     sc = scales[:ng * S].view(ng, S)
-    out = {"theta": u16(theta[:n]), "rho": i8(rec[:, 0].reshape(-1)[:n]),
-           "m_code": i8(rec[:, 1].reshape(-1)[:n]), "m_scale": u16(sc[:, 0])}
+    out = {"theta": u16(theta[:n]), "rho": i8(fld[:, 0].reshape(-1)[:n]),
+           "m_code": i8(fld[:, 1].reshape(-1)[:n]), "m_scale": u16(sc[:, 0])}
     if S == 2:
-        out["v_code"] = u8(rec[:, 2].reshape(-1)[:n])
+        out["v_code"] = u8(fld[:, 2].reshape(-1)[:n])
         out["v_scale"] = u16(sc[:, 1])
     return out
 

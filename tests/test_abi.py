@@ -82,7 +82,9 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_workspace_bytes(291) >= 291 * 64
     out = P()
     A, S = 0, 1                                        # flashopt_kind
-    assert lib.flashopt_codes_bytes(A, 17) == 3 * 24 and lib.flashopt_codes_bytes(S, 17) == 3 * 16
+    # AdamW: whole 1536-byte blocks of 512 elements; SGD: 16-byte records of 8
+    assert lib.flashopt_codes_bytes(A, 17) == 1536 and lib.flashopt_codes_bytes(S, 17) == 3 * 16
+    assert lib.flashopt_codes_bytes(A, 513) == 2 * 1536 and lib.flashopt_codes_bytes(A, 0) == 0
     assert lib.flashopt_scales_bytes(A, 33) == 2 * 4 and lib.flashopt_scales_bytes(S, 33) == 2 * 2
     assert lib.flashopt_codes_bytes(7, 17) == 0 and lib.flashopt_scales_bytes(A, -1) == 0
     arr = (F.Tensor * 1)(F.Tensor(10, fake, fake, fake, fake))
@@ -100,7 +102,7 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_create(mis_s, 1, A, ws, need, None, ctypes.byref(out)) == -3
     assert lib.flashopt_list_create(mis_s, 1, 6, ws, need, None, ctypes.byref(out)) == -3
     # the linear-variance ablation kind has the AdamW layout
-    assert lib.flashopt_codes_bytes(6, 17) == 3 * 24 and lib.flashopt_scales_bytes(6, 33) == 8
+    assert lib.flashopt_codes_bytes(6, 17) == 1536 and lib.flashopt_scales_bytes(6, 33) == 8
     neg = (F.Tensor * 1)(F.Tensor(-5, fake, fake, fake, fake))
     assert lib.flashopt_list_create(neg, 1, A, ws, need, None, ctypes.byref(out)) == -2
     assert lib.flashopt_tensor_init(arr, 7, fake, None) == -4

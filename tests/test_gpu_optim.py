@@ -106,10 +106,12 @@ def test_checkpoint_resumes_bit_for_bit(kind):
         assert torch.equal(pa.view(torch.int16), pc.view(torch.int16))
         sa, sc = oa.state[pa]["flash"], oc.state[pc]["flash"]
         assert torch.equal(sa.codes, sc.codes) and torch.equal(sa.scales, sc.scales)
+    # the state and its padding only: AdamW's codes in whole 1536-byte blocks of
+    # 512 elements, Lion's in 16-byte records of 8; the scales per 32
     per = {"adamw": 3.125, "lion": 2.0625}[kind]
-    rec, scl = {"adamw": (24, 4), "lion": (16, 2)}[kind]
-    exact = sum((p.numel() + 7) // 8 * rec + (p.numel() + 31) // 32 * scl for p in c)
-    assert nbytes == exact and nbytes <= per * numel + 64 * len(c)
+    blk, unit, scl, pad = {"adamw": (512, 1536, 4, 1536), "lion": (8, 16, 2, 64)}[kind]
+    exact = sum((p.numel() + blk - 1) // blk * unit + (p.numel() + 31) // 32 * scl for p in c)
+    assert nbytes == exact and nbytes <= per * numel + pad * len(c)
 
 
 @pytest.mark.parametrize("streams", [1, 2])

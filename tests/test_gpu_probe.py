@@ -1,7 +1,7 @@
 """The bandwidth probe (include/flashopt_probe.h) reads and writes every byte
 of the AdamW step's state and gradients: its documented XOR of the values it
 read, checked on every element of a ragged list (full tiles and partial
-tails), through the interleaved code records."""
+tails), through the code planes."""
 import numpy as np
 import pytest
 import torch
@@ -93,12 +93,14 @@ def test_stream_sweep_values(rw, in_place):
         assert torch.equal(dr[k].cpu(), reads[k])
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
 def test_pattern_probe_variants(variant):
-    """flashopt_pattern_probe: theta ^= grad; codes per record (a^b, b^c, c^a)
-    for variants 0, 3 and 4, every byte ^= 0x5A for 1 and 2; every scale word ^=
-    0x00010001; over 7 tiles and nothing beyond (variant 4: every tile once,
-    in its hashed order)."""
+    """flashopt_pattern_probe: theta ^= grad; each lane's three 8-byte code
+    words (a, b, c) -> (a^b, b^c, c^a), the words one per 512-byte plane of a
+    1536-byte sub-tile block for variants 0, 3 and 4 and one 24-byte record
+    for 5; every byte ^= 0x5A for 1 and 2; every scale word ^= 0x00010001;
+    over 7 tiles and nothing beyond (variant 4: every tile once, in its
+    hashed order)."""
     gen = torch.Generator().manual_seed(10 + variant)
     n = 2048 * 7
     pad = 64
@@ -112,10 +114,12 @@ def test_pattern_probe_variants(variant):
     th, gr, cd, sc = (t.cpu() for t in d)
     assert torch.equal(th[:n], theta[:n] ^ grad[:n]) and torch.equal(th[n:], theta[n:])
     assert torch.equal(gr, grad)
-    if variant in (0, 3, 4):
-        w = codes[:3 * n].view(torch.int64).view(-1, 3)
+    if variant in (0, 3, 4, 5):
+        # words of one lane: [block][plane][lane] for the planes, [record][word] for 5
+        shape = (-1, 3, 64) if variant != 5 else (-1, 3)
+        w = codes[:3 * n].view(torch.int64).view(shape)
         exp = torch.stack([w[:, 0] ^ w[:, 1], w[:, 1] ^ w[:, 2], w[:, 2] ^ w[:, 0]], 1)
-        assert torch.equal(cd[:3 * n].view(torch.int64).view(-1, 3), exp)
+        assert torch.equal(cd[:3 * n].view(torch.int64).view(shape), exp)
     else:
         assert torch.equal(cd[:3 * n], codes[:3 * n] ^ 0x5A)
     assert torch.equal(cd[3 * n:], codes[3 * n:])
