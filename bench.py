@@ -85,14 +85,19 @@ def read_profile(kind: str, workload: str, kernel_hash: str) -> dict:
     return kv if kv.get("source_sha256_16") == kernel_hash else {}
 
 
-def build_state(w: W.Workload, grad_sets: int):
+def build_state(w: W.Workload, grad_sets: int, candidates: int = 1, placement: dict = None):
     """The workload's state and `grad_sets` gradient sets, all in one
-    StateArena (theta', gradients, code records and scales each in a region
-    of their own), and one list handle per gradient set."""
+    StateArena (theta', gradients, codes and scales each in a region of their
+    own), and one list handle per gradient set.  candidates > 1: the arena's
+    placement search (StateArena) picks the allocation; its probe times go
+    into `placement`."""
     dev = torch.device("cuda")
     states = []
     arena = F.StateArena([spec.numel for spec in w.tensors], w.optimizer, dev, theta=True,
-                         grad_sets=grad_sets)
+                         grad_sets=grad_sets, candidates=candidates)
+    if placement is not None and arena.placement_ms is not None:
+        placement.update({"candidates": candidates, "allocations": len(arena.placement_ms),
+                          "probe_ms": arena.placement_ms, "chosen": arena.placement_choice})
     for i, spec in enumerate(w.tensors):
         theta = W.draw_theta(w, i, dev)
         st = arena.state(i)
@@ -644,6 +649,10 @@ def main():
                     help="time only the placement study and print it as JSON: three allocations "
                          "of the byte-mix buffers at Llama-3.1-8B size, timed in alternation, "
                          "in two tile orders, with arrays swapped between them and alone")
+    ap.add_argument("--placement-candidates", type=int, default=3,
+                    help="allocations of the benchmark state tried by the arena's placement "
+                         "search (the fastest under the step's own access probe is kept; 1: "
+                         "the first allocation, no search)")
     ap.add_argument("--secondary", default=None, metavar="WORKLOAD",
                     help="time only this secondary workload (--steps steps) and print its "
                          "record: a profiling aid, not the benchmark line")
@@ -683,8 +692,12 @@ def main():
     assert w.optimizer == "adamw" and not w.release
     log(f"bench: building {w.name} state ({w.numel} params, {len(w.tensors)} tensors)")
     t0 = time.perf_counter()
-    states, grads, lists = build_state(w, grad_sets=2)
-    log(f"bench: state ready in {time.perf_counter() - t0:.1f} s")
+    placement_search = {}
+    states, grads, lists = build_state(w, grad_sets=2, candidates=args.placement_candidates,
+                                       placement=placement_search)
+    log(f"bench: state ready in {time.perf_counter() - t0:.1f} s"
+        + (f"; placement search: probe {placement_search['probe_ms']} ms, kept allocation "
+           f"{placement_search['chosen']}" if placement_search else ""))
     hp = w.hparams
     stream = torch.cuda.current_stream()
 
@@ -743,7 +756,11 @@ def main():
                                f"{nparams} params, AdamW lr 1e-3 betas (0.9, 0.999) eps 1e-8 "
                                f"wd 0.01, bf16 grads N(0, 1e-4)",
                    "state": "theta' bf16 + int8 rho, int8 m and uint8 v code planes per 512-element block + fp16 scale pair per 32",
-                   "launches_per_step": 1},
+                   "launches_per_step": 1,
+                   "placement": (f"best of {placement_search['allocations']} arena allocations "
+                                 f"by the step's own access probe" if placement_search
+                                 else "first allocation")},
+        "placement_search": placement_search or None,
         "hbm_gb_s": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBS,
         "step_ms_median": float(np.median(per) * 1e3),

@@ -298,27 +298,39 @@ class TensorState:
 class StateArena:
     """The state of a list of tensors in one device buffer with one region per
     stream the fused step reads or writes: optionally theta' (theta=True),
-    optionally `grad_sets` sets of BF16 gradients, then the code records,
-    then the FP16 scales.  Each region starts on a 2 MiB boundary and each
-    tensor's slice within it on a 4096-byte boundary; code records and scales
-    are zeroed.  state(i) builds tensor i's TensorState on its slices (theta'
-    from the arena, or a given tensor such as a parameter's own storage);
-    grad(j, i) is tensor i's gradient of set j.
+    optionally `grad_sets` sets of BF16 gradients, then the codes, then the
+    FP16 scales.  Each region starts on a 2 MiB boundary and each tensor's
+    slice within it on a 4096-byte boundary; codes and scales are zeroed.
+    state(i) builds tensor i's TensorState on its slices (theta' from the
+    arena, or a given tensor such as a parameter's own storage); grad(j, i) is
+    tensor i's gradient of set j.
 
     Why one buffer with a region per stream: one allocation for the whole
     state instead of four per tensor, and each stream the step reads or
     writes contiguous across the list's tensors.  The step's rate on MI355X
     does not depend on the layout inside the buffer so much as on where the
     allocation's physical pages land: the same byte mix over different
-    allocations of the same buffers takes 16.3-19.0 ms at Llama-3.1-8B size,
-    whatever the order of the tiles, and each
-    array alone streams at the same rate in every allocation."""
+    allocations of the same buffers takes 16.2-19.0 ms at Llama-3.1-8B size,
+    whatever the order of the tiles, and each array alone streams at the same
+    rate in every allocation.
+
+    candidates > 1 (AdamW, with theta' and at least one gradient set): a
+    placement search.  Up to `candidates` allocations of the buffer are made,
+    all alive at once (fewer if the device runs short of free memory); on
+    each, the AdamW step's own loads and stores over the list
+    (flashopt_stream_probe, best of three launches after one untimed) are
+    timed, the fastest allocation is kept and the others are freed and
+    handed back to the device (torch.cuda.empty_cache).  The probe's time on
+    an allocation ranks the step's on it; `placement_ms` holds the probe
+    times in allocation order and `placement_choice` the index kept.  The
+    search needs `candidates` times the buffer's memory while it runs."""
 
     ALIGN = 4096
     REGION = 1 << 21
+    HEADROOM = 1 << 30           # free memory left on the device by the search
 
     def __init__(self, numels: Sequence[int], optimizer: str, device, theta: bool = False,
-                 grad_sets: int = 0):
+                 grad_sets: int = 0, candidates: int = 1):
         self.numels = [int(n) for n in numels]
         self.optimizer = optimizer
         kind = KIND[optimizer]
@@ -335,10 +347,46 @@ class StateArena:
             self._gs.append(gs)
         self._cs, start = self._slices(cb, start)
         self._ss, end = self._slices(sb, start)
-        self.buffer = torch.empty(max(end, 1), dtype=torch.uint8, device=device)
+        nbytes = max(end, 1)
+        self.placement_ms, self.placement_choice = None, None
+        if candidates > 1:
+            if optimizer != "adamw" or not theta or grad_sets < 1:
+                raise ValueError("the placement search needs an AdamW arena with theta' and "
+                                 "a gradient set")
+            self._search(nbytes, device, candidates)
+        else:
+            self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.device = self.buffer.device
         c0 = min([o for o, _ in self._cs] + [end])
-        self.buffer[c0:end].zero_()                            # code records and scales
+        self.buffer[c0:end].zero_()                            # codes and scales
+
+    def _search(self, nbytes: int, device, candidates: int) -> None:
+        dev = torch.device(device)
+        stream = torch.cuda.current_stream(dev)
+        n = len(self.numels)
+        bufs, times = [], []
+        for c in range(candidates):
+            if c and torch.cuda.mem_get_info(dev)[0] < nbytes + self.HEADROOM:
+                break
+            self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            self.device = self.buffer.device
+            lst = FlashoptList([self.state(i) for i in range(n)],
+                               [self.grad(0, i) for i in range(n)])
+            flashopt_stream_probe(lst, stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(stream)
+            for k in range(3):
+                flashopt_stream_probe(lst, stream)
+                ev[k + 1].record(stream)
+            torch.cuda.synchronize(dev)
+            times.append(min(ev[k].elapsed_time(ev[k + 1]) for k in range(3)))
+            bufs.append(self.buffer)
+            del lst
+        best = min(range(len(times)), key=times.__getitem__)
+        self.buffer = bufs[best]
+        self.placement_ms, self.placement_choice = times, best
+        del bufs
+        torch.cuda.empty_cache()
 
     @classmethod
     def _slices(cls, sizes, start):

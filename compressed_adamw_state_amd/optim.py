@@ -52,6 +52,11 @@ import torch
 
 from . import flashopt as F
 
+# Placement of the codes in a checkpoint's "codes" tensors (include/flashopt.h):
+# "blocks512" -- AdamW's rho, m and v planes per 512-element block, SGD's and
+# Lion's 16-byte records of 8 elements; the _FP32 kinds' FP32 field blocks.
+CODES_LAYOUT = "blocks512"
+
 
 class _FlashOptimizer(torch.optim.Optimizer):
     kind = ""                                    # "adamw" | "sgd" | "lion"
@@ -344,7 +349,7 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._join_release()             # an open release bucket belongs to this state
         if self.capturable:
             self._sync_steps()
-        sd = {"kind": self.kind, "param_groups": [], "state": {}}
+        sd = {"kind": self.kind, "codes_layout": CODES_LAYOUT, "param_groups": [], "state": {}}
         index = 0
         for group in self.param_groups:
             g = {k: v for k, v in group.items() if k != "params"}
@@ -363,6 +368,10 @@ class _FlashOptimizer(torch.optim.Optimizer):
         self._join_release()             # stepped and finished, then overwritten below
         if sd.get("kind") != self.kind:
             raise ValueError(f"checkpoint is for {sd.get('kind')}, not {self.kind}")
+        if sd.get("codes_layout") != CODES_LAYOUT:
+            # same byte counts can hold differently placed codes: refuse, do not reinterpret
+            raise ValueError(f"checkpoint codes layout {sd.get('codes_layout')!r} is not "
+                             f"{CODES_LAYOUT!r}")
         saved = sd["param_groups"]
         if len(saved) != len(self.param_groups) or any(
                 len(a["params"]) != len(b["params"]) for a, b in zip(saved, self.param_groups)):

@@ -1,5 +1,5 @@
 """StateArena's slicing on the host (CPU tensors; no GPU call): each tensor's
-code records, scales and (when asked) theta' and gradient buffers are views
+codes, scales and (when asked) theta' and gradient buffers are views
 of the one shared buffer, of exactly the layout's sizes, starting on
 4096-byte boundaries, disjoint, one region per stream in a fixed order."""
 import pytest
@@ -72,3 +72,13 @@ def test_theta_taken_and_checked():
 def test_empty_list():
     arena = F.StateArena([], "adamw", "cpu", theta=True, grad_sets=1)
     assert arena.buffer.numel() >= 1
+
+
+@pytest.mark.parametrize("opt,theta,grad_sets", [("sgd", True, 1), ("lion", True, 1),
+                                                 ("adamw", False, 1), ("adamw", True, 0),
+                                                 ("adamw_fp32", True, 1)])
+def test_placement_search_needs_an_adamw_arena_with_theta_and_grads(opt, theta, grad_sets):
+    # refused on the host, before any allocation: the search times the AdamW
+    # step's own probe, which reads theta' and a gradient
+    with pytest.raises(ValueError, match="placement search"):
+        F.StateArena(SIZES, opt, "cpu", theta=theta, grad_sets=grad_sets, candidates=2)

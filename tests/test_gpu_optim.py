@@ -112,6 +112,10 @@ def test_checkpoint_resumes_bit_for_bit(kind):
     blk, unit, scl, pad = {"adamw": (512, 1536, 4, 1536), "lion": (8, 16, 2, 64)}[kind]
     exact = sum((p.numel() + blk - 1) // blk * unit + (p.numel() + 31) // 32 * scl for p in c)
     assert nbytes == exact and nbytes <= per * numel + pad * len(c)
+    # a checkpoint whose codes are placed otherwise is refused, not reinterpreted
+    for tag in ("records24", None):
+        with pytest.raises(ValueError, match="codes layout"):
+            oc.load_state_dict({**sd, "codes_layout": tag})
 
 
 @pytest.mark.parametrize("streams", [1, 2])
@@ -453,8 +457,8 @@ def test_checkpoint_and_export_wait_for_side_stream_release(what):
         elif what == "export_fp32":
             runs.append([opt.export_fp32(p) for p in params])
         else:
-            ckpt = {"kind": "adamw", "param_groups": [dict(opt.param_groups[0],
-                                                           params=list(range(layers)))],
+            ckpt = {"kind": "adamw", "codes_layout": O.CODES_LAYOUT,
+                    "param_groups": [dict(opt.param_groups[0], params=list(range(layers)))],
                     "state": {i: {"numel": p.numel(),
                                   "codes": torch.full_like(opt.state[p]["flash"].codes, 7),
                                   "scales": torch.full_like(opt.state[p]["flash"].scales, 9),
