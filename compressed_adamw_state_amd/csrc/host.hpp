@@ -119,7 +119,8 @@ static inline int check_tensor(const flashopt_tensor& t, int32_t kind) {
         return FLASHOPT_OK;
     }
     if (!t.theta || !t.codes || !t.scales) return FLASHOPT_ERR_NULL;
-    if (!aligned(t.theta, 16) || !aligned(t.codes, 8) ||
+    // codes: SGD's and Lion's 16-byte records are read and written whole
+    if (!aligned(t.theta, 16) || !aligned(t.codes, 16) ||
         !aligned(t.scales, opt_of(kind) == kAdamW ? 4 : 2) || (t.grad && !aligned(t.grad, 16)))
         return FLASHOPT_ERR_ALIGN;
     return FLASHOPT_OK;

@@ -50,7 +50,7 @@
  * (its scale covers only its valid elements).  BF16 and FP16 values are passed
  * as their uint16 bit patterns.
  *
- * Alignment: BF16 arrays (theta', grad) 16 bytes; code records and flat
+ * Alignment: BF16 arrays (theta', grad) and a tensor's codes 16 bytes; flat
  * INT8/UINT8 code arrays 8 bytes; AdamW scale arrays 4 bytes, SGD / Lion and
  * flat scale arrays 2 bytes; FP32 arrays and the _FP32 kinds' state blocks 16
  * bytes (the ablation entry points, element by element: their element size).
@@ -145,7 +145,7 @@ typedef enum flashopt_kind {
 typedef struct flashopt_tensor {
     int64_t numel;           /* n >= 0                                                   */
     uint16_t* theta;         /* [n] BF16 theta'; the model weight the forward pass reads */
-    uint8_t* codes;          /* code records, layout above                               */
+    uint8_t* codes;          /* codes (planes or records), layout above                  */
     uint16_t* scales;        /* FP16 scales, layout above                                */
     const uint16_t* grad;    /* [n] BF16 gradient, read only; may be NULL when only the
                                 *_step_one entry points (gradient release) are used    */

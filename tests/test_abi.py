@@ -98,6 +98,9 @@ def test_host_validation_without_gpu():
     assert lib.flashopt_list_create(nul, 1, A, ws, need, None, ctypes.byref(out)) == -1
     mis_t = (F.Tensor * 1)(F.Tensor(10, P(0x10008), fake, fake, fake))
     assert lib.flashopt_list_create(mis_t, 1, A, ws, need, None, ctypes.byref(out)) == -3
+    for k in (A, S, 2):                                # codes: 16 B for every compressed kind
+        mis_c = (F.Tensor * 1)(F.Tensor(10, fake, P(0x10008), fake, fake))
+        assert lib.flashopt_list_create(mis_c, 1, k, ws, need, None, ctypes.byref(out)) == -3
     mis_s = (F.Tensor * 1)(F.Tensor(10, fake, fake, P(0x10002), fake))  # AdamW scales need 4 B
     assert lib.flashopt_list_create(mis_s, 1, A, ws, need, None, ctypes.byref(out)) == -3
     assert lib.flashopt_list_create(mis_s, 1, 6, ws, need, None, ctypes.byref(out)) == -3
