@@ -34,6 +34,7 @@ METRIC = "fused AdamW step params/s + achieved HBM GB/s (% peak) at Llama-3.1-8B
 HBM_PEAK_GBS = 8000.0
 KERNEL = "step_kernel<0, false, false>"   # the fused AdamW step kernel, one wave per tile
 # the fused step kernel's sources (a committed profile applies while their hash is unchanged)
+PEAK_CLOCK_GHZ = 2.4        # MI355X peak engine clock (256 CUs x 4 SIMDs)
 SOURCES = ["compressed_adamw_state_amd/csrc/step.hip",
            "compressed_adamw_state_amd/csrc/device.hpp",
            "compressed_adamw_state_amd/csrc/host.hpp",
@@ -778,6 +779,10 @@ def main():
                      # the shader clock at which that issue alone fills this run's launch
                      "valu_cycles_per_simd": valu_cycles,
                      "valu_bound_clock_ghz": (valu_cycles / (avg * 1e9)) if valu_cycles else None,
+                     # the same issue time over this launch at the part's peak engine clock
+                     # (2.4 GHz): the fraction of VALU issue capacity the launch uses
+                     "valu_issue_frac_at_peak_clock":
+                         (valu_cycles / (avg * PEAK_CLOCK_GHZ * 1e9)) if valu_cycles else None,
                      "shader_clock_ghz_in_profiled_run":
                          float(sq["shader_clock_ghz"]) if "shader_clock_ghz" in sq else None},
         "cpu_baseline": None,
