@@ -151,7 +151,7 @@ def release_buckets(sizes, bucket_bytes: int):
 
 
 def other_optimizer(name: str, steps: int, stream, release_streams: int = 1,
-                    bucket_bytes: int = 0, release: bool = False) -> dict:
+                    bucket_bytes: int = 0, release: bool = False, candidates: int = 3) -> dict:
     """Time `steps` list steps of another optimizer's workload (after warm-up);
     state built fresh, freed on return.  In gradient-release mode (the
     workload's own, or `release`) the tensors are stepped in backward order,
@@ -159,10 +159,15 @@ def other_optimizer(name: str, steps: int, stream, release_streams: int = 1,
     bucket of consecutive tensors (release_buckets); the launches go
     round-robin over `release_streams` streams (tensors are independent, so
     one launch's tail can overlap the next); each step is bracketed on
-    `stream`."""
+    `stream`.  The state's arena is placed by the placement search over
+    `candidates` allocations (compressed kinds; the _fp32 kinds take the
+    first allocation)."""
     w = W.WORKLOADS[name]
     release = release or w.release
-    states, grads, lists = build_state(w, grad_sets=2)
+    placement = {}
+    states, grads, lists = build_state(
+        w, grad_sets=2, candidates=1 if w.optimizer in F.FP32_FIELDS else candidates,
+        placement=placement)
     side = [stream] + [torch.cuda.Stream() for _ in range(release_streams - 1)]
     buckets = release_buckets([t.numel for t in w.tensors], bucket_bytes)
 
@@ -207,7 +212,8 @@ def other_optimizer(name: str, steps: int, stream, release_streams: int = 1,
             "streams": len(side) if release else 1,
             "bytes_per_param": algorithmic_bytes(w) / w.numel, "step_ms_median": ms,
             "step_ms_min": float(per.min()), "params_s": w.numel / (ms * 1e-3),
-            "algorithmic_gb_s": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS}
+            "algorithmic_gb_s": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+            "placement_search": placement or None}
 
 
 def wrapper_adamw(steps: int, stream) -> dict:
@@ -651,9 +657,9 @@ def main():
                          "of the byte-mix buffers at Llama-3.1-8B size, timed in alternation, "
                          "in two tile orders, with arrays swapped between them and alone")
     ap.add_argument("--placement-candidates", type=int, default=3,
-                    help="allocations of the benchmark state tried by the arena's placement "
+                    help="allocations of each benchmark state tried by the arena's placement "
                          "search (the fastest under the step's own access probe is kept; 1: "
-                         "the first allocation, no search)")
+                         "the first allocation, no search; the _fp32 kinds never search)")
     ap.add_argument("--secondary", default=None, metavar="WORKLOAD",
                     help="time only this secondary workload (--steps steps) and print its "
                          "record: a profiling aid, not the benchmark line")
@@ -673,7 +679,7 @@ def main():
 
     if args.secondary:
         r = other_optimizer(args.secondary, args.steps, torch.cuda.current_stream(),
-                            release=args.release)
+                            release=args.release, candidates=args.placement_candidates)
         print(json.dumps(r), flush=True)
         return
     if args.access_patterns:
@@ -802,20 +808,20 @@ def main():
     out["mix_ceiling"]["step_over_ceiling"] = avg * 1e3 / out["mix_ceiling"]["best_ms"]
     log(f"bench: byte-mix ceiling {out['mix_ceiling']['gb_s']:.0f} GB/s")
     if not args.no_other_optimizers:
-        out["other_optimizers"] = [other_optimizer("llama31_8b_lion", 10, stream),
-                                   other_optimizer("llama31_8b_adamw_fp32", 5, stream),
-                                   other_optimizer("resnet50", 10, stream),
-                                   other_optimizer("flat1m", 10, stream),
-                                   other_optimizer("gpt2_small", 10, stream),
-                                   other_optimizer("llama2_13b", 5, stream),
-                                   other_optimizer("llama2_13b", 5, stream, release_streams=2),
-                                   other_optimizer("llama2_13b", 5, stream,
-                                                   bucket_bytes=64 << 20),
-                                   other_optimizer("llama2_13b", 5, stream, release_streams=2,
-                                                   bucket_bytes=64 << 20),
-                                   other_optimizer("gpt2_small", 10, stream, release=True),
-                                   other_optimizer("gpt2_small", 10, stream, release=True,
-                                                   bucket_bytes=16 << 20),
+        oo = lambda *a, **k: other_optimizer(*a, candidates=args.placement_candidates, **k)
+        out["other_optimizers"] = [oo("llama31_8b_lion", 10, stream),
+                                   oo("llama31_8b_adamw_fp32", 5, stream),
+                                   oo("resnet50", 10, stream),
+                                   oo("flat1m", 10, stream),
+                                   oo("gpt2_small", 10, stream),
+                                   oo("llama2_13b", 5, stream),
+                                   oo("llama2_13b", 5, stream, release_streams=2),
+                                   oo("llama2_13b", 5, stream, bucket_bytes=64 << 20),
+                                   oo("llama2_13b", 5, stream, release_streams=2,
+                                      bucket_bytes=64 << 20),
+                                   oo("gpt2_small", 10, stream, release=True),
+                                   oo("gpt2_small", 10, stream, release=True,
+                                      bucket_bytes=16 << 20),
                                    wrapper_adamw(10, stream),
                                    graph_replay_adamw(10),
                                    release_memory(5, stream)]

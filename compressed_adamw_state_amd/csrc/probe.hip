@@ -9,27 +9,36 @@ namespace flashopt {
 
 // ---- bandwidth probe ---------------------------------------------------------
 //
-// The AdamW step's memory traffic with the arithmetic taken out: the same
-// tiles, launch shape, loads (with the same two-buffer pipeline) and stores,
-// and one XOR per word in place of the update (theta' ^= g, rho ^= q_m,
-// q_m ^= q_v, q_v ^= rho, both scales ^= 1).  Its time is the practical floor
-// of the step's access pattern on this device.
+// A step's memory traffic with the arithmetic taken out: the same tiles,
+// launch shape, loads (with the same two-buffer pipeline) and stores, and one
+// XOR per word in place of the update.  AdamW: theta' ^= g, rho ^= q_m,
+// q_m ^= q_v, q_v ^= rho, both scales ^= 1; SGD and Lion: theta' ^= g,
+// rho ^= q_m, q_m = ~q_m, the scale ^= 1.  Its time is the practical floor of
+// the step's access pattern on this device.
 __device__ __forceinline__ uint2 xor2(const uint2 a, const uint2 b) {
     return make_uint2(a.x ^ b.x, a.y ^ b.y);
 }
 
-__device__ __forceinline__ void probe_sub(const TileAddr<kAdamW>& A, int k, int lane,
+template <int kOpt>
+__device__ __forceinline__ void probe_sub(const TileAddr<kOpt>& A, int k, int lane,
                                           const Raw& R) {
     GLOBAL uint8_t* rec = A.rc(k);
     st4nt(A.th(k), make_uint4(R.th.x ^ R.gr.x, R.th.y ^ R.gr.y, R.th.z ^ R.gr.z,
                               R.th.w ^ R.gr.w));
-    st2nt(rec, xor2(R.rho, R.qm));
-    st2nt(rec + Layout<kAdamW>::kField, xor2(R.qm, R.qv));
-    st2nt(rec + 2 * Layout<kAdamW>::kField, xor2(R.qv, R.rho));
-    if ((lane & 3) == 0)
-        *(GLOBAL uint32_t*)A.sc(k) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
+    const uint2 rho = xor2(R.rho, R.qm);
+    if (kOpt == kAdamW) {
+        st2nt(rec, rho);
+        st2nt(rec + Layout<kOpt>::kField, xor2(R.qm, R.qv));
+        st2nt(rec + 2 * Layout<kOpt>::kField, xor2(R.qv, R.rho));
+        if ((lane & 3) == 0)
+            *(GLOBAL uint32_t*)A.sc(k) = (R.ms | (R.vs << 16)) ^ 0x00010001u;
+    } else {
+        st4nt(rec, make_uint4(rho.x, rho.y, ~R.qm.x, ~R.qm.y));
+        if ((lane & 3) == 0) *(GLOBAL uint16_t*)A.sc(k) = (uint16_t)(R.ms ^ 1u);
+    }
 }
 
+template <int kOpt>
 __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict__ table,
                                                     const int64_t* __restrict__ tile_begin,
                                                     int32_t count, int64_t total_tiles) {
@@ -44,14 +53,14 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
         const GTensor& T = cur.T;
         const int64_t e0 = (tile - cur.begin) * kTile;
         if (e0 + kTile <= T.numel) {
-            const TileAddr<kAdamW> A(T, e0);
+            const TileAddr<kOpt> A(T, e0);
             Raw R[2];
-            load_raw<kAdamW>(A, 0, R[0]);
-            if (kSubTiles > 1) load_raw<kAdamW>(A, 1, R[1]);
+            load_raw<kOpt>(A, 0, R[0]);
+            if (kSubTiles > 1) load_raw<kOpt>(A, 1, R[1]);
 #pragma unroll
             for (int k = 0; k < kSubTiles; ++k) {
-                probe_sub(A, k, lane, R[k & 1]);
-                if (k + 2 < kSubTiles) load_raw<kAdamW>(A, k + 2, R[k & 1]);
+                probe_sub<kOpt>(A, k, lane, R[k & 1]);
+                if (k + 2 < kSubTiles) load_raw<kOpt>(A, k + 2, R[k & 1]);
             }
         } else {
             for (int k = 0; k < kSubTiles; ++k) {
@@ -59,19 +68,28 @@ __global__ __launch_bounds__(256) void probe_kernel(const DevTensor* __restrict_
                 for (int j = 0; j < 8; ++j) {
                     const int64_t i = e + j;
                     if (i < T.numel) {
-                        GLOBAL uint8_t* r = code_at<kAdamW>(T, i, kRho);
-                        GLOBAL uint8_t* m = code_at<kAdamW>(T, i, kM);
-                        GLOBAL uint8_t* v = code_at<kAdamW>(T, i, kV);
-                        const uint8_t rho = *r, qm = *m, qv = *v;
+                        GLOBAL uint8_t* r = code_at<kOpt>(T, i, kRho);
+                        GLOBAL uint8_t* m = code_at<kOpt>(T, i, kM);
+                        const uint8_t rho = *r, qm = *m;
                         T.theta[i] = (uint16_t)(T.theta[i] ^ T.grad[i]);
                         *r = (uint8_t)(rho ^ qm);
-                        *m = (uint8_t)(qm ^ qv);
-                        *v = (uint8_t)(qv ^ rho);
+                        if (kOpt == kAdamW) {
+                            GLOBAL uint8_t* v = code_at<kOpt>(T, i, kV);
+                            const uint8_t qv = *v;
+                            *m = (uint8_t)(qm ^ qv);
+                            *v = (uint8_t)(qv ^ rho);
+                        } else {
+                            *m = (uint8_t)~qm;
+                        }
                     }
                 }
                 if ((lane & 3) == 0 && e < T.numel) {
-                    GLOBAL uint32_t* w = (GLOBAL uint32_t*)(T.scales + 2 * (e >> 5));
-                    *w = *w ^ 0x00010001u;
+                    if (kOpt == kAdamW) {
+                        GLOBAL uint32_t* w = (GLOBAL uint32_t*)(T.scales + 2 * (e >> 5));
+                        *w = *w ^ 0x00010001u;
+                    } else {
+                        T.scales[e >> 5] = (uint16_t)(T.scales[e >> 5] ^ 1u);
+                    }
                 }
             }
         }
@@ -388,12 +406,27 @@ extern "C" {
 
 int flashopt_stream_probe(const flashopt_list* L, void* stream) {
     if (!L) return FLASHOPT_ERR_NULL;
-    if (L->kind != FLASHOPT_KIND_ADAMW) return FLASHOPT_ERR_ARG;
+    if (is_fp32(L->kind)) return FLASHOPT_ERR_ARG;
     if (!L->all_have_grad) return FLASHOPT_ERR_NULL;
     if (L->total_tiles == 0) return FLASHOPT_OK;
-    hipLaunchKernelGGL(probe_kernel, dim3(grid_for(L->total_tiles)), dim3(kBlock), 0,
-                       (hipStream_t)stream, (const DevTensor*)L->d_table,
-                       (const int64_t*)L->d_tile_begin, L->count, L->total_tiles);
+    const dim3 grid(grid_for(L->total_tiles)), block(kBlock);
+    const hipStream_t s = (hipStream_t)stream;
+    const DevTensor* table = (const DevTensor*)L->d_table;
+    const int64_t* begin = (const int64_t*)L->d_tile_begin;
+    switch (opt_of(L->kind)) {
+    case kAdamW:
+        hipLaunchKernelGGL(probe_kernel<kAdamW>, grid, block, 0, s, table, begin, L->count,
+                           L->total_tiles);
+        break;
+    case kSgd:
+        hipLaunchKernelGGL(probe_kernel<kSgd>, grid, block, 0, s, table, begin, L->count,
+                           L->total_tiles);
+        break;
+    default:
+        hipLaunchKernelGGL(probe_kernel<kLion>, grid, block, 0, s, table, begin, L->count,
+                           L->total_tiles);
+        break;
+    }
     return launch_status();
 }
 

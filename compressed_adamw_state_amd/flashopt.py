@@ -314,10 +314,10 @@ class StateArena:
     whatever the order of the tiles, and each array alone streams at the same
     rate in every allocation.
 
-    candidates > 1 (AdamW, with theta' and at least one gradient set): a
-    placement search.  Up to `candidates` allocations of the buffer are made,
-    all alive at once (fewer if the device runs short of free memory); on
-    each, the AdamW step's own loads and stores over the list
+    candidates > 1 (a compressed kind, with theta' and at least one gradient
+    set): a placement search.  Up to `candidates` allocations of the buffer
+    are made, all alive at once (fewer if the device runs short of free
+    memory); on each, the step's own loads and stores over the list
     (flashopt_stream_probe, best of three launches after one untimed) are
     timed, the fastest allocation is kept and the others are freed and
     handed back to the device (torch.cuda.empty_cache).  The probe's time on
@@ -350,9 +350,9 @@ class StateArena:
         nbytes = max(end, 1)
         self.placement_ms, self.placement_choice = None, None
         if candidates > 1:
-            if optimizer != "adamw" or not theta or grad_sets < 1:
-                raise ValueError("the placement search needs an AdamW arena with theta' and "
-                                 "a gradient set")
+            if optimizer in FP32_FIELDS or not theta or grad_sets < 1:
+                raise ValueError("the placement search needs a compressed arena with theta' "
+                                 "and a gradient set")
             self._search(nbytes, device, candidates)
         else:
             self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -479,9 +479,9 @@ def flashopt_state_zero(lst: FlashoptList, stream=None) -> None:
 
 
 def flashopt_stream_probe(lst: FlashoptList, stream=None) -> None:
-    """Bandwidth probe (include/flashopt_probe.h): the AdamW step's exact
-    loads and stores with one XOR per word instead of the update.  Overwrites
-    the state."""
+    """Bandwidth probe (include/flashopt_probe.h): the list's step's exact
+    loads and stores (AdamW, SGD or Lion) with one XOR per word instead of
+    the update.  Overwrites the state."""
     _check("flashopt_stream_probe", lib().flashopt_stream_probe(lst.handle, _stream(stream)))
 
 

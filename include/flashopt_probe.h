@@ -1,5 +1,5 @@
 /*
- * flashopt_probe.h -- measurement aid for the fused AdamW step of flashopt.h.
+ * flashopt_probe.h -- measurement aids for the fused steps of flashopt.h.
  *
  * The fused-step section of "FlashOptim: Optimizers for Memory Efficient
  * Training" (digest page, "Core method > Fused optimizer step", Alg. 4) fuses
@@ -17,16 +17,20 @@
 extern "C" {
 #endif
 
-/* Moves exactly the bytes flashopt_adamw_step moves for `list` -- the same
- * tiles, launch shape, loads and stores (12.25 bytes per element plus the
- * partial-group scales) -- with the arithmetic replaced by one XOR per word:
- *   theta' ^= grad (16-bit words), rho ^= m_code, m_code ^= v_code,
- *   v_code ^= rho (bytes; right-hand sides are the values read), and
- *   m_scale ^= 1, v_scale ^= 1 (every group).
- * DESTRUCTIVE: the state then holds meaningless bits.  Requirements and
- * errors as flashopt_adamw_step (v_code / v_scale and a gradient on every
- * tensor: FLASHOPT_ERR_ARG / FLASHOPT_ERR_NULL otherwise); one launch on
- * `stream`, nothing allocated, no synchronisation. */
+/* Moves exactly the bytes the list's step (flashopt_adamw_step,
+ * flashopt_sgd_step or flashopt_lion_step, by the list's kind) moves for
+ * `list` -- the same tiles, launch shape, loads and stores (12.25 bytes per
+ * element for AdamW, 10.125 for SGD and Lion, plus the partial-group scales)
+ * -- with the arithmetic replaced by one XOR per word:
+ *   theta' ^= grad (16-bit words);
+ *   AdamW: rho ^= m_code, m_code ^= v_code, v_code ^= rho (bytes; right-hand
+ *          sides are the values read), m_scale ^= 1, v_scale ^= 1;
+ *   SGD, Lion: rho ^= m_code, m_code = ~m_code, m_scale ^= 1 (every group).
+ * DESTRUCTIVE: the state then holds meaningless bits (any bits may be probed,
+ * the contents do not change the traffic).  Requirements and errors as the
+ * step (a gradient on every tensor: FLASHOPT_ERR_NULL otherwise); the _FP32
+ * kinds: FLASHOPT_ERR_ARG.  One launch on `stream`, nothing allocated, no
+ * synchronisation. */
 int flashopt_stream_probe(const flashopt_list* list, void* stream);
 
 /* The practical ceiling of the AdamW step's traffic: the same bytes per

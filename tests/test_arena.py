@@ -74,11 +74,10 @@ def test_empty_list():
     assert arena.buffer.numel() >= 1
 
 
-@pytest.mark.parametrize("opt,theta,grad_sets", [("sgd", True, 1), ("lion", True, 1),
-                                                 ("adamw", False, 1), ("adamw", True, 0),
-                                                 ("adamw_fp32", True, 1)])
-def test_placement_search_needs_an_adamw_arena_with_theta_and_grads(opt, theta, grad_sets):
-    # refused on the host, before any allocation: the search times the AdamW
-    # step's own probe, which reads theta' and a gradient
+@pytest.mark.parametrize("opt,theta,grad_sets", [("adamw_fp32", True, 1), ("lion_fp32", True, 1),
+                                                 ("adamw", False, 1), ("sgd", True, 0)])
+def test_placement_search_needs_a_compressed_arena_with_theta_and_grads(opt, theta, grad_sets):
+    # refused on the host, before any allocation: the search times the step's
+    # own probe (compressed kinds only), which reads theta' and a gradient
     with pytest.raises(ValueError, match="placement search"):
         F.StateArena(SIZES, opt, "cpu", theta=theta, grad_sets=grad_sets, candidates=2)

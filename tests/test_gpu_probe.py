@@ -1,7 +1,7 @@
 """The bandwidth probe (include/flashopt_probe.h) reads and writes every byte
-of the AdamW step's state and gradients: its documented XOR of the values it
-read, checked on every element of a ragged list (full tiles and partial
-tails), through the code planes."""
+of the AdamW, SGD and Lion steps' state and gradients: its documented XOR of
+the values it read, checked on every element of a ragged list (full tiles and
+partial tails), through the code planes and records."""
 import numpy as np
 import pytest
 import torch
@@ -13,12 +13,13 @@ from parity import state_fields
 pytestmark = pytest.mark.gpu
 
 
-def test_stream_probe_touches_every_byte():
+@pytest.mark.parametrize("kind", ["adamw", "sgd", "lion"])
+def test_stream_probe_touches_every_byte(kind):
     gen = torch.Generator().manual_seed(7)
     sizes = [2048 * 5, 2048 + 7, 33, 8192 + 2047]
     states, grads, before = [], [], []
     for n in sizes:
-        st = F.TensorState(n, "adamw", "cuda")
+        st = F.TensorState(n, kind, "cuda")
         st.theta.view(torch.int16).copy_(torch.randint(-2 ** 15, 2 ** 15, (n,), generator=gen,
                                                        dtype=torch.int16))
         st.codes.copy_(torch.randint(0, 256, st.codes.shape, generator=gen, dtype=torch.uint8))
@@ -36,10 +37,20 @@ def test_stream_probe_touches_every_byte():
         g = gr.view(torch.int16).cpu().numpy().view(np.uint16)
         np.testing.assert_array_equal(f["theta"], b["theta"] ^ g)
         np.testing.assert_array_equal(f["rho"], b["rho"] ^ b["m_code"])
-        np.testing.assert_array_equal(f["m_code"], b["m_code"] ^ b["v_code"].view(np.int8))
-        np.testing.assert_array_equal(f["v_code"], b["v_code"] ^ b["rho"].view(np.uint8))
         np.testing.assert_array_equal(f["m_scale"], b["m_scale"] ^ 1)
-        np.testing.assert_array_equal(f["v_scale"], b["v_scale"] ^ 1)
+        if kind == "adamw":
+            np.testing.assert_array_equal(f["m_code"], b["m_code"] ^ b["v_code"].view(np.int8))
+            np.testing.assert_array_equal(f["v_code"], b["v_code"] ^ b["rho"].view(np.uint8))
+            np.testing.assert_array_equal(f["v_scale"], b["v_scale"] ^ 1)
+        else:
+            np.testing.assert_array_equal(f["m_code"], ~b["m_code"])
+
+
+def test_stream_probe_refuses_the_fp32_kinds():
+    st = F.TensorState(2048, "adamw_fp32", "cuda")
+    lst = F.FlashoptList([st], [torch.zeros(2048, dtype=torch.bfloat16, device="cuda")])
+    with pytest.raises(F.FlashoptError):
+        F.flashopt_stream_probe(lst)
 
 
 def test_mix_ceiling_touches_every_byte():
