@@ -362,6 +362,12 @@ class StateArena:
 
     def _search(self, nbytes: int, device, candidates: int) -> None:
         dev = torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError("the placement search needs a GPU arena")
+        with torch.cuda.device(dev):
+            self._search_on(nbytes, dev, candidates)
+
+    def _search_on(self, nbytes: int, dev: torch.device, candidates: int) -> None:
         stream = torch.cuda.current_stream(dev)
         n = len(self.numels)
         bufs, times = [], []

@@ -81,3 +81,8 @@ def test_placement_search_needs_a_compressed_arena_with_theta_and_grads(opt, the
     # own probe (compressed kinds only), which reads theta' and a gradient
     with pytest.raises(ValueError, match="placement search"):
         F.StateArena(SIZES, opt, "cpu", theta=theta, grad_sets=grad_sets, candidates=2)
+
+
+def test_placement_search_needs_a_gpu_arena():
+    with pytest.raises(ValueError, match="GPU arena"):
+        F.StateArena(SIZES, "adamw", "cpu", theta=True, grad_sets=1, candidates=2)
