@@ -1,6 +1,7 @@
 """Parity at full size, every element: the fused step over the GPT-2-small
-(124 M parameters), Llama-3.1-8B (8.03 B) and Llama-2-13B (13.0 B, gradient
-release) workloads, in the launch configuration the benchmark times, against
+(124 M parameters), Llama-3.1-8B (8.03 B; AdamW and Lion) and Llama-2-13B
+(13.0 B, gradient release) workloads, in the launch configuration the
+benchmark times, against
 the oracle ("FlashOptim: Optimizers for Memory Efficient Training", digest
 page, "Core method > Fused optimizer step", Alg. 4).
 
@@ -70,6 +71,21 @@ class TestLlama31_8B:
     @pytest.mark.parametrize("t", [1, 20])
     def test_every_element(self, run, t):
         _check(run, t, "llama8b", 5)
+
+
+class TestLlama31_8B_Lion:
+    """Llama-3.1-8B, Lion (the 16-byte code records), in the benchmark's
+    launch: every element at the first and the last step."""
+
+    @pytest.fixture(scope="class")
+    def run(self):
+        r = _run("llama31_8b_lion", 4)
+        yield r
+        _free(r)
+
+    @pytest.mark.parametrize("t", [1, W.WORKLOADS["llama31_8b_lion"].steps])
+    def test_every_element(self, run, t):
+        _check(run, t, "llama8b lion", 5)
 
 
 class TestLlama2_13B_Release:
