@@ -144,6 +144,15 @@ __device__ __forceinline__ int32_t find_tensor(const int64_t* __restrict__ tile_
 // Walks a wave's increasing tile indices through the tensor list: one binary
 // search for the first tile, then a forward scan (scalar loads of the small
 // tile_begin table; a wave's next tile is at most a few tensors further).
+// Pins a descriptor read from the (wave-uniform) table in scalar registers
+// and keeps the compiler from merging that read with the read of a by-value
+// kernel argument into one load through a generic pointer (a flat load into
+// vector registers, which then carried every tile address as 64-bit vector
+// arithmetic).
+__device__ __forceinline__ void scalar_fence(GTensor& T) {
+    asm volatile("" : "+s"(T.theta), "+s"(T.codes), "+s"(T.scales), "+s"(T.grad), "+s"(T.numel));
+}
+
 struct TileCursor {
     int32_t i;
     int64_t begin, end;
@@ -157,6 +166,7 @@ struct TileCursor {
             begin = tile_begin[i];
             end = tile_begin[i + 1];
             T = view(table[i]);
+            scalar_fence(T);
         } else {
             i = 0;
             begin = 0;
