@@ -30,8 +30,11 @@ def kernels(tmp_path_factory):
     for m in re.finditer(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S):
         body = m.group(2)
         field = lambda k: int(re.search(rf"\.{k} (\d+)", body).group(1))
-        found[m.group(1)] = {"scratch": field("amdhsa_private_segment_fixed_size"),
-                             "vgpr": field("amdhsa_next_free_vgpr")}
+        name = m.group(1)
+        code = re.search(rf"^{re.escape(name)}:.*?s_endpgm", text, re.S | re.M)
+        found[name] = {"scratch": field("amdhsa_private_segment_fixed_size"),
+                       "vgpr": field("amdhsa_next_free_vgpr"),
+                       "flat": len(re.findall(r"^\s+flat_", code.group(0), re.M)) if code else -1}
     return found
 
 
@@ -52,3 +55,11 @@ def test_whole_tile_kernels_fit_five_waves_per_simd(kernels):
     for k, v in kernels.items():
         if "step_kernel" in k:
             assert v["vgpr"] <= 96, (k, v)
+
+
+def test_no_step_kernel_uses_flat_memory_instructions(kernels):
+    # every descriptor field and address is global (or scalar): a flat access
+    # means the cursor's descriptor was read through a generic pointer again,
+    # which puts it and every tile address in vector registers
+    flat = {k: v["flat"] for k, v in kernels.items() if "step_kernel" in k and v["flat"] != 0}
+    assert not flat, flat
